@@ -1,0 +1,376 @@
+"""CPU oracle of the DFlash block-diffusion draft round. TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package entry's smoke check and the benchmark's CPU
+baseline leg may import this module. The product path (the HIP library and
+its Python binding) never imports, calls or links anything here, and this
+module imports nothing from the product path.
+
+What it computes (sources are the four pages on DFlash):
+  * fuse:   fc over the concatenated tap planes, then the hidden_norm RMSNorm,
+            one fused context row per token (TensorFold pull request #1851,
+            "What this changes", items 3 and 4; DFlash explainer, section 3,
+            "Target knows best").
+  * inject: the fused rows projected to k and v only, written into every draft
+            layer's cache (TensorFold #1851, item 4; explainer section 3,
+            "KV injection into every layer").
+  * draft:  one non-causal forward of a qwen3 body over an anchor plus B-1 mask
+            rows: eleven tensors a layer, two residual adds a layer, final norm;
+            sliding layers see only their own window of the context, the full
+            layer sees all of it (TensorFold #1851, items 1 and 4; explainer
+            section 3, "Block diffusion parallel drafting"); then the shared
+            LM head and an independent top-1 at every mask row (explainer
+            section 5, "Candidate path selector", which states that the
+            original DFlash picks top-1 at each position independently).
+  * verify: greedy acceptance of the longest prefix equal to the target's
+            argmax, plus the target's token at the first mismatch (explainer
+            section 4, "Greedy decoding"; "Port the DFlash2 protocol, not its
+            checkpoint", "What is portable" and "Golden replay before
+            training").
+
+Numerics: every product and reduction is float64. Values are rounded to the
+activation dtype (bf16 by round-to-nearest-even straight from float64, or
+fp32) only at the points the round stores a tensor:
+  R1 fused row, R2 context K/V, R3 normed layer input, R4 q/k/v of the block,
+  R5 attention output, R6 residual after attention, R7 SwiGLU product,
+  R8 residual after the MLP, R9 final-normed mask rows.
+Logits stay float64. This follows the TensorFold page's "Exactness" list
+(bf16 activations with fp32 sums) and the Strata page's "Validation" list
+(a native drafter checked against an f64 host reference).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  taps concatenated in ascending tap-id order; fc then hidden_norm; RMSNorm is
+  x / sqrt(mean(x^2) + eps) * g; no biases; the eleven layer tensors are
+  in_norm, wq, wk, wv, wo, q_norm, k_norm, post_norm, w_gate, w_up, w_down;
+  context K/V use the layer's own wk/wv (+ k_norm, RoPE) on the fused row with
+  no input norm; context rows sit at positions 0..C-1, the anchor at C and mask
+  row j at C+j; rotate-half RoPE over the whole head; a sliding layer with
+  window W sees context rows [max(0, C-W), C) plus all B block rows; q head h
+  reads kv head h // (n_q / n_kv); scale 1/sqrt(head_dim); mask row j predicts
+  the token at position C+j; argmax ties go to the lowest index.
+"""
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Storage formats
+
+
+def bf16_bits_to_f64(u):
+    """Decode bf16 bit patterns (uint16) to float64 values, exactly."""
+    u = np.asarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def as_f64(a):
+    """Tensor storage (uint16 bf16 bits, float32, or float64) -> float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x):
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits: a finite value with frexp exponent e lies on
+    the grid k * 2**(e-8); the grid never gets finer than the subnormal step
+    2**-133. Rounding happens once, straight from float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133)
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    y = np.where(np.abs(y) > _BF16_MAX, np.copysign(np.inf, x), y)
+    return np.where(np.isfinite(x), y, x)
+
+
+def round_f32(x):
+    """Round float64 values to the nearest fp32 value (IEEE cast, ties to even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_to(x, dtype):
+    """Round to the activation dtype: "bf16", "f32", or "f64" (no rounding; pins only)."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return round_f32(x)
+    assert dtype == "f64", dtype
+    return np.asarray(x, dtype=np.float64)
+
+
+def bf16_bits(x):
+    """bf16 bit patterns of float64 values that are already bf16-representable."""
+    return (np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Building blocks
+
+
+def rms_norm(x, g, eps):
+    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding over the last axis (length d).
+
+    Pair (i, i + d/2) turns by the angle pos * theta**(-2i/d).
+    `pos` has the shape of x without its last axis, or broadcasts to it.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def softmax(s):
+    s = s - np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def linear(x, w):
+    """x [.., K] times w [N, K] transposed -> [.., N] (w in storage format)."""
+    return np.asarray(x, dtype=np.float64) @ as_f64(w).T
+
+
+# --------------------------------------------------------------------------
+# Step 1: tap fusion (fc, then hidden_norm)
+
+
+def fuse_taps(cfg, taps, W):
+    """Fused context rows [R, hidden], rounded (R1).
+
+    taps: list of n_taps planes [R, hidden] in ascending tap-id order.
+    """
+    x = np.concatenate([as_f64(t) for t in taps], axis=-1)        # [R, n*h]
+    y = linear(x, W["fc"])                                        # [R, h]
+    return round_to(rms_norm(y, as_f64(W["hidden_norm"]), cfg.rms_eps), cfg.dtype)
+
+
+# --------------------------------------------------------------------------
+# Step 2: context K/V injection (k and v only)
+
+
+def inject_kv(cfg, fused, pos, W):
+    """Per layer (K, V), each [R, n_kv, head_dim], rounded (R2).
+
+    K = RoPE_pos(k_norm(wk . f)) per kv head; V = wv . f. The fused row enters
+    without the layer's input norm.
+    """
+    f = as_f64(fused)
+    R = f.shape[0]
+    nkv, d = cfg.n_kv_heads, cfg.head_dim
+    pos = np.asarray(pos, dtype=np.float64)
+    out = []
+    for l in range(cfg.n_layers):
+        pre = f"layers.{l}."
+        k = linear(f, W[pre + "wk"]).reshape(R, nkv, d)
+        k = rms_norm(k, as_f64(W[pre + "k_norm"]), cfg.rms_eps)
+        k = rope(k, pos[:, None], cfg.rope_theta)
+        v = linear(f, W[pre + "wv"]).reshape(R, nkv, d)
+        out.append((round_to(k, cfg.dtype), round_to(v, cfg.dtype)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 3: the non-causal block forward
+
+
+def block_attention(q, keys, values, n_kv):
+    """Non-causal attention of every block query over the same key set.
+
+    q [B, n_q, d]; keys/values [N, n_kv, d]. q head h reads kv head h // g.
+    """
+    B, nq, d = q.shape
+    g = nq // n_kv
+    o = np.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    for h in range(nq):
+        kvh = h // g
+        s = (q[:, h, :] @ keys[:, kvh, :].T) * scale                 # [B, N]
+        o[:, h, :] = softmax(s) @ values[:, kvh, :]
+    return o
+
+
+def context_reach(C, window):
+    """Context positions [lo, C) a layer attends: all for window 0, else the last W."""
+    return (0 if window == 0 else max(0, C - window)), C
+
+
+def draft_layer(cfg, l, X, W, k_ctx, v_ctx, C, trace=None):
+    """One qwen3 layer over the block rows X [B, h] (two residual adds)."""
+    pre = f"layers.{l}."
+    dt, eps = cfg.dtype, cfg.rms_eps
+    B = X.shape[0]
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    pos = C + np.arange(B)
+
+    a = round_to(rms_norm(X, as_f64(W[pre + "in_norm"]), eps), dt)                    # R3
+    q = rms_norm(linear(a, W[pre + "wq"]).reshape(B, nq, d), as_f64(W[pre + "q_norm"]), eps)
+    k = rms_norm(linear(a, W[pre + "wk"]).reshape(B, nkv, d), as_f64(W[pre + "k_norm"]), eps)
+    v = linear(a, W[pre + "wv"]).reshape(B, nkv, d)
+    q = round_to(rope(q, pos[:, None], cfg.rope_theta), dt)                           # R4
+    k = round_to(rope(k, pos[:, None], cfg.rope_theta), dt)
+    v = round_to(v, dt)
+
+    lo, hi = context_reach(C, cfg.layer_window[l])
+    keys = np.concatenate([as_f64(k_ctx[lo:hi]), k], axis=0)
+    vals = np.concatenate([as_f64(v_ctx[lo:hi]), v], axis=0)
+    o = round_to(block_attention(q, keys, vals, nkv).reshape(B, nq * d), dt)          # R5
+
+    X1 = round_to(X + linear(o, W[pre + "wo"]), dt)                                   # R6: add #1
+    b = round_to(rms_norm(X1, as_f64(W[pre + "post_norm"]), eps), dt)                 # R3
+    m = round_to(silu(linear(b, W[pre + "w_gate"])) * linear(b, W[pre + "w_up"]), dt)  # R7
+    X2 = round_to(X1 + linear(m, W[pre + "w_down"]), dt)                              # R8: add #2
+    if trace is not None:
+        trace.setdefault("layers", []).append(
+            dict(a=a, q=q, k=k, v=v, o=o, x_attn=X1, b=b, m=m, x_out=X2, reach=(lo, hi)))
+    return X2
+
+
+def lm_head_logits(z, lm_head, chunk=16384):
+    """Logits z . lm_head^T in float64, computed over vocab chunks."""
+    V = lm_head.shape[0]
+    out = np.empty((z.shape[0], V), dtype=np.float64)
+    for c0 in range(0, V, chunk):
+        c1 = min(V, c0 + chunk)
+        out[:, c0:c1] = z @ as_f64(lm_head[c0:c1]).T
+    return out
+
+
+def argmax_lowest(logits):
+    """Index of the maximum of each row; on a tie the lowest index wins."""
+    logits = np.asarray(logits)
+    assert np.all(np.isfinite(logits)), "oracle expects finite logits"
+    return np.argmax(logits, axis=-1).astype(np.int64)   # numpy returns the first maximum
+
+
+def draft_stream(cfg, W, k_ctx, v_ctx, C, anchor, trace=None):
+    """Draft one block for one stream.
+
+    k_ctx/v_ctx: per layer, context rows [>= C, n_kv, d] (positions 0..C-1).
+    Returns (logits [B-1, V] float64, tokens [B-1]).
+    """
+    B = cfg.block_size
+    toks = np.full(B, cfg.mask_token_id, dtype=np.int64)
+    toks[0] = int(anchor)
+    X = as_f64(W["embed"][toks])                                                       # [B, h]
+    if trace is not None:
+        trace["x0"] = X
+    for l in range(cfg.n_layers):
+        X = draft_layer(cfg, l, X, W, k_ctx[l], v_ctx[l], C, trace)
+    z = round_to(rms_norm(X[1:], as_f64(W["norm"]), cfg.rms_eps), cfg.dtype)         # R9
+    logits = lm_head_logits(z, W["lm_head"])
+    if trace is not None:
+        trace["z"] = z
+    return logits, argmax_lowest(logits)
+
+
+def top2(logits):
+    """Largest and second-largest value of each row (float64)."""
+    srt = np.sort(logits, axis=-1)
+    return srt[..., -1], srt[..., -2]
+
+
+# --------------------------------------------------------------------------
+# Step 4: greedy verify
+
+
+def verify_greedy(draft, target):
+    """Greedy acceptance per stream.
+
+    draft [S, B-1] holds d_1..d_{B-1}; target [S, B] holds t_0..t_{B-1}, the
+    target's argmax after the anchor and after each drafted token. The
+    accepted length a is the number of leading j with d_j = t_{j-1}; the bonus
+    token is t_a; committed = d_1..d_a, t_a, padded with -1 to length B.
+    """
+    draft = np.asarray(draft, dtype=np.int64)
+    target = np.asarray(target, dtype=np.int64)
+    S, Bm1 = draft.shape
+    accept = np.zeros(S, dtype=np.int64)
+    bonus = np.zeros(S, dtype=np.int64)
+    committed = np.full((S, Bm1 + 1), -1, dtype=np.int64)
+    for s in range(S):
+        a = 0
+        while a < Bm1 and draft[s, a] == target[s, a]:
+            a += 1
+        accept[s] = a
+        bonus[s] = target[s, a]
+        committed[s, :a] = draft[s, :a]
+        committed[s, a] = target[s, a]
+    return accept, bonus, committed
+
+
+# --------------------------------------------------------------------------
+# Storage closed forms (the prompt-memory planner and the fused ring)
+
+
+def fused_row_bytes(hidden, elem_bytes=2):
+    """One fused context row: a single hidden-wide plane."""
+    return hidden * elem_bytes
+
+
+def raw_tap_row_bytes(n_taps, hidden, elem_bytes=2):
+    """One token's raw tap planes."""
+    return n_taps * hidden * elem_bytes
+
+
+def tap_row_bytes(n_taps, hidden, fusing, elem_bytes=2):
+    """Planner price of a prompt row's taps.
+
+    A fusing (v1) drafter holds its tap planes, their row-major copy, fc's
+    output row and the fused row: (2n + 2) rows of hidden. A non-fusing
+    drafter holds only its raw planes.
+    """
+    if fusing:
+        return (2 * n_taps + 2) * hidden * elem_bytes
+    return n_taps * hidden * elem_bytes
+
+
+# --------------------------------------------------------------------------
+# A whole round for several streams (reference driver for the tests)
+
+
+def run_round(cfg, W, streams, target_rows=None):
+    """One round over several independent streams.
+
+    streams: list of dicts with keys taps (list of [R, h] planes), C (context
+    length the block sees after this round's injection), k_ctx/v_ctx (per
+    layer, rows for positions 0..C-R-1 already in the cache), anchor.
+    The R new rows are fused and injected at positions C-R..C-1.
+    Returns per-stream dicts with fused, kv (new rows), logits, tokens, and
+    (when target_rows is given) accept, bonus, committed.
+    """
+    out = []
+    for s, st in enumerate(streams):
+        fused = fuse_taps(cfg, st["taps"], W)
+        R = fused.shape[0]
+        C = st["C"]
+        pos = np.arange(C - R, C)
+        kv = inject_kv(cfg, fused, pos, W)
+        k_full = [np.concatenate([as_f64(st["k_ctx"][l][:C - R]), kv[l][0]], 0) for l in range(cfg.n_layers)]
+        v_full = [np.concatenate([as_f64(st["v_ctx"][l][:C - R]), kv[l][1]], 0) for l in range(cfg.n_layers)]
+        logits, toks = draft_stream(cfg, W, k_full, v_full, C, st["anchor"])
+        out.append(dict(fused=fused, kv=kv, logits=logits, tokens=toks))
+    if target_rows is not None:
+        draft = np.stack([o["tokens"] for o in out])
+        acc, bon, com = verify_greedy(draft, target_rows)
+        for s, o in enumerate(out):
+            o.update(accept=int(acc[s]), bonus=int(bon[s]), committed=com[s])
+    return out
