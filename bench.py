@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash draft round on one MI355X.
+
+A step is one whole round on one batch of synthetic input already resident in HBM:
+fuse the round's new rows (fc + hidden_norm), inject their K/V into every layer's
+paged cache, draft one block per stream (non-causal forward + LM-head argmax), and
+greedy-verify against a synthetic target row. Every step repeats the same round
+(the context length is not advanced), so all steps do identical work.
+
+    python bench.py [--steps K] [--warmup W] [--workload 9b_ctx4k] [--no-cpu-baseline]
+
+Prints one JSON line. `value` is drafted tokens per second (streams x (block - 1)
+per round); the line also carries the achieved algorithmic HBM bandwidth of the
+round, the roofline of the dominant kernel (per-kernel times from HIP events the
+library records around its own launches, in a second timed pass), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "drafted tokens/sec per draft round + achieved HBM GB/s (9B shape, block 16, 1 GPU)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_TFLOPS = 2500.0      # dense bf16
+FP32_TFLOPS = 157.3
+
+
+def kernel_costs(p, ctx, rows):
+    """Algorithmic bytes and FLOPs per launch of each kernel of one round.
+
+    Bytes: each weight once per call that reads it, inputs read once, outputs written
+    once, context K/V read once per layer within the layer's reach.
+    """
+    es = 4 if p.dtype == "f32" else 2
+    h, L, d, I, V, B = p.hidden, p.n_layers, p.head_dim, p.intermediate, p.vocab, p.block_size
+    nq, nkv, n = p.n_q_heads * d, p.n_kv_heads * d, p.n_taps
+    S = len(ctx)
+    R = sum(rows)
+    M, Mm = S * B, S * (B - 1)
+    k = {}
+    k["fuse_fc_gemm"] = dict(bytes=(h * n * h + R * n * h) * es + R * h * 4, flops=2 * R * n * h * h)
+    k["fuse_rownorm"] = dict(bytes=R * h * 4 + R * h * es + h * es, flops=3 * R * h)
+    k["inject_kv_gemm"] = dict(bytes=(L * 2 * nkv * h + R * h + L * 2 * R * nkv) * es, flops=2 * R * h * L * 2 * nkv)
+    k["embed"] = dict(bytes=2 * M * h * es, flops=2 * M * h)
+    k["qkv_gemm"] = dict(bytes=((nq + 2 * nkv) * h + M * h + M * (nq + 2 * nkv)) * es, flops=2 * M * h * (nq + 2 * nkv))
+    for kind, sel in (("attention_full", lambda w: w == 0), ("attention_sliding", lambda w: w > 0)):
+        layers = [w for w in p.layer_window[:L] if sel(w)]
+        if not layers:
+            continue
+        wdw = layers[0]
+        keys = [min(c, wdw) if wdw > 0 else c for c in ctx]
+        k[kind] = dict(bytes=(sum(keys) * 2 * nkv + M * (nq + 2 * nkv) + M * nq) * es,
+                       flops=sum(4 * p.n_q_heads * B * d * (kk + B) for kk in keys),
+                       launches=len(layers))
+    k["o_proj_gemm"] = dict(bytes=(h * nq + M * nq + 2 * M * h) * es, flops=2 * M * nq * h)
+    k["gate_up_gemm"] = dict(bytes=(2 * I * h + M * h + M * I) * es, flops=4 * M * h * I)
+    k["down_gemm"] = dict(bytes=(h * I + M * I + 2 * M * h) * es, flops=2 * M * I * h)
+    k["lm_head_argmax_gemm"] = dict(bytes=(V * h + Mm * h) * es + Mm * 4, flops=2 * Mm * h * V)
+    k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
+    per_layer = ["qkv_gemm", "o_proj_gemm", "gate_up_gemm", "down_gemm"]
+    for name in per_layer:
+        k[name]["launches"] = L
+    for name, v in k.items():
+        v.setdefault("launches", 1)
+    return k
+
+
+def round_totals(costs):
+    b = sum(v["bytes"] * v["launches"] for v in costs.values())
+    f = sum(v["flops"] * v["launches"] for v in costs.values())
+    return b, f
+
+
+def cpu_baseline(case, sample_streams):
+    """The oracle, as it stands, on one round of the chosen streams."""
+    from oracle import dflash_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    W = case.weights_np()
+    streams = case.oracle_streams(sample_streams)
+    t0 = time.perf_counter()
+    out = O.run_round(case.p, W, streams)
+    dt = time.perf_counter() - t0
+    drafted = len(sample_streams) * (case.p.block_size - 1)
+    return dict(value=drafted / dt, unit="drafted tokens/s", cores=int(threads), kind="oracle",
+                sample=f"one whole round (fuse {sum(case.rows[s] for s in sample_streams)} rows, inject, "
+                       f"draft, verify inputs) of streams {sample_streams} of the same workload, float64 numpy; "
+                       f"{dt:.2f} s", seconds=dt), out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="9b_ctx4k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the round shards by "
+              f"streams with no exchange, so N GPUs run N independent copies).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    from workloads.round_case import RoundCase
+
+    torch.cuda.init()
+    p = wl.preset(args.workload)
+    print(f"[bench] workload {p.name}: setting up", file=sys.stderr, flush=True)
+    case = RoundCase(p)
+    S, B = p.n_streams, p.block_size
+
+    # target row from an untimed round of the same inputs
+    case.run_gpu()
+    case.set_target_from(case.draft.cpu().numpy())
+    torch.cuda.synchronize()
+
+    def step():
+        case.fuse()
+        case.inject()
+        case.draft_block(logits=False, top2=False)
+        case.verify()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel pass: the library brackets each of its launches with events on this stream
+    case.dr.set_profiling(True)
+    case.dr.profile_read()
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = case.dr.profile_read()
+    case.dr.set_profiling(False)
+    print(f"[bench] timed {ms:.4f} ms/step; per-kernel pass done", file=sys.stderr, flush=True)
+
+    costs = kernel_costs(p, case.ctx, case.rows)
+    tot_bytes, tot_flops = round_totals(costs)
+    drafted = S * (B - 1)
+    value = drafted / (ms * 1e-3)
+    kernels = {}
+    for name, (cnt, total) in prof.items():
+        per = total / cnt
+        c = costs.get(name, {"bytes": 0, "flops": 0})
+        kernels[name] = dict(launches_per_step=cnt / args.profile_steps, avg_ms=per,
+                             ms_per_step=total / args.profile_steps,
+                             gbps=c["bytes"] / (per * 1e-3) / 1e9 if per > 0 else None,
+                             tflops=c["flops"] / (per * 1e-3) / 1e12 if per > 0 else None)
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    kd = kernels[dom]
+    mfma_dtype_peak = FP32_TFLOPS if p.dtype == "f32" else MFMA_BF16_TFLOPS
+    ai = costs[dom]["flops"] / max(1, costs[dom]["bytes"])
+    if ai * HBM_PEAK_GBS * 1e9 < mfma_dtype_peak * 1e12:
+        roof = dict(bound="hbm", achieved=round(kd["gbps"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(kd["gbps"] / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(kd["tflops"], 2), peak=mfma_dtype_peak, unit="TFLOP/s",
+                    frac=round(kd["tflops"] / mfma_dtype_peak, 4))
+    roof.update(kernel=dom, bytes_per_launch=costs[dom]["bytes"], flops_per_launch=costs[dom]["flops"],
+                avg_launch_ms=round(kd["avg_ms"], 5), traffic=None)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "drafted tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": p.note or p.name, "preset": p.name, "streams": S, "block": B,
+                   "context": case.ctx if S > 1 else case.ctx[0], "rows_fused": case.R,
+                   "hidden": p.hidden, "layers": p.n_layers, "vocab": p.vocab},
+        "hbm_gbps": round(tot_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_of_peak": round(tot_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac_of_peak": round(tot_flops / (ms * 1e-3) / 1e12 / mfma_dtype_peak, 5),
+        "round_bytes": tot_bytes, "round_flops": tot_flops, "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline (one round)", file=sys.stderr, flush=True)
+        sample = [0] if S == 1 else [int(min(range(S), key=lambda s: case.ctx[s]))]
+        cb, _ = cpu_baseline(case, sample)
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,761 @@
+// Host side of the DFlash draft-round library: config validation, weight binding,
+// workspace planning and the launch sequence of each C-ABI call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace dfl;
+
+namespace {
+
+thread_local std::string g_create_error = "";
+
+constexpr int64_t kSplitCounters = 1 << 16;   // per-tile split-K counters (shared by all kernels)
+constexpr int64_t kRowCounters = 1 << 12;     // per-row-group counters
+constexpr int64_t kCounterInts = kSplitCounters + kRowCounters;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+
+struct dflash {
+  dflash_config cfg;
+  dflash_weights w;
+  bool bound = false;
+  std::string err;
+  std::vector<std::pair<const void*, size_t>> ws_ready;
+  bool profiling = false;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> event_pool;
+
+  ~dflash() {
+    for (auto& r : prof) {
+      hipEventDestroy(r.a);
+      hipEventDestroy(r.b);
+    }
+    for (auto e : event_pool) hipEventDestroy(e);
+  }
+  hipEvent_t take_event() {
+    if (!event_pool.empty()) {
+      hipEvent_t e = event_pool.back();
+      event_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+
+  int esize() const { return cfg.dtype == DFLASH_F32 ? 4 : 2; }
+  int nq() const { return cfg.n_q_heads * cfg.head_dim; }
+  int nkv() const { return cfg.n_kv_heads * cfg.head_dim; }
+};
+
+static int fail(dflash* h, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (h) h->err = buf;
+  else g_create_error = buf;
+  return code;
+}
+
+// ------------------------------------------------------------------ planning
+
+namespace {
+
+struct GemmPlan {
+  int mt, mgroups, n_tiles, splits, iters;
+  size_t partial_bytes;
+};
+
+GemmPlan plan_gemm(int dtype, int M, int n_tiles, int K) {
+  GemmPlan g;
+  g.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  g.mgroups = (M + 16 * g.mt - 1) / (16 * g.mt);
+  g.n_tiles = n_tiles;
+  g.iters = K / gemm_k_per_iter(dtype);
+  // The split depends on the weight shape only, never on M: each row's sums are then
+  // formed in the same order whatever the batch, so batched rows equal solo rows bit
+  // for bit.
+  const int target_wg = 1024;
+  g.splits = 1;
+  while ((int64_t)n_tiles * g.splits * 2 <= target_wg && g.iters / (g.splits * 2) >= 4) g.splits *= 2;
+  g.partial_bytes = g.splits > 1 ? (size_t)g.splits * g.mgroups * 16 * g.mt * n_tiles * 128 * 4 : 0;
+  return g;
+}
+
+struct AttnPlan {
+  int n_chunks, qt;
+  size_t part_o_bytes, part_ml_bytes;
+};
+
+AttnPlan plan_attn(const dflash_config& c, int S, int max_ctx, int window) {
+  AttnPlan a;
+  const int reach = window > 0 ? std::min(window, max_ctx) : max_ctx;
+  a.n_chunks = attention_chunks(reach);
+  a.qt = attention_query_tiles(c.n_q_heads / c.n_kv_heads, c.block_size);
+  const size_t sh = (size_t)S * c.n_kv_heads * a.n_chunks;
+  a.part_o_bytes = a.n_chunks > 1 ? sh * a.qt * 64 * (c.head_dim / 16) * 4 * 4 : 0;
+  a.part_ml_bytes = a.n_chunks > 1 ? sh * a.qt * 16 * 2 * 4 : 0;
+  return a;
+}
+
+struct Region {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+struct FuseLayout {
+  GemmPlan g;
+  size_t partials, y, ssq, end;
+};
+FuseLayout layout_fuse(const dflash& h, int R) {
+  FuseLayout L;
+  const auto& c = h.cfg;
+  L.g = plan_gemm(c.dtype, R, c.hidden / 128, c.n_taps * c.hidden);
+  Region r;
+  r.take(kCounterInts * 4);
+  L.partials = r.take(L.g.partial_bytes);
+  L.y = r.take((size_t)R * c.hidden * 4);
+  L.ssq = r.take((size_t)R * L.g.n_tiles * 4);
+  L.end = r.off;
+  return L;
+}
+
+struct InjectLayout {
+  GemmPlan g;
+  size_t partials, end;
+};
+InjectLayout layout_inject(const dflash& h, int R) {
+  InjectLayout L;
+  const auto& c = h.cfg;
+  L.g = plan_gemm(c.dtype, R, c.n_layers * 2 * h.nkv() / 128, c.hidden);
+  Region r;
+  r.take(kCounterInts * 4);
+  L.partials = r.take(L.g.partial_bytes);
+  L.end = r.off;
+  return L;
+}
+
+struct DraftLayout {
+  GemmPlan qkv, o, gu, down, lm;
+  std::vector<AttnPlan> attn;
+  size_t x, inv_in, inv_post, q, kb, vb, o_buf, m, partials, ssq, part_o, part_ml, tile_res, end;
+};
+DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
+  DraftLayout L;
+  const auto& c = h.cfg;
+  const int M = S * c.block_size, Mm = S * (c.block_size - 1);
+  const int es = h.esize();
+  L.qkv = plan_gemm(c.dtype, M, (h.nq() + 2 * h.nkv()) / 128, c.hidden);
+  L.o = plan_gemm(c.dtype, M, c.hidden / 128, h.nq());
+  L.gu = plan_gemm(c.dtype, M, c.intermediate / 64, c.hidden);
+  L.down = plan_gemm(c.dtype, M, c.hidden / 128, c.intermediate);
+  L.lm = plan_gemm(c.dtype, Mm, (c.vocab + 127) / 128, c.hidden);
+  L.lm.splits = 1;
+  L.lm.partial_bytes = 0;
+  size_t part = std::max({L.qkv.partial_bytes, L.o.partial_bytes, L.gu.partial_bytes, L.down.partial_bytes});
+  size_t po = 0, pml = 0;
+  for (int l = 0; l < c.n_layers; ++l) {
+    L.attn.push_back(plan_attn(c, S, max_ctx, c.layer_window[l]));
+    po = std::max(po, L.attn.back().part_o_bytes);
+    pml = std::max(pml, L.attn.back().part_ml_bytes);
+  }
+  Region r;
+  r.take(kCounterInts * 4);
+  L.x = r.take((size_t)M * c.hidden * es);
+  L.inv_in = r.take((size_t)M * 4);
+  L.inv_post = r.take((size_t)M * 4);
+  L.q = r.take((size_t)M * h.nq() * es);
+  L.kb = r.take((size_t)M * h.nkv() * es);
+  L.vb = r.take((size_t)M * h.nkv() * es);
+  L.o_buf = r.take((size_t)M * h.nq() * es);
+  L.m = r.take((size_t)M * c.intermediate * es);
+  L.partials = r.take(part);
+  L.ssq = r.take((size_t)M * (c.hidden / 128) * 4);
+  L.part_o = r.take(po);
+  L.part_ml = r.take(pml);
+  L.tile_res = r.take((size_t)L.lm.mgroups * 16 * L.lm.mt * L.lm.n_tiles * 16);
+  L.end = r.off;
+  return L;
+}
+
+bool counters_fit(const GemmPlan& g) {
+  return (int64_t)g.mgroups * g.n_tiles <= kSplitCounters && g.mgroups <= kRowCounters;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ C-ABI
+
+extern "C" {
+
+const char* dflash_version(void) { return "dflash-mi355x 0.1"; }
+
+void dflash_config_init(dflash_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->dtype = DFLASH_BF16;
+  cfg->rope_theta = 1.0e6f;
+  cfg->rms_eps = 1.0e-6f;
+  cfg->page_size = 16;
+  cfg->max_streams = 1;
+  cfg->pool_pages = 1;
+}
+
+int32_t dflash_tensor_count(const dflash_config* cfg) { return cfg ? 11 * cfg->n_layers + 3 : -1; }
+
+static int validate(const dflash_config* c) {
+#define REFUSE(...) return fail(nullptr, DFLASH_ERR_CONFIG, __VA_ARGS__)
+  if (!c) return fail(nullptr, DFLASH_ERR_ARG, "config is NULL");
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) REFUSE("dtype %d is neither F32 nor BF16", c->dtype);
+  if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) REFUSE("n_layers %d outside 1..64", c->n_layers);
+  if (c->head_dim != 64 && c->head_dim != 128) REFUSE("head_dim %d is not 64 or 128", c->head_dim);
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
+    REFUSE("n_q_heads %d is not a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+  if (c->hidden < 128 || c->hidden % 128) REFUSE("hidden %d is not a positive multiple of 128", c->hidden);
+  if (c->intermediate < 128 || c->intermediate % 128) REFUSE("intermediate %d is not a positive multiple of 128", c->intermediate);
+  if ((c->n_q_heads * c->head_dim) % 128 || (c->n_kv_heads * c->head_dim) % 128)
+    REFUSE("head projections (n_q*d=%d, n_kv*d=%d) are not multiples of 128", c->n_q_heads * c->head_dim,
+           c->n_kv_heads * c->head_dim);
+  if (c->vocab < 2) REFUSE("vocab %d < 2", c->vocab);
+  if (c->n_taps < 1 || c->n_taps > DFLASH_MAX_TAPS) REFUSE("n_taps %d outside 1..8", c->n_taps);
+  if (c->target_n_layers < 1) REFUSE("target_n_layers %d < 1", c->target_n_layers);
+  for (int i = 0; i < c->n_taps; ++i) {
+    if (c->tap_layer_ids[i] < 0 || c->tap_layer_ids[i] >= c->target_n_layers)
+      REFUSE("tap %d reads layer %d, past the target's %d layers", i, c->tap_layer_ids[i], c->target_n_layers);
+    if (i > 0 && c->tap_layer_ids[i] == c->tap_layer_ids[i - 1]) REFUSE("tap layer %d is repeated", c->tap_layer_ids[i]);
+    if (i > 0 && c->tap_layer_ids[i] < c->tap_layer_ids[i - 1])
+      REFUSE("tap layer ids must be ascending (tap %d: %d after %d)", i, c->tap_layer_ids[i], c->tap_layer_ids[i - 1]);
+  }
+  if (c->block_size < 2 || c->block_size > 32) REFUSE("block_size %d outside 2..32", c->block_size);
+  if ((c->n_q_heads / c->n_kv_heads) * c->block_size > 128)
+    REFUSE("a kv head's block queries ((n_q/n_kv) * block = %d) exceed 128", (c->n_q_heads / c->n_kv_heads) * c->block_size);
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) REFUSE("mask_token_id %d outside the vocab", c->mask_token_id);
+  if (c->causal != 0) REFUSE("a causal draft is refused: the block forward is non-causal");
+  for (int l = 0; l < c->n_layers; ++l)
+    if (c->layer_window[l] < 0) REFUSE("layer %d window %d < 0", l, c->layer_window[l]);
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) REFUSE("rope_theta must be positive");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) REFUSE("rms_eps must be >= 0");
+  if (c->max_streams < 1) REFUSE("max_streams %d < 1", c->max_streams);
+  if (c->page_size != 16) REFUSE("page_size %d is not 16", c->page_size);
+  if (c->pool_pages < 1) REFUSE("pool_pages %d < 1", c->pool_pages);
+#undef REFUSE
+  return DFLASH_OK;
+}
+
+int dflash_create(const dflash_config* cfg, dflash** out) {
+  if (!out) return fail(nullptr, DFLASH_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc != DFLASH_OK) return rc;
+  dflash* h = new dflash();
+  h->cfg = *cfg;
+  std::memset(&h->w, 0, sizeof h->w);
+  *out = h;
+  g_create_error = "";
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash* h) { delete h; }
+
+const char* dflash_last_error(const dflash* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
+
+int64_t dflash_fused_row_bytes(const dflash_config* cfg) {
+  if (!cfg) return -1;
+  return (int64_t)cfg->hidden * (cfg->dtype == DFLASH_F32 ? 4 : 2);
+}
+
+int64_t dflash_tap_row_bytes(const dflash_config* cfg, int32_t fusing) {
+  if (!cfg) return -1;
+  const int64_t row = (int64_t)cfg->hidden * (cfg->dtype == DFLASH_F32 ? 4 : 2);
+  return fusing ? (2 * (int64_t)cfg->n_taps + 2) * row : (int64_t)cfg->n_taps * row;
+}
+
+int dflash_bind_weights(dflash* h, const dflash_weights* w, const int64_t* shapes) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (!w || !shapes) return fail(h, DFLASH_ERR_ARG, "weights or shapes is NULL");
+  const auto& c = h->cfg;
+  const int64_t H = c.hidden, V = c.vocab, I = c.intermediate, d = c.head_dim;
+  struct Want { const void* p; int64_t r, k; std::string name; };
+  std::vector<Want> want = {
+      {w->embed, V, H, "embed"}, {w->lm_head, V, H, "lm_head"}, {w->fc, H, (int64_t)c.n_taps * H, "fc"},
+      {w->hidden_norm, H, 1, "hidden_norm"}, {w->norm, H, 1, "norm"}};
+  for (int l = 0; l < c.n_layers; ++l) {
+    std::string p = "layers." + std::to_string(l) + ".";
+    want.push_back({w->in_norm[l], H, 1, p + "in_norm"});
+    want.push_back({w->wq[l], h->nq(), H, p + "wq"});
+    want.push_back({w->wk[l], h->nkv(), H, p + "wk"});
+    want.push_back({w->wv[l], h->nkv(), H, p + "wv"});
+    want.push_back({w->wo[l], H, h->nq(), p + "wo"});
+    want.push_back({w->q_norm[l], d, 1, p + "q_norm"});
+    want.push_back({w->k_norm[l], d, 1, p + "k_norm"});
+    want.push_back({w->post_norm[l], H, 1, p + "post_norm"});
+    want.push_back({w->w_gate[l], I, H, p + "w_gate"});
+    want.push_back({w->w_up[l], I, H, p + "w_up"});
+    want.push_back({w->w_down[l], H, I, p + "w_down"});
+  }
+  for (size_t i = 0; i < want.size(); ++i) {
+    const Want& t = want[i];
+    if (!t.p) return fail(h, DFLASH_ERR_ARG, "tensor %s: NULL pointer (nothing bound)", t.name.c_str());
+    if (!aligned16(t.p)) return fail(h, DFLASH_ERR_ARG, "tensor %s: pointer not 16-byte aligned (nothing bound)", t.name.c_str());
+    if (shapes[2 * i] != t.r || shapes[2 * i + 1] != t.k)
+      return fail(h, DFLASH_ERR_SHAPE, "tensor %s: shape (%lld, %lld), expected (%lld, %lld) (nothing bound)",
+                  t.name.c_str(), (long long)shapes[2 * i], (long long)shapes[2 * i + 1], (long long)t.r,
+                  (long long)t.k);
+  }
+  h->w = *w;
+  h->bound = true;
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_streams, int32_t max_ctx) {
+  if (!h || max_rows < 0 || n_streams < 1 || n_streams > h->cfg.max_streams || max_ctx < 0) return 0;
+  size_t b = align_up(kCounterInts * 4);
+  if (max_rows > 0) {
+    b = std::max(b, layout_fuse(*h, max_rows).end);
+    b = std::max(b, layout_inject(*h, max_rows).end);
+  }
+  b = std::max(b, layout_draft(*h, n_streams, max_ctx).end);
+  return b;
+}
+
+int dflash_workspace_init(dflash* h, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (!ws || !aligned16(ws)) return fail(h, DFLASH_ERR_ARG, "workspace is NULL or misaligned");
+  if (ws_bytes < (size_t)kCounterInts * 4)
+    return fail(h, DFLASH_ERR_CAPACITY, "workspace of %zu bytes is smaller than its counter block", ws_bytes);
+  hipError_t e = launch_fill_zero(static_cast<int*>(ws), kCounterInts, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "workspace init: %s", hipGetErrorString(e));
+  for (auto& r : h->ws_ready)
+    if (r.first == ws) {
+      r.second = ws_bytes;
+      return DFLASH_OK;
+    }
+  h->ws_ready.push_back({ws, ws_bytes});
+  return DFLASH_OK;
+}
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+  dflash* h;
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(dflash* h_, const char* n, hipStream_t s) : h(h_), name(n), st(s) {
+    if (h->profiling) {
+      a = h->take_event();
+      if (a) hipEventRecord(a, st);
+    }
+  }
+  ~ProfScope() {
+    if (a) {
+      hipEvent_t b = h->take_event();
+      if (b) {
+        hipEventRecord(b, st);
+        h->prof.push_back({name, a, b});
+      } else {
+        h->event_pool.push_back(a);
+      }
+    }
+  }
+};
+
+static int check_ws(dflash* h, void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || !aligned16(ws)) return fail(h, DFLASH_ERR_ARG, "workspace is NULL or misaligned");
+  bool ready = false;
+  for (auto& r : h->ws_ready)
+    if (r.first == ws && ws_bytes <= r.second) ready = true;
+  if (!ready) return fail(h, DFLASH_ERR_STATE, "workspace was not initialised with dflash_workspace_init");
+  if (ws_bytes < need) return fail(h, DFLASH_ERR_CAPACITY, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
+  return DFLASH_OK;
+}
+
+static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K, char* ws, size_t partials_off) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.n_tiles = g.n_tiles;
+  p.splits = g.splits;
+  p.iters = g.iters;
+  p.partials = reinterpret_cast<float*>(ws + partials_off);
+  p.counters = reinterpret_cast<int*>(ws);
+  p.counters2 = reinterpret_cast<int*>(ws) + kSplitCounters;
+  return p;
+}
+
+static_assert(sizeof(GemmParams) <= 4000, "kernel argument block too large");
+
+int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row_stride, int32_t n_rows,
+                     void* fused_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const auto& c = h->cfg;
+  if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
+  if (n_rows < 0) return fail(h, DFLASH_ERR_ARG, "n_rows %d < 0", n_rows);
+  if (n_rows == 0) return DFLASH_OK;
+  if (!tap_planes || !fused_out || !aligned16(fused_out)) return fail(h, DFLASH_ERR_ARG, "tap_planes or fused_out invalid");
+  for (int t = 0; t < c.n_taps; ++t)
+    if (!tap_planes[t] || !aligned16(tap_planes[t])) return fail(h, DFLASH_ERR_ARG, "tap plane %d is NULL or misaligned", t);
+  if (plane_row_stride < c.hidden || plane_row_stride % 8)
+    return fail(h, DFLASH_ERR_ARG, "plane_row_stride %lld must be >= hidden and a multiple of 8", (long long)plane_row_stride);
+  FuseLayout L = layout_fuse(*h, n_rows);
+  int rc = check_ws(h, ws, ws_bytes, L.end);
+  if (rc) return rc;
+  if (!counters_fit(L.g)) return fail(h, DFLASH_ERR_CAPACITY, "n_rows %d exceeds the counter block", n_rows);
+  char* W = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  GemmParams p = gemm_base(L.g, n_rows, c.hidden, c.n_taps * c.hidden, W, L.partials);
+  p.a_mode = A_TAPS;
+  for (int t = 0; t < c.n_taps; ++t) p.taps[t] = tap_planes[t];
+  p.tap_h = c.hidden;
+  p.tap_stride = plane_row_stride;
+  p.w0 = h->w.fc;
+  p.y_out = reinterpret_cast<float*>(W + L.y);
+  p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
+  hipError_t e;
+  {
+    ProfScope ps(h, "fuse_fc_gemm", st);
+    e = launch_gemm(c.dtype, EPI_FC, p, L.g.mt, L.g.mgroups, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
+  RowNormParams rn;
+  rn.R = n_rows;
+  rn.hidden = c.hidden;
+  rn.n_tiles = L.g.n_tiles;
+  rn.y = p.y_out;
+  rn.ssq_part = p.ssq_part;
+  rn.gain = h->w.hidden_norm;
+  rn.out = fused_out;
+  rn.eps = c.rms_eps;
+  {
+    ProfScope ps(h, "fuse_rownorm", st);
+    e = launch_rownorm(c.dtype, rn, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse norm: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+static int check_kv(dflash* h, const dflash_kv* kv) {
+  const auto& c = h->cfg;
+  if (!kv || !kv->page_table) return fail(h, DFLASH_ERR_ARG, "kv or its page table is NULL");
+  if (kv->pages_per_stream < 1) return fail(h, DFLASH_ERR_ARG, "pages_per_stream %d < 1", kv->pages_per_stream);
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!kv->k_pool[l] || !kv->v_pool[l] || !aligned16(kv->k_pool[l]) || !aligned16(kv->v_pool[l]))
+      return fail(h, DFLASH_ERR_ARG, "layer %d K/V pool is NULL or misaligned", l);
+  return DFLASH_OK;
+}
+
+int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t* row_stream,
+                     const int32_t* row_pos, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const auto& c = h->cfg;
+  if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
+  if (n_rows < 0) return fail(h, DFLASH_ERR_ARG, "n_rows %d < 0", n_rows);
+  if (n_rows == 0) return DFLASH_OK;
+  if (!fused || !aligned16(fused) || !row_stream || !row_pos) return fail(h, DFLASH_ERR_ARG, "fused, row_stream or row_pos invalid");
+  int rc = check_kv(h, kv);
+  if (rc) return rc;
+  InjectLayout L = layout_inject(*h, n_rows);
+  rc = check_ws(h, ws, ws_bytes, L.end);
+  if (rc) return rc;
+  if (!counters_fit(L.g)) return fail(h, DFLASH_ERR_CAPACITY, "n_rows %d exceeds the counter block", n_rows);
+  char* W = static_cast<char*>(ws);
+  GemmParams p = gemm_base(L.g, n_rows, c.n_layers * 2 * h->nkv(), c.hidden, W, L.partials);
+  p.a_mode = A_PLAIN;
+  p.a = fused;
+  p.lda = c.hidden;
+  p.nkv = h->nkv();
+  for (int l = 0; l < c.n_layers; ++l) {
+    p.wk_l[l] = h->w.wk[l];
+    p.wv_l[l] = h->w.wv[l];
+    p.kn_l[l] = h->w.k_norm[l];
+    p.kpool_l[l] = kv->k_pool[l];
+    p.vpool_l[l] = kv->v_pool[l];
+  }
+  p.head_dim = c.head_dim;
+  p.theta = c.rope_theta;
+  p.eps = c.rms_eps;
+  p.row_stream = row_stream;
+  p.row_pos = row_pos;
+  p.page_table = kv->page_table;
+  p.pages_per_stream = kv->pages_per_stream;
+  p.page_size = c.page_size;
+  p.pool_pages = c.pool_pages;
+  p.max_streams = c.max_streams;
+  p.n_kv_heads = c.n_kv_heads;
+  hipError_t e;
+  {
+    ProfScope ps(h, "inject_kv_gemm", (hipStream_t)stream);
+    e = launch_gemm(c.dtype, EPI_INJECT, p, L.g.mt, L.g.mgroups, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,
+                       int32_t max_ctx_len, const dflash_kv* kv, int32_t* draft_out, void* logits_out,
+                       float* top2_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const auto& c = h->cfg;
+  if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
+  if (n_streams < 1 || n_streams > c.max_streams)
+    return fail(h, DFLASH_ERR_CAPACITY, "n_streams %d outside 1..max_streams (%d)", n_streams, c.max_streams);
+  if (!anchor || !ctx_len || !draft_out) return fail(h, DFLASH_ERR_ARG, "anchor, ctx_len or draft_out is NULL");
+  if ((logits_out && !aligned16(logits_out)) || (top2_out && ((uintptr_t)top2_out & 7)))
+    return fail(h, DFLASH_ERR_ARG, "logits_out / top2_out misaligned");
+  int rc = check_kv(h, kv);
+  if (rc) return rc;
+  if (max_ctx_len < 0) return fail(h, DFLASH_ERR_ARG, "max_ctx_len %d < 0", max_ctx_len);
+  if ((int64_t)max_ctx_len > (int64_t)kv->pages_per_stream * c.page_size)
+    return fail(h, DFLASH_ERR_CAPACITY, "max_ctx_len %d is past the cache span of %d tokens", max_ctx_len,
+                kv->pages_per_stream * c.page_size);
+  DraftLayout L = layout_draft(*h, n_streams, max_ctx_len);
+  rc = check_ws(h, ws, ws_bytes, L.end);
+  if (rc) return rc;
+  for (const GemmPlan* g : {&L.qkv, &L.o, &L.gu, &L.down, &L.lm})
+    if (!counters_fit(*g)) return fail(h, DFLASH_ERR_CAPACITY, "n_streams %d exceeds the counter block", n_streams);
+  if ((int64_t)n_streams * c.n_kv_heads > kSplitCounters) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
+
+  const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
+  char* W = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  void* X = W + L.x;
+  float* inv_in = reinterpret_cast<float*>(W + L.inv_in);
+  float* inv_post = reinterpret_cast<float*>(W + L.inv_post);
+  hipError_t e;
+
+  EmbedParams ep;
+  ep.S = n_streams;
+  ep.B = B;
+  ep.hidden = c.hidden;
+  ep.vocab = c.vocab;
+  ep.mask_token = c.mask_token_id;
+  ep.anchor = anchor;
+  ep.embed = h->w.embed;
+  ep.x = X;
+  ep.inv = inv_in;
+  ep.eps = c.rms_eps;
+  {
+    ProfScope ps(h, "embed", st);
+    e = launch_embed(c.dtype, ep, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "embed: %s", hipGetErrorString(e));
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    // a = round(RMSNorm(X) * in_norm); q, k, v with per-head norms and RoPE
+    GemmParams p = gemm_base(L.qkv, M, h->nq() + 2 * h->nkv(), c.hidden, W, L.partials);
+    p.a_mode = A_NORMED;
+    p.a = X;
+    p.lda = c.hidden;
+    p.a_inv = inv_in;
+    p.a_gain = h->w.in_norm[l];
+    p.w0 = h->w.wq[l];
+    p.w1 = h->w.wk[l];
+    p.w2 = h->w.wv[l];
+    p.nq = h->nq();
+    p.nkv = h->nkv();
+    p.q_out = W + L.q;
+    p.k_out = W + L.kb;
+    p.v_out = W + L.vb;
+    p.qn_gain = h->w.q_norm[l];
+    p.kn_gain = h->w.k_norm[l];
+    p.head_dim = c.head_dim;
+    p.theta = c.rope_theta;
+    p.eps = c.rms_eps;
+    p.ctx_len = ctx_len;
+    p.max_ctx = max_ctx_len;
+    p.block = B;
+    {
+      ProfScope ps(h, "qkv_gemm", st);
+      e = launch_gemm(c.dtype, EPI_QKV, p, L.qkv.mt, L.qkv.mgroups, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv: %s", l, hipGetErrorString(e));
+
+    AttnParams ap;
+    std::memset(&ap, 0, sizeof ap);
+    ap.S = n_streams;
+    ap.B = B;
+    ap.n_q_heads = c.n_q_heads;
+    ap.n_kv_heads = c.n_kv_heads;
+    ap.head_dim = c.head_dim;
+    ap.group = c.n_q_heads / c.n_kv_heads;
+    ap.window = c.layer_window[l];
+    ap.n_chunks = L.attn[l].n_chunks;
+    ap.max_ctx = max_ctx_len;
+    ap.ctx_len = ctx_len;
+    ap.q = W + L.q;
+    ap.kb = W + L.kb;
+    ap.vb = W + L.vb;
+    ap.kpool = kv->k_pool[l];
+    ap.vpool = kv->v_pool[l];
+    ap.page_table = kv->page_table;
+    ap.pages_per_stream = kv->pages_per_stream;
+    ap.page_size = c.page_size;
+    ap.pool_pages = c.pool_pages;
+    ap.o = W + L.o_buf;
+    ap.part_o = reinterpret_cast<float*>(W + L.part_o);
+    ap.part_ml = reinterpret_cast<float*>(W + L.part_ml);
+    ap.counters = reinterpret_cast<int*>(W);
+    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    {
+      ProfScope ps(h, c.layer_window[l] > 0 ? "attention_sliding" : "attention_full", st);
+      e = launch_attention(c.dtype, ap, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d attention: %s", l, hipGetErrorString(e));
+
+    // X += wo . o   (residual add 1), then 1 / rms for the post-attention norm
+    p = gemm_base(L.o, M, c.hidden, h->nq(), W, L.partials);
+    p.a_mode = A_PLAIN;
+    p.a = W + L.o_buf;
+    p.lda = h->nq();
+    p.w0 = h->w.wo[l];
+    p.x_io = X;
+    p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
+    p.inv_out = inv_post;
+    p.eps = c.rms_eps;
+    {
+      ProfScope ps(h, "o_proj_gemm", st);
+      e = launch_gemm(c.dtype, EPI_RESID, p, L.o.mt, L.o.mgroups, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d o_proj: %s", l, hipGetErrorString(e));
+
+    // m = round(silu(w_gate . b) * (w_up . b)), b = round(RMSNorm(X) * post_norm)
+    p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden, W, L.partials);
+    p.a_mode = A_NORMED;
+    p.a = X;
+    p.lda = c.hidden;
+    p.a_inv = inv_post;
+    p.a_gain = h->w.post_norm[l];
+    p.w0 = h->w.w_gate[l];
+    p.w1 = h->w.w_up[l];
+    p.m_out = W + L.m;
+    p.ld_out = c.intermediate;
+    {
+      ProfScope ps(h, "gate_up_gemm", st);
+      e = launch_gemm(c.dtype, EPI_SWIGLU, p, L.gu.mt, L.gu.mgroups, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d gate/up: %s", l, hipGetErrorString(e));
+
+    // X += w_down . m   (residual add 2), then 1 / rms for the next norm
+    p = gemm_base(L.down, M, c.hidden, c.intermediate, W, L.partials);
+    p.a_mode = A_PLAIN;
+    p.a = W + L.m;
+    p.lda = c.intermediate;
+    p.w0 = h->w.w_down[l];
+    p.x_io = X;
+    p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
+    p.inv_out = inv_in;
+    p.eps = c.rms_eps;
+    {
+      ProfScope ps(h, "down_gemm", st);
+      e = launch_gemm(c.dtype, EPI_RESID, p, L.down.mt, L.down.mgroups, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d down: %s", l, hipGetErrorString(e));
+  }
+
+  // Final norm of the mask rows, LM head, argmax (lowest index on a tie).
+  GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden, W, 0);
+  p.a_mode = A_NORMED;
+  p.a = X;
+  p.lda = c.hidden;
+  p.a_inv = inv_in;
+  p.a_gain = h->w.norm;
+  p.a_rowmap_bm1 = B - 1;
+  p.w0 = h->w.lm_head;
+  p.logits_out = logits_out;
+  p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
+  p.draft_out = draft_out;
+  p.top2_out = top2_out;
+  {
+    ProfScope ps(h, "lm_head_argmax_gemm", st);
+    e = launch_gemm(c.dtype, EPI_LMHEAD, p, L.lm.mt, L.lm.mgroups, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "lm head: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+int dflash_verify_greedy(dflash* h, int32_t n_streams, const int32_t* draft, const int32_t* target_argmax,
+                         int32_t* accept_len, int32_t* bonus, int32_t* committed, int32_t* ctx_len_inout,
+                         void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (n_streams < 1) return fail(h, DFLASH_ERR_ARG, "n_streams %d < 1", n_streams);
+  if (!draft || !target_argmax || !accept_len || !bonus || !committed)
+    return fail(h, DFLASH_ERR_ARG, "a verify pointer is NULL");
+  VerifyParams vp;
+  vp.S = n_streams;
+  vp.B = h->cfg.block_size;
+  vp.draft = draft;
+  vp.target = target_argmax;
+  vp.accept = accept_len;
+  vp.bonus = bonus;
+  vp.committed = committed;
+  vp.ctx_len = ctx_len_inout;
+  hipError_t e;
+  {
+    ProfScope ps(h, "verify", (hipStream_t)stream);
+    e = launch_verify(vp, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "verify: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+int dflash_set_profiling(dflash* h, int32_t enable) {
+  if (!h) return DFLASH_ERR_ARG;
+  h->profiling = enable != 0;
+  return DFLASH_OK;
+}
+
+int dflash_profile_read(dflash* h, char* buf, size_t len) {
+  if (!h || !buf || len == 0) return DFLASH_ERR_ARG;
+  std::map<std::string, std::pair<long, double>> acc;
+  for (auto& r : h->prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "profile: event wait failed");
+    auto& a = acc[r.name];
+    a.first += 1;
+    a.second += ms;
+    h->event_pool.push_back(r.a);
+    h->event_pool.push_back(r.b);
+  }
+  h->prof.clear();
+  std::string out;
+  for (auto& kv : acc) {
+    char line[256];
+    snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  size_t n = std::min(out.size(), len - 1);
+  std::memcpy(buf, out.data(), n);
+  buf[n] = 0;
+  return (int)n;
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+/*
+ * dflash.h -- C-ABI of the DFlash block-diffusion draft round on MI355X (gfx950).
+ *
+ * One draft round has four calls, in this order:
+ *   dflash_fuse_taps      target tap planes -> fused context rows (fc, hidden_norm)
+ *   dflash_inject_kv      fused rows -> k and v of every draft layer, written into a paged cache
+ *   dflash_draft_block    one non-causal forward over anchor + (B-1) mask rows, LM-head argmax
+ *   dflash_verify_greedy  longest prefix equal to the target's argmax, plus the bonus token
+ *
+ * The round is the one described by TensorFold pull request #1851 ("What this
+ * changes", items 1-4), the DFlash explainer (sections 3 and 4) and "Port the
+ * DFlash2 protocol, not its checkpoint" ("What is portable").
+ *
+ * Conventions shared by every call:
+ *   - Every call returns a dflash_status; on failure dflash_last_error() names the cause.
+ *   - Arguments, shapes and capacities are checked on the host BEFORE anything is
+ *     enqueued, so a refused call has no side effect on device memory.
+ *   - All device memory (weights, caches, inputs, outputs, workspace) is owned by the
+ *     caller; the library never allocates or frees device memory and never copies weights.
+ *   - Calls are asynchronous on the given stream (a hipStream_t passed as void *;
+ *     NULL is the null stream). A device fault surfaces on the caller's next sync.
+ *   - A handle is used by one host thread at a time. Calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Device pointers must be 16-byte aligned. Tensors are dense row-major.
+ *   - Element type of every weight, activation and cache is the config's dtype
+ *     (DFLASH_BF16: bfloat16 bit patterns; DFLASH_F32: IEEE float).
+ *   - Token ids, positions, lengths and page ids are int32.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_LAYERS 64
+#define DFLASH_MAX_TAPS 8
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_ARG = -1,        /* null / misaligned pointer, bad count */
+  DFLASH_ERR_CONFIG = -2,     /* the config is refused (see dflash_create) */
+  DFLASH_ERR_SHAPE = -3,      /* a weight's shape does not match the config */
+  DFLASH_ERR_CAPACITY = -4,   /* a request past the cache span, the stream count or the workspace */
+  DFLASH_ERR_STATE = -5,      /* weights not bound, or workspace not initialised */
+  DFLASH_ERR_DEVICE = -6,     /* a HIP launch failed */
+  DFLASH_ERR_UNIMPLEMENTED = -7
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/*
+ * Drafter config (a DFlash v1 drafter: a plain qwen3 body, no conv, no selector).
+ * TensorFold #1851 item 1: taps (up to eight), block, mask token and layer kinds
+ * come from the config; a causal draft and taps past the target or repeated are
+ * refused. Item 4: sliding layers attend their own window, the full layer all.
+ *
+ * dflash_create refuses (DFLASH_ERR_CONFIG) when any of these fails:
+ *   dtype is DFLASH_F32 or DFLASH_BF16;
+ *   1 <= n_layers <= 64; head_dim is 64 or 128; n_q_heads % n_kv_heads == 0;
+ *   hidden, intermediate, n_q_heads*head_dim, n_kv_heads*head_dim are multiples of 128;
+ *   vocab >= 2; 1 <= n_taps <= 8; tap ids strictly ascending (so never repeated),
+ *   each in [0, target_n_layers); 2 <= block_size <= 32; 0 <= mask_token_id < vocab;
+ *   causal == 0; layer_window[l] >= 0 (0 = full attention) for l < n_layers;
+ *   rope_theta > 0; rms_eps >= 0; max_streams >= 1; page_size == 16; pool_pages >= 1.
+ */
+typedef struct {
+  int32_t dtype;
+  int32_t hidden, n_layers, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  int32_t n_taps, tap_layer_ids[DFLASH_MAX_TAPS], target_n_layers;
+  int32_t block_size, mask_token_id, causal;
+  int32_t layer_window[DFLASH_MAX_LAYERS];
+  float rope_theta, rms_eps;
+  int32_t max_streams, page_size, pool_pages;
+} dflash_config;
+
+/*
+ * Weight pointers (device). Shapes, [rows, cols] row-major:
+ *   embed, lm_head [vocab, hidden]  (shared with the target, frozen)
+ *   fc [hidden, n_taps*hidden]; hidden_norm, norm [hidden]
+ *   per layer l: in_norm, post_norm [hidden]; wq [n_q*d, hidden]; wk, wv [n_kv*d, hidden];
+ *   wo [hidden, n_q*d]; q_norm, k_norm [d]; w_gate, w_up [intermediate, hidden];
+ *   w_down [hidden, intermediate].
+ * That is 11 tensors a layer plus fc, hidden_norm and norm (TensorFold #1851, item 1).
+ */
+typedef struct {
+  const void *embed, *lm_head, *fc, *hidden_norm, *norm;
+  const void *in_norm[DFLASH_MAX_LAYERS], *wq[DFLASH_MAX_LAYERS], *wk[DFLASH_MAX_LAYERS],
+      *wv[DFLASH_MAX_LAYERS], *wo[DFLASH_MAX_LAYERS], *q_norm[DFLASH_MAX_LAYERS],
+      *k_norm[DFLASH_MAX_LAYERS], *post_norm[DFLASH_MAX_LAYERS], *w_gate[DFLASH_MAX_LAYERS],
+      *w_up[DFLASH_MAX_LAYERS], *w_down[DFLASH_MAX_LAYERS];
+} dflash_weights;
+
+/*
+ * Paged draft K/V cache (device), one K pool and one V pool per layer, each
+ * [pool_pages, n_kv_heads, page_size, head_dim]. Stream s's position p lives in
+ * page page_table[s * pages_per_stream + p / page_size], slot p % page_size.
+ * Every layer's cache holds the whole served span; a sliding layer only reads
+ * its window of it (TensorFold #1851, item 4). page_table is device int32
+ * [max_streams, pages_per_stream]; entries outside [0, pool_pages) are never
+ * dereferenced (such keys are skipped on read and on write).
+ */
+typedef struct {
+  void *k_pool[DFLASH_MAX_LAYERS], *v_pool[DFLASH_MAX_LAYERS];
+  const int32_t *page_table;
+  int32_t pages_per_stream;
+} dflash_kv;
+
+typedef struct dflash dflash;
+
+/* Fill a config with the defaults: rope_theta 1e6, rms_eps 1e-6, page_size 16, causal 0,
+ * all layers full attention; shape fields zero. */
+void dflash_config_init(dflash_config *cfg);
+
+/* Validate a config and create a handle. No device work. On DFLASH_ERR_CONFIG *out is
+ * NULL and dflash_last_error(NULL) names the failed check. */
+int dflash_create(const dflash_config *cfg, dflash **out);
+
+/* Number of drafter tensors, 11 * n_layers + 3 (TensorFold #1851, item 1: 69 names at 6 layers). */
+int32_t dflash_tensor_count(const dflash_config *cfg);
+
+/*
+ * Bind weights by pointer. `shapes` holds 2 int64 per tensor in this order:
+ * embed, lm_head, fc, hidden_norm, norm, then for each layer in_norm, wq, wk, wv, wo,
+ * q_norm, k_norm, post_norm, w_gate, w_up, w_down; a vector's shape is (n, 1).
+ * Every pointer must be non-null and 16-byte aligned and every shape must match the
+ * config, or the whole bind is refused (DFLASH_ERR_SHAPE / DFLASH_ERR_ARG) and any
+ * previous binding is left as it was: there is no partial bind ("Port the DFlash2
+ * protocol, not its checkpoint", "The public configs prove target binding").
+ */
+int dflash_bind_weights(dflash *h, const dflash_weights *w, const int64_t *shapes);
+
+/* Bytes of one fused context row: hidden * element size (8 KiB at hidden 4096 bf16;
+ * TensorFold #1851, item 4). */
+int64_t dflash_fused_row_bytes(const dflash_config *cfg);
+
+/* Planner price of a prompt row's taps (TensorFold #1851, item 3): with fusing != 0,
+ * (2 * n_taps + 2) * hidden * element size (planes, their row-major copy, fc's output
+ * row, the fused row: 18 x hidden x 2 bytes for eight bf16 taps); with fusing == 0 the
+ * raw planes only, n_taps * hidden * element size. Returns -1 for a null config. */
+int64_t dflash_tap_row_bytes(const dflash_config *cfg, int32_t fusing);
+
+/*
+ * Workspace bytes for calls with at most `max_rows` fused/injected rows, `n_streams`
+ * streams in a draft, and context length at most `max_ctx`. The workspace holds split-K
+ * partials, block activations, attention partials and self-resetting counters.
+ * Returns 0 if the arguments are out of range.
+ */
+size_t dflash_workspace_bytes(const dflash *h, int32_t max_rows, int32_t n_streams, int32_t max_ctx);
+
+/* Clear a workspace's counters (one small kernel on `stream`). Required once for every
+ * workspace buffer before its first use; afterwards the library keeps it consistent.
+ * Calls given a workspace that was not initialised on this handle are refused
+ * (DFLASH_ERR_STATE). */
+int dflash_workspace_init(dflash *h, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Fuse: for each of n_rows rows r, x = [T_0[r] | T_1[r] | ... | T_{n-1}[r]] (planes in
+ * ascending tap-id order), y = fc . x (fp32 sums), fused[r] = y / sqrt(mean(y^2) + eps)
+ * * hidden_norm, stored in the dtype (TensorFold #1851, items 3 and 4: the taps pass runs
+ * fc and hidden_norm once a row's planes are complete).
+ *   tap_planes: host array of n_taps device pointers; plane t is [n_rows, hidden] with
+ *               a row stride of plane_row_stride elements (>= hidden, multiple of 8).
+ *   fused_out:  device [n_rows, hidden].
+ * n_rows == 0 is a no-op. n_rows beyond the workspace's max_rows -> DFLASH_ERR_CAPACITY.
+ */
+int dflash_fuse_taps(dflash *h, const void *const *tap_planes, int64_t plane_row_stride,
+                     int32_t n_rows, void *fused_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Inject: for each fused row r (device [n_rows, hidden]) of stream row_stream[r] at
+ * position row_pos[r], and for each layer l:
+ *   K_l = RoPE_pos(k_norm_l(wk_l . f)) per kv head,  V_l = wv_l . f,
+ * written into the layer's paged pools (k and v only; no q, no MLP, no input norm:
+ * TensorFold #1851 item 4; DFlash explainer section 3, KV injection into every layer).
+ * row_stream / row_pos are device int32 [n_rows]; rows with a stream outside
+ * [0, max_streams), a position outside [0, pages_per_stream * page_size) or an invalid
+ * page are skipped. n_rows == 0 is a no-op.
+ */
+int dflash_inject_kv(dflash *h, const void *fused, int32_t n_rows, const int32_t *row_stream,
+                     const int32_t *row_pos, const dflash_kv *kv, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Draft one block per stream. Stream s's block is [anchor[s], mask x (B-1)] at
+ * positions C_s .. C_s+B-1 with C_s = ctx_len[s]; one non-causal forward of the qwen3
+ * body (two residual adds a layer); layer l attends the context positions
+ * [max(0, C_s - W_l), C_s) (all of [0, C_s) when W_l == 0) plus all B block rows.
+ * After the final norm the shared LM head scores each mask row, and
+ * draft_out[s, j-1] = argmax (lowest index on a tie) of mask row j, j = 1..B-1
+ * (TensorFold #1851 items 1 and 4; DFlash explainer section 3 and section 5: top-1
+ * at each position independently).
+ *   anchor, ctx_len: device int32 [n_streams]; ctx_len[s] must be <= max_ctx_len
+ *                    (larger values are clamped to it); anchor ids are clamped to
+ *                    [0, vocab).
+ *   max_ctx_len:     host bound used to size the launch; must satisfy
+ *                    max_ctx_len <= kv->pages_per_stream * page_size (else
+ *                    DFLASH_ERR_CAPACITY).
+ *   draft_out:       device int32 [n_streams, B-1].
+ *   logits_out:      NULL, or device dtype [n_streams, B-1, vocab].
+ *   top2_out:        NULL, or device float [n_streams, B-1, 2] (largest and second
+ *                    largest logit, fp32).
+ * The block's own K/V are never written to the cache: only committed rows are, by
+ * the next round's dflash_inject_kv, so rollback is rewinding ctx_len.
+ */
+int dflash_draft_block(dflash *h, int32_t n_streams, const int32_t *anchor,
+                       const int32_t *ctx_len, int32_t max_ctx_len, const dflash_kv *kv,
+                       int32_t *draft_out, void *logits_out, float *top2_out, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/*
+ * Greedy verify (DFlash explainer section 4, greedy decoding; "Port the DFlash2
+ * protocol", golden replay items 4-5). For each stream, with draft d_1..d_{B-1}
+ * (device int32 [n_streams, B-1]) and target argmax t_0..t_{B-1} (device int32
+ * [n_streams, B]):
+ *   accept_len[s] = largest a <= B-1 with d_j == t_{j-1} for all j <= a;
+ *   bonus[s]      = t_a;
+ *   committed[s]  = d_1..d_a, t_a, then -1 up to B entries  (device int32 [n_streams, B]);
+ *   ctx_len_inout[s] += a + 1 when ctx_len_inout is not NULL.
+ * Works without bound weights (it touches no weight).
+ */
+int dflash_verify_greedy(dflash *h, int32_t n_streams, const int32_t *draft,
+                         const int32_t *target_argmax, int32_t *accept_len, int32_t *bonus,
+                         int32_t *committed, int32_t *ctx_len_inout, void *stream);
+
+/*
+ * Instrumentation (not part of the round). With profiling enabled, every kernel the
+ * handle launches is bracketed by two hipEvents on its stream; dflash_profile_read
+ * waits for the recorded events and writes one line per kernel name,
+ * "<name> <launches> <total_ms>\n", into buf (NUL-terminated, truncated to len), then
+ * clears the record. Returns the number of bytes written, or a negative status.
+ */
+int dflash_set_profiling(dflash *h, int32_t enable);
+int dflash_profile_read(dflash *h, char *buf, size_t len);
+
+/* The last error message of a handle (or of dflash_create when h is NULL). Never NULL. */
+const char *dflash_last_error(const dflash *h);
+
+/* Destroy a handle (host memory only). NULL is allowed. */
+void dflash_destroy(dflash *h);
+
+/* Library version string. */
+const char *dflash_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

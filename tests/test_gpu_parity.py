@@ -1,0 +1,387 @@
+"""GPU parity of the HIP draft round against the CPU oracle, through the C-ABI.
+
+Bars (the oracle keeps float64; the GPU sums in fp32):
+  * fused rows and injected K/V: within 1 bf16 ulp of the oracle's bf16 value
+    (fp32 presets: |d| <= 2e-5 |x| + 2e-6, from fp32 sums of up to 32768 terms);
+  * logits: bf16 GPU logits within max-abs 2e-2 of the float64 oracle logits
+    (fp32 presets: 1e-4);
+  * drafted tokens: equal to the oracle's wherever the oracle's top-2 gap exceeds
+    2e-2, elsewhere the GPU token's oracle logit lies within 2e-2 of the maximum;
+  * greedy verify: bit-exact.
+"""
+import json
+import os
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_drafter_dflash_amd as D
+import workloads as wl
+from oracle import dflash_oracle as O
+from workloads.presets import small_variant
+
+from workloads.round_case import RoundCase, to_np
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LOGIT_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ comparison helpers
+
+def ulp_bf16(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    u = np.exp2(e - 7)
+    return np.where(ax > 0, u, 2.0 ** -133)
+
+
+def assert_close_storage(gpu, orc, dtype, what):
+    g = O.as_f64(gpu)
+    o = np.asarray(orc, dtype=np.float64)
+    assert g.shape == o.shape, (what, g.shape, o.shape)
+    tol = ulp_bf16(o) if dtype == "bf16" else 2e-5 * np.abs(o) + 2e-6
+    bad = np.abs(g - o) > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} elements off, worst {np.max(np.abs(g - o) - tol):.3g} past tolerance"
+
+
+def check_tokens(gpu_tok, orc_logits, tol=2e-2):
+    srt = np.sort(orc_logits, axis=-1)
+    gap = srt[..., -1] - srt[..., -2]
+    otok = O.argmax_lowest(orc_logits)
+    near = 0
+    for i in range(orc_logits.shape[0]):
+        if gap[i] > tol:
+            assert gpu_tok[i] == otok[i], f"row {i}: gpu {gpu_tok[i]} oracle {otok[i]} (gap {gap[i]:.3g})"
+        else:
+            near += 1
+            assert orc_logits[i, gpu_tok[i]] >= srt[i, -1] - tol, f"row {i}: near-tie token out of tolerance"
+    return near
+
+
+def compare_round(case, streams, orc):
+    p = case.p
+    logits = O.as_f64(to_np(case.logits))
+    top2 = case.top2.cpu().numpy()
+    toks = case.draft.cpu().numpy()
+    fused = to_np(case.fused)
+    off = np.cumsum([0] + case.rows)
+    worst = 0.0
+    for k, s in enumerate(streams):
+        o = orc[k]
+        if case.rows[s] > 0:
+            assert_close_storage(fused[off[s]:off[s + 1]], o["fused"], p.dtype, f"fused rows of stream {s}")
+            for l in range(p.n_layers):
+                kg, vg = case.kv.read_rows(l, s, case.ctx[s] - case.rows[s], case.rows[s])
+                assert_close_storage(to_np(kg), o["kv"][l][0], p.dtype, f"K layer {l} stream {s}")
+                assert_close_storage(to_np(vg), o["kv"][l][1], p.dtype, f"V layer {l} stream {s}")
+        d = np.max(np.abs(logits[s] - o["logits"]))
+        worst = max(worst, d)
+        assert d <= LOGIT_TOL[p.dtype], f"stream {s}: logits max-abs {d:.4g}"
+        t1, t2 = O.top2(o["logits"])
+        assert np.max(np.abs(top2[s, :, 0] - t1)) <= LOGIT_TOL[p.dtype]
+        assert np.max(np.abs(top2[s, :, 1] - t2)) <= LOGIT_TOL[p.dtype]
+        assert np.max(np.abs(o["logits"])) < 8, "a logit reached 8: the bf16 grid is coarser than the tolerance there"
+        check_tokens(toks[s], o["logits"], LOGIT_TOL[p.dtype])
+    return worst
+
+
+def run_case(case, streams):
+    log(f"[case] {case.p.name} S={case.p.n_streams} ctx={case.ctx} rows={case.rows} streams={streams}")
+    case.run_gpu()
+    orc = O.run_round(case.p, case.weights_np(), case.oracle_streams(streams))
+    worst = compare_round(case, streams, orc)
+    # verify against a synthetic target built from the oracle's tokens
+    S = case.p.n_streams
+    toks_gpu = case.draft.cpu().numpy()
+    toks_orc = toks_gpu.copy()
+    for k, s in enumerate(streams):
+        toks_orc[s] = orc[k]["tokens"]
+    tgt = case.set_target_from(toks_orc)
+    ctx_io = case.ctx_len.clone()
+    case.verify(ctx_io)
+    torch.cuda.synchronize()
+    acc, bon, com = case.accept.cpu().numpy(), case.bonus.cpu().numpy(), case.committed.cpu().numpy()
+    B = case.p.block_size
+    for s in range(S):
+        # valid by the definition: leading matches, then the target's token
+        a = 0
+        while a < B - 1 and toks_gpu[s, a] == tgt[s, a]:
+            a += 1
+        assert acc[s] == a and bon[s] == tgt[s, a]
+        assert list(com[s]) == list(toks_gpu[s, :a]) + [tgt[s, a]] + [-1] * (B - 1 - a)
+    assert np.array_equal(ctx_io.cpu().numpy(), np.array(case.ctx) + acc + 1)
+    for k, s in enumerate(streams):
+        if np.array_equal(toks_gpu[s], orc[k]["tokens"]):      # unique result: equal to the oracle's
+            a2, b2, c2 = O.verify_greedy(orc[k]["tokens"][None], tgt[s][None])
+            assert acc[s] == a2[0] and bon[s] == b2[0] and np.array_equal(com[s], c2[0])
+    log(f"[case] {case.p.name}: logits worst max-abs {worst:.3g}")
+    return orc
+
+
+# ------------------------------------------------------------------ small presets with ragged shapes
+
+MID = small_variant(wl.preset("9b_ctx32k"), name="mid_bf16", hidden=384, n_layers=3, n_q_heads=6,
+                    n_kv_heads=2, head_dim=128, intermediate=640, vocab=1000, n_taps=3,
+                    tap_layer_ids=[0, 4, 11], target_n_layers=12, layer_window=[100, 0, 37],
+                    n_streams=4, ctx_spec=[300, 77, 1030, 0], accept_spec=("uniform",), seed=2001)
+MID64 = small_variant(wl.preset("tiny_f32"), name="mid_d64_bf16", dtype="bf16", hidden=256, n_layers=2,
+                      n_q_heads=8, n_kv_heads=2, head_dim=64, intermediate=384, vocab=3000, n_taps=2,
+                      tap_layer_ids=[3, 6], target_n_layers=8, block_size=8, layer_window=[24, 0],
+                      n_streams=9, ctx_spec=("uniform", 1, 700), accept_spec=("uniform",), seed=2002)
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ verify
+
+@pytest.mark.parametrize("B", [2, 5, 8, 16, 32])
+def test_verify_parity_random(B):
+    log(f"[verify] B={B}")
+    rng = np.random.default_rng(B)
+    S = 300
+    V = 7
+    draft = rng.integers(0, V, (S, B - 1)).astype(np.int32)
+    L = rng.integers(0, B + 1, S)
+    target = wl.make_target_rows(draft, L, V, seed=B)
+    p = small_variant(wl.preset("tiny_f32"), block_size=B, n_streams=S)
+    dr = D.Drafter(D.config_from_preset(p, max_streams=S))
+    dev = "cuda"
+    d_t, t_t = torch.from_numpy(draft).to(dev), torch.from_numpy(target).to(dev)
+    acc = torch.zeros(S, dtype=torch.int32, device=dev)
+    bon = torch.zeros_like(acc)
+    com = torch.zeros((S, B), dtype=torch.int32, device=dev)
+    ctx = torch.arange(S, dtype=torch.int32, device=dev)
+    dr.dflash_verify_greedy(d_t, t_t, acc, bon, com, ctx_len_inout=ctx)
+    torch.cuda.synchronize()
+    a, b, c = O.verify_greedy(draft, target)
+    assert np.array_equal(acc.cpu().numpy(), a)
+    assert np.array_equal(bon.cpu().numpy(), b)
+    assert np.array_equal(com.cpu().numpy(), c)
+    assert np.array_equal(ctx.cpu().numpy(), np.arange(S) + a + 1)
+    assert set(np.unique(a)) == set(range(B)) or B > 16   # zero, partial and full all occur
+
+
+def test_verify_golden_cases_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "verify_greedy_cases.json")))
+    for case in g["cases"]:
+        B = len(case["target"])
+        p = small_variant(wl.preset("tiny_f32"), block_size=B, n_streams=1)
+        dr = D.Drafter(D.config_from_preset(p))
+        d = torch.tensor([case["draft"]], dtype=torch.int32, device="cuda")
+        t = torch.tensor([case["target"]], dtype=torch.int32, device="cuda")
+        acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        bon = torch.zeros_like(acc)
+        com = torch.zeros((1, B), dtype=torch.int32, device="cuda")
+        dr.dflash_verify_greedy(d, t, acc, bon, com)
+        torch.cuda.synchronize()
+        assert acc.item() == case["accept"] and bon.item() == case["bonus"], case["name"]
+        assert com.cpu().numpy()[0].tolist() == case["committed"], case["name"]
+
+
+# ------------------------------------------------------------------ fuse and inject
+
+@pytest.mark.parametrize("preset,rows", [("tiny_f32", [8]), ("tiny_f32", [5]), ("tiny_f32", [70]),
+                                         ("mid", [37]), ("mid", [100]), ("mid64", [17])])
+def test_fuse_and_inject_parity(preset, rows):
+    p = {"mid": MID, "mid64": MID64}.get(preset) or wl.preset(preset)
+    p = small_variant(p, n_streams=1)
+    ctx = [max(rows[0], 128)]
+    case = RoundCase(p, ctx=ctx, rows=rows)
+    log(f"[fuse/inject] {p.name} rows={rows}")
+    case.fuse()
+    W = case.weights_np()
+    taps = [to_np(t) for t in case.taps]
+    fused = O.fuse_taps(p, taps, W)
+    torch.cuda.synchronize()
+    assert_close_storage(to_np(case.fused[:case.R]), fused, p.dtype, "fused")
+    # inject on seeded rows given to both sides
+    rows_in = wl.make_taps(small_variant(p, n_taps=1), rows[0], device="cuda", seed=p.seed + 7)[0]
+    case.dr.dflash_inject_kv(rows_in, case.row_stream, case.row_pos, case.kv, case.ws, n_rows=rows[0])
+    torch.cuda.synchronize()
+    pos = np.arange(ctx[0] - rows[0], ctx[0])
+    kv = O.inject_kv(p, to_np(rows_in), pos, W)
+    for l in range(p.n_layers):
+        kg, vg = case.kv.read_rows(l, 0, pos[0], rows[0])
+        assert_close_storage(to_np(kg), kv[l][0], p.dtype, f"K layer {l}")
+        assert_close_storage(to_np(vg), kv[l][1], p.dtype, f"V layer {l}")
+
+
+def test_inject_skips_invalid_rows_and_touches_nothing_else():
+    p = small_variant(MID, n_streams=2)
+    case = RoundCase(p, ctx=[64, 64], rows=[0, 0])
+    case.ws = case.dr.new_workspace(6, 2, 64)
+    fused = wl.make_taps(small_variant(p, n_taps=1), 6, device="cuda", seed=77)[0]
+    span = case.kv.pages_per_stream * 16
+    rs = torch.tensor([0, -1, 2, 1, 0, 1], dtype=torch.int32, device="cuda")
+    rp = torch.tensor([3, 5, 7, span, -2, 9], dtype=torch.int32, device="cuda")
+    before = [(k.clone(), v.clone()) for k, v in zip(case.kv.k, case.kv.v)]
+    case.dr.dflash_inject_kv(fused, rs, rp, case.kv, case.ws)
+    torch.cuda.synchronize()
+    kv = O.inject_kv(p, to_np(fused), np.array([3, 5, 7, 0, 0, 9]), case.weights_np())
+    for l in range(p.n_layers):
+        k0, v0 = case.kv.read_rows(l, 0, 3, 1)
+        assert_close_storage(to_np(k0), kv[l][0][0:1], p.dtype, "row 0 K")
+        k5, v5 = case.kv.read_rows(l, 1, 9, 1)
+        assert_close_storage(to_np(v5), kv[l][1][5:6], p.dtype, "row 5 V")
+        changed = (case.kv.k[l] != before[l][0]).any(-1).any(1).sum().item()
+        assert changed == 2, f"layer {l}: {changed} slots written, expected exactly the two valid rows"
+
+
+# ------------------------------------------------------------------ whole rounds
+
+def test_round_parity_tiny_f32():
+    run_case(RoundCase(wl.preset("tiny_f32")), [0])
+
+
+def test_round_parity_mid_ragged():
+    run_case(RoundCase(MID), [0, 1, 2, 3])
+
+
+def test_round_parity_mid_d64_two_row_groups():
+    case = RoundCase(MID64)
+    assert case.p.n_streams * case.p.block_size > 64      # more than one 64-row group
+    run_case(case, list(range(MID64.n_streams)))
+
+
+def test_round_parity_9b_ctx4k():
+    run_case(RoundCase(wl.preset("9b_ctx4k")), [0])
+
+
+def test_round_parity_9b_ctx32k():
+    run_case(RoundCase(wl.preset("9b_ctx32k")), [0])
+
+
+def test_round_parity_dflash2_x16_sampled_streams():
+    run_case(RoundCase(wl.preset("dflash2_x16")), [8])
+
+
+def test_round_parity_9b_long_x4_short_stream():
+    run_case(RoundCase(wl.preset("9b_long_x4")), [3])
+
+
+def test_round_parity_9b_long_x4_longest_stream():
+    run_case(RoundCase(wl.preset("9b_long_x4")), [0])
+
+
+# ------------------------------------------------------------------ invariants (bit-exact)
+
+def test_run_to_run_bit_identity_and_reset_rerun():
+    case = RoundCase(MID)
+    case.run_gpu()
+    a = case.logits.clone()
+    d = case.draft.clone()
+    case.inject()            # rewriting the same rows, then drafting again, is a fresh round
+    case.draft_block()
+    torch.cuda.synchronize()
+    assert torch.equal(case.logits.view(torch.int16), a.view(torch.int16))
+    assert torch.equal(case.draft, d)
+
+
+def test_batched_equals_solo_bitwise():
+    case = RoundCase(MID)
+    case.run_gpu()
+    batched = case.logits.clone()
+    for s in range(MID.n_streams):
+        kv1 = SimpleNamespace(struct=D.KV())
+        for l in range(MID.n_layers):
+            kv1.struct.k_pool[l] = case.kv.k[l].data_ptr()
+            kv1.struct.v_pool[l] = case.kv.v[l].data_ptr()
+        pt = case.kv.page_table[s:s + 1].contiguous()
+        kv1.struct.page_table = pt.data_ptr()
+        kv1.struct.pages_per_stream = case.kv.pages_per_stream
+        out = torch.zeros((1, MID.block_size - 1, MID.vocab), dtype=torch.bfloat16, device="cuda")
+        dr = torch.zeros((1, MID.block_size - 1), dtype=torch.int32, device="cuda")
+        case.dr.dflash_draft_block(case.anchor[s:s + 1].contiguous(), case.ctx_len[s:s + 1].contiguous(),
+                                   case.max_ctx, kv1, dr, case.ws, logits_out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0].view(torch.int16), batched[s].view(torch.int16)), f"stream {s}"
+        assert torch.equal(dr[0], case.draft[s])
+
+
+def test_chunked_inject_equals_one_shot_and_page_order_is_invisible():
+    a = RoundCase(MID, permute_pages=True)
+    a.fuse()
+    a.inject()
+    a.draft_block()
+    b = RoundCase(MID, permute_pages=False)
+    b.fuse()
+    cut = a.R // 3
+    b.dr.dflash_inject_kv(b.fused[:cut], b.row_stream[:cut], b.row_pos[:cut], b.kv, b.ws, n_rows=cut)
+    b.dr.dflash_inject_kv(b.fused[cut:a.R].contiguous(), b.row_stream[cut:].contiguous(),
+                          b.row_pos[cut:].contiguous(), b.kv, b.ws, n_rows=a.R - cut)
+    b.draft_block()
+    torch.cuda.synchronize()
+    for l in range(MID.n_layers):
+        for s in range(MID.n_streams):
+            ka, va = a.kv.read_rows(l, s, 0, a.ctx[s])
+            kb, vb = b.kv.read_rows(l, s, 0, b.ctx[s])
+            assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+            assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
+    assert torch.equal(a.logits.view(torch.int16), b.logits.view(torch.int16))
+
+
+def test_sliding_reach_and_rollback_by_perturbation():
+    """Cache rows a sliding layer cannot reach, and rows past C, never change the round."""
+    p = small_variant(MID, n_streams=1, ctx_spec=[1030], layer_window=[100, 0, 37])
+    case = RoundCase(p, ctx=[1030], rows=[5])
+    case.run_gpu()
+    base = case.logits.clone()
+    C = 1030
+    for l, wdw in enumerate(p.layer_window):
+        if wdw > 0:
+            k, v = case.kv.read_rows(l, 0, 0, C - wdw)
+            case.kv.write_rows(l, 0, 0, k.float() + 3.0, v.float() - 2.0)
+    # positions past C inside the last page: poisoned
+    tail = case.kv.pages_per_stream * 16 - C
+    for l in range(p.n_layers):
+        if tail > 0:
+            junk = torch.full((tail, p.n_kv_heads, p.head_dim), 7.0, device="cuda")
+            case.kv.write_rows(l, 0, C, junk, junk)
+    case.draft_block()
+    torch.cuda.synchronize()
+    assert torch.equal(case.logits.view(torch.int16), base.view(torch.int16))
+    # one row inside the sliding window does move the result
+    k, v = case.kv.read_rows(0, 0, C - 100, 1)
+    case.kv.write_rows(0, 0, C - 100, k.float() + 1.0, v.float())
+    case.draft_block()
+    torch.cuda.synchronize()
+    assert not torch.equal(case.logits.view(torch.int16), base.view(torch.int16))
+
+
+def test_argmax_ties_pick_the_lowest_index():
+    case = RoundCase(MID)
+    case.run_gpu()
+    toks = case.draft.cpu().numpy()
+    # copy each winning lm_head row to a lower index: both then score identically
+    lm = case.W["lm_head"]
+    winners = sorted(set(int(t) for t in toks.ravel() if t > 0))
+    for t in winners:
+        lm[t - 1] = lm[t]
+    case.draft_block()
+    torch.cuda.synchronize()
+    new = case.draft.cpu().numpy()
+    for s in range(MID.n_streams):
+        for j in range(MID.block_size - 1):
+            if toks[s, j] > 0:
+                assert new[s, j] == toks[s, j] - 1, (s, j, toks[s, j], new[s, j])
+
+
+def test_zero_rows_are_a_no_op():
+    case = RoundCase(MID)
+    before = case.fused.clone()
+    case.dr.dflash_fuse_taps(case.taps, case.fused, case.ws, n_rows=0)
+    case.dr.dflash_inject_kv(case.fused, case.row_stream, case.row_pos, case.kv, case.ws, n_rows=0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, case.fused)
