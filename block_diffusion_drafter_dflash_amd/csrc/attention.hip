@@ -117,7 +117,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnParams p) {
       for (int f = 0; f < NF; ++f) mma_frag(sacc[mt], *reinterpret_cast<const uint4*>(krow + f * E), qf[f], T());
     }
 
-    // ---- online softmax (base 2), probabilities rounded to the MFMA input type
+    // ---- online softmax (base 2)
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -137,8 +137,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnParams p) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float pv = (m_new == -INFINITY) ? 0.f : exp2f(sacc[mt][i] - m_new);
-        pv = Elem<T>::round(pv);
+        const float pv = (m_new == -INFINITY) ? 0.f : exp2f(sacc[mt][i] - m_new);
         sacc[mt][i] = pv;
         psum += pv;
       }
@@ -149,17 +148,27 @@ __global__ __launch_bounds__(512) void k_attn(const AttnParams p) {
 
     // ---- O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
+      // P enters the bf16 MFMA as hi + lo parts (P - hi rounded again), so the
+      // probabilities keep ~16 significant bits instead of 8.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        float pl[8] = {sacc[2 * kk][0], sacc[2 * kk][1], sacc[2 * kk][2], sacc[2 * kk][3],
-                       sacc[2 * kk + 1][0], sacc[2 * kk + 1][1], sacc[2 * kk + 1][2], sacc[2 * kk + 1][3]};
-        const uint4 pb = pack(pl, T());
+        float ph[8], pl[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[i] = Elem<T>::round(sacc[2 * kk][i]);
+          ph[4 + i] = Elem<T>::round(sacc[2 * kk + 1][i]);
+          pl[i] = sacc[2 * kk][i] - ph[i];
+          pl[4 + i] = sacc[2 * kk + 1][i] - ph[4 + i];
+        }
+        const uint4 pbh = pack(ph, T()), pbl = pack(pl, T());
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const T* vrow = &vt[16 * dt + lr][0];
           uint2 lo2 = *reinterpret_cast<const uint2*>(vrow + 32 * kk + 4 * lg);
           uint2 hi2 = *reinterpret_cast<const uint2*>(vrow + 32 * kk + 16 + 4 * lg);
-          mma_frag(oacc[dt], make_uint4(lo2.x, lo2.y, hi2.x, hi2.y), pb, T());
+          const uint4 av = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+          mma_frag(oacc[dt], av, pbh, T());
+          mma_frag(oacc[dt], av, pbl, T());
         }
       }
     } else {
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnParams p) {
   float* op = p.part_o + ((sh * p.n_chunks + c) * QT + w) * ofrag;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<floatx4*>(op + (dt * kWave + lane) * 4) = oacc[dt];
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
     int old = atomicAdd(p.counters + sh, 1);
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnParams p) {
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (tid == 0) p.counters[sh] = 0;
 
   float M = -INFINITY;

@@ -40,9 +40,18 @@ __device__ __forceinline__ void top_xor_merge(float& v1, int& i1, float& v2, int
   }
 }
 
+// How each epilogue's GEMM reads its A operand (fixed at compile time).
+template <int EPI>
+struct AModeOf {
+  static constexpr int value = EPI == EPI_FC ? A_TAPS
+                               : (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LMHEAD) ? A_NORMED
+                                                                                            : A_PLAIN;
+};
+
 template <typename T, int MT, int EPI>
 __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
   using C = GemmCfg<T>;
+  constexpr int AM = AModeOf<EPI>::value;
   constexpr int E = C::E, U = C::U, KI = C::KI;
   constexpr int ROWS = 16 * MT;
   constexpr int LDT = kTileN + 4;
@@ -86,8 +95,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
     int r = row0 + 16 * mt + lr;
     r = r < p.M ? r : p.M - 1;
     int xr = p.a_rowmap_bm1 > 0 ? (r / p.a_rowmap_bm1) * (p.a_rowmap_bm1 + 1) + 1 + r % p.a_rowmap_bm1 : r;
-    aoff[mt] = p.a_mode == A_TAPS ? (int64_t)r * p.tap_stride : (int64_t)xr * p.lda;
-    ainv[mt] = p.a_mode == A_NORMED ? p.a_inv[xr] : 1.0f;
+    aoff[mt] = AM == A_TAPS ? (int64_t)r * p.tap_stride : (int64_t)xr * p.lda;
+    ainv[mt] = AM == A_NORMED ? p.a_inv[xr] : 1.0f;
   }
   const T* abase = static_cast<const T*>(p.a);
 
@@ -102,7 +111,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
 
   auto load_a = [&](int it, uint4 (&a)[MT][U], uint4 (&g)[U]) {
     const int k = it * KI + lane_k;
-    if (p.a_mode == A_TAPS) {
+    if constexpr (AM == A_TAPS) {
       // An iteration's KI columns never straddle two planes (hidden % KI == 0).
       const int plane = (it * KI) / p.tap_h;
       const T* tp = static_cast<const T*>(p.taps[plane]) + (k - plane * p.tap_h);
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) a[mt][u] = ldg16(abase + aoff[mt] + k + u * E);
     }
-    if (p.a_mode == A_NORMED) {
+    if constexpr (AM == A_NORMED) {
 #pragma unroll
       for (int u = 0; u < U; ++u) g[u] = ldg16(static_cast<const T*>(p.a_gain) + k + u * E);
     }
@@ -141,11 +150,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float gf[E];
-        if (p.a_mode == A_NORMED) unpack(g_c[u], gf, T());
+        if constexpr (AM == A_NORMED) unpack(g_c[u], gf, T());
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           uint4 av = a_c[mt][u];
-          if (p.a_mode == A_NORMED) {
+          if constexpr (AM == A_NORMED) {
             float xf[E];
             unpack(av, xf, T());
 #pragma unroll
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         *reinterpret_cast<floatx4*>(mine + ((mt * 2 + nt) * kWave + lane) * 4) = acc[mt][nt];
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0) {
       int old = atomicAdd(p.counters + tile_id, 1);
@@ -186,18 +195,33 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float* src = p.partials + ((s2 * ntile_total + tile_id) * 4 + w) * frag_stride;
+    // Loads of four splits are issued together, then added in split order.
+    constexpr int SB = 4;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      floatx4 v[SB][MT][2];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int i = 0; i < SB; ++i) {
+        const int s2 = s0 + i < S ? s0 + i : S - 1;
+        const float* src = p.partials + ((s2 * ntile_total + tile_id) * 4 + w) * frag_stride;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] += *reinterpret_cast<const floatx4*>(src + ((mt * 2 + nt) * kWave + lane) * 4);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            v[i][mt][nt] = *reinterpret_cast<const floatx4*>(src + ((mt * 2 + nt) * kWave + lane) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < SB; ++i)
+        if (s0 + i < S) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] += v[i][mt][nt];
+        }
     }
     if (tid == 0) p.counters[tile_id] = 0;   // every split has arrived: reset for the next use
   }
@@ -395,7 +419,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
 
   // ---------------- second level: per-row statistics over all column tiles
   if constexpr (EPI == EPI_RESID || EPI == EPI_LMHEAD) {
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0) {
       int old = atomicAdd(p.counters2 + mg, 1);
@@ -403,7 +427,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gemm(const GemmParams p) {
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid == 0) p.counters2[mg] = 0;
     if constexpr (EPI == EPI_RESID) {
       for (int rl = tid; rl < ROWS; rl += kBlockThreads) {

@@ -24,7 +24,7 @@ def to_np(t):
 
 
 class RoundCase:
-    def __init__(self, p, ctx=None, rows=None, device="cuda", permute_pages=True, seed=None, bench_only=False):
+    def __init__(self, p, ctx=None, rows=None, device="cuda", permute_pages=True, seed=None, weights=None):
         self.p = p
         self.device = device
         seed = p.seed if seed is None else seed
@@ -34,7 +34,7 @@ class RoundCase:
         self.rows = list(rows) if rows is not None else wl.round_rows(p, seed)
         self.rows = [min(r, c) for r, c in zip(self.rows, self.ctx)]
         self.dtype = torch.float32 if p.dtype == "f32" else torch.bfloat16
-        self.W = wl.make_weights(p, device=device, seed=seed)
+        self.W = weights if weights is not None else wl.make_weights(p, device=device, seed=seed)
         R = sum(self.rows)
         self.R = R
         self.taps = wl.make_taps(p, R, device=device, seed=seed)
