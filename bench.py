@@ -43,24 +43,26 @@ def kernel_costs(p, ctx, rows):
     R = sum(rows)
     M, Mm = S * B, S * (B - 1)
     k = {}
-    k["fuse_fc_gemm"] = dict(bytes=(h * n * h + R * n * h) * es + R * h * 4, flops=2 * R * n * h * h)
-    k["fuse_rownorm"] = dict(bytes=R * h * 4 + R * h * es + h * es, flops=3 * R * h)
-    k["inject_kv_gemm"] = dict(bytes=(L * 2 * nkv * h + R * h + L * 2 * R * nkv) * es, flops=2 * R * h * L * 2 * nkv)
+    k["fuse_fc_gemm"] = dict(bytes=(h * n * h + R * n * h) * es + R * h * 8, flops=2 * R * n * h * h)
+    k["fuse_rownorm"] = dict(bytes=R * h * 8 + R * h * es + h * es, flops=3 * R * h)
+    k["inject_kv_gemm"] = dict(bytes=(L * 2 * nkv * h + R * h) * es + L * 2 * R * nkv * 8, flops=2 * R * h * L * 2 * nkv)
+    k["inject_kv_finish"] = dict(bytes=L * 2 * R * nkv * (8 + es) + L * d * es, flops=6 * L * R * nkv)
     k["embed"] = dict(bytes=2 * M * h * es, flops=2 * M * h)
-    k["qkv_gemm"] = dict(bytes=((nq + 2 * nkv) * h + M * h + M * (nq + 2 * nkv)) * es, flops=2 * M * h * (nq + 2 * nkv))
+    k["qkv_gemm"] = dict(bytes=((nq + 2 * nkv) * h + M * h) * es + M * (nq + 2 * nkv) * 8, flops=2 * M * h * (nq + 2 * nkv))
     for kind, sel in (("attention_full", lambda w: w == 0), ("attention_sliding", lambda w: w > 0)):
         layers = [w for w in p.layer_window[:L] if sel(w)]
         if not layers:
             continue
         wdw = layers[0]
         keys = [min(c, wdw) if wdw > 0 else c for c in ctx]
-        k[kind] = dict(bytes=(sum(keys) * 2 * nkv + M * (nq + 2 * nkv) + M * nq) * es,
+        k[kind] = dict(bytes=(sum(keys) * 2 * nkv + M * nq) * es + M * (nq + 2 * nkv) * 8,
                        flops=sum(4 * p.n_q_heads * B * d * (kk + B) for kk in keys),
                        launches=len(layers))
     k["o_proj_gemm"] = dict(bytes=(h * nq + M * nq + 2 * M * h) * es, flops=2 * M * nq * h)
     k["gate_up_gemm"] = dict(bytes=(2 * I * h + M * h + M * I) * es, flops=4 * M * h * I)
     k["down_gemm"] = dict(bytes=(h * I + M * I + 2 * M * h) * es, flops=2 * M * I * h)
-    k["lm_head_argmax_gemm"] = dict(bytes=(V * h + Mm * h) * es + Mm * 4, flops=2 * Mm * h * V)
+    k["lm_head_gemm"] = dict(bytes=(V * h + Mm * h) * es + Mm * ((V + 31) // 32) * 16, flops=2 * Mm * h * V)
+    k["argmax_final"] = dict(bytes=Mm * ((V + 31) // 32) * 16 + Mm * 12, flops=0)
     k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
     per_layer = ["qkv_gemm", "o_proj_gemm", "gate_up_gemm", "down_gemm"]
     for name in per_layer:

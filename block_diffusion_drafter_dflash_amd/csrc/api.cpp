@@ -20,9 +20,7 @@ namespace {
 
 thread_local std::string g_create_error = "";
 
-constexpr int64_t kSplitCounters = 1 << 16;   // per-tile split-K counters (shared by all kernels)
-constexpr int64_t kRowCounters = 1 << 12;     // per-row-group counters
-constexpr int64_t kCounterInts = kSplitCounters + kRowCounters;
+constexpr int64_t kCounterInts = 1 << 16;     // attention chunk counters (self-resetting)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -83,23 +81,18 @@ static int fail(dflash* h, int code, const char* fmt, ...) {
 namespace {
 
 struct GemmPlan {
-  int mt, mgroups, n_tiles, splits, iters;
-  size_t partial_bytes;
+  int mt, mgroups, n_tiles, iters;
 };
 
-GemmPlan plan_gemm(int dtype, int M, int n_tiles, int K) {
+// Rows are processed in groups of 16 * mt (mt = 1 or 2); every workgroup owns one
+// column tile over the whole K, so the per-row arithmetic never depends on M.
+GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K) {
   GemmPlan g;
-  g.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  g.mt = M <= 16 ? 1 : 2;
   g.mgroups = (M + 16 * g.mt - 1) / (16 * g.mt);
-  g.n_tiles = n_tiles;
+  const int cols = gemm_tile_cols(epi);
+  g.n_tiles = (N + cols - 1) / cols;
   g.iters = K / gemm_k_per_iter(dtype);
-  // The split depends on the weight shape only, never on M: each row's sums are then
-  // formed in the same order whatever the batch, so batched rows equal solo rows bit
-  // for bit.
-  const int target_wg = 1024;
-  g.splits = 1;
-  while ((int64_t)n_tiles * g.splits * 2 <= target_wg && g.iters / (g.splits * 2) >= 4) g.splits *= 2;
-  g.partial_bytes = g.splits > 1 ? (size_t)g.splits * g.mgroups * 16 * g.mt * n_tiles * 128 * 4 : 0;
   return g;
 }
 
@@ -130,32 +123,32 @@ struct Region {
 
 struct FuseLayout {
   GemmPlan g;
-  size_t partials, y, ssq, end;
+  size_t y, ssq, end;
 };
 FuseLayout layout_fuse(const dflash& h, int R) {
   FuseLayout L;
   const auto& c = h.cfg;
-  L.g = plan_gemm(c.dtype, R, c.hidden / 128, c.n_taps * c.hidden);
+  L.g = plan_gemm(c.dtype, EPI_FC, R, c.hidden, c.n_taps * c.hidden);
   Region r;
   r.take(kCounterInts * 4);
-  L.partials = r.take(L.g.partial_bytes);
-  L.y = r.take((size_t)R * c.hidden * 4);
-  L.ssq = r.take((size_t)R * L.g.n_tiles * 4);
+  L.y = r.take((size_t)R * c.hidden * 8);
+  L.ssq = r.take((size_t)R * L.g.n_tiles * 8);
   L.end = r.off;
   return L;
 }
 
 struct InjectLayout {
   GemmPlan g;
-  size_t partials, end;
+  size_t raw, end;
 };
 InjectLayout layout_inject(const dflash& h, int R) {
   InjectLayout L;
   const auto& c = h.cfg;
-  L.g = plan_gemm(c.dtype, R, c.n_layers * 2 * h.nkv() / 128, c.hidden);
+  const int N = c.n_layers * 2 * h.nkv();
+  L.g = plan_gemm(c.dtype, EPI_INJECT, R, N, c.hidden);
   Region r;
   r.take(kCounterInts * 4);
-  L.partials = r.take(L.g.partial_bytes);
+  L.raw = r.take((size_t)R * N * 8);
   L.end = r.off;
   return L;
 }
@@ -163,21 +156,20 @@ InjectLayout layout_inject(const dflash& h, int R) {
 struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
-  size_t x, inv_in, inv_post, q, kb, vb, o_buf, m, partials, ssq, part_o, part_ml, tile_res, end;
+  int ssq_ld;
+  size_t x, ssq_a, ssq_b, qkv_raw, o_buf, m, part_o, part_ml, tile_res, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
   const auto& c = h.cfg;
   const int M = S * c.block_size, Mm = S * (c.block_size - 1);
   const int es = h.esize();
-  L.qkv = plan_gemm(c.dtype, M, (h.nq() + 2 * h.nkv()) / 128, c.hidden);
-  L.o = plan_gemm(c.dtype, M, c.hidden / 128, h.nq());
-  L.gu = plan_gemm(c.dtype, M, c.intermediate / 64, c.hidden);
-  L.down = plan_gemm(c.dtype, M, c.hidden / 128, c.intermediate);
-  L.lm = plan_gemm(c.dtype, Mm, (c.vocab + 127) / 128, c.hidden);
-  L.lm.splits = 1;
-  L.lm.partial_bytes = 0;
-  size_t part = std::max({L.qkv.partial_bytes, L.o.partial_bytes, L.gu.partial_bytes, L.down.partial_bytes});
+  L.qkv = plan_gemm(c.dtype, EPI_QKV, M, h.nq() + 2 * h.nkv(), c.hidden);
+  L.o = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, h.nq());
+  L.gu = plan_gemm(c.dtype, EPI_SWIGLU, M, 2 * c.intermediate, c.hidden);
+  L.down = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, c.intermediate);
+  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, Mm, c.vocab, c.hidden);
+  L.ssq_ld = L.o.n_tiles;            // sums of squares per 16-column tile of the residual stream
   size_t po = 0, pml = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     L.attn.push_back(plan_attn(c, S, max_ctx, c.layer_window[l]));
@@ -187,24 +179,16 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   Region r;
   r.take(kCounterInts * 4);
   L.x = r.take((size_t)M * c.hidden * es);
-  L.inv_in = r.take((size_t)M * 4);
-  L.inv_post = r.take((size_t)M * 4);
-  L.q = r.take((size_t)M * h.nq() * es);
-  L.kb = r.take((size_t)M * h.nkv() * es);
-  L.vb = r.take((size_t)M * h.nkv() * es);
+  L.ssq_a = r.take((size_t)M * L.ssq_ld * 8);
+  L.ssq_b = r.take((size_t)M * L.ssq_ld * 8);
+  L.qkv_raw = r.take((size_t)M * (h.nq() + 2 * h.nkv()) * 8);
   L.o_buf = r.take((size_t)M * h.nq() * es);
   L.m = r.take((size_t)M * c.intermediate * es);
-  L.partials = r.take(part);
-  L.ssq = r.take((size_t)M * (c.hidden / 128) * 4);
   L.part_o = r.take(po);
   L.part_ml = r.take(pml);
-  L.tile_res = r.take((size_t)L.lm.mgroups * 16 * L.lm.mt * L.lm.n_tiles * 16);
+  L.tile_res = r.take((size_t)Mm * L.lm.n_tiles * 16);
   L.end = r.off;
   return L;
-}
-
-bool counters_fit(const GemmPlan& g) {
-  return (int64_t)g.mgroups * g.n_tiles <= kSplitCounters && g.mgroups <= kRowCounters;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -396,18 +380,15 @@ static int check_ws(dflash* h, void* ws, size_t ws_bytes, size_t need) {
   return DFLASH_OK;
 }
 
-static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K, char* ws, size_t partials_off) {
+static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
   GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.M = M;
   p.N = N;
   p.K = K;
   p.n_tiles = g.n_tiles;
-  p.splits = g.splits;
+  p.mgroups = g.mgroups;
   p.iters = g.iters;
-  p.partials = reinterpret_cast<float*>(ws + partials_off);
-  p.counters = reinterpret_cast<int*>(ws);
-  p.counters2 = reinterpret_cast<int*>(ws) + kSplitCounters;
   return p;
 }
 
@@ -428,21 +409,20 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   FuseLayout L = layout_fuse(*h, n_rows);
   int rc = check_ws(h, ws, ws_bytes, L.end);
   if (rc) return rc;
-  if (!counters_fit(L.g)) return fail(h, DFLASH_ERR_CAPACITY, "n_rows %d exceeds the counter block", n_rows);
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
-  GemmParams p = gemm_base(L.g, n_rows, c.hidden, c.n_taps * c.hidden, W, L.partials);
-  p.a_mode = A_TAPS;
+  GemmParams p = gemm_base(L.g, n_rows, c.hidden, c.n_taps * c.hidden);
   for (int t = 0; t < c.n_taps; ++t) p.taps[t] = tap_planes[t];
   p.tap_h = c.hidden;
   p.tap_stride = plane_row_stride;
   p.w0 = h->w.fc;
-  p.y_out = reinterpret_cast<float*>(W + L.y);
-  p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
+  p.y_out = reinterpret_cast<double*>(W + L.y);
+  p.ssq_out = reinterpret_cast<double*>(W + L.ssq);
+  p.ssq_ld = L.g.n_tiles;
   hipError_t e;
   {
     ProfScope ps(h, "fuse_fc_gemm", st);
-    e = launch_gemm(c.dtype, EPI_FC, p, L.g.mt, L.g.mgroups, st);
+    e = launch_gemm(c.dtype, EPI_FC, p, L.g.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
   RowNormParams rn;
@@ -450,7 +430,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   rn.hidden = c.hidden;
   rn.n_tiles = L.g.n_tiles;
   rn.y = p.y_out;
-  rn.ssq_part = p.ssq_part;
+  rn.ssq_part = p.ssq_out;
   rn.gain = h->w.hidden_norm;
   rn.out = fused_out;
   rn.eps = c.rms_eps;
@@ -485,37 +465,50 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   InjectLayout L = layout_inject(*h, n_rows);
   rc = check_ws(h, ws, ws_bytes, L.end);
   if (rc) return rc;
-  if (!counters_fit(L.g)) return fail(h, DFLASH_ERR_CAPACITY, "n_rows %d exceeds the counter block", n_rows);
   char* W = static_cast<char*>(ws);
-  GemmParams p = gemm_base(L.g, n_rows, c.n_layers * 2 * h->nkv(), c.hidden, W, L.partials);
-  p.a_mode = A_PLAIN;
+  hipStream_t st = (hipStream_t)stream;
+  const int N = c.n_layers * 2 * h->nkv();
+  GemmParams p = gemm_base(L.g, n_rows, N, c.hidden);
   p.a = fused;
   p.lda = c.hidden;
   p.nkv = h->nkv();
   for (int l = 0; l < c.n_layers; ++l) {
     p.wk_l[l] = h->w.wk[l];
     p.wv_l[l] = h->w.wv[l];
-    p.kn_l[l] = h->w.k_norm[l];
-    p.kpool_l[l] = kv->k_pool[l];
-    p.vpool_l[l] = kv->v_pool[l];
   }
-  p.head_dim = c.head_dim;
-  p.theta = c.rope_theta;
-  p.eps = c.rms_eps;
-  p.row_stream = row_stream;
-  p.row_pos = row_pos;
-  p.page_table = kv->page_table;
-  p.pages_per_stream = kv->pages_per_stream;
-  p.page_size = c.page_size;
-  p.pool_pages = c.pool_pages;
-  p.max_streams = c.max_streams;
-  p.n_kv_heads = c.n_kv_heads;
+  p.y_out = reinterpret_cast<double*>(W + L.raw);
   hipError_t e;
   {
-    ProfScope ps(h, "inject_kv_gemm", (hipStream_t)stream);
-    e = launch_gemm(c.dtype, EPI_INJECT, p, L.g.mt, L.g.mgroups, (hipStream_t)stream);
+    ProfScope ps(h, "inject_kv_gemm", st);
+    e = launch_gemm(c.dtype, EPI_INJECT, p, L.g.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
+  KvFinishParams kf;
+  std::memset(&kf, 0, sizeof kf);
+  kf.R = n_rows;
+  kf.n_layers = c.n_layers;
+  kf.n_kv_heads = c.n_kv_heads;
+  kf.head_dim = c.head_dim;
+  kf.raw = p.y_out;
+  kf.row_stream = row_stream;
+  kf.row_pos = row_pos;
+  for (int l = 0; l < c.n_layers; ++l) {
+    kf.kn_l[l] = h->w.k_norm[l];
+    kf.kpool_l[l] = kv->k_pool[l];
+    kf.vpool_l[l] = kv->v_pool[l];
+  }
+  kf.page_table = kv->page_table;
+  kf.pages_per_stream = kv->pages_per_stream;
+  kf.page_size = c.page_size;
+  kf.pool_pages = c.pool_pages;
+  kf.max_streams = c.max_streams;
+  kf.theta = c.rope_theta;
+  kf.eps = c.rms_eps;
+  {
+    ProfScope ps(h, "inject_kv_finish", st);
+    e = launch_kv_finish(c.dtype, kf, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject finish: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 
@@ -539,16 +532,15 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   DraftLayout L = layout_draft(*h, n_streams, max_ctx_len);
   rc = check_ws(h, ws, ws_bytes, L.end);
   if (rc) return rc;
-  for (const GemmPlan* g : {&L.qkv, &L.o, &L.gu, &L.down, &L.lm})
-    if (!counters_fit(*g)) return fail(h, DFLASH_ERR_CAPACITY, "n_streams %d exceeds the counter block", n_streams);
-  if ((int64_t)n_streams * c.n_kv_heads > kSplitCounters) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
+  if ((int64_t)n_streams * c.n_kv_heads > kCounterInts) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
 
   const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   void* X = W + L.x;
-  float* inv_in = reinterpret_cast<float*>(W + L.inv_in);
-  float* inv_post = reinterpret_cast<float*>(W + L.inv_post);
+  double* ssq_a = reinterpret_cast<double*>(W + L.ssq_a);   // feeds in_norm and the final norm
+  double* ssq_b = reinterpret_cast<double*>(W + L.ssq_b);   // feeds post_norm
+  double* qkv_raw = reinterpret_cast<double*>(W + L.qkv_raw);
   hipError_t e;
 
   EmbedParams ep;
@@ -560,41 +552,34 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   ep.anchor = anchor;
   ep.embed = h->w.embed;
   ep.x = X;
-  ep.inv = inv_in;
-  ep.eps = c.rms_eps;
+  ep.ssq = ssq_a;
   {
     ProfScope ps(h, "embed", st);
     e = launch_embed(c.dtype, ep, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "embed: %s", hipGetErrorString(e));
 
+  // embed leaves one sum of squares per row (row stride 1); the GEMMs leave one per tile
+  int ssq_parts = 1, ssq_ld_a = 1;
   for (int l = 0; l < c.n_layers; ++l) {
-    // a = round(RMSNorm(X) * in_norm); q, k, v with per-head norms and RoPE
-    GemmParams p = gemm_base(L.qkv, M, h->nq() + 2 * h->nkv(), c.hidden, W, L.partials);
-    p.a_mode = A_NORMED;
+    // raw q | k | v of round(RMSNorm(X) * in_norm); norms and RoPE follow in attention
+    GemmParams p = gemm_base(L.qkv, M, h->nq() + 2 * h->nkv(), c.hidden);
     p.a = X;
     p.lda = c.hidden;
-    p.a_inv = inv_in;
+    p.a_ssq = ssq_a;
+    p.a_ssq_parts = ssq_parts;
+    p.a_ssq_ld = ssq_ld_a;
     p.a_gain = h->w.in_norm[l];
+    p.eps = c.rms_eps;
     p.w0 = h->w.wq[l];
     p.w1 = h->w.wk[l];
     p.w2 = h->w.wv[l];
     p.nq = h->nq();
     p.nkv = h->nkv();
-    p.q_out = W + L.q;
-    p.k_out = W + L.kb;
-    p.v_out = W + L.vb;
-    p.qn_gain = h->w.q_norm[l];
-    p.kn_gain = h->w.k_norm[l];
-    p.head_dim = c.head_dim;
-    p.theta = c.rope_theta;
-    p.eps = c.rms_eps;
-    p.ctx_len = ctx_len;
-    p.max_ctx = max_ctx_len;
-    p.block = B;
+    p.y_out = qkv_raw;
     {
       ProfScope ps(h, "qkv_gemm", st);
-      e = launch_gemm(c.dtype, EPI_QKV, p, L.qkv.mt, L.qkv.mgroups, st);
+      e = launch_gemm(c.dtype, EPI_QKV, p, L.qkv.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv: %s", l, hipGetErrorString(e));
 
@@ -610,9 +595,14 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     ap.n_chunks = L.attn[l].n_chunks;
     ap.max_ctx = max_ctx_len;
     ap.ctx_len = ctx_len;
-    ap.q = W + L.q;
-    ap.kb = W + L.kb;
-    ap.vb = W + L.vb;
+    ap.qkv_raw = qkv_raw;
+    ap.ld_raw = h->nq() + 2 * h->nkv();
+    ap.nq = h->nq();
+    ap.nkv = h->nkv();
+    ap.q_norm = h->w.q_norm[l];
+    ap.k_norm = h->w.k_norm[l];
+    ap.theta = c.rope_theta;
+    ap.eps = c.rms_eps;
     ap.kpool = kv->k_pool[l];
     ap.vpool = kv->v_pool[l];
     ap.page_table = kv->page_table;
@@ -622,7 +612,6 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     ap.o = W + L.o_buf;
     ap.part_o = reinterpret_cast<float*>(W + L.part_o);
     ap.part_ml = reinterpret_cast<float*>(W + L.part_ml);
-    ap.counters = reinterpret_cast<int*>(W);
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     {
       ProfScope ps(h, c.layer_window[l] > 0 ? "attention_sliding" : "attention_full", st);
@@ -630,74 +619,79 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d attention: %s", l, hipGetErrorString(e));
 
-    // X += wo . o   (residual add 1), then 1 / rms for the post-attention norm
-    p = gemm_base(L.o, M, c.hidden, h->nq(), W, L.partials);
-    p.a_mode = A_PLAIN;
+    // X += wo . o   (residual add 1)
+    p = gemm_base(L.o, M, c.hidden, h->nq());
     p.a = W + L.o_buf;
     p.lda = h->nq();
     p.w0 = h->w.wo[l];
     p.x_io = X;
-    p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
-    p.inv_out = inv_post;
-    p.eps = c.rms_eps;
+    p.ssq_out = ssq_b;
+    p.ssq_ld = L.ssq_ld;
     {
       ProfScope ps(h, "o_proj_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RESID, p, L.o.mt, L.o.mgroups, st);
+      e = launch_gemm(c.dtype, EPI_RESID, p, L.o.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d o_proj: %s", l, hipGetErrorString(e));
 
-    // m = round(silu(w_gate . b) * (w_up . b)), b = round(RMSNorm(X) * post_norm)
-    p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden, W, L.partials);
-    p.a_mode = A_NORMED;
+    // m = round(silu(w_gate . b) * (w_up . b)),  b = round(RMSNorm(X) * post_norm)
+    p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden);
     p.a = X;
     p.lda = c.hidden;
-    p.a_inv = inv_post;
+    p.a_ssq = ssq_b;
+    p.a_ssq_parts = L.ssq_ld;
+    p.a_ssq_ld = L.ssq_ld;
     p.a_gain = h->w.post_norm[l];
+    p.eps = c.rms_eps;
     p.w0 = h->w.w_gate[l];
     p.w1 = h->w.w_up[l];
     p.m_out = W + L.m;
     p.ld_out = c.intermediate;
     {
       ProfScope ps(h, "gate_up_gemm", st);
-      e = launch_gemm(c.dtype, EPI_SWIGLU, p, L.gu.mt, L.gu.mgroups, st);
+      e = launch_gemm(c.dtype, EPI_SWIGLU, p, L.gu.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d gate/up: %s", l, hipGetErrorString(e));
 
-    // X += w_down . m   (residual add 2), then 1 / rms for the next norm
-    p = gemm_base(L.down, M, c.hidden, c.intermediate, W, L.partials);
-    p.a_mode = A_PLAIN;
+    // X += w_down . m   (residual add 2)
+    p = gemm_base(L.down, M, c.hidden, c.intermediate);
     p.a = W + L.m;
     p.lda = c.intermediate;
     p.w0 = h->w.w_down[l];
     p.x_io = X;
-    p.ssq_part = reinterpret_cast<float*>(W + L.ssq);
-    p.inv_out = inv_in;
-    p.eps = c.rms_eps;
+    p.ssq_out = ssq_a;
+    p.ssq_ld = L.ssq_ld;
     {
       ProfScope ps(h, "down_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RESID, p, L.down.mt, L.down.mgroups, st);
+      e = launch_gemm(c.dtype, EPI_RESID, p, L.down.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d down: %s", l, hipGetErrorString(e));
+    ssq_parts = L.ssq_ld;
+    ssq_ld_a = L.ssq_ld;
   }
 
   // Final norm of the mask rows, LM head, argmax (lowest index on a tie).
-  GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden, W, 0);
-  p.a_mode = A_NORMED;
+  GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden);
   p.a = X;
   p.lda = c.hidden;
-  p.a_inv = inv_in;
+  p.a_ssq = ssq_a;
+  p.a_ssq_parts = ssq_parts;
+  p.a_ssq_ld = ssq_ld_a;
   p.a_gain = h->w.norm;
+  p.eps = c.rms_eps;
   p.a_rowmap_bm1 = B - 1;
   p.w0 = h->w.lm_head;
-  p.logits_out = logits_out;
+  p.logits_out = static_cast<float*>(logits_out);
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
-  p.draft_out = draft_out;
-  p.top2_out = top2_out;
   {
-    ProfScope ps(h, "lm_head_argmax_gemm", st);
-    e = launch_gemm(c.dtype, EPI_LMHEAD, p, L.lm.mt, L.lm.mgroups, st);
+    ProfScope ps(h, "lm_head_gemm", st);
+    e = launch_gemm(c.dtype, EPI_LMHEAD, p, L.lm.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "lm head: %s", hipGetErrorString(e));
+  {
+    ProfScope ps(h, "argmax_final", st);
+    e = launch_argmax_final(p.tile_res, L.lm.n_tiles, Mm, draft_out, top2_out, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "argmax: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 

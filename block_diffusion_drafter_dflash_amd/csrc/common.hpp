@@ -10,20 +10,39 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kTileN = 128;   // output columns per GEMM workgroup
-constexpr int kBlockThreads = 256;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t u16) {
   return __uint_as_float(u16 << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even (the hardware conversion).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two fp32 values -> two bf16 in one 32-bit word (low half first), one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const bf16x2_t v = __builtin_convertvector((float2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// float64 -> fp32 rounded to odd: the truncation toward zero with its last bit set
+// when inexact. Rounding that result to bf16 (to nearest, ties to even) equals
+// rounding the float64 value to bf16 directly, because fp32 keeps more than two
+// extra bits.
+__device__ __forceinline__ float f32_round_odd(double d) {
+  float f = (float)d;
+  if ((double)f != d && __builtin_isfinite(f)) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs((double)f) > fabs(d)) u -= 1u;
+    u |= 1u;
+    f = __uint_as_float(u);
+  }
+  return f;
+}
+__device__ __forceinline__ uint32_t bf16_from_double(double d) { return f32_to_bf16(f32_round_odd(d)); }
 
 // Element traits: E elements per 16-byte fragment, KF = k-elements one 16-byte-per-lane
 // fragment covers across the four 16-lane groups of a wave.
@@ -33,12 +52,16 @@ template <> struct Elem<float> {
   static constexpr int KF = 16;
   __device__ static __forceinline__ float load1(const float* p) { return *p; }
   __device__ static __forceinline__ float round(float x) { return x; }
+  __device__ static __forceinline__ float round_d(double x) { return (float)x; }
+  __device__ static __forceinline__ void store_d(float* p, double x) { *p = (float)x; }
 };
 template <> struct Elem<bf16_t> {
   static constexpr int E = 8;
   static constexpr int KF = 32;
   __device__ static __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(*p); }
   __device__ static __forceinline__ float round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+  __device__ static __forceinline__ float round_d(double x) { return bf16_to_f32(bf16_from_double(x)); }
+  __device__ static __forceinline__ void store_d(bf16_t* p, double x) { *p = (bf16_t)bf16_from_double(x); }
 };
 
 // Unpack a 16-byte fragment into floats.
@@ -58,10 +81,20 @@ __device__ __forceinline__ uint4 pack(const float* in, float) {
                     __float_as_uint(in[3]));
 }
 __device__ __forceinline__ uint4 pack(const float* in, bf16_t) {
-  return make_uint4(f32_to_bf16(in[0]) | (f32_to_bf16(in[1]) << 16),
-                    f32_to_bf16(in[2]) | (f32_to_bf16(in[3]) << 16),
-                    f32_to_bf16(in[4]) | (f32_to_bf16(in[5]) << 16),
-                    f32_to_bf16(in[6]) | (f32_to_bf16(in[7]) << 16));
+  return make_uint4(f32x2_to_bf16x2(in[0], in[1]), f32x2_to_bf16x2(in[2], in[3]),
+                    f32x2_to_bf16x2(in[4], in[5]), f32x2_to_bf16x2(in[6], in[7]));
+}
+
+// Pack float64 values into a 16-byte fragment, each rounded once to the element type.
+__device__ __forceinline__ uint4 pack_d(const double* in, float) {
+  return make_uint4(__float_as_uint((float)in[0]), __float_as_uint((float)in[1]), __float_as_uint((float)in[2]),
+                    __float_as_uint((float)in[3]));
+}
+__device__ __forceinline__ uint4 pack_d(const double* in, bf16_t) {
+  return make_uint4(f32x2_to_bf16x2(f32_round_odd(in[0]), f32_round_odd(in[1])),
+                    f32x2_to_bf16x2(f32_round_odd(in[2]), f32_round_odd(in[3])),
+                    f32x2_to_bf16x2(f32_round_odd(in[4]), f32_round_odd(in[5])),
+                    f32x2_to_bf16x2(f32_round_odd(in[6]), f32_round_odd(in[7])));
 }
 
 // acc[16x16] += A_frag x B_frag over one fragment's KF k-elements.

@@ -14,17 +14,18 @@ constexpr int kMaxTaps = 8;
 // One skinny GEMM launch. Every field not used by the epilogue stays zero.
 struct GemmParams {
   int M, N, K;          // rows, output columns (all segments), reduction length
-  int n_tiles;          // 128-column tiles
-  int splits;           // K splits (workgroups per tile)
+  int n_tiles;          // column tiles (16 or 32 columns each)
+  int mgroups;          // row groups of 16 * MT rows
   int iters;            // K / k-elements per iteration
   // A operand
-  int a_mode;
   const void* a;        // A_PLAIN / A_NORMED: [rows, lda]
   int64_t lda;
-  const float* a_inv;   // A_NORMED: 1 / rms per source row
-  const void* a_gain;   // A_NORMED: [K]
   int a_rowmap_bm1;     // > 0: logical row r reads source row (r / bm1) * (bm1 + 1) + 1 + r % bm1
-  const void* taps[kMaxTaps];
+  const double* a_ssq;  // A_NORMED: per-row sum-of-squares partials of the source rows
+  int a_ssq_parts, a_ssq_ld;
+  const void* a_gain;   // A_NORMED: [K]
+  float eps;
+  const void* taps[kMaxTaps];   // A_TAPS
   int tap_h;
   int64_t tap_stride;
   // B operand
@@ -34,35 +35,15 @@ struct GemmParams {
   int nq, nkv;          // n_q*d, n_kv*d
   const void* wk_l[kMaxLayers];
   const void* wv_l[kMaxLayers];
-  // split-K and row statistics
-  float* partials;
-  int* counters;        // [mgroups * n_tiles]
-  int* counters2;       // [mgroups]
-  float* ssq_part;      // [rows, n_tiles]
-  float eps;
   // epilogue outputs
-  float* y_out;         // EPI_FC: [M, N] fp32
+  double* y_out;        // EPI_FC: y [M, N]; EPI_QKV / EPI_INJECT: raw projections [M, N] (float64)
+  double* ssq_out;      // EPI_FC / EPI_RESID: [M, ssq_ld] per-tile sums of squares
+  int ssq_ld;
   void* x_io;           // EPI_RESID: residual stream [M, N], updated in place
-  float* inv_out;       // EPI_RESID: [M]
-  void* m_out;          // EPI_SWIGLU
+  void* m_out;          // EPI_SWIGLU: [M, ld_out]
   int ld_out;
-  void *q_out, *k_out, *v_out;      // EPI_QKV
-  const void *qn_gain, *kn_gain;    // EPI_QKV
-  const void* kn_l[kMaxLayers];     // EPI_INJECT
-  int head_dim;
-  float theta;
-  const int* ctx_len;   // EPI_QKV: positions ctx_len[s] + j
-  int max_ctx, block;
-  const int* row_stream;  // EPI_INJECT
-  const int* row_pos;
-  void* kpool_l[kMaxLayers];
-  void* vpool_l[kMaxLayers];
-  const int* page_table;
-  int pages_per_stream, page_size, pool_pages, max_streams, n_kv_heads;
-  void* logits_out;     // EPI_LMHEAD
-  float* tile_res;      // EPI_LMHEAD: [mgroups, n_tiles, rows] x (v1, i1, v2, -)
-  int* draft_out;
-  float* top2_out;
+  float* logits_out;    // EPI_LMHEAD (nullable), fp32
+  float* tile_res;      // EPI_LMHEAD: [M, n_tiles] x (max, argmax bits, second max, -)
 };
 
 struct AttnParams {
@@ -71,18 +52,32 @@ struct AttnParams {
   int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max reach)
   int max_ctx;
   const int* ctx_len;
-  const void* q;        // [S*B, n_q*d]
-  const void* kb;       // [S*B, n_kv*d]
-  const void* vb;
+  const double* qkv_raw;  // [S*B, ld_raw]: raw q | k | v projections of the block rows
+  int ld_raw, nq, nkv;
+  const void* q_norm;   // [d]
+  const void* k_norm;   // [d]
+  float theta, eps;
   const void* kpool;
   const void* vpool;
   const int* page_table;
   int pages_per_stream, page_size, pool_pages;
   void* o;              // [S*B, n_q*d]
-  float* part_o;        // [S, n_kv, n_chunks, QT, 64 lanes, d/4 dims...] fp32
+  float* part_o;        // [S, n_kv, n_chunks, QT, d/16, 64 lanes, 4] fp32
   float* part_ml;       // [S, n_kv, n_chunks, QT*16, 2]
-  int* counters;        // [S * n_kv]
   float scale_log2;     // log2(e) / sqrt(d)
+};
+
+struct KvFinishParams {
+  int R, n_layers, n_kv_heads, head_dim;
+  const double* raw;    // [R, n_layers * 2 * n_kv * d]: per layer k | v
+  const int* row_stream;
+  const int* row_pos;
+  const void* kn_l[kMaxLayers];
+  void* kpool_l[kMaxLayers];
+  void* vpool_l[kMaxLayers];
+  const int* page_table;
+  int pages_per_stream, page_size, pool_pages, max_streams;
+  float theta, eps;
 };
 
 struct EmbedParams {
@@ -90,14 +85,13 @@ struct EmbedParams {
   const int* anchor;
   const void* embed;
   void* x;              // [S*B, hidden]
-  float* inv;           // [S*B]  1 / rms of each row
-  float eps;
+  double* ssq;          // [S*B]  sum of squares of each row (one part)
 };
 
 struct RowNormParams {
   int R, hidden, n_tiles;
-  const float* y;       // [R, hidden]
-  const float* ssq_part;// [R, n_tiles]
+  const double* y;      // [R, hidden]
+  const double* ssq_part;  // [R, n_tiles]
   const void* gain;
   void* out;            // [R, hidden]
   float eps;
@@ -130,7 +124,11 @@ __host__ __device__ inline int attention_chunk_len(int reach) {
 }
 
 int gemm_k_per_iter(int dtype);
-hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, int mgroups, hipStream_t st);
+int gemm_tile_cols(int epi);
+hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStream_t st);
+hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
+                               hipStream_t st);
+hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnParams& p, hipStream_t st);
 int attention_query_tiles(int group, int block);
 hipError_t launch_embed(int dtype, const EmbedParams& p, hipStream_t st);

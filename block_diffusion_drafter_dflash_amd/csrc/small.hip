@@ -7,8 +7,8 @@ namespace dfl {
 
 // Deterministic sum over a workgroup of 256 threads: butterfly inside each wave,
 // then the four wave sums in wave order.
-__device__ float block_sum_256(float v, float* red) {
-  v = xor_sum(v, kWave);
+__device__ double block_sum_256(double v, double* red) {
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = v;
@@ -17,53 +17,114 @@ __device__ float block_sum_256(float v, float* red) {
 }
 
 // Block rows: X[s*B] = embed[anchor[s]], X[s*B + j] = embed[mask] for j >= 1, and
-// 1 / rms of each row for the first layer's input norm.
+// each row's sum of squares for the first layer's input norm.
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(const EmbedParams p) {
   constexpr int E = Elem<T>::E;
-  __shared__ float red[4];
+  __shared__ double red[4];
   const int r = blockIdx.x;
   const int s = r / p.B, j = r % p.B;
   int tok = j == 0 ? p.anchor[s] : p.mask_token;
   tok = tok < 0 ? 0 : (tok >= p.vocab ? p.vocab - 1 : tok);
   const T* src = static_cast<const T*>(p.embed) + (int64_t)tok * p.hidden;
   T* dst = static_cast<T*>(p.x) + (int64_t)r * p.hidden;
-  float ss = 0.f;
+  double ss = 0.0;
   for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
     uint4 v = ldg16(src + c);
     stg16(dst + c, v);
     float f[E];
     unpack(v, f, T());
 #pragma unroll
-    for (int e = 0; e < E; ++e) ss += f[e] * f[e];
+    for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
   }
   ss = block_sum_256(ss, red);
-  if (threadIdx.x == 0) p.inv[r] = (float)(1.0 / sqrt((double)ss / (double)p.hidden + (double)p.eps));
+  if (threadIdx.x == 0) p.ssq[r] = ss;
+}
+
+// Context K/V of injected rows: K = RoPE_pos(k_norm(raw k)) per kv head, V = raw v,
+// rounded and written to the row's page slot. One workgroup per (row, layer);
+// D/8 consecutive threads own one head (8 dims each).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
+  __shared__ double2 tab[D / 2];
+  const int r = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+  const int s = p.row_stream[r], pos = p.row_pos[r];
+  const int span = p.pages_per_stream * p.page_size;
+  if (s < 0 || s >= p.max_streams || pos < 0 || pos >= span) return;
+  const int page = p.page_table[(int64_t)s * p.pages_per_stream + pos / p.page_size];
+  if (page < 0 || page >= p.pool_pages) return;
+  for (int i = tid; i < D / 2; i += 256) {
+    const double inv_freq = pow((double)p.theta, -2.0 * (double)i / (double)D);
+    double sn, cs;
+    sincos((double)pos * inv_freq, &sn, &cs);
+    tab[i] = make_double2(cs, sn);
+  }
+  __syncthreads();
+  constexpr int TPH = D / 8;
+  const int nkvd = p.n_kv_heads * D;
+  const double* raw = p.raw + (int64_t)r * (p.n_layers * 2 * nkvd) + (int64_t)l * 2 * nkvd;
+  const int items = 2 * p.n_kv_heads * TPH;
+  for (int it = tid; it < items; it += 256) {
+    const int kind = it / (p.n_kv_heads * TPH), rem = it % (p.n_kv_heads * TPH);
+    const int head = rem / TPH, part = rem % TPH;
+    double x[8];
+    const double* src = raw + kind * nkvd + head * D + part * 8;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const double2 v = *reinterpret_cast<const double2*>(src + i);
+      x[i] = v.x; x[i + 1] = v.y;
+    }
+    // norm and rotation are computed for every item (shuffles stay inside a head's
+    // TPH lanes); only K items keep them
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+    for (int m = 1; m < TPH; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+    const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
+    const T* gk = static_cast<const T*>(p.kn_l[l]) + part * 8;
+    double xn[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xn[i] = x[i] * inv * (double)Elem<T>::load1(gk + i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double xp = __shfl_xor(xn[i], TPH / 2, kWave);
+      const int j = part * 8 + i;
+      const double2 cs = tab[j < D / 2 ? j : j - D / 2];
+      const double rot = j < D / 2 ? xn[i] * cs.x - xp * cs.y : xn[i] * cs.x + xp * cs.y;
+      o[i] = kind == 0 ? rot : x[i];
+    }
+    T* pool = static_cast<T*>(kind == 0 ? p.kpool_l[l] : p.vpool_l[l]);
+    T* dst = pool + (((int64_t)page * p.n_kv_heads + head) * p.page_size + pos % p.page_size) * D + part * 8;
+    constexpr int E = Elem<T>::E;
+#pragma unroll
+    for (int i = 0; i < 8; i += E) stg16(dst + i, pack_d(o + i, T()));
+  }
 }
 
 // Fused rows: out[r] = y[r] / sqrt(mean(y[r]^2) + eps) * gain, with the squares summed
-// per 128-column tile by the fc GEMM and here over tiles in order.
+// per column tile by the fc GEMM and here over tiles in order.
 template <typename T>
 __global__ __launch_bounds__(256) void k_rownorm(const RowNormParams p) {
   constexpr int E = Elem<T>::E;
-  __shared__ float s_inv;
+  __shared__ double s_inv;
   const int r = blockIdx.x;
   if (threadIdx.x == 0) {
-    float ss = 0.f;
+    double ss = 0.0;
     for (int t = 0; t < p.n_tiles; ++t) ss += p.ssq_part[(int64_t)r * p.n_tiles + t];
-    s_inv = (float)(1.0 / sqrt((double)ss / (double)p.hidden + (double)p.eps));
+    s_inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
   }
   __syncthreads();
-  const float inv = s_inv;
-  const float* y = p.y + (int64_t)r * p.hidden;
+  const double inv = s_inv;
+  const double* y = p.y + (int64_t)r * p.hidden;
   const T* gn = static_cast<const T*>(p.gain);
   T* out = static_cast<T*>(p.out) + (int64_t)r * p.hidden;
   for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
-    float f[E], gf[E];
+    float gf[E];
+    double f[E];
     unpack(ldg16(gn + c), gf, T());
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = y[c + e] * inv * gf[e];
-    stg16(out + c, pack(f, T()));
+    for (int e = 0; e < E; ++e) f[e] = y[c + e] * inv * (double)gf[e];
+    stg16(out + c, pack_d(f, T()));
   }
 }
 
@@ -97,6 +158,18 @@ __global__ void k_fill_zero(int* p, int64_t n) {
 hipError_t launch_embed(int dtype, const EmbedParams& p, hipStream_t st) {
   if (dtype == 0) hipLaunchKernelGGL(k_embed<float>, dim3(p.S * p.B), dim3(256), 0, st, p);
   else hipLaunchKernelGGL(k_embed<bf16_t>, dim3(p.S * p.B), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st) {
+  dim3 grid(p.R, p.n_layers);
+  if (dtype == 0) {
+    if (p.head_dim == 64) hipLaunchKernelGGL((k_kv_finish<float, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_kv_finish<float, 128>), grid, dim3(256), 0, st, p);
+  } else {
+    if (p.head_dim == 64) hipLaunchKernelGGL((k_kv_finish<bf16_t, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_kv_finish<bf16_t, 128>), grid, dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

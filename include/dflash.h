@@ -200,7 +200,7 @@ int dflash_inject_kv(dflash *h, const void *fused, int32_t n_rows, const int32_t
  *                    max_ctx_len <= kv->pages_per_stream * page_size (else
  *                    DFLASH_ERR_CAPACITY).
  *   draft_out:       device int32 [n_streams, B-1].
- *   logits_out:      NULL, or device dtype [n_streams, B-1, vocab].
+ *   logits_out:      NULL, or device float [n_streams, B-1, vocab] (fp32 logits).
  *   top2_out:        NULL, or device float [n_streams, B-1, 2] (largest and second
  *                    largest logit, fp32).
  * The block's own K/V are never written to the cache: only committed rows are, by

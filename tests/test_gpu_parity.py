@@ -52,14 +52,14 @@ def ulp_bf16(x):
     return np.where(ax > 0, u, 2.0 ** -133)
 
 
-def storage_excess(gpu, orc, dtype, ulps=1):
+def storage_excess(gpu, orc, dtype, ulps=1, row_frac=2.0 ** -16):
     """How far the GPU's stored values exceed the bar (<= 0 means within it)."""
     g = O.as_f64(gpu)
     o = np.asarray(orc, dtype=np.float64)
     assert g.shape == o.shape, (g.shape, o.shape)
     if dtype == "bf16":
         rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
-        tol = ulps * ulp_bf16(o) + 2.0 ** -16 * rms
+        tol = ulps * ulp_bf16(o) + row_frac * rms
     else:
         tol = ulps * (2e-5 * np.abs(o) + 2e-6)
     ex = np.abs(g - o) - tol
@@ -89,7 +89,9 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
     """All checks of one round; every figure is logged before any assertion fails.
 
     K/V written in the round come from each side's own fused rows (which may differ
-    by the 1-ulp bar), so they are held to 3 ulps here; with identical inputs the
+    by the 1-ulp bar): a one-ulp change of a fused element moves every K/V element of
+    its row by about |w| * 2^-8 * |f|, independently of that element's own size, so
+    here they are held to 2 ulps plus 2^-9 of the row RMS; with identical inputs the
     1-ulp bar applies (test_fuse_and_inject_parity).
     """
     p = case.p
@@ -110,9 +112,9 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
             for l in range(p.n_layers):
                 kg, vg = case.kv.read_rows(l, s, case.ctx[s] - case.rows[s], case.rows[s])
                 for nm, gpu_v, orc_v in (("K", kg, o["kv"][l][0]), ("V", vg, o["kv"][l][1])):
-                    ex, n = storage_excess(to_np(gpu_v), orc_v, p.dtype, ulps=3)
+                    ex, n = storage_excess(to_np(gpu_v), orc_v, p.dtype, ulps=2, row_frac=2.0 ** -9)
                     if n:
-                        problems.append(f"stream {s} {nm} layer {l}: {n} elements past 3 ulps (worst {ex:.3g})")
+                        problems.append(f"stream {s} {nm} layer {l}: {n} elements past the propagated bar (worst {ex:.3g})")
         d = float(np.max(np.abs(logits[s] - o["logits"])))
         worst = max(worst, d)
         t1, t2 = O.top2(o["logits"])
@@ -126,8 +128,6 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
             problems.append(f"stream {s}: logits mean-abs {dm:.4g} > {mean_tol:.3g}")
         if dt > tol:
             problems.append(f"stream {s}: top-2 max-abs {dt:.4g} > {tol:.3g}")
-        if np.max(np.abs(o["logits"])) >= 8:
-            problems.append("a logit reached 8: the bf16 grid there is coarser than the tolerance")
         try:
             check_tokens(toks[s], o["logits"], tol)
         except AssertionError as e:
@@ -386,7 +386,7 @@ def test_run_to_run_bit_identity_and_reset_rerun():
     case.inject()            # rewriting the same rows, then drafting again, is a fresh round
     case.draft_block()
     torch.cuda.synchronize()
-    assert torch.equal(case.logits.view(torch.int16), a.view(torch.int16))
+    assert torch.equal(case.logits.view(torch.int32), a.view(torch.int32))
     assert torch.equal(case.draft, d)
 
 
@@ -402,12 +402,12 @@ def test_batched_equals_solo_bitwise():
         pt = case.kv.page_table[s:s + 1].contiguous()
         kv1.struct.page_table = pt.data_ptr()
         kv1.struct.pages_per_stream = case.kv.pages_per_stream
-        out = torch.zeros((1, MID.block_size - 1, MID.vocab), dtype=torch.bfloat16, device="cuda")
+        out = torch.zeros((1, MID.block_size - 1, MID.vocab), dtype=torch.float32, device="cuda")
         dr = torch.zeros((1, MID.block_size - 1), dtype=torch.int32, device="cuda")
         case.dr.dflash_draft_block(case.anchor[s:s + 1].contiguous(), case.ctx_len[s:s + 1].contiguous(),
                                    case.max_ctx, kv1, dr, case.ws, logits_out=out)
         torch.cuda.synchronize()
-        assert torch.equal(out[0].view(torch.int16), batched[s].view(torch.int16)), f"stream {s}"
+        assert torch.equal(out[0].view(torch.int32), batched[s].view(torch.int32)), f"stream {s}"
         assert torch.equal(dr[0], case.draft[s])
 
 
@@ -430,7 +430,7 @@ def test_chunked_inject_equals_one_shot_and_page_order_is_invisible():
             kb, vb = b.kv.read_rows(l, s, 0, b.ctx[s])
             assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
             assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
-    assert torch.equal(a.logits.view(torch.int16), b.logits.view(torch.int16))
+    assert torch.equal(a.logits.view(torch.int32), b.logits.view(torch.int32))
 
 
 def test_sliding_reach_and_rollback_by_perturbation():
@@ -452,13 +452,13 @@ def test_sliding_reach_and_rollback_by_perturbation():
             case.kv.write_rows(l, 0, C, junk, junk)
     case.draft_block()
     torch.cuda.synchronize()
-    assert torch.equal(case.logits.view(torch.int16), base.view(torch.int16))
+    assert torch.equal(case.logits.view(torch.int32), base.view(torch.int32))
     # one row inside the sliding window does move the result
     k, v = case.kv.read_rows(0, 0, C - 100, 1)
     case.kv.write_rows(0, 0, C - 100, k.float() + 1.0, v.float())
     case.draft_block()
     torch.cuda.synchronize()
-    assert not torch.equal(case.logits.view(torch.int16), base.view(torch.int16))
+    assert not torch.equal(case.logits.view(torch.int32), base.view(torch.int32))
 
 
 def test_argmax_ties_pick_the_lowest_index():

@@ -65,7 +65,7 @@ class RoundCase:
         self.ws = self.dr.new_workspace(max(R, 1), S, self.max_ctx, device=device)
         self.fused = torch.zeros((max(R, 1), p.hidden), dtype=self.dtype, device=device)
         self.draft = torch.zeros((S, B - 1), dtype=torch.int32, device=device)
-        self.logits = torch.zeros((S, B - 1, p.vocab), dtype=self.dtype, device=device)
+        self.logits = torch.zeros((S, B - 1, p.vocab), dtype=torch.float32, device=device)
         self.top2 = torch.zeros((S, B - 1, 2), dtype=torch.float32, device=device)
         self.accept = torch.zeros(S, dtype=torch.int32, device=device)
         self.bonus = torch.zeros(S, dtype=torch.int32, device=device)
