@@ -252,12 +252,17 @@ class Drafter:
 
 
 class PagedKV:
-    """Caller-owned paged draft caches: per layer K and V pools [pool_pages, n_kv, 16, d] and a page table."""
+    """Caller-owned paged draft caches and their page table.
+
+    Per layer a K pool [pool_pages, n_kv, 16, d] (a page holds 16 key rows) and a V pool
+    [pool_pages, n_kv, d, 16] (a page holds the same 16 positions' values transposed).
+    """
 
     def __init__(self, cfg: Config, page_table: torch.Tensor, pool_pages: int, dtype, device="cuda"):
-        shape = (pool_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
-        self.k = [torch.zeros(shape, dtype=dtype, device=device) for _ in range(cfg.n_layers)]
-        self.v = [torch.zeros(shape, dtype=dtype, device=device) for _ in range(cfg.n_layers)]
+        kshape = (pool_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        vshape = (pool_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
+        self.k = [torch.zeros(kshape, dtype=dtype, device=device) for _ in range(cfg.n_layers)]
+        self.v = [torch.zeros(vshape, dtype=dtype, device=device) for _ in range(cfg.n_layers)]
         self.page_table = page_table.to(device=device, dtype=torch.int32).contiguous()
         self.pages_per_stream = self.page_table.shape[1]
         self.page_size = cfg.page_size
@@ -269,17 +274,18 @@ class PagedKV:
         s.pages_per_stream = self.pages_per_stream
         self.struct = s
 
+    def _slots(self, stream, start, n):
+        pos = torch.arange(start, start + n, device=self.page_table.device)
+        pages = self.page_table[stream, (pos // self.page_size).long()].long()
+        return pages, (pos % self.page_size).long()
+
     def write_rows(self, layer, stream, start, k_rows, v_rows):
         """Write context rows [n, n_kv, d] for positions start.. of a stream (host-side setup of inputs)."""
-        n = k_rows.shape[0]
-        pos = torch.arange(start, start + n, device=self.page_table.device)
-        pages = self.page_table[stream, (pos // self.page_size).long()].long()
-        slots = (pos % self.page_size).long()
+        pages, slots = self._slots(stream, start, k_rows.shape[0])
         self.k[layer][pages, :, slots, :] = k_rows.to(self.k[layer].dtype)
-        self.v[layer][pages, :, slots, :] = v_rows.to(self.v[layer].dtype)
+        self.v[layer][pages, :, :, slots] = v_rows.to(self.v[layer].dtype)
 
     def read_rows(self, layer, stream, start, n):
-        pos = torch.arange(start, start + n, device=self.page_table.device)
-        pages = self.page_table[stream, (pos // self.page_size).long()].long()
-        slots = (pos % self.page_size).long()
-        return self.k[layer][pages, :, slots, :], self.v[layer][pages, :, slots, :]
+        """K and V rows [n, n_kv, d] of positions start.. of a stream."""
+        pages, slots = self._slots(stream, start, n)
+        return self.k[layer][pages, :, slots, :], self.v[layer][pages, :, :, slots]

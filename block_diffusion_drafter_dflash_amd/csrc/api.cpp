@@ -81,7 +81,7 @@ static int fail(dflash* h, int code, const char* fmt, ...) {
 namespace {
 
 struct GemmPlan {
-  int mt, mgroups, n_tiles, iters;
+  int mt, mgroups, n_tiles, iters, n_work;
 };
 
 // Rows are processed in groups of 16 * mt (mt = 1 or 2); every workgroup owns one
@@ -93,6 +93,7 @@ GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K) {
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
   g.iters = K / gemm_k_per_iter(dtype);
+  g.n_work = g.n_tiles * g.mgroups;
   return g;
 }
 
@@ -101,10 +102,16 @@ struct AttnPlan {
   size_t part_o_bytes, part_ml_bytes;
 };
 
+// The most pages any stream's reach can touch: all of [0, max_ctx) for a full layer;
+// for a window W, W keys starting anywhere in a page (ceil((W + 15) / 16) pages).
+int max_reach_pages(int max_ctx, int window) {
+  const int all = (max_ctx + 15) / 16;
+  return window > 0 ? std::min(all, (window + 30) / 16) : all;
+}
+
 AttnPlan plan_attn(const dflash_config& c, int S, int max_ctx, int window) {
   AttnPlan a;
-  const int reach = window > 0 ? std::min(window, max_ctx) : max_ctx;
-  a.n_chunks = attention_chunks(reach);
+  a.n_chunks = attention_chunks(max_reach_pages(max_ctx, window));
   a.qt = attention_query_tiles(c.n_q_heads / c.n_kv_heads, c.block_size);
   const size_t sh = (size_t)S * c.n_kv_heads * a.n_chunks;
   a.part_o_bytes = a.n_chunks > 1 ? sh * a.qt * 64 * (c.head_dim / 16) * 4 * 4 : 0;
@@ -145,7 +152,7 @@ InjectLayout layout_inject(const dflash& h, int R) {
   InjectLayout L;
   const auto& c = h.cfg;
   const int N = c.n_layers * 2 * h.nkv();
-  L.g = plan_gemm(c.dtype, EPI_INJECT, R, N, c.hidden);
+  L.g = plan_gemm(c.dtype, EPI_RAW, R, N, c.hidden);
   Region r;
   r.take(kCounterInts * 4);
   L.raw = r.take((size_t)R * N * 8);
@@ -157,14 +164,14 @@ struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
   int ssq_ld;
-  size_t x, ssq_a, ssq_b, qkv_raw, o_buf, m, part_o, part_ml, tile_res, end;
+  size_t x, a, ssq_a, ssq_b, qkv_raw, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
   const auto& c = h.cfg;
   const int M = S * c.block_size, Mm = S * (c.block_size - 1);
   const int es = h.esize();
-  L.qkv = plan_gemm(c.dtype, EPI_QKV, M, h.nq() + 2 * h.nkv(), c.hidden);
+  L.qkv = plan_gemm(c.dtype, EPI_RAW, M, h.nq() + 2 * h.nkv(), c.hidden);
   L.o = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, h.nq());
   L.gu = plan_gemm(c.dtype, EPI_SWIGLU, M, 2 * c.intermediate, c.hidden);
   L.down = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, c.intermediate);
@@ -179,9 +186,13 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   Region r;
   r.take(kCounterInts * 4);
   L.x = r.take((size_t)M * c.hidden * es);
+  L.a = r.take((size_t)M * c.hidden * es);
   L.ssq_a = r.take((size_t)M * L.ssq_ld * 8);
   L.ssq_b = r.take((size_t)M * L.ssq_ld * 8);
   L.qkv_raw = r.take((size_t)M * (h.nq() + 2 * h.nkv()) * 8);
+  L.q = r.take((size_t)M * h.nq() * es);
+  L.kblk = r.take((size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim * es);
+  L.vblk = r.take((size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim * es);
   L.o_buf = r.take((size_t)M * h.nq() * es);
   L.m = r.take((size_t)M * c.intermediate * es);
   L.part_o = r.take(po);
@@ -389,6 +400,7 @@ static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
   p.n_tiles = g.n_tiles;
   p.mgroups = g.mgroups;
   p.iters = g.iters;
+  p.n_work = g.n_work;
   return p;
 }
 
@@ -472,6 +484,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   p.a = fused;
   p.lda = c.hidden;
   p.nkv = h->nkv();
+  p.seg_layers = c.n_layers;
   for (int l = 0; l < c.n_layers; ++l) {
     p.wk_l[l] = h->w.wk[l];
     p.wv_l[l] = h->w.wv[l];
@@ -480,7 +493,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   hipError_t e;
   {
     ProfScope ps(h, "inject_kv_gemm", st);
-    e = launch_gemm(c.dtype, EPI_INJECT, p, L.g.mt, st);
+    e = launch_gemm(c.dtype, EPI_RAW, p, L.g.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
   KvFinishParams kf;
@@ -538,8 +551,9 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   void* X = W + L.x;
-  double* ssq_a = reinterpret_cast<double*>(W + L.ssq_a);   // feeds in_norm and the final norm
-  double* ssq_b = reinterpret_cast<double*>(W + L.ssq_b);   // feeds post_norm
+  void* A = W + L.a;
+  double* ssq_a = reinterpret_cast<double*>(W + L.ssq_a);   // after the down projection
+  double* ssq_b = reinterpret_cast<double*>(W + L.ssq_b);   // after the o projection
   double* qkv_raw = reinterpret_cast<double*>(W + L.qkv_raw);
   hipError_t e;
 
@@ -551,26 +565,42 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   ep.mask_token = c.mask_token_id;
   ep.anchor = anchor;
   ep.embed = h->w.embed;
+  ep.gain = h->w.in_norm[0];
+  ep.eps = c.rms_eps;
   ep.x = X;
-  ep.ssq = ssq_a;
+  ep.a = A;
   {
     ProfScope ps(h, "embed", st);
     e = launch_embed(c.dtype, ep, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "embed: %s", hipGetErrorString(e));
 
-  // embed leaves one sum of squares per row (row stride 1); the GEMMs leave one per tile
-  int ssq_parts = 1, ssq_ld_a = 1;
+  auto norm = [&](const char* name, const double* ssq, const void* gain, int rows, int rowmap_bm1) {
+    NormParams np;
+    np.R = rows;
+    np.hidden = c.hidden;
+    np.ssq_parts = L.ssq_ld;
+    np.ssq_ld = L.ssq_ld;
+    np.rowmap_bm1 = rowmap_bm1;
+    np.x = X;
+    np.ssq = ssq;
+    np.gain = gain;
+    np.eps = c.rms_eps;
+    np.a = A;
+    ProfScope ps(h, name, st);
+    return launch_norm(c.dtype, np, st);
+  };
+
   for (int l = 0; l < c.n_layers; ++l) {
-    // raw q | k | v of round(RMSNorm(X) * in_norm); norms and RoPE follow in attention
+    // a = round(RMSNorm(X) * in_norm)   (layer 0: written by embed)
+    if (l > 0) {
+      e = norm("norm_in", ssq_a, h->w.in_norm[l], M, 0);
+      if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d input norm: %s", l, hipGetErrorString(e));
+    }
+    // raw q | k | v = a . [wq | wk | wv]^T
     GemmParams p = gemm_base(L.qkv, M, h->nq() + 2 * h->nkv(), c.hidden);
-    p.a = X;
+    p.a = A;
     p.lda = c.hidden;
-    p.a_ssq = ssq_a;
-    p.a_ssq_parts = ssq_parts;
-    p.a_ssq_ld = ssq_ld_a;
-    p.a_gain = h->w.in_norm[l];
-    p.eps = c.rms_eps;
     p.w0 = h->w.wq[l];
     p.w1 = h->w.wk[l];
     p.w2 = h->w.wv[l];
@@ -579,9 +609,32 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.y_out = qkv_raw;
     {
       ProfScope ps(h, "qkv_gemm", st);
-      e = launch_gemm(c.dtype, EPI_QKV, p, L.qkv.mt, st);
+      e = launch_gemm(c.dtype, EPI_RAW, p, L.qkv.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv: %s", l, hipGetErrorString(e));
+
+    // q, k = RoPE(q_norm / k_norm(raw)), v = raw, into the attention layouts
+    QkvFinishParams qf;
+    qf.S = n_streams;
+    qf.B = B;
+    qf.n_q_heads = c.n_q_heads;
+    qf.n_kv_heads = c.n_kv_heads;
+    qf.head_dim = c.head_dim;
+    qf.raw = qkv_raw;
+    qf.ctx_len = ctx_len;
+    qf.max_ctx = max_ctx_len;
+    qf.q_norm = h->w.q_norm[l];
+    qf.k_norm = h->w.k_norm[l];
+    qf.theta = c.rope_theta;
+    qf.eps = c.rms_eps;
+    qf.q = W + L.q;
+    qf.kblk = W + L.kblk;
+    qf.vblk = W + L.vblk;
+    {
+      ProfScope ps(h, "qkv_finish", st);
+      e = launch_qkv_finish(c.dtype, qf, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv finish: %s", l, hipGetErrorString(e));
 
     AttnParams ap;
     std::memset(&ap, 0, sizeof ap);
@@ -595,14 +648,9 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     ap.n_chunks = L.attn[l].n_chunks;
     ap.max_ctx = max_ctx_len;
     ap.ctx_len = ctx_len;
-    ap.qkv_raw = qkv_raw;
-    ap.ld_raw = h->nq() + 2 * h->nkv();
-    ap.nq = h->nq();
-    ap.nkv = h->nkv();
-    ap.q_norm = h->w.q_norm[l];
-    ap.k_norm = h->w.k_norm[l];
-    ap.theta = c.rope_theta;
-    ap.eps = c.rms_eps;
+    ap.q = W + L.q;
+    ap.kblk = W + L.kblk;
+    ap.vblk = W + L.vblk;
     ap.kpool = kv->k_pool[l];
     ap.vpool = kv->v_pool[l];
     ap.page_table = kv->page_table;
@@ -633,15 +681,12 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d o_proj: %s", l, hipGetErrorString(e));
 
-    // m = round(silu(w_gate . b) * (w_up . b)),  b = round(RMSNorm(X) * post_norm)
+    // a = round(RMSNorm(X) * post_norm);  m = round(silu(w_gate . a) * (w_up . a))
+    e = norm("norm_post", ssq_b, h->w.post_norm[l], M, 0);
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d post norm: %s", l, hipGetErrorString(e));
     p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden);
-    p.a = X;
+    p.a = A;
     p.lda = c.hidden;
-    p.a_ssq = ssq_b;
-    p.a_ssq_parts = L.ssq_ld;
-    p.a_ssq_ld = L.ssq_ld;
-    p.a_gain = h->w.post_norm[l];
-    p.eps = c.rms_eps;
     p.w0 = h->w.w_gate[l];
     p.w1 = h->w.w_up[l];
     p.m_out = W + L.m;
@@ -665,20 +710,14 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
       e = launch_gemm(c.dtype, EPI_RESID, p, L.down.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d down: %s", l, hipGetErrorString(e));
-    ssq_parts = L.ssq_ld;
-    ssq_ld_a = L.ssq_ld;
   }
 
-  // Final norm of the mask rows, LM head, argmax (lowest index on a tie).
+  // Final norm of the mask rows (compacted), LM head, argmax (lowest index on a tie).
+  e = norm("norm_final", ssq_a, h->w.norm, Mm, B - 1);
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "final norm: %s", hipGetErrorString(e));
   GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden);
-  p.a = X;
+  p.a = A;
   p.lda = c.hidden;
-  p.a_ssq = ssq_a;
-  p.a_ssq_parts = ssq_parts;
-  p.a_ssq_ld = ssq_ld_a;
-  p.a_gain = h->w.norm;
-  p.eps = c.rms_eps;
-  p.a_rowmap_bm1 = B - 1;
   p.w0 = h->w.lm_head;
   p.logits_out = static_cast<float*>(logits_out);
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);

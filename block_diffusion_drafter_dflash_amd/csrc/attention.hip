@@ -3,12 +3,15 @@
 // Workgroup = (context chunk, kv head, stream) with QT waves; wave w owns 16 of the
 // kv head's g * B queries (its g q-heads times the B block rows). Keys are the
 // context rows in the layer's reach, read from the paged cache, plus all B block
-// rows (added by the stream's last chunk). K and V^T tiles of 64 keys are staged in
-// LDS, the next tile's cache reads already in flight while the current one is
-// used. Scores are computed transposed (S^T = K Q^T) so that each lane owns one
-// query: the softmax statistics are lane-local plus two cross-lane-group shuffles,
-// and the probabilities feed the P.V MFMA without a transpose. P (fp32) enters the
-// bf16 MFMA as three bf16 parts (hi, mid, lo) that hold all of its 24 bits, and the
+// rows (added by the stream's last chunk). A step covers two 16-key pages: every
+// lane loads its MFMA fragments straight from the pages with 16-byte reads (K pages
+// are [16 keys][d]; V pages are stored transposed, [d][16 keys], so both operands
+// are contiguous along the MFMA's reduction), and the next step's reads are in
+// flight while the current one is multiplied.
+// Scores are computed transposed (S^T = K Q^T) so that each lane owns one query:
+// the softmax statistics are lane-local plus two cross-lane-group shuffles, and the
+// probabilities feed the P.V MFMA without a transpose. P (fp32) enters the bf16
+// MFMA as three bf16 parts (hi, mid, lo) that hold all of its 24 bits, and the
 // running output and denominator are kept in float64.
 // A stream whose reach spans several chunks leaves per-chunk partials (max, sum,
 // unnormalised output); k_attn_combine adds them in chunk order.
@@ -17,61 +20,58 @@
 
 namespace dfl {
 
-constexpr int kKT = 64;       // keys per LDS tile
-constexpr int kMaxBlock = 32; // block rows
-
 template <typename T, int D>
 struct AttnCfg {
+  static constexpr bool BF = sizeof(T) == 2;
   static constexpr int E = Elem<T>::E;
-  static constexpr int PADK = 16 / sizeof(T);         // K rows padded by 16 bytes
-  static constexpr int PADV = sizeof(T) == 2 ? 8 : 4; // V^T rows padded
-  static constexpr int LDK = D + PADK;
-  static constexpr int LDV = kKT + PADV;
-  static constexpr int NF = D / 4 / E;                // 16-byte fragments per lane per query row
-  static constexpr int CPK = D / E;                   // 16-byte chunks per key row
+  static constexpr int NF = D / 4 / E;                // 16-byte K fragments per lane per 16-key tile
   static constexpr int NDT = D / 16;                  // 16-dim output tiles
+  static constexpr int NV = BF ? NDT : 2 * NDT;       // 16-byte V fragments per lane per step
+};
+
+// Key (0..31 within the step's two pages) supplied as row r of S^T tile t. For bf16
+// the rows are arranged so that lane group lg ends up holding the probabilities of
+// keys 8lg..8lg+7, exactly the eight reduction slots it feeds to the 32-deep P.V MFMA.
+template <bool BF>
+__device__ __forceinline__ int key_of_row(int t, int r) {
+  return BF ? 8 * (r >> 2) + 4 * t + (r & 3) : 16 * t + r;
+}
+
+struct StepSrc {
+  const void* k[2];     // K page base ([16][D]) of each half, or null (no keys there)
+  const void* v[2];     // V^T page base ([D][vld]) of each half, or null
+  int vld;              // V^T row stride (16 for cache pages, 32 for the block)
+  int key0;             // absolute position of the step's first key; -1 for the block
 };
 
 template <typename T, int D, int QT>
 __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
   using C = AttnCfg<T, D>;
-  constexpr int E = C::E, NF = C::NF, CPK = C::CPK, NDT = C::NDT;
-  constexpr int NTHR = 64 * QT;
-  constexpr int NI = (kKT * CPK + NTHR - 1) / NTHR;   // cache chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) T ks[kKT][C::LDK];
-  __shared__ __attribute__((aligned(16))) T vt[D][C::LDV];
-  __shared__ double2 rope_tab[kMaxBlock][D / 2];      // (cos, sin) of the block positions
+  constexpr bool BF = C::BF;
+  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NV = C::NV;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int g = p.group, B = p.B, D_all_q = p.n_q_heads * D;
+  const int g = p.group, B = p.B;
   const int nq_local = g * B;
 
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
-  const int reach = Cs - lo;
-  // Chunk length from this stream's own reach; its chunk count never exceeds the grid's.
-  const int cl = reach > 0 ? attention_chunk_len(reach) : kKT;
-  const int c_lo = lo + c * cl;
-  const int c_hi = (c_lo + cl < Cs) ? c_lo + cl : Cs;
-  const bool last_chunk = (c == p.n_chunks - 1);
+  const int pg_lo = lo / 16;
+  const int n_pages = span_pages(lo, Cs);
+  // This stream's own chunking; the grid's chunks past it are empty.
+  const int n_own = attention_chunks(n_pages);
+  const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages) : 0;
+  const int cp0 = c * cpp;
+  const int cp1 = c < n_own ? ((c + 1) * cpp < n_pages ? (c + 1) * cpp : n_pages) : cp0;
+  const bool has_block = (c == n_own - 1);
+  const int n_ctx_steps = cp1 > cp0 ? (cp1 - cp0 + 1) / 2 : 0;
+  const int n_steps = n_ctx_steps + (has_block ? 1 : 0);
 
-  // Rotary angles of the block positions Cs + j (float64).
-  for (int i = tid; i < B * (D / 2); i += NTHR) {
-    const int j = i / (D / 2), f = i % (D / 2);
-    const double inv_freq = pow((double)p.theta, -2.0 * (double)f / (double)D);
-    double sn, cs;
-    sincos((double)(Cs + j) * inv_freq, &sn, &cs);
-    rope_tab[j][f] = make_double2(cs, sn);
-  }
-  __syncthreads();
-
-  // Queries owned by this lane (MFMA column lr of wave w): q = RoPE(q_norm(raw q)),
-  // rounded once to the MFMA input type. Lane group lg holds dims [lg*D/4, (lg+1)*D/4),
-  // so the head's sum of squares is two shuffles away and each RoPE pair
-  // (j, j + D/2) sits in lane groups lg and lg ^ 2.
+  // Queries owned by this lane (column lr of wave w's MFMA tiles): dims
+  // [lg*D/4, (lg+1)*D/4) of query row (hl, jrow), as NF 16-byte fragments.
   const int qi = 16 * w + lr;
   const bool q_valid = qi < nq_local;
   const int hl = q_valid ? qi / B : 0, jrow = q_valid ? qi % B : 0;
@@ -79,33 +79,9 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
   const int qcol = (h * g + hl) * D;
   uint4 qf[NF];
   {
-    constexpr int DL = D / 4;
-    double x[DL];
-    const double* qp = p.qkv_raw + (int64_t)qrow * p.ld_raw + qcol + lg * DL;
+    const T* qp = static_cast<const T*>(p.q) + (int64_t)qrow * (p.n_q_heads * D) + qcol + lg * (D / 4);
 #pragma unroll
-    for (int i = 0; i < DL; i += 2) {
-      const double2 v = q_valid ? *reinterpret_cast<const double2*>(qp + i) : make_double2(0.0, 0.0);
-      x[i] = v.x; x[i + 1] = v.y;
-    }
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 16, kWave);
-    ss += __shfl_xor(ss, 32, kWave);
-    const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
-    const T* gq = static_cast<const T*>(p.q_norm) + lg * DL;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) x[i] = x[i] * inv * (double)Elem<T>::load1(gq + i);
-    double o[DL];
-#pragma unroll
-    for (int i = 0; i < DL; ++i) {
-      const double xp = __shfl_xor(x[i], 32, kWave);
-      const int j = lg * DL + i;
-      const double2 cs = rope_tab[jrow][j < D / 2 ? j : j - D / 2];
-      o[i] = q_valid ? (j < D / 2 ? x[i] * cs.x - xp * cs.y : x[i] * cs.x + xp * cs.y) : 0.0;
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) qf[f] = pack_d(o + f * E, T());
+    for (int f = 0; f < NF; ++f) qf[f] = q_valid ? ldg16(qp + f * E) : make_uint4(0, 0, 0, 0);
   }
 
   double oacc[NDT][4];
@@ -116,112 +92,107 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
   float m_run = -INFINITY;
   double l_run = 0.0;
 
-  const int64_t head_stride = (int64_t)p.page_size * D;
-  const int n_ctx_tiles = c_hi > c_lo ? (c_hi - c_lo + kKT - 1) / kKT : 0;
-  const int n_tiles = n_ctx_tiles + (last_chunk ? 1 : 0);
-
-  // Cache reads of one context tile into registers (invalid keys read as zero).
-  uint4 kr[NI], vr[NI];
-  auto fetch = [&](int t) {
-    const int k0 = c_lo + t * kKT;
+  const int64_t kv_page = (int64_t)p.page_size * D;   // elements per (page, head)
+  auto source = [&](int step) {
+    StepSrc src;
+    if (step < n_ctx_steps) {
+      const int pg = pg_lo + cp0 + 2 * step;
+      src.vld = 16;
+      src.key0 = pg * 16;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int ci = tid + i * NTHR;
-      const int key = ci / CPK, part = ci % CPK;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (ci < kKT * CPK && k0 + key < c_hi) {
-        const int pos = k0 + key;
-        const int page = p.page_table[(int64_t)s * p.pages_per_stream + pos / p.page_size];
-        if (page >= 0 && page < p.pool_pages) {
-          const int64_t off = ((int64_t)page * p.n_kv_heads + h) * head_stride + (int64_t)(pos % p.page_size) * D + part * E;
-          kr[i] = ldg16(static_cast<const T*>(p.kpool) + off);
-          vr[i] = ldg16(static_cast<const T*>(p.vpool) + off);
+      for (int hf = 0; hf < 2; ++hf) {
+        src.k[hf] = nullptr;
+        src.v[hf] = nullptr;
+        if (cp0 + 2 * step + hf < cp1) {
+          const int page = p.page_table[(int64_t)s * p.pages_per_stream + pg + hf];
+          if (page >= 0 && page < p.pool_pages) {
+            const int64_t off = ((int64_t)page * p.n_kv_heads + h) * kv_page;
+            src.k[hf] = static_cast<const T*>(p.kpool) + off;
+            src.v[hf] = static_cast<const T*>(p.vpool) + off;
+          }
         }
+      }
+    } else {
+      const int64_t off = ((int64_t)s * p.n_kv_heads + h) * (kBlockSlots * D);
+      src.vld = kBlockSlots;
+      src.key0 = -1;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        src.k[hf] = static_cast<const T*>(p.kblk) + off + hf * 16 * D;
+        src.v[hf] = static_cast<const T*>(p.vblk) + off + hf * 16;
+      }
+    }
+    return src;
+  };
+  // A key's validity: on a page, and inside the reach (context) or a block row (block).
+  auto key_ok = [&](const StepSrc& src, int kk) {
+    if (!src.k[kk >> 4]) return false;
+    if (src.key0 < 0) return kk < B;
+    const int pos = src.key0 + kk;
+    return pos >= lo && pos < Cs;
+  };
+  auto fetch = [&](const StepSrc& src, uint4 (&kf)[2][NF], uint4 (&vf)[NV]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kk = key_of_row<BF>(t, lr);
+      const T* kb = static_cast<const T*>(src.k[kk >> 4]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        kf[t][f] = kb ? ldg16(kb + (kk & 15) * D + lg * (D / 4) + f * E) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (BF) {
+      // lane group lg: keys 8lg..8lg+7 = half lg/2, slots 8(lg&1)..
+      const T* vb = static_cast<const T*>(src.v[lg >> 1]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        vf[dt] = vb ? ldg16(vb + (int64_t)(16 * dt + lr) * src.vld + 8 * (lg & 1)) : make_uint4(0, 0, 0, 0);
+    } else {
+      // tile t, lane group lg: keys 16t + 4lg.. = half t, slots 4lg..
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const T* vb = static_cast<const T*>(src.v[t]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vf[t * NDT + dt] = vb ? ldg16(vb + (int64_t)(16 * dt + lr) * src.vld + 4 * lg) : make_uint4(0, 0, 0, 0);
       }
     }
   };
-  if (n_ctx_tiles > 0) fetch(0);
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool blk = (t == n_ctx_tiles);
-    const int nkeys = blk ? B : ((c_hi - (c_lo + t * kKT)) < kKT ? (c_hi - (c_lo + t * kKT)) : kKT);
-
-    // ---- stage K rows and V^T into LDS
-    if (blk) {
-      // The block's own keys: k = RoPE(k_norm(raw k)), v = raw v, each rounded once.
-      // D/8 consecutive threads own one key (8 dims each).
-      constexpr int TPK = D / 8;
-      for (int ci = tid; ci < kKT * TPK; ci += NTHR) {
-        const int key = ci / TPK, part = ci % TPK;
-        double kx[8], vx[8];
-        const bool kvalid = key < nkeys;
-        const double* kp = p.qkv_raw + (int64_t)(s * B + (kvalid ? key : 0)) * p.ld_raw + p.nq + h * D + part * 8;
-        const double* vp = kp + p.nkv;
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const double2 a = kvalid ? *reinterpret_cast<const double2*>(kp + i) : make_double2(0.0, 0.0);
-          const double2 b = kvalid ? *reinterpret_cast<const double2*>(vp + i) : make_double2(0.0, 0.0);
-          kx[i] = a.x; kx[i + 1] = a.y;
-          vx[i] = b.x; vx[i + 1] = b.y;
-        }
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss += kx[i] * kx[i];
-        for (int m = 1; m < TPK; m <<= 1) ss += __shfl_xor(ss, m, kWave);
-        const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
-        const T* gk = static_cast<const T*>(p.k_norm) + part * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kx[i] = kx[i] * inv * (double)Elem<T>::load1(gk + i);
-        double ko[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const double kp2 = __shfl_xor(kx[i], TPK / 2, kWave);
-          const int j = part * 8 + i;
-          const double2 cs = rope_tab[kvalid ? key : 0][j < D / 2 ? j : j - D / 2];
-          ko[i] = kvalid ? (j < D / 2 ? kx[i] * cs.x - kp2 * cs.y : kx[i] * cs.x + kp2 * cs.y) : 0.0;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; i += E) *reinterpret_cast<uint4*>(&ks[key][part * 8 + i]) = pack_d(ko + i, T());
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Elem<T>::store_d(&vt[part * 8 + i][key], kvalid ? vx[i] : 0.0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int ci = tid + i * NTHR;
-        if (ci < kKT * CPK) {
-          const int key = ci / CPK, part = ci % CPK;
-          *reinterpret_cast<uint4*>(&ks[key][part * E]) = kr[i];
-          const T* ve = reinterpret_cast<const T*>(&vr[i]);
-#pragma unroll
-          for (int e = 0; e < E; ++e) vt[part * E + e][key] = ve[e];
-        }
-      }
+  uint4 kc[2][NF], vc[NV];
+  StepSrc cur;
+  if (n_steps > 0) {
+    cur = source(0);
+    fetch(cur, kc, vc);
+  }
+  for (int st = 0; st < n_steps; ++st) {
+    StepSrc nxt = cur;
+    uint4 kn[2][NF], vn[NV];
+    const bool more = st + 1 < n_steps;
+    if (more) {
+      nxt = source(st + 1);
+      fetch(nxt, kn, vn);
     }
-    __syncthreads();
-    if (!blk && t + 1 < n_ctx_tiles) fetch(t + 1);   // next tile's reads overlap this tile's math
 
-    // ---- S^T = K Q^T: lane holds query lr, keys 16 mt + 4 lg + i
-    floatx4 sacc[4];
+    // ---- S^T = K Q^T: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i)
+    floatx4 sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const T* krow = &ks[16 * mt + lr][lg * (D / 4)];
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int f = 0; f < NF; ++f) mma_frag(sacc[mt], *reinterpret_cast<const uint4*>(krow + f * E), qf[f], T());
+      for (int f = 0; f < NF; ++f) mma_frag(sacc[t], kc[t][f], qf[f], T());
     }
 
     // ---- online softmax (base 2); the denominator sums in float64
+    const bool edge = cur.key0 < 0 || !cur.k[0] || !cur.k[1] || cur.key0 < lo || cur.key0 + 32 > Cs;
+    float pf[2][4];
     float mx = -INFINITY;
-    float pf[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 16 * mt + 4 * lg + i;
-        pf[mt][i] = key < nkeys ? sacc[mt][i] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, pf[mt][i]);
+        const bool ok = !edge || key_ok(cur, key_of_row<BF>(t, 4 * lg + i));
+        pf[t][i] = ok ? sacc[t][i] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, pf[t][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
@@ -229,62 +200,94 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
     const double corr = (m_new == -INFINITY) ? 1.0 : (double)exp2f(m_run - m_new);
     double psum = 0.0;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pf[mt][i] = (m_new == -INFINITY || pf[mt][i] == -INFINITY) ? 0.f : exp2f(pf[mt][i] - m_new);
-        psum += (double)pf[mt][i];
+        pf[t][i] = (pf[t][i] == -INFINITY) ? 0.f : exp2f(pf[t][i] - m_new);
+        psum += (double)pf[t][i];
       }
     l_run = l_run * corr + psum;
     m_run = m_new;
 
-    // ---- this tile's O^T = V^T P^T, added to the float64 running output
+    // Values of keys outside the reach may be stale or never written: zero them so
+    // that a zero probability times a non-finite value cannot reach the output.
+    if (edge) {
+      if constexpr (BF) {
+        const int kb = 8 * lg;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          uint32_t wv[4] = {vc[dt].x, vc[dt].y, vc[dt].z, vc[dt].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t m0 = key_ok(cur, kb + 2 * q) ? 0x0000ffffu : 0u;
+            const uint32_t m1 = key_ok(cur, kb + 2 * q + 1) ? 0xffff0000u : 0u;
+            wv[q] &= (m0 | m1);
+          }
+          vc[dt] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            uint4& v = vc[t * NDT + dt];
+            const int k0 = 16 * t + 4 * lg;
+            v.x = key_ok(cur, k0) ? v.x : 0u;
+            v.y = key_ok(cur, k0 + 1) ? v.y : 0u;
+            v.z = key_ok(cur, k0 + 2) ? v.z : 0u;
+            v.w = key_ok(cur, k0 + 3) ? v.w : 0u;
+          }
+      }
+    }
+
+    // ---- this step's O^T = V^T P^T, added to the float64 running output
     floatx4 ot[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) ot[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (sizeof(T) == 2) {
-      // P as hi + mid + lo bf16 parts: about 24 significant bits.
+    if constexpr (BF) {
+      // P as hi + mid + lo bf16 parts (each remainder is exact in fp32): 24 bits.
+      const float pv[8] = {pf[0][0], pf[0][1], pf[0][2], pf[0][3], pf[1][0], pf[1][1], pf[1][2], pf[1][3]};
+      uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const float pv[8] = {pf[2 * kk][0], pf[2 * kk][1], pf[2 * kk][2], pf[2 * kk][3],
-                             pf[2 * kk + 1][0], pf[2 * kk + 1][1], pf[2 * kk + 1][2], pf[2 * kk + 1][3]};
-        float ph[8], pm[8], pl[8];
+      for (int q = 0; q < 4; ++q) {
+        hw[q] = f32x2_to_bf16x2(pv[2 * q], pv[2 * q + 1]);
+        const float r0 = pv[2 * q] - bf16_to_f32(hw[q] & 0xffffu);
+        const float r1 = pv[2 * q + 1] - bf16_to_f32(hw[q] >> 16);
+        mw[q] = f32x2_to_bf16x2(r0, r1);
+        lw[q] = f32x2_to_bf16x2(r0 - bf16_to_f32(mw[q] & 0xffffu), r1 - bf16_to_f32(mw[q] >> 16));
+      }
+      const uint4 bh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      const uint4 bm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+      const uint4 bl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ph[i] = Elem<T>::round(pv[i]);
-          const float r1 = pv[i] - ph[i];     // exact: the leading 8 bits are gone
-          pm[i] = Elem<T>::round(r1);
-          pl[i] = Elem<T>::round(r1 - pm[i]);
-        }
-        const uint4 bh = pack(ph, T()), bm = pack(pm, T()), bl = pack(pl, T());
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const T* vrow = &vt[16 * dt + lr][0];
-          const uint2 lo2 = *reinterpret_cast<const uint2*>(vrow + 32 * kk + 4 * lg);
-          const uint2 hi2 = *reinterpret_cast<const uint2*>(vrow + 32 * kk + 16 + 4 * lg);
-          const uint4 av = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
-          mma_frag(ot[dt], av, bh, T());
-          mma_frag(ot[dt], av, bm, T());
-          mma_frag(ot[dt], av, bl, T());
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        mma_frag(ot[dt], vc[dt], bh, T());
+        mma_frag(ot[dt], vc[dt], bm, T());
+        mma_frag(ot[dt], vc[dt], bl, T());
       }
     } else {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float pq[4] = {pf[mt][0], pf[mt][1], pf[mt][2], pf[mt][3]};
-        const uint4 pb = pack(pq, T());
+      for (int t = 0; t < 2; ++t) {
+        const uint4 pb = make_uint4(__float_as_uint(pf[t][0]), __float_as_uint(pf[t][1]), __float_as_uint(pf[t][2]),
+                                    __float_as_uint(pf[t][3]));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const uint4 av = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][16 * mt + 4 * lg]);
-          mma_frag(ot[dt], av, pb, T());
-        }
+        for (int dt = 0; dt < NDT; ++dt) mma_frag(ot[dt], vc[t * NDT + dt], pb, T());
       }
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[dt][i] = oacc[dt][i] * corr + (double)ot[dt][i];
-    __syncthreads();
+
+    if (more) {
+      cur = nxt;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) kc[t][f] = kn[t][f];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) vc[i] = vn[i];
+    }
   }
 
   double l_tot = l_run;
@@ -292,17 +295,20 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
   l_tot += __shfl_xor(l_tot, 32, kWave);
 
   if (p.n_chunks == 1) {
+    // Same arithmetic as the combine of a single chunk (fp32 partials), so a stream's
+    // output does not depend on how many chunks the batch's longest reach needs.
     if (!q_valid) return;
-    T* op = static_cast<T*>(p.o) + (int64_t)qrow * D_all_q + qcol;
+    const double L = (double)(float)l_tot;
+    T* op = static_cast<T*>(p.o) + (int64_t)qrow * (p.n_q_heads * D) + qcol;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       double v4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = oacc[dt][i] / l_tot;
+      for (int i = 0; i < 4; ++i) v4[i] = (double)(float)oacc[dt][i] / L;
       T* dst = op + 16 * dt + 4 * lg;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_from_double(v4[0]) | (bf16_from_double(v4[1]) << 16),
-                                                    bf16_from_double(v4[2]) | (bf16_from_double(v4[3]) << 16));
+      if constexpr (BF) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2(f32_round_odd(v4[0]), f32_round_odd(v4[1])),
+                                                    f32x2_to_bf16x2(f32_round_odd(v4[2]), f32_round_odd(v4[3])));
       } else {
         *reinterpret_cast<float4*>(dst) = make_float4((float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]);
       }
@@ -338,6 +344,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(const AttnParams p, int QT)
   for (int cc = 0; cc < p.n_chunks; ++cc)
     M = fmaxf(M, p.part_ml[(((int64_t)sh * p.n_chunks + cc) * (QT * 16) + qi) * 2]);
   double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
   for (int cc = 0; cc < p.n_chunks; ++cc) {
     const int64_t chunk_id = (int64_t)sh * p.n_chunks + cc;
     const float* ml = p.part_ml + (chunk_id * (QT * 16) + qi) * 2;

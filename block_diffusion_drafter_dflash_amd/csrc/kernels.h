@@ -5,38 +5,37 @@
 
 namespace dfl {
 
-enum AMode { A_PLAIN = 0, A_NORMED = 1, A_TAPS = 2 };
-enum Epi { EPI_FC = 0, EPI_INJECT = 1, EPI_QKV = 2, EPI_RESID = 3, EPI_SWIGLU = 4, EPI_LMHEAD = 5 };
+enum AMode { A_PLAIN = 0, A_TAPS = 1 };
+enum Epi { EPI_FC = 0, EPI_RAW = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 
 constexpr int kMaxLayers = 64;
 constexpr int kMaxTaps = 8;
+constexpr int kBlockSlots = 32;   // block rows held by a stream's block K/V pages (block_size <= 32)
 
-// One skinny GEMM launch. Every field not used by the epilogue stays zero.
+// One skinny GEMM launch: Y[M, N] = A[M, K] . W[N, K]^T. Every field not used by the
+// epilogue stays zero.
 struct GemmParams {
   int M, N, K;          // rows, output columns (all segments), reduction length
   int n_tiles;          // column tiles (16 or 32 columns each)
   int mgroups;          // row groups of 16 * MT rows
   int iters;            // K / k-elements per iteration
+  int n_work;           // n_tiles * mgroups work items, dealt to the grid
   // A operand
-  const void* a;        // A_PLAIN / A_NORMED: [rows, lda]
+  const void* a;        // A_PLAIN: [M, lda]
   int64_t lda;
-  int a_rowmap_bm1;     // > 0: logical row r reads source row (r / bm1) * (bm1 + 1) + 1 + r % bm1
-  const double* a_ssq;  // A_NORMED: per-row sum-of-squares partials of the source rows
-  int a_ssq_parts, a_ssq_ld;
-  const void* a_gain;   // A_NORMED: [K]
-  float eps;
-  const void* taps[kMaxTaps];   // A_TAPS
+  const void* taps[kMaxTaps];   // A_TAPS: plane t holds columns [t * tap_h, (t + 1) * tap_h)
   int tap_h;
   int64_t tap_stride;
-  // B operand
+  // B operand: one matrix, or segments picked by column
   const void* w0;       // single matrix; or wq / w_gate
   const void* w1;       // wk / w_up
   const void* w2;       // wv
   int nq, nkv;          // n_q*d, n_kv*d
+  int seg_layers;       // > 0: columns are per layer [wk_l | wv_l] segments (inject)
   const void* wk_l[kMaxLayers];
   const void* wv_l[kMaxLayers];
   // epilogue outputs
-  double* y_out;        // EPI_FC: y [M, N]; EPI_QKV / EPI_INJECT: raw projections [M, N] (float64)
+  double* y_out;        // EPI_FC: y [M, N]; EPI_RAW: projections [M, N] (float64)
   double* ssq_out;      // EPI_FC / EPI_RESID: [M, ssq_ld] per-tile sums of squares
   int ssq_ld;
   void* x_io;           // EPI_RESID: residual stream [M, N], updated in place
@@ -49,22 +48,35 @@ struct GemmParams {
 struct AttnParams {
   int S, B, n_q_heads, n_kv_heads, head_dim, group;
   int window;           // 0 = full
-  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max reach)
+  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages)
   int max_ctx;
   const int* ctx_len;
-  const double* qkv_raw;  // [S*B, ld_raw]: raw q | k | v projections of the block rows
-  int ld_raw, nq, nkv;
-  const void* q_norm;   // [d]
-  const void* k_norm;   // [d]
-  float theta, eps;
-  const void* kpool;
-  const void* vpool;
+  const void* q;        // [S*B, n_q*d] rotated, normalised queries
+  const void* kblk;     // [S, n_kv, 32, d]   block keys (rows >= B are zero)
+  const void* vblk;     // [S, n_kv, d, 32]   block values, transposed
+  const void* kpool;    // [pool_pages, n_kv, 16, d]
+  const void* vpool;    // [pool_pages, n_kv, d, 16]
   const int* page_table;
   int pages_per_stream, page_size, pool_pages;
   void* o;              // [S*B, n_q*d]
   float* part_o;        // [S, n_kv, n_chunks, QT, d/16, 64 lanes, 4] fp32
   float* part_ml;       // [S, n_kv, n_chunks, QT*16, 2]
   float scale_log2;     // log2(e) / sqrt(d)
+};
+
+// Block rows' q | k | v projections -> rotated, normalised q and k, and v, in the
+// layouts the attention kernel reads.
+struct QkvFinishParams {
+  int S, B, n_q_heads, n_kv_heads, head_dim;
+  const double* raw;    // [S*B, nq + 2 nkv]
+  const int* ctx_len;
+  int max_ctx;
+  const void* q_norm;
+  const void* k_norm;
+  float theta, eps;
+  void* q;              // [S*B, nq]
+  void* kblk;           // [S, n_kv, 32, d]
+  void* vblk;           // [S, n_kv, d, 32]
 };
 
 struct KvFinishParams {
@@ -84,8 +96,22 @@ struct EmbedParams {
   int S, B, hidden, vocab, mask_token;
   const int* anchor;
   const void* embed;
-  void* x;              // [S*B, hidden]
-  double* ssq;          // [S*B]  sum of squares of each row (one part)
+  const void* gain;     // first layer's input-norm gain
+  float eps;
+  void* x;              // [S*B, hidden] residual stream
+  void* a;              // [S*B, hidden] round(RMSNorm(x) * gain)
+};
+
+// a[r] = round(x[src(r)] / sqrt(mean(x^2) + eps) * gain); the row's sum of squares
+// is the in-order sum of ssq_parts per-tile partials. src(r) = r, or with rowmap_bm1
+// > 0 the r-th mask row: (r / bm1) * (bm1 + 1) + 1 + r % bm1.
+struct NormParams {
+  int R, hidden, ssq_parts, ssq_ld, rowmap_bm1;
+  const void* x;
+  const double* ssq;
+  const void* gain;
+  float eps;
+  void* a;
 };
 
 struct RowNormParams {
@@ -107,24 +133,28 @@ struct VerifyParams {
   int* ctx_len;
 };
 
-// Context chunking of one stream's reach, a function of that reach alone (so a
-// stream's result does not depend on the other streams of the batch):
-//   up to 4096 keys: chunks of ~256 keys; up to 65536: 16 chunks; beyond: ~4096 keys.
-// The chunk count is non-decreasing in the reach, so a grid sized for the longest
+// Context chunking, in pages of 16 keys, of one stream's reach: a function of that
+// reach alone, so a stream's result does not depend on the other streams of the batch.
+// Up to 256 pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 4096 pages
+// the chunk count stays at 256 / kChunkPagesShort; beyond, chunks hold 64 pages.
+// The count never decreases as the reach grows, so a grid sized for the longest
 // reach covers every stream.
-__host__ __device__ inline int attention_chunks(int reach) {
-  if (reach <= 4096) return reach <= 256 ? 1 : (reach + 255) / 256;
-  if (reach <= 65536) return 16;
-  return (reach + 4095) / 4096;
+constexpr int kChunkPagesShort = 8;
+__host__ __device__ inline int attention_chunks(int pages) {
+  if (pages <= 256) return pages <= kChunkPagesShort ? 1 : (pages + kChunkPagesShort - 1) / kChunkPagesShort;
+  if (pages <= 256 / kChunkPagesShort * 64) return 256 / kChunkPagesShort;
+  return (pages + 63) / 64;
 }
-__host__ __device__ inline int attention_chunk_len(int reach) {
-  const int n = attention_chunks(reach);
-  int cl = (reach + n - 1) / n;
-  return (cl + 63) / 64 * 64;
+__host__ __device__ inline int attention_chunk_pages(int pages) {
+  const int n = attention_chunks(pages);
+  return (pages + n - 1) / n;
 }
+// Pages touched by the key range [lo, hi) (page-aligned span).
+__host__ __device__ inline int span_pages(int lo, int hi) { return hi > lo ? (hi + 15) / 16 - lo / 16 : 0; }
 
 int gemm_k_per_iter(int dtype);
 int gemm_tile_cols(int epi);
+int gemm_grid(int n_work);
 hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st);
@@ -133,6 +163,8 @@ hipError_t launch_attention(int dtype, const AttnParams& p, hipStream_t st);
 int attention_query_tiles(int group, int block);
 hipError_t launch_embed(int dtype, const EmbedParams& p, hipStream_t st);
 hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st);
+hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st);
+hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st);
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
 hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st);
 

@@ -1,5 +1,5 @@
-// Small kernels of the draft round: block input gather, fused-row RMSNorm, greedy
-// verify, workspace counter clearing (gfx950).
+// Small kernels of the draft round (gfx950): block input gather, row RMSNorms, the
+// block heads' norm + RoPE, injected K/V placement, greedy verify, workspace clearing.
 #include "common.hpp"
 #include "kernels.h"
 
@@ -16,8 +16,8 @@ __device__ double block_sum_256(double v, double* red) {
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
-// Block rows: X[s*B] = embed[anchor[s]], X[s*B + j] = embed[mask] for j >= 1, and
-// each row's sum of squares for the first layer's input norm.
+// Block rows: X[s*B] = embed[anchor[s]], X[s*B + j] = embed[mask] for j >= 1, and the
+// first layer's normalised input a = round(X / sqrt(mean(X^2) + eps) * gain).
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(const EmbedParams p) {
   constexpr int E = Elem<T>::E;
@@ -38,11 +38,114 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedParams p) {
     for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
   }
   ss = block_sum_256(ss, red);
-  if (threadIdx.x == 0) p.ssq[r] = ss;
+  const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
+  T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
+  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
+    float f[E], gf[E];
+    double y[E];
+    unpack(ldg16(src + c), f, T());
+    unpack(ldg16(static_cast<const T*>(p.gain) + c), gf, T());
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
+    stg16(a + c, pack_d(y, T()));
+  }
+}
+
+// a[r] = round(x[src(r)] * inv_rms * gain), the row's sum of squares being the
+// per-tile partials of the kernel that wrote x, added in a fixed tree order.
+template <typename T>
+__global__ __launch_bounds__(256) void k_norm(const NormParams p) {
+  constexpr int E = Elem<T>::E;
+  __shared__ double red[4];
+  const int r = blockIdx.x;
+  const int bm1 = p.rowmap_bm1;
+  const int xr = bm1 > 0 ? (r / bm1) * (bm1 + 1) + 1 + r % bm1 : r;
+  double ss = 0.0;
+  for (int t = threadIdx.x; t < p.ssq_parts; t += 256) ss += p.ssq[(int64_t)xr * p.ssq_ld + t];
+  ss = block_sum_256(ss, red);
+  const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
+  const T* x = static_cast<const T*>(p.x) + (int64_t)xr * p.hidden;
+  T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
+  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
+    float f[E], gf[E];
+    double y[E];
+    unpack(ldg16(x + c), f, T());
+    unpack(ldg16(static_cast<const T*>(p.gain) + c), gf, T());
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
+    stg16(a + c, pack_d(y, T()));
+  }
+}
+
+// Block rows' heads: q = RoPE(q_norm(raw q)), k = RoPE(k_norm(raw k)), v = raw v,
+// each rounded once. One wave per (row, head); lane l holds the rotary pair
+// (l, l + D/2). k goes to the stream's block key page [32][D], v to its transposed
+// value page [D][32]; the row-0 wave of a head also clears slots B..31 of both.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
+  __shared__ double2 tab[D / 2];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int s = r / p.B, j = r % p.B;
+  int Cs = p.ctx_len[s];
+  Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
+  const int pos = Cs + j;
+  for (int i = tid; i < D / 2; i += 256) {
+    const double inv_freq = pow((double)p.theta, -2.0 * (double)i / (double)D);
+    double sn, cs;
+    sincos((double)pos * inv_freq, &sn, &cs);
+    tab[i] = make_double2(cs, sn);
+  }
+  __syncthreads();
+  const int n_heads = p.n_q_heads + 2 * p.n_kv_heads;
+  const int hi = blockIdx.y * 4 + (tid >> 6);
+  if (hi >= n_heads) return;
+  const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
+  const bool on = lane < D / 2;
+  const double* src = p.raw + (int64_t)r * ld + (int64_t)hi * D;
+  const double x0 = on ? src[lane] : 0.0, x1 = on ? src[lane + D / 2] : 0.0;
+  if (hi >= p.n_q_heads + p.n_kv_heads) {
+    const int vh = hi - p.n_q_heads - p.n_kv_heads;
+    T* vb = static_cast<T*>(p.vblk) + ((int64_t)s * p.n_kv_heads + vh) * (D * kBlockSlots);
+    if (on) {
+      Elem<T>::store_d(vb + lane * kBlockSlots + j, x0);
+      Elem<T>::store_d(vb + (lane + D / 2) * kBlockSlots + j, x1);
+      if (j == 0)
+        for (int jj = p.B; jj < kBlockSlots; ++jj) {
+          Elem<T>::store_d(vb + lane * kBlockSlots + jj, 0.0);
+          Elem<T>::store_d(vb + (lane + D / 2) * kBlockSlots + jj, 0.0);
+        }
+    }
+    return;
+  }
+  const bool is_q = hi < p.n_q_heads;
+  double ss = x0 * x0 + x1 * x1;
+  for (int m = 1; m < kWave; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+  if (!on) return;
+  const double inv = 1.0 / sqrt(ss / (double)D + (double)p.eps);
+  const T* gn = static_cast<const T*>(is_q ? p.q_norm : p.k_norm);
+  const double y0 = x0 * inv * (double)Elem<T>::load1(gn + lane);
+  const double y1 = x1 * inv * (double)Elem<T>::load1(gn + lane + D / 2);
+  const double2 cs = tab[lane];
+  const double o0 = y0 * cs.x - y1 * cs.y, o1 = y1 * cs.x + y0 * cs.y;
+  if (is_q) {
+    T* q = static_cast<T*>(p.q) + (int64_t)r * nq + (int64_t)hi * D;
+    Elem<T>::store_d(q + lane, o0);
+    Elem<T>::store_d(q + lane + D / 2, o1);
+  } else {
+    const int kh = hi - p.n_q_heads;
+    T* kb = static_cast<T*>(p.kblk) + ((int64_t)s * p.n_kv_heads + kh) * (kBlockSlots * D);
+    Elem<T>::store_d(kb + j * D + lane, o0);
+    Elem<T>::store_d(kb + j * D + lane + D / 2, o1);
+    if (j == 0)
+      for (int jj = p.B; jj < kBlockSlots; ++jj) {
+        Elem<T>::store_d(kb + jj * D + lane, 0.0);
+        Elem<T>::store_d(kb + jj * D + lane + D / 2, 0.0);
+      }
+  }
 }
 
 // Context K/V of injected rows: K = RoPE_pos(k_norm(raw k)) per kv head, V = raw v,
-// rounded and written to the row's page slot. One workgroup per (row, layer);
+// rounded and written to the row's page slot (K pages [16][D], V pages [D][16]). One workgroup per (row, layer);
 // D/8 consecutive threads own one head (8 dims each).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
@@ -93,11 +196,17 @@ __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
       const double rot = j < D / 2 ? xn[i] * cs.x - xp * cs.y : xn[i] * cs.x + xp * cs.y;
       o[i] = kind == 0 ? rot : x[i];
     }
-    T* pool = static_cast<T*>(kind == 0 ? p.kpool_l[l] : p.vpool_l[l]);
-    T* dst = pool + (((int64_t)page * p.n_kv_heads + head) * p.page_size + pos % p.page_size) * D + part * 8;
-    constexpr int E = Elem<T>::E;
+    const int64_t ph = (int64_t)page * p.n_kv_heads + head;
+    if (kind == 0) {   // K page [16][D]
+      T* dst = static_cast<T*>(p.kpool_l[l]) + (ph * p.page_size + pos % p.page_size) * D + part * 8;
+      constexpr int E = Elem<T>::E;
 #pragma unroll
-    for (int i = 0; i < 8; i += E) stg16(dst + i, pack_d(o + i, T()));
+      for (int i = 0; i < 8; i += E) stg16(dst + i, pack_d(o + i, T()));
+    } else {           // V page stored transposed, [D][16]
+      T* dst = static_cast<T*>(p.vpool_l[l]) + (ph * D + part * 8) * p.page_size + pos % p.page_size;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Elem<T>::store_d(dst + i * p.page_size, o[i]);
+    }
   }
 }
 
@@ -169,6 +278,24 @@ hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st) 
   } else {
     if (p.head_dim == 64) hipLaunchKernelGGL((k_kv_finish<bf16_t, 64>), grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL((k_kv_finish<bf16_t, 128>), grid, dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st) {
+  if (dtype == 0) hipLaunchKernelGGL(k_norm<float>, dim3(p.R), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(k_norm<bf16_t>, dim3(p.R), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st) {
+  dim3 grid(p.S * p.B, (p.n_q_heads + 2 * p.n_kv_heads + 3) / 4);
+  if (dtype == 0) {
+    if (p.head_dim == 64) hipLaunchKernelGGL((k_qkv_finish<float, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_qkv_finish<float, 128>), grid, dim3(256), 0, st, p);
+  } else {
+    if (p.head_dim == 64) hipLaunchKernelGGL((k_qkv_finish<bf16_t, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_qkv_finish<bf16_t, 128>), grid, dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }
