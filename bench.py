@@ -16,6 +16,7 @@ library records around its own launches, in a second timed pass), and the CPU
 oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -78,14 +79,60 @@ def kernel_costs(p, ctx, rows):
     return k
 
 
+# Source files whose kernels a committed traffic measurement covers, per kernel name.
+KERNEL_SOURCES = {
+    "gate_up_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
+    "lm_head_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
+    "down_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
+    "attention_full": ["attention.hip", "common.hpp", "kernels.h"],
+}
+COPY_CALIBRATION_BYTES = 256 << 20
+
+
+def sources_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "block_diffusion_drafter_dflash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed PMC measurement, or None when
+    there is none for this kernel and workload or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("kernels", []):
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("sources_sha256") == sources_digest(kernel):
+            return int(r["fetch_bytes"] + r["write_bytes"])
+    return None
+
+
+def copy_calibration():
+    """One plain copy-like kernel of known traffic (reads and writes COPY_CALIBRATION_BYTES),
+    outside every timed region, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = COPY_CALIBRATION_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def round_totals(costs):
     b = sum(v["bytes"] * v["launches"] for v in costs.values())
     f = sum(v["flops"] * v["launches"] for v in costs.values())
     return b, f
 
 
-def cpu_baseline(case, sample_streams):
-    """The oracle, as it stands, on one round of the chosen streams."""
+def cpu_baseline(case, sample_streams, min_seconds=10.0):
+    """The oracle, as it stands, on whole rounds of the chosen streams, repeated until
+    at least min_seconds of CPU work have been timed."""
     from oracle import dflash_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -94,14 +141,18 @@ def cpu_baseline(case, sample_streams):
         threads = os.cpu_count() or 1
     W = case.weights_np()
     streams = case.oracle_streams(sample_streams)
-    t0 = time.perf_counter()
-    out = O.run_round(case.p, W, streams)
-    dt = time.perf_counter() - t0
+    reps, total, out = 0, 0.0, None
+    while total < min_seconds:
+        t0 = time.perf_counter()
+        out = O.run_round(case.p, W, streams)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
     drafted = len(sample_streams) * (case.p.block_size - 1)
-    return dict(value=drafted / dt, unit="drafted tokens/s", cores=int(threads), kind="oracle",
-                sample=f"one whole round (fuse {sum(case.rows[s] for s in sample_streams)} rows, inject, "
-                       f"draft, verify inputs) of streams {sample_streams} of the same workload, float64 numpy; "
-                       f"{dt:.2f} s", seconds=dt), out
+    return dict(value=round(drafted / dt, 3), unit="drafted tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{reps} whole rounds (fuse {sum(case.rows[s] for s in sample_streams)} rows, inject, "
+                       f"draft) of stream(s) {sample_streams} of the same workload, float64 numpy; "
+                       f"{dt:.2f} s per round", seconds=round(total, 2)), out
 
 
 def main():
@@ -188,7 +239,7 @@ def main():
         roof = dict(bound="mfma", achieved=round(kd["tflops"], 2), peak=mfma_dtype_peak, unit="TFLOP/s",
                     frac=round(kd["tflops"] / mfma_dtype_peak, 4))
     roof.update(kernel=dom, bytes_per_launch=costs[dom]["bytes"], flops_per_launch=costs[dom]["flops"],
-                avg_launch_ms=round(kd["avg_ms"], 5), traffic=None)
+                avg_launch_ms=round(kd["avg_ms"], 5), traffic=measured_traffic(dom, p.name))
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "drafted tokens/s", "n_gpus": 1,
@@ -205,6 +256,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])},
     }
+    copy_calibration()
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline (one round)", file=sys.stderr, flush=True)
         sample = [0] if S == 1 else [int(min(range(S), key=lambda s: case.ctx[s]))]

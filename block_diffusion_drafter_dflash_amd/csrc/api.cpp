@@ -27,6 +27,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
 
+namespace dfl {
+thread_local ProfEvents* g_prof = nullptr;
+}
+
 struct ProfRec {
   std::string name;
   hipEvent_t a, b;
@@ -44,10 +48,10 @@ struct dflash {
 
   ~dflash() {
     for (auto& r : prof) {
-      hipEventDestroy(r.a);
-      hipEventDestroy(r.b);
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
     }
-    for (auto e : event_pool) hipEventDestroy(e);
+    for (auto e : event_pool) (void)hipEventDestroy(e);
   }
   hipEvent_t take_event() {
     if (!event_pool.empty()) {
@@ -356,27 +360,36 @@ int dflash_workspace_init(dflash* h, void* ws, size_t ws_bytes, void* stream) {
   return DFLASH_OK;
 }
 
-// Brackets one launch with events when profiling is on.
+// Times the launches made inside it when profiling is on: the events are recorded by
+// the dispatches themselves (start of the first, end of the last), so the interval
+// is the kernels' own execution, free of event-packet overhead.
 struct ProfScope {
   dflash* h;
   const char* name;
-  hipStream_t st;
-  hipEvent_t a = nullptr;
-  ProfScope(dflash* h_, const char* n, hipStream_t s) : h(h_), name(n), st(s) {
-    if (h->profiling) {
-      a = h->take_event();
-      if (a) hipEventRecord(a, st);
+  ProfEvents ev{nullptr, nullptr, false};
+  ProfEvents* prev = nullptr;
+  bool active = false;
+  ProfScope(dflash* h_, const char* n, hipStream_t) : h(h_), name(n) {
+    if (!h->profiling) return;
+    ev.start = h->take_event();
+    ev.stop = h->take_event();
+    if (!ev.start || !ev.stop) {
+      if (ev.start) h->event_pool.push_back(ev.start);
+      if (ev.stop) h->event_pool.push_back(ev.stop);
+      return;
     }
+    prev = g_prof;
+    g_prof = &ev;
+    active = true;
   }
   ~ProfScope() {
-    if (a) {
-      hipEvent_t b = h->take_event();
-      if (b) {
-        hipEventRecord(b, st);
-        h->prof.push_back({name, a, b});
-      } else {
-        h->event_pool.push_back(a);
-      }
+    if (!active) return;
+    g_prof = prev;
+    if (ev.used) {
+      h->prof.push_back({name, ev.start, ev.stop});
+    } else {
+      h->event_pool.push_back(ev.start);
+      h->event_pool.push_back(ev.stop);
     }
   }
 };

@@ -3,11 +3,12 @@
 // Workgroup = (context chunk, kv head, stream) with QT waves; wave w owns 16 of the
 // kv head's g * B queries (its g q-heads times the B block rows). Keys are the
 // context rows in the layer's reach, read from the paged cache, plus all B block
-// rows (added by the stream's last chunk). A step covers two 16-key pages: every
-// lane loads its MFMA fragments straight from the pages with 16-byte reads (K pages
-// are [16 keys][d]; V pages are stored transposed, [d][16 keys], so both operands
-// are contiguous along the MFMA's reduction), and the next step's reads are in
-// flight while the current one is multiplied.
+// rows (added by the stream's last chunk). A step covers two 16-key pages. The
+// workgroup stages each step once into LDS - K pages are [16 keys][d] and V pages
+// are stored transposed, [d][16 keys], so every thread copies whole 16-byte pieces
+// and both MFMA operands are contiguous along the reduction - with the cache reads
+// of the next two steps in flight, and every wave reads its MFMA fragments from
+// LDS (padded rows: conflict-free 16-byte reads).
 // Scores are computed transposed (S^T = K Q^T) so that each lane owns one query:
 // the softmax statistics are lane-local plus two cross-lane-group shuffles, and the
 // probabilities feed the P.V MFMA without a transpose. P (fp32) enters the bf16
@@ -20,13 +21,17 @@
 
 namespace dfl {
 
-template <typename T, int D>
+template <typename T, int D, int QT>
 struct AttnCfg {
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int E = Elem<T>::E;
   static constexpr int NF = D / 4 / E;                // 16-byte K fragments per lane per 16-key tile
   static constexpr int NDT = D / 16;                  // 16-dim output tiles
-  static constexpr int NV = BF ? NDT : 2 * NDT;       // 16-byte V fragments per lane per step
+  static constexpr int NTHR = 64 * QT;
+  static constexpr int LDK = D + 16 / (int)sizeof(T); // K row stride (elements): +16 bytes
+  static constexpr int LDV = 32 + 16 / (int)sizeof(T);// V^T row stride (elements): +16 bytes
+  static constexpr int NC = 32 * D / E;               // 16-byte pieces of K (and of V) per step
+  static constexpr int NI = (NC + NTHR - 1) / NTHR;   // pieces of each per thread per step
 };
 
 // Key (0..31 within the step's two pages) supplied as row r of S^T tile t. For bf16
@@ -44,11 +49,19 @@ struct StepSrc {
   int key0;             // absolute position of the step's first key; -1 for the block
 };
 
+template <int NI>
+struct Stage {
+  uint4 k[NI], v[NI];
+};
+
 template <typename T, int D, int QT>
-__global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
-  using C = AttnCfg<T, D>;
+__global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const AttnParams p) {
+  using C = AttnCfg<T, D, QT>;
   constexpr bool BF = C::BF;
-  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NV = C::NV;
+  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NTHR = C::NTHR, NC = C::NC, NI = C::NI;
+  constexpr int LDK = C::LDK, LDV = C::LDV;
+  __shared__ __attribute__((aligned(16))) T ks[2][32][LDK];
+  __shared__ __attribute__((aligned(16))) T vts[2][D][LDV];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -126,60 +139,53 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
   };
   // A key's validity: on a page, and inside the reach (context) or a block row (block).
   auto key_ok = [&](const StepSrc& src, int kk) {
-    if (!src.k[kk >> 4]) return false;
+    if (!(kk < 16 ? src.k[0] : src.k[1])) return false;
     if (src.key0 < 0) return kk < B;
     const int pos = src.key0 + kk;
     return pos >= lo && pos < Cs;
   };
-  auto fetch = [&](const StepSrc& src, uint4 (&kf)[2][NF], uint4 (&vf)[NV]) {
+  // Cooperative cache reads of one step: piece i of K is (half, key row, 16-byte part),
+  // piece i of V^T is (half, dim, 16-byte part of the half's 16 keys).
+  auto fetch = [&](int step, Stage<NI>& r) {
+    const StepSrc src = source(step);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int kk = key_of_row<BF>(t, lr);
-      const T* kb = static_cast<const T*>(src.k[kk >> 4]);
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        kf[t][f] = kb ? ldg16(kb + (kk & 15) * D + lg * (D / 4) + f * E) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int i = tid + j * NTHR;
+      r.k[j] = make_uint4(0, 0, 0, 0);
+      r.v[j] = make_uint4(0, 0, 0, 0);
+      if (i < NC) {
+        const int hf = i / (NC / 2), rem = i % (NC / 2);
+        const T* kb = static_cast<const T*>(hf ? src.k[1] : src.k[0]);
+        const T* vb = static_cast<const T*>(hf ? src.v[1] : src.v[0]);
+        if (kb) r.k[j] = ldg16(kb + (rem / (D / E)) * D + (rem % (D / E)) * E);
+        if (vb) r.v[j] = ldg16(vb + (int64_t)(rem / (16 / E)) * src.vld + (rem % (16 / E)) * E);
+      }
     }
-    if constexpr (BF) {
-      // lane group lg: keys 8lg..8lg+7 = half lg/2, slots 8(lg&1)..
-      const T* vb = static_cast<const T*>(src.v[lg >> 1]);
+  };
+  auto stage = [&](int buf, const Stage<NI>& r) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        vf[dt] = vb ? ldg16(vb + (int64_t)(16 * dt + lr) * src.vld + 8 * (lg & 1)) : make_uint4(0, 0, 0, 0);
-    } else {
-      // tile t, lane group lg: keys 16t + 4lg.. = half t, slots 4lg..
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const T* vb = static_cast<const T*>(src.v[t]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          vf[t * NDT + dt] = vb ? ldg16(vb + (int64_t)(16 * dt + lr) * src.vld + 4 * lg) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int i = tid + j * NTHR;
+      if (i < NC) {
+        const int hf = i / (NC / 2), rem = i % (NC / 2);
+        *reinterpret_cast<uint4*>(&ks[buf][hf * 16 + rem / (D / E)][(rem % (D / E)) * E]) = r.k[j];
+        *reinterpret_cast<uint4*>(&vts[buf][rem / (16 / E)][hf * 16 + (rem % (16 / E)) * E]) = r.v[j];
       }
     }
   };
 
-  uint4 kc[2][NF], vc[NV];
-  StepSrc cur;
-  if (n_steps > 0) {
-    cur = source(0);
-    fetch(cur, kc, vc);
-  }
-  for (int st = 0; st < n_steps; ++st) {
-    StepSrc nxt = cur;
-    uint4 kn[2][NF], vn[NV];
-    const bool more = st + 1 < n_steps;
-    if (more) {
-      nxt = source(st + 1);
-      fetch(nxt, kn, vn);
-    }
+  auto compute = [&](int step) {
+    const int buf = step & 1;
+    const StepSrc cur = source(step);
 
     // ---- S^T = K Q^T: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i)
     floatx4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const T* krow = &ks[buf][key_of_row<BF>(t, lr)][lg * (D / 4)];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) mma_frag(sacc[t], kc[t][f], qf[f], T());
+      for (int f = 0; f < NF; ++f) mma_frag(sacc[t], *reinterpret_cast<const uint4*>(krow + f * E), qf[f], T());
     }
 
     // ---- online softmax (base 2); the denominator sums in float64
@@ -209,45 +215,16 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
     l_run = l_run * corr + psum;
     m_run = m_new;
 
-    // Values of keys outside the reach may be stale or never written: zero them so
-    // that a zero probability times a non-finite value cannot reach the output.
-    if (edge) {
-      if constexpr (BF) {
-        const int kb = 8 * lg;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          uint32_t wv[4] = {vc[dt].x, vc[dt].y, vc[dt].z, vc[dt].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t m0 = key_ok(cur, kb + 2 * q) ? 0x0000ffffu : 0u;
-            const uint32_t m1 = key_ok(cur, kb + 2 * q + 1) ? 0xffff0000u : 0u;
-            wv[q] &= (m0 | m1);
-          }
-          vc[dt] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            uint4& v = vc[t * NDT + dt];
-            const int k0 = 16 * t + 4 * lg;
-            v.x = key_ok(cur, k0) ? v.x : 0u;
-            v.y = key_ok(cur, k0 + 1) ? v.y : 0u;
-            v.z = key_ok(cur, k0 + 2) ? v.z : 0u;
-            v.w = key_ok(cur, k0 + 3) ? v.w : 0u;
-          }
-      }
-    }
-
-    // ---- this step's O^T = V^T P^T, added to the float64 running output
+    // ---- this step's O^T = V^T P^T, added to the float64 running output. Values of
+    // keys outside the reach may be stale or never written: they are zeroed so that a
+    // zero probability times a non-finite value cannot reach the output.
     floatx4 ot[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) ot[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if constexpr (BF) {
       // P as hi + mid + lo bf16 parts (each remainder is exact in fp32): 24 bits.
       const float pv[8] = {pf[0][0], pf[0][1], pf[0][2], pf[0][3], pf[1][0], pf[1][1], pf[1][2], pf[1][3]};
-      uint32_t hw[4], mw[4], lw[4];
+      uint32_t hw[4], mw[4], lw[4], keep[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         hw[q] = f32x2_to_bf16x2(pv[2 * q], pv[2 * q + 1]);
@@ -255,39 +232,68 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
         const float r1 = pv[2 * q + 1] - bf16_to_f32(hw[q] >> 16);
         mw[q] = f32x2_to_bf16x2(r0, r1);
         lw[q] = f32x2_to_bf16x2(r0 - bf16_to_f32(mw[q] & 0xffffu), r1 - bf16_to_f32(mw[q] >> 16));
+        keep[q] = 0xffffffffu;
+        if (edge)
+          keep[q] = (key_ok(cur, 8 * lg + 2 * q) ? 0x0000ffffu : 0u) | (key_ok(cur, 8 * lg + 2 * q + 1) ? 0xffff0000u : 0u);
       }
       const uint4 bh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       const uint4 bm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       const uint4 bl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        mma_frag(ot[dt], vc[dt], bh, T());
-        mma_frag(ot[dt], vc[dt], bm, T());
-        mma_frag(ot[dt], vc[dt], bl, T());
+        uint4 vf = *reinterpret_cast<const uint4*>(&vts[buf][16 * dt + lr][8 * lg]);
+        vf.x &= keep[0];
+        vf.y &= keep[1];
+        vf.z &= keep[2];
+        vf.w &= keep[3];
+        mma_frag(ot[dt], vf, bh, T());
+        mma_frag(ot[dt], vf, bm, T());
+        mma_frag(ot[dt], vf, bl, T());
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint4 pb = make_uint4(__float_as_uint(pf[t][0]), __float_as_uint(pf[t][1]), __float_as_uint(pf[t][2]),
                                     __float_as_uint(pf[t][3]));
+        const int k0 = 16 * t + 4 * lg;
+        const bool ok0 = !edge || key_ok(cur, k0), ok1 = !edge || key_ok(cur, k0 + 1);
+        const bool ok2 = !edge || key_ok(cur, k0 + 2), ok3 = !edge || key_ok(cur, k0 + 3);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) mma_frag(ot[dt], vc[t * NDT + dt], pb, T());
+        for (int dt = 0; dt < NDT; ++dt) {
+          uint4 vf = *reinterpret_cast<const uint4*>(&vts[buf][16 * dt + lr][k0]);
+          vf.x = ok0 ? vf.x : 0u;
+          vf.y = ok1 ? vf.y : 0u;
+          vf.z = ok2 ? vf.z : 0u;
+          vf.w = ok3 ? vf.w : 0u;
+          mma_frag(ot[dt], vf, pb, T());
+        }
       }
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[dt][i] = oacc[dt][i] * corr + (double)ot[dt][i];
+  };
 
-    if (more) {
-      cur = nxt;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) kc[t][f] = kn[t][f];
-#pragma unroll
-      for (int i = 0; i < NV; ++i) vc[i] = vn[i];
-    }
+  // Pipeline: step st is in LDS buffer st & 1 while the cache reads of steps st + 1
+  // and st + 2 are in flight in two register stages used alternately.
+  Stage<NI> ra, rb;
+  if (n_steps > 0) {
+    fetch(0, ra);
+    if (n_steps > 1) fetch(1, rb);
+    stage(0, ra);
+  }
+  __syncthreads();
+  // body(st, nxt, fre): nxt holds step st + 1's reads; fre is free for step st + 2.
+  auto body = [&](int st, Stage<NI>& nxt, Stage<NI>& fre) {
+    if (st + 2 < n_steps) fetch(st + 2, fre);
+    compute(st);
+    if (st + 1 < n_steps) stage((st + 1) & 1, nxt);
+    __syncthreads();
+  };
+  for (int st = 0; st < n_steps; st += 2) {
+    body(st, rb, ra);
+    if (st + 1 < n_steps) body(st + 1, ra, rb);
   }
 
   double l_tot = l_run;
@@ -318,13 +324,11 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
 
   // ---- this chunk's (max, sum, unnormalised output) for k_attn_combine
   const int64_t sh = (int64_t)s * p.n_kv_heads + h;
-  const int64_t chunk_id = sh * p.n_chunks + c;
   if (lg == 0) {
-    float* ml = p.part_ml + (chunk_id * (QT * 16) + qi) * 2;
-    ml[0] = m_run;
-    ml[1] = (float)l_tot;
+    float* ml = p.part_ml + ((sh * (QT * 16) + qi) * p.n_chunks + c) * 2;
+    *reinterpret_cast<float2*>(ml) = make_float2(m_run, (float)l_tot);
   }
-  float* op = p.part_o + ((chunk_id * QT + w) * NDT) * (kWave * 4);
+  float* op = p.part_o + (((sh * p.n_chunks + c) * QT + w) * NDT) * (kWave * 4);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
     *reinterpret_cast<float4*>(op + (dt * kWave + lane) * 4) =
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(64 * QT) void k_attn(const AttnParams p) {
 }
 
 // Combine the chunks of one (stream, kv head, query tile, 16-dim slice) in chunk order.
+// A lane's query has its chunks' (max, sum) pairs contiguous.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_attn_combine(const AttnParams p, int QT) {
   constexpr int NDT = D / 16;
@@ -340,18 +345,18 @@ __global__ __launch_bounds__(64) void k_attn_combine(const AttnParams p, int QT)
   const int s = sh / p.n_kv_heads, h = sh % p.n_kv_heads;
   const int qi = 16 * qt + lr;
   if (qi >= p.group * p.B) return;
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + qi) * p.n_chunks;
   float M = -INFINITY;
-  for (int cc = 0; cc < p.n_chunks; ++cc)
-    M = fmaxf(M, p.part_ml[(((int64_t)sh * p.n_chunks + cc) * (QT * 16) + qi) * 2]);
+  for (int cc = 0; cc < p.n_chunks; ++cc) M = fmaxf(M, ml[cc].x);
   double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
+  const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
+  const int64_t cstride = (int64_t)QT * NDT * (kWave * 4);
+#pragma unroll 8
   for (int cc = 0; cc < p.n_chunks; ++cc) {
-    const int64_t chunk_id = (int64_t)sh * p.n_chunks + cc;
-    const float* ml = p.part_ml + (chunk_id * (QT * 16) + qi) * 2;
-    const double f = (ml[0] == -INFINITY) ? 0.0 : exp2((double)ml[0] - (double)M);
-    L += (double)ml[1] * f;
-    const float4 v =
-        *reinterpret_cast<const float4*>(p.part_o + ((chunk_id * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4);
+    const float2 m = ml[cc];
+    const float4 v = *reinterpret_cast<const float4*>(po + cc * cstride);
+    const double f = (m.x == -INFINITY) ? 0.0 : exp2((double)m.x - (double)M);
+    L += (double)m.y * f;
     o[0] += (double)v.x * f;
     o[1] += (double)v.y * f;
     o[2] += (double)v.z * f;
@@ -368,7 +373,7 @@ int attention_query_tiles(int group, int block) { return (group * block + 15) / 
 template <typename T, int D, int QT>
 static void launch_qt(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.n_chunks, p.n_kv_heads, p.S);
-  hipLaunchKernelGGL((k_attn<T, D, QT>), grid, dim3(64 * QT), 0, st, p);
+  launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
 }
 
 template <typename T, int D>
@@ -386,7 +391,7 @@ static hipError_t launch_td(const AttnParams& p, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
-  hipLaunchKernelGGL((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64), 0, st, p, qt);
+  launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64), st, p, qt);
   return hipGetLastError();
 }
 

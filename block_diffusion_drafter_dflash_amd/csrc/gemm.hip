@@ -276,7 +276,7 @@ int gemm_grid(int n_work) {
 
 template <typename T, int MT, int NT, int EPI>
 static hipError_t launch_t(const GemmParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm<T, MT, NT, EPI>), dim3(gemm_grid(p.n_work)), dim3(kGemmThreads), 0, st, p);
+  launch_k((k_gemm<T, MT, NT, EPI>), dim3(gemm_grid(p.n_work)), dim3(kGemmThreads), st, p);
   return hipGetLastError();
 }
 
@@ -308,7 +308,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStrea
 
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax_final, dim3(rows), dim3(256), 0, st, reinterpret_cast<const float4*>(tile_res),
+  launch_k(k_argmax_final, dim3(rows), dim3(256), st, reinterpret_cast<const float4*>(tile_res),
                      n_tiles, draft_out, top2_out);
   return hipGetLastError();
 }

@@ -1,7 +1,10 @@
 // Kernel parameter blocks and launchers of the draft round (host + device).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 namespace dfl {
 
@@ -151,6 +154,27 @@ __host__ __device__ inline int attention_chunk_pages(int pages) {
 }
 // Pages touched by the key range [lo, hi) (page-aligned span).
 __host__ __device__ inline int span_pages(int lo, int hi) { return hi > lo ? (hi + 15) / 16 - lo / 16 : 0; }
+
+// Launch timing for the library's own profiling: while a scope is active on this
+// thread, the first launch records `start` as its dispatch begins and every launch
+// records `stop` as it ends (the last one's time stands), both on the launch's stream.
+struct ProfEvents {
+  hipEvent_t start, stop;
+  bool used;
+};
+extern thread_local ProfEvents* g_prof;
+
+template <typename F, typename... Args>
+inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_prof) {
+    if (!g_prof->used) a = g_prof->start;
+    g_prof->used = true;
+    b = g_prof->stop;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+  return hipGetLastError();
+}
 
 int gemm_k_per_iter(int dtype);
 int gemm_tile_cols(int epi);
