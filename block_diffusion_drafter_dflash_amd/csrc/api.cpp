@@ -90,13 +90,13 @@ struct GemmPlan {
 
 // Rows are processed in groups of 16 * mt (mt = 1 or 2); every workgroup owns one
 // column tile over the whole K, so the per-row arithmetic never depends on M.
-GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K) {
+GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int tap_h = 0) {
   GemmPlan g;
   g.mt = M <= 16 ? 1 : 2;
   g.mgroups = (M + 16 * g.mt - 1) / (16 * g.mt);
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
-  g.iters = K / gemm_k_per_iter(dtype);
+  g.iters = K / gemm_k_per_iter(dtype, epi, K, tap_h);
   g.n_work = g.n_tiles * g.mgroups;
   return g;
 }
@@ -139,7 +139,7 @@ struct FuseLayout {
 FuseLayout layout_fuse(const dflash& h, int R) {
   FuseLayout L;
   const auto& c = h.cfg;
-  L.g = plan_gemm(c.dtype, EPI_FC, R, c.hidden, c.n_taps * c.hidden);
+  L.g = plan_gemm(c.dtype, EPI_FC, R, c.hidden, c.n_taps * c.hidden, c.hidden);
   Region r;
   r.take(kCounterInts * 4);
   L.y = r.take((size_t)R * c.hidden * 8);

@@ -373,7 +373,7 @@ int attention_query_tiles(int group, int block) { return (group * block + 15) / 
 template <typename T, int D, int QT>
 static void launch_qt(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.n_chunks, p.n_kv_heads, p.S);
-  launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
+  (void)launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
 }
 
 template <typename T, int D>
@@ -391,7 +391,7 @@ static hipError_t launch_td(const AttnParams& p, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
-  launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64), st, p, qt);
+  (void)launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64), st, p, qt);
   return hipGetLastError();
 }
 

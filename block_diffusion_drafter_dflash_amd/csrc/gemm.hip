@@ -18,17 +18,23 @@
 
 namespace dfl {
 
-constexpr int kKW = 8;                  // waves per workgroup, splitting K
-constexpr int kGemmThreads = kKW * kWave;
-constexpr int kGemmGroupsPerCU = 2;
-constexpr int kCUs = 256;
+// Tuning of one GEMM kernel: KW waves per workgroup split K; each lane reads U
+// 16-byte fragments (U * 16 contiguous bytes) of each of its rows per iteration.
+template <int KW_, int U_>
+struct GemmTune {
+  static constexpr int KW = KW_;
+  static constexpr int U = U_;
+};
+using DefaultTune = GemmTune<8, 4>;
 
-template <typename T>
+template <typename T, typename Tune>
 struct GemmCfg {
   static constexpr int E = Elem<T>::E;
   static constexpr int KF = Elem<T>::KF;
-  static constexpr int U = 4;           // 16-byte fragments per lane per row per iteration
+  static constexpr int KW = Tune::KW;
+  static constexpr int U = Tune::U;
   static constexpr int KI = U * KF;     // k-elements per iteration
+  static constexpr int THREADS = KW * kWave;
 };
 
 __device__ __forceinline__ void top_merge(float& v1, int& i1, float& v2, float bv1, int bi1, float bv2) {
@@ -72,10 +78,10 @@ __device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile, in
   }
 }
 
-template <typename T, int MT, int NT, int EPI>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmParams p) {
-  using C = GemmCfg<T>;
-  constexpr int E = C::E, U = C::U, KI = C::KI;
+template <typename T, int MT, int NT, int EPI, typename Tune = DefaultTune>
+__global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
+  using C = GemmCfg<T, Tune>;
+  constexpr int E = C::E, U = C::U, KI = C::KI, kKW = C::KW, kGemmThreads = C::THREADS;
   constexpr int AM = EPI == EPI_FC ? A_TAPS : A_PLAIN;
   constexpr int ROWS = 16 * MT, COLS = 16 * NT;
   __shared__ float red[kKW][ROWS][COLS + 1];
@@ -269,15 +275,52 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float4* tile_res, in
 
 // ------------------------------------------------------------------ host launchers
 
-int gemm_grid(int n_work) {
-  const int cap = kCUs * kGemmGroupsPerCU;
-  return n_work < cap ? n_work : cap;
+// Persistent grid: as many workgroups as the device holds at once (its CU count times
+// the kernel's resident workgroups per CU), capped by the work items.
+template <typename T, int MT, int NT, int EPI, typename Tune>
+static int resident_grid(int n_work) {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm<T, MT, NT, EPI, Tune>,
+                                                     GemmCfg<T, Tune>::THREADS, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    cached[dev] = cus * per_cu;
+  }
+  return n_work < cached[dev] ? n_work : cached[dev];
+}
+
+// Tuning per GEMM kind, from a sweep over (waves, bytes per lane per row and
+// iteration, grid) on the 9B round's shapes: the wide-N kinds run one workgroup per
+// tile with 32-byte reads per lane and row, the fc GEMM (N = hidden, K = taps x
+// hidden) keeps a resident grid with 128-byte reads when hidden allows it.
+enum TuneId { TUNE_W8_U2 = 0, TUNE_W4_U2 = 1, TUNE_W4_U8 = 2, TUNE_W8_U4 = 3 };
+
+static int tune_of(int epi, int K, int tap_h) {
+  if (epi == EPI_LMHEAD) return TUNE_W4_U2;
+  if (epi == EPI_FC) return tap_h % 256 == 0 && K % 256 == 0 ? TUNE_W4_U8 : TUNE_W8_U4;
+  return TUNE_W8_U2;
+}
+
+template <typename T, int MT, int NT, int EPI, typename Tune>
+static hipError_t launch_tuned(const GemmParams& p, bool persistent, hipStream_t st) {
+  const int grid = persistent ? resident_grid<T, MT, NT, EPI, Tune>(p.n_work) : p.n_work;
+  (void)launch_k(k_gemm<T, MT, NT, EPI, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
+  return hipGetLastError();
 }
 
 template <typename T, int MT, int NT, int EPI>
 static hipError_t launch_t(const GemmParams& p, hipStream_t st) {
-  launch_k((k_gemm<T, MT, NT, EPI>), dim3(gemm_grid(p.n_work)), dim3(kGemmThreads), st, p);
-  return hipGetLastError();
+  switch (tune_of(EPI, p.K, p.tap_h)) {
+    case TUNE_W4_U2: return launch_tuned<T, MT, NT, EPI, GemmTune<4, 2>>(p, false, st);
+    case TUNE_W4_U8: return launch_tuned<T, MT, NT, EPI, GemmTune<4, 8>>(p, true, st);
+    case TUNE_W8_U4: return launch_tuned<T, MT, NT, EPI, GemmTune<8, 4>>(p, true, st);
+    default: return launch_tuned<T, MT, NT, EPI, GemmTune<8, 2>>(p, false, st);
+  }
 }
 
 template <typename T, int EPI, int NT>
@@ -297,7 +340,14 @@ static hipError_t launch_epi(const GemmParams& p, int epi, int mt, hipStream_t s
   }
 }
 
-int gemm_k_per_iter(int dtype) { return dtype == 0 ? GemmCfg<float>::KI : GemmCfg<bf16_t>::KI; }
+int gemm_k_per_iter(int dtype, int epi, int K, int tap_h) {
+  const int kf = dtype == 0 ? Elem<float>::KF : Elem<bf16_t>::KF;
+  switch (tune_of(epi, K, tap_h)) {
+    case TUNE_W4_U8: return 8 * kf;
+    case TUNE_W8_U4: return 4 * kf;
+    default: return 2 * kf;
+  }
+}
 
 int gemm_tile_cols(int epi) { return (epi == EPI_SWIGLU || epi == EPI_LMHEAD) ? 32 : 16; }
 
@@ -308,7 +358,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStrea
 
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st) {
-  launch_k(k_argmax_final, dim3(rows), dim3(256), st, reinterpret_cast<const float4*>(tile_res),
+  (void)launch_k(k_argmax_final, dim3(rows), dim3(256), st, reinterpret_cast<const float4*>(tile_res),
                      n_tiles, draft_out, top2_out);
   return hipGetLastError();
 }

@@ -176,9 +176,8 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t st, Args
   return hipGetLastError();
 }
 
-int gemm_k_per_iter(int dtype);
+int gemm_k_per_iter(int dtype, int epi, int K, int tap_h);
 int gemm_tile_cols(int epi);
-int gemm_grid(int n_work);
 hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st);

@@ -265,56 +265,56 @@ __global__ void k_fill_zero(int* p, int64_t n) {
 }
 
 hipError_t launch_embed(int dtype, const EmbedParams& p, hipStream_t st) {
-  if (dtype == 0) launch_k(k_embed<float>, dim3(p.S * p.B), dim3(256), st, p);
-  else launch_k(k_embed<bf16_t>, dim3(p.S * p.B), dim3(256), st, p);
+  if (dtype == 0) (void)launch_k(k_embed<float>, dim3(p.S * p.B), dim3(256), st, p);
+  else (void)launch_k(k_embed<bf16_t>, dim3(p.S * p.B), dim3(256), st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st) {
   dim3 grid(p.R, p.n_layers);
   if (dtype == 0) {
-    if (p.head_dim == 64) launch_k((k_kv_finish<float, 64>), grid, dim3(256), st, p);
-    else launch_k((k_kv_finish<float, 128>), grid, dim3(256), st, p);
+    if (p.head_dim == 64) (void)launch_k((k_kv_finish<float, 64>), grid, dim3(256), st, p);
+    else (void)launch_k((k_kv_finish<float, 128>), grid, dim3(256), st, p);
   } else {
-    if (p.head_dim == 64) launch_k((k_kv_finish<bf16_t, 64>), grid, dim3(256), st, p);
-    else launch_k((k_kv_finish<bf16_t, 128>), grid, dim3(256), st, p);
+    if (p.head_dim == 64) (void)launch_k((k_kv_finish<bf16_t, 64>), grid, dim3(256), st, p);
+    else (void)launch_k((k_kv_finish<bf16_t, 128>), grid, dim3(256), st, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st) {
-  if (dtype == 0) launch_k(k_norm<float>, dim3(p.R), dim3(256), st, p);
-  else launch_k(k_norm<bf16_t>, dim3(p.R), dim3(256), st, p);
+  if (dtype == 0) (void)launch_k(k_norm<float>, dim3(p.R), dim3(256), st, p);
+  else (void)launch_k(k_norm<bf16_t>, dim3(p.R), dim3(256), st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st) {
   dim3 grid(p.S * p.B, (p.n_q_heads + 2 * p.n_kv_heads + 3) / 4);
   if (dtype == 0) {
-    if (p.head_dim == 64) launch_k((k_qkv_finish<float, 64>), grid, dim3(256), st, p);
-    else launch_k((k_qkv_finish<float, 128>), grid, dim3(256), st, p);
+    if (p.head_dim == 64) (void)launch_k((k_qkv_finish<float, 64>), grid, dim3(256), st, p);
+    else (void)launch_k((k_qkv_finish<float, 128>), grid, dim3(256), st, p);
   } else {
-    if (p.head_dim == 64) launch_k((k_qkv_finish<bf16_t, 64>), grid, dim3(256), st, p);
-    else launch_k((k_qkv_finish<bf16_t, 128>), grid, dim3(256), st, p);
+    if (p.head_dim == 64) (void)launch_k((k_qkv_finish<bf16_t, 64>), grid, dim3(256), st, p);
+    else (void)launch_k((k_qkv_finish<bf16_t, 128>), grid, dim3(256), st, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st) {
-  if (dtype == 0) launch_k(k_rownorm<float>, dim3(p.R), dim3(256), st, p);
-  else launch_k(k_rownorm<bf16_t>, dim3(p.R), dim3(256), st, p);
+  if (dtype == 0) (void)launch_k(k_rownorm<float>, dim3(p.R), dim3(256), st, p);
+  else (void)launch_k(k_rownorm<bf16_t>, dim3(p.R), dim3(256), st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st) {
-  launch_k(k_verify, dim3(p.S), dim3(64), st, p);
+  (void)launch_k(k_verify, dim3(p.S), dim3(64), st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st) {
   int blocks = (int)((n + 255) / 256);
   blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-  launch_k(k_fill_zero, dim3(blocks), dim3(256), st, p, n);
+  (void)launch_k(k_fill_zero, dim3(blocks), dim3(256), st, p, n);
   return hipGetLastError();
 }
 
