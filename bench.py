@@ -34,9 +34,11 @@ FP32_TFLOPS = 157.3
 def kernel_costs(p, ctx, rows):
     """Algorithmic bytes and FLOPs per launch of each kernel of one round.
 
-    Bytes: each weight once per call that reads it, activations read and written once
-    per kernel, float64 intermediates at 8 bytes, context K/V read once per layer over
-    the exact keys of each stream's reach (no page rounding).
+    Bytes are what the method itself must move: each weight once per call that reads
+    it, the tap planes, the stored activations at their storage size (bf16, or fp32
+    for fp32 presets) read and written once, context K/V read once over the exact keys
+    of each stream's reach. Implementation intermediates (float64 partial sums, chunk
+    partials) are not counted.
     """
     es = 4 if p.dtype == "f32" else 2
     h, L, d, I, V, B = p.hidden, p.n_layers, p.head_dim, p.intermediate, p.vocab, p.block_size
@@ -44,19 +46,18 @@ def kernel_costs(p, ctx, rows):
     S = len(ctx)
     R = sum(rows)
     M, Mm = S * B, S * (B - 1)
-    n16 = h // 16                       # per-tile sums of squares of a residual row
     k = {}
-    k["fuse_fc_gemm"] = dict(bytes=(h * n * h + R * n * h) * es + R * h * 8 + R * n16 * 8, flops=2 * R * n * h * h)
-    k["fuse_rownorm"] = dict(bytes=R * h * 8 + R * n16 * 8 + R * h * es + h * es, flops=3 * R * h)
-    k["inject_kv_gemm"] = dict(bytes=(L * 2 * nkv * h + R * h) * es + L * 2 * R * nkv * 8, flops=2 * R * h * L * 2 * nkv)
-    k["inject_kv_finish"] = dict(bytes=L * 2 * R * nkv * (8 + es) + L * d * es, flops=6 * L * R * nkv)
-    k["embed"] = dict(bytes=M * h * es * 3 + h * es, flops=4 * M * h)
-    norm = dict(bytes=M * h * es * 2 + M * n16 * 8 + h * es, flops=3 * M * h)
+    k["fuse_fc_gemm"] = dict(bytes=(h * n * h + R * n * h) * es, flops=2 * R * n * h * h)
+    k["fuse_rownorm"] = dict(bytes=(R * h + h) * es, flops=3 * R * h)
+    k["inject_kv_gemm"] = dict(bytes=(L * 2 * nkv * h + R * h) * es, flops=2 * R * h * L * 2 * nkv)
+    k["inject_kv_finish"] = dict(bytes=(L * 2 * R * nkv + L * d) * es, flops=6 * L * R * nkv)
+    k["embed"] = dict(bytes=(3 * M * h + h) * es, flops=4 * M * h)
+    norm = dict(bytes=(3 * M * h + h) * es, flops=4 * M * h)
     k["norm_in"] = dict(norm, launches=L - 1)
     k["norm_post"] = dict(norm, launches=L)
-    k["norm_final"] = dict(bytes=Mm * h * es * 2 + Mm * n16 * 8 + h * es, flops=3 * Mm * h)
-    k["qkv_gemm"] = dict(bytes=((nq + 2 * nkv) * h + M * h) * es + M * (nq + 2 * nkv) * 8, flops=2 * M * h * (nq + 2 * nkv))
-    k["qkv_finish"] = dict(bytes=M * (nq + 2 * nkv) * (8 + es) + 2 * d * es, flops=8 * M * (nq + nkv))
+    k["norm_final"] = dict(bytes=(3 * Mm * h + h) * es, flops=4 * Mm * h)
+    k["qkv_gemm"] = dict(bytes=((nq + 2 * nkv) * h + M * h) * es, flops=2 * M * h * (nq + 2 * nkv))
+    k["qkv_finish"] = dict(bytes=(M * (nq + 2 * nkv) + 2 * d) * es, flops=8 * M * (nq + nkv))
     for kind, sel in (("attention_full", lambda w: w == 0), ("attention_sliding", lambda w: w > 0)):
         layers = [w for w in p.layer_window[:L] if sel(w)]
         if not layers:
@@ -66,11 +67,11 @@ def kernel_costs(p, ctx, rows):
         k[kind] = dict(bytes=(sum(keys) * 2 * nkv + 2 * M * nq + 2 * M * nkv) * es,
                        flops=sum(4 * p.n_q_heads * B * d * (kk + B) for kk in keys),
                        launches=len(layers))
-    k["o_proj_gemm"] = dict(bytes=(h * nq + M * nq + 2 * M * h) * es + M * n16 * 8, flops=2 * M * nq * h)
+    k["o_proj_gemm"] = dict(bytes=(h * nq + M * nq) * es, flops=2 * M * nq * h)
     k["gate_up_gemm"] = dict(bytes=(2 * I * h + M * h + M * I) * es, flops=4 * M * h * I)
-    k["down_gemm"] = dict(bytes=(h * I + M * I + 2 * M * h) * es + M * n16 * 8, flops=2 * M * I * h)
-    k["lm_head_gemm"] = dict(bytes=(V * h + Mm * h) * es + Mm * ((V + 31) // 32) * 16, flops=2 * Mm * h * V)
-    k["argmax_final"] = dict(bytes=Mm * ((V + 31) // 32) * 16 + Mm * 12, flops=0)
+    k["down_gemm"] = dict(bytes=(h * I + M * I) * es, flops=2 * M * I * h)
+    k["lm_head_gemm"] = dict(bytes=(V * h + Mm * h) * es, flops=2 * Mm * h * V)
+    k["argmax_final"] = dict(bytes=Mm * 4, flops=0)
     k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
     for name in ("qkv_gemm", "qkv_finish", "o_proj_gemm", "gate_up_gemm", "down_gemm"):
         k[name]["launches"] = L

@@ -85,19 +85,23 @@ static int fail(dflash* h, int code, const char* fmt, ...) {
 namespace {
 
 struct GemmPlan {
-  int mt, mgroups, n_tiles, iters, n_work;
+  int am, mt, mgroups, n_tiles, iters, ksplit, n_work;
+  size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * 8; }
 };
 
-// Rows are processed in groups of 16 * mt (mt = 1 or 2); every workgroup owns one
-// column tile over the whole K, so the per-row arithmetic never depends on M.
-GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int tap_h = 0) {
+// Rows are processed in groups of 16 * mt (mt = 1 or 2). The tiling of N, the K
+// ranges and the wave split of each range depend only on the weight's shape, so
+// the per-row arithmetic never depends on M.
+GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h = 0) {
   GemmPlan g;
+  g.am = am;
   g.mt = M <= 16 ? 1 : 2;
   g.mgroups = (M + 16 * g.mt - 1) / (16 * g.mt);
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
-  g.iters = K / gemm_k_per_iter(dtype, epi, K, tap_h);
-  g.n_work = g.n_tiles * g.mgroups;
+  g.iters = K / gemm_k_per_iter(dtype, epi, am, K, tap_h);
+  g.ksplit = gemm_ksplit(epi, g.n_tiles, g.iters);
+  g.n_work = g.n_tiles * g.mgroups * g.ksplit;
   return g;
 }
 
@@ -134,16 +138,15 @@ struct Region {
 
 struct FuseLayout {
   GemmPlan g;
-  size_t y, ssq, end;
+  size_t y, end;
 };
 FuseLayout layout_fuse(const dflash& h, int R) {
   FuseLayout L;
   const auto& c = h.cfg;
-  L.g = plan_gemm(c.dtype, EPI_FC, R, c.hidden, c.n_taps * c.hidden, c.hidden);
+  L.g = plan_gemm(c.dtype, EPI_RAW, A_TAPS, R, c.hidden, c.n_taps * c.hidden, c.hidden);
   Region r;
   r.take(kCounterInts * 4);
-  L.y = r.take((size_t)R * c.hidden * 8);
-  L.ssq = r.take((size_t)R * L.g.n_tiles * 8);
+  L.y = r.take(L.g.part_bytes(R, c.hidden));
   L.end = r.off;
   return L;
 }
@@ -156,10 +159,10 @@ InjectLayout layout_inject(const dflash& h, int R) {
   InjectLayout L;
   const auto& c = h.cfg;
   const int N = c.n_layers * 2 * h.nkv();
-  L.g = plan_gemm(c.dtype, EPI_RAW, R, N, c.hidden);
+  L.g = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, R, N, c.hidden);
   Region r;
   r.take(kCounterInts * 4);
-  L.raw = r.take((size_t)R * N * 8);
+  L.raw = r.take(L.g.part_bytes(R, N));
   L.end = r.off;
   return L;
 }
@@ -167,20 +170,18 @@ InjectLayout layout_inject(const dflash& h, int R) {
 struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
-  int ssq_ld;
-  size_t x, a, ssq_a, ssq_b, qkv_raw, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
+  size_t x, a, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
   const auto& c = h.cfg;
   const int M = S * c.block_size, Mm = S * (c.block_size - 1);
   const int es = h.esize();
-  L.qkv = plan_gemm(c.dtype, EPI_RAW, M, h.nq() + 2 * h.nkv(), c.hidden);
-  L.o = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, h.nq());
-  L.gu = plan_gemm(c.dtype, EPI_SWIGLU, M, 2 * c.intermediate, c.hidden);
-  L.down = plan_gemm(c.dtype, EPI_RESID, M, c.hidden, c.intermediate);
-  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, Mm, c.vocab, c.hidden);
-  L.ssq_ld = L.o.n_tiles;            // sums of squares per 16-column tile of the residual stream
+  L.qkv = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, h.nq() + 2 * h.nkv(), c.hidden);
+  L.o = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, h.nq());
+  L.gu = plan_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, M, 2 * c.intermediate, c.hidden);
+  L.down = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, c.intermediate);
+  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, Mm, c.vocab, c.hidden);
   size_t po = 0, pml = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     L.attn.push_back(plan_attn(c, S, max_ctx, c.layer_window[l]));
@@ -191,9 +192,9 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   r.take(kCounterInts * 4);
   L.x = r.take((size_t)M * c.hidden * es);
   L.a = r.take((size_t)M * c.hidden * es);
-  L.ssq_a = r.take((size_t)M * L.ssq_ld * 8);
-  L.ssq_b = r.take((size_t)M * L.ssq_ld * 8);
-  L.qkv_raw = r.take((size_t)M * (h.nq() + 2 * h.nkv()) * 8);
+  L.qkv_raw = r.take(L.qkv.part_bytes(M, h.nq() + 2 * h.nkv()));
+  L.o_parts = r.take(L.o.part_bytes(M, c.hidden));
+  L.d_parts = r.take(L.down.part_bytes(M, c.hidden));
   L.q = r.take((size_t)M * h.nq() * es);
   L.kblk = r.take((size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim * es);
   L.vblk = r.take((size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim * es);
@@ -413,6 +414,7 @@ static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
   p.n_tiles = g.n_tiles;
   p.mgroups = g.mgroups;
   p.iters = g.iters;
+  p.ksplit = g.ksplit;
   p.n_work = g.n_work;
   return p;
 }
@@ -442,20 +444,17 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   p.tap_stride = plane_row_stride;
   p.w0 = h->w.fc;
   p.y_out = reinterpret_cast<double*>(W + L.y);
-  p.ssq_out = reinterpret_cast<double*>(W + L.ssq);
-  p.ssq_ld = L.g.n_tiles;
   hipError_t e;
   {
     ProfScope ps(h, "fuse_fc_gemm", st);
-    e = launch_gemm(c.dtype, EPI_FC, p, L.g.mt, st);
+    e = launch_gemm(c.dtype, EPI_RAW, A_TAPS, p, L.g.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
   RowNormParams rn;
   rn.R = n_rows;
   rn.hidden = c.hidden;
-  rn.n_tiles = L.g.n_tiles;
-  rn.y = p.y_out;
-  rn.ssq_part = p.ssq_out;
+  rn.ksplit = L.g.ksplit;
+  rn.parts = p.y_out;
   rn.gain = h->w.hidden_norm;
   rn.out = fused_out;
   rn.eps = c.rms_eps;
@@ -506,7 +505,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   hipError_t e;
   {
     ProfScope ps(h, "inject_kv_gemm", st);
-    e = launch_gemm(c.dtype, EPI_RAW, p, L.g.mt, st);
+    e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.g.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
   KvFinishParams kf;
@@ -516,6 +515,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   kf.n_kv_heads = c.n_kv_heads;
   kf.head_dim = c.head_dim;
   kf.raw = p.y_out;
+  kf.ksplit = L.g.ksplit;
   kf.row_stream = row_stream;
   kf.row_pos = row_pos;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -565,8 +565,8 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   hipStream_t st = (hipStream_t)stream;
   void* X = W + L.x;
   void* A = W + L.a;
-  double* ssq_a = reinterpret_cast<double*>(W + L.ssq_a);   // after the down projection
-  double* ssq_b = reinterpret_cast<double*>(W + L.ssq_b);   // after the o projection
+  double* o_parts = reinterpret_cast<double*>(W + L.o_parts);   // wo . o, per K range
+  double* d_parts = reinterpret_cast<double*>(W + L.d_parts);   // w_down . m, per K range
   double* qkv_raw = reinterpret_cast<double*>(W + L.qkv_raw);
   hipError_t e;
 
@@ -588,15 +588,17 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "embed: %s", hipGetErrorString(e));
 
-  auto norm = [&](const char* name, const double* ssq, const void* gain, int rows, int rowmap_bm1) {
+  // x = round(x + branch) (the branch's K-range partials added in order), then the
+  // next normalised input a = round(RMSNorm(x) * gain)
+  auto norm = [&](const char* name, const double* parts, int ksplit, const void* gain, int rows, int rowmap_bm1) {
     NormParams np;
     np.R = rows;
     np.hidden = c.hidden;
-    np.ssq_parts = L.ssq_ld;
-    np.ssq_ld = L.ssq_ld;
     np.rowmap_bm1 = rowmap_bm1;
     np.x = X;
-    np.ssq = ssq;
+    np.parts = parts;
+    np.ksplit = ksplit;
+    np.part_rows = M;
     np.gain = gain;
     np.eps = c.rms_eps;
     np.a = A;
@@ -605,9 +607,10 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   };
 
   for (int l = 0; l < c.n_layers; ++l) {
-    // a = round(RMSNorm(X) * in_norm)   (layer 0: written by embed)
+    // X += w_down . m of the previous layer (residual add 2); a = round(RMSNorm(X) * in_norm)
+    // (layer 0: a is written by embed)
     if (l > 0) {
-      e = norm("norm_in", ssq_a, h->w.in_norm[l], M, 0);
+      e = norm("norm_in", d_parts, L.down.ksplit, h->w.in_norm[l], M, 0);
       if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d input norm: %s", l, hipGetErrorString(e));
     }
     // raw q | k | v = a . [wq | wk | wv]^T
@@ -622,7 +625,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.y_out = qkv_raw;
     {
       ProfScope ps(h, "qkv_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RAW, p, L.qkv.mt, st);
+      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.qkv.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv: %s", l, hipGetErrorString(e));
 
@@ -634,6 +637,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     qf.n_kv_heads = c.n_kv_heads;
     qf.head_dim = c.head_dim;
     qf.raw = qkv_raw;
+    qf.ksplit = L.qkv.ksplit;
     qf.ctx_len = ctx_len;
     qf.max_ctx = max_ctx_len;
     qf.q_norm = h->w.q_norm[l];
@@ -680,22 +684,21 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d attention: %s", l, hipGetErrorString(e));
 
-    // X += wo . o   (residual add 1)
+    // wo . o, per K range
     p = gemm_base(L.o, M, c.hidden, h->nq());
     p.a = W + L.o_buf;
     p.lda = h->nq();
     p.w0 = h->w.wo[l];
-    p.x_io = X;
-    p.ssq_out = ssq_b;
-    p.ssq_ld = L.ssq_ld;
+    p.y_out = o_parts;
     {
       ProfScope ps(h, "o_proj_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RESID, p, L.o.mt, st);
+      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.o.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d o_proj: %s", l, hipGetErrorString(e));
 
-    // a = round(RMSNorm(X) * post_norm);  m = round(silu(w_gate . a) * (w_up . a))
-    e = norm("norm_post", ssq_b, h->w.post_norm[l], M, 0);
+    // X += wo . o (residual add 1); a = round(RMSNorm(X) * post_norm);
+    // m = round(silu(w_gate . a) * (w_up . a))
+    e = norm("norm_post", o_parts, L.o.ksplit, h->w.post_norm[l], M, 0);
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d post norm: %s", l, hipGetErrorString(e));
     p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden);
     p.a = A;
@@ -706,27 +709,26 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.ld_out = c.intermediate;
     {
       ProfScope ps(h, "gate_up_gemm", st);
-      e = launch_gemm(c.dtype, EPI_SWIGLU, p, L.gu.mt, st);
+      e = launch_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, p, L.gu.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d gate/up: %s", l, hipGetErrorString(e));
 
-    // X += w_down . m   (residual add 2)
+    // w_down . m, per K range (added to X by the next norm: residual add 2)
     p = gemm_base(L.down, M, c.hidden, c.intermediate);
     p.a = W + L.m;
     p.lda = c.intermediate;
     p.w0 = h->w.w_down[l];
-    p.x_io = X;
-    p.ssq_out = ssq_a;
-    p.ssq_ld = L.ssq_ld;
+    p.y_out = d_parts;
     {
       ProfScope ps(h, "down_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RESID, p, L.down.mt, st);
+      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.down.mt, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d down: %s", l, hipGetErrorString(e));
   }
 
-  // Final norm of the mask rows (compacted), LM head, argmax (lowest index on a tie).
-  e = norm("norm_final", ssq_a, h->w.norm, Mm, B - 1);
+  // Last residual add and final norm of the mask rows (compacted), LM head, argmax
+  // (lowest index on a tie).
+  e = norm("norm_final", d_parts, L.down.ksplit, h->w.norm, Mm, B - 1);
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "final norm: %s", hipGetErrorString(e));
   GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden);
   p.a = A;
@@ -736,7 +738,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
   {
     ProfScope ps(h, "lm_head_gemm", st);
-    e = launch_gemm(c.dtype, EPI_LMHEAD, p, L.lm.mt, st);
+    e = launch_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, p, L.lm.mt, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "lm head: %s", hipGetErrorString(e));
   {

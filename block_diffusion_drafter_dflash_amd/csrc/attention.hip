@@ -3,12 +3,12 @@
 // Workgroup = (context chunk, kv head, stream) with QT waves; wave w owns 16 of the
 // kv head's g * B queries (its g q-heads times the B block rows). Keys are the
 // context rows in the layer's reach, read from the paged cache, plus all B block
-// rows (added by the stream's last chunk). A step covers two 16-key pages. The
-// workgroup stages each step once into LDS - K pages are [16 keys][d] and V pages
-// are stored transposed, [d][16 keys], so every thread copies whole 16-byte pieces
-// and both MFMA operands are contiguous along the reduction - with the cache reads
-// of the next two steps in flight, and every wave reads its MFMA fragments from
-// LDS (padded rows: conflict-free 16-byte reads).
+// rows (added by the stream's last chunk). K pages are [16 keys][d] and V pages are
+// stored transposed, [d][16 keys], so both MFMA operands are contiguous along the
+// reduction. The chunk's pages are copied straight from HBM into LDS in batches
+// (global_load_lds, 16 bytes a lane, every read of a batch in flight at once and no
+// registers held), with an XOR swizzle of 16-byte pieces that keeps the fragment
+// reads free of bank conflicts; each wave then reads its fragments from LDS.
 // Scores are computed transposed (S^T = K Q^T) so that each lane owns one query:
 // the softmax statistics are lane-local plus two cross-lane-group shuffles, and the
 // probabilities feed the P.V MFMA without a transpose. P (fp32) enters the bf16
@@ -21,17 +21,29 @@
 
 namespace dfl {
 
-template <typename T, int D, int QT>
+constexpr int kAttnLdsBytes = 64 * 1024;   // one batch of pages
+
+template <typename T, int D>
 struct AttnCfg {
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int E = Elem<T>::E;
-  static constexpr int NF = D / 4 / E;                // 16-byte K fragments per lane per 16-key tile
-  static constexpr int NDT = D / 16;                  // 16-dim output tiles
-  static constexpr int NTHR = 64 * QT;
-  static constexpr int LDK = D + 16 / (int)sizeof(T); // K row stride (elements): +16 bytes
-  static constexpr int LDV = 32 + 16 / (int)sizeof(T);// V^T row stride (elements): +16 bytes
-  static constexpr int NC = 32 * D / E;               // 16-byte pieces of K (and of V) per step
-  static constexpr int NI = (NC + NTHR - 1) / NTHR;   // pieces of each per thread per step
+  static constexpr int NF = D / 4 / E;                   // 16-byte K fragments per lane per 16-key tile
+  static constexpr int NDT = D / 16;                     // 16-dim output tiles
+  static constexpr int KROW = D * (int)sizeof(T);        // bytes of a key row
+  static constexpr int NCK = KROW / 16;                  // 16-byte pieces of a key row
+  static constexpr int VROW = 16 * (int)sizeof(T);       // bytes of a value dim row in a page
+  static constexpr int NCV = VROW / 16;
+  static constexpr int KBYTES = 16 * KROW;               // K part of a page in LDS
+  static constexpr int SLOT = KBYTES + D * VROW;         // one page (K and V^T) in LDS
+  static constexpr int NBP = kAttnLdsBytes / SLOT;       // pages per batch (even)
+  static constexpr int NKI = KBYTES / 1024;              // wave-wide 16-byte loads per page: K
+  static constexpr int NVI = D * VROW / 1024;            //   and V^T
+  // XOR swizzles of 16-byte pieces: 16 lanes reading the same piece of 16 key rows,
+  // or of 16 value dims, touch 16 distinct bank groups.
+  __device__ static __forceinline__ int kswz(int row) {
+    return (KROW >= 256 ? row : row / (256 / KROW)) % NCK;
+  }
+  __device__ static __forceinline__ int vswz(int d) { return (d / (256 / VROW)) % NCV; }
 };
 
 // Key (0..31 within the step's two pages) supplied as row r of S^T tile t. For bf16
@@ -49,19 +61,19 @@ struct StepSrc {
   int key0;             // absolute position of the step's first key; -1 for the block
 };
 
-template <int NI>
-struct Stage {
-  uint4 k[NI], v[NI];
-};
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
 
 template <typename T, int D, int QT>
-__global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const AttnParams p) {
-  using C = AttnCfg<T, D, QT>;
+__global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
+  using C = AttnCfg<T, D>;
   constexpr bool BF = C::BF;
-  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NTHR = C::NTHR, NC = C::NC, NI = C::NI;
-  constexpr int LDK = C::LDK, LDV = C::LDV;
-  __shared__ __attribute__((aligned(16))) T ks[2][32][LDK];
-  __shared__ __attribute__((aligned(16))) T vts[2][D][LDV];
+  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NBP = C::NBP, SLOT = C::SLOT;
+  constexpr int KROW = C::KROW, VROW = C::VROW, KBYTES = C::KBYTES, NKI = C::NKI, NVI = C::NVI;
+  static_assert(NBP >= 2 && NBP % 2 == 0, "a batch holds whole steps");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBP * SLOT];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -144,38 +156,30 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
     const int pos = src.key0 + kk;
     return pos >= lo && pos < Cs;
   };
-  // Cooperative cache reads of one step: piece i of K is (half, key row, 16-byte part),
-  // piece i of V^T is (half, dim, 16-byte part of the half's 16 keys).
-  auto fetch = [&](int step, Stage<NI>& r) {
-    const StepSrc src = source(step);
+  // Copy page hf of step `step` into LDS slot `slot`: the wave-wide loads of the slot
+  // are dealt to the workgroup's waves; lane l of load j fills bytes [j*1024 + 16 l,
+  // + 16) of the slot's K part (then V part) from the piece that the swizzle puts there.
+  auto issue = [&](const StepSrc& src, int hf, int slot, int& seq) {
+    const T* kp = static_cast<const T*>(hf ? src.k[1] : src.k[0]);
+    const T* vp = static_cast<const T*>(hf ? src.v[1] : src.v[0]);
+    unsigned char* base = lds + slot * SLOT;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int i = tid + j * NTHR;
-      r.k[j] = make_uint4(0, 0, 0, 0);
-      r.v[j] = make_uint4(0, 0, 0, 0);
-      if (i < NC) {
-        const int hf = i / (NC / 2), rem = i % (NC / 2);
-        const T* kb = static_cast<const T*>(hf ? src.k[1] : src.k[0]);
-        const T* vb = static_cast<const T*>(hf ? src.v[1] : src.v[0]);
-        if (kb) r.k[j] = ldg16(kb + (rem / (D / E)) * D + (rem % (D / E)) * E);
-        if (vb) r.v[j] = ldg16(vb + (int64_t)(rem / (16 / E)) * src.vld + (rem % (16 / E)) * E);
-      }
-    }
-  };
-  auto stage = [&](int buf, const Stage<NI>& r) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int i = tid + j * NTHR;
-      if (i < NC) {
-        const int hf = i / (NC / 2), rem = i % (NC / 2);
-        *reinterpret_cast<uint4*>(&ks[buf][hf * 16 + rem / (D / E)][(rem % (D / E)) * E]) = r.k[j];
-        *reinterpret_cast<uint4*>(&vts[buf][rem / (16 / E)][hf * 16 + (rem % (16 / E)) * E]) = r.v[j];
+    for (int j = 0; j < NKI + NVI; ++j, ++seq) {
+      if (seq % QT != w || !kp) continue;
+      const int b = (j < NKI ? j : j - NKI) * 1024 + lane * 16;
+      if (j < NKI) {
+        const int row = b / KROW, pc = (b % KROW) / 16;
+        const int piece = pc ^ C::kswz(row);
+        load_lds16(kp + row * D + piece * (16 / (int)sizeof(T)), base + j * 1024);
+      } else {
+        const int d = b / VROW, ph = (b % VROW) / 16;
+        const int piece = ph ^ C::vswz(d);
+        load_lds16(vp + (int64_t)d * src.vld + piece * (16 / (int)sizeof(T)), base + KBYTES + (j - NKI) * 1024);
       }
     }
   };
 
-  auto compute = [&](int step) {
-    const int buf = step & 1;
+  auto compute = [&](int step, const unsigned char* sb) {
     const StepSrc cur = source(step);
 
     // ---- S^T = K Q^T: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i)
@@ -183,9 +187,13 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const T* krow = &ks[buf][key_of_row<BF>(t, lr)][lg * (D / 4)];
+      const int kk = key_of_row<BF>(t, lr), row = kk & 15;
+      const unsigned char* krow = sb + (kk >> 4) * SLOT + row * KROW;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) mma_frag(sacc[t], *reinterpret_cast<const uint4*>(krow + f * E), qf[f], T());
+      for (int f = 0; f < NF; ++f) {
+        const int piece = (lg * (D / 4) + f * E) * (int)sizeof(T) / 16;
+        mma_frag(sacc[t], *reinterpret_cast<const uint4*>(krow + ((piece ^ C::kswz(row)) * 16)), qf[f], T());
+      }
     }
 
     // ---- online softmax (base 2); the denominator sums in float64
@@ -216,8 +224,8 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
     m_run = m_new;
 
     // ---- this step's O^T = V^T P^T, added to the float64 running output. Values of
-    // keys outside the reach may be stale or never written: they are zeroed so that a
-    // zero probability times a non-finite value cannot reach the output.
+    // keys outside the reach (or of pages never loaded) may be stale or non-finite:
+    // they are zeroed so that a zero probability times them cannot reach the output.
     floatx4 ot[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) ot[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -239,9 +247,12 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
       const uint4 bh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       const uint4 bm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       const uint4 bl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      // lane group lg: keys 8lg..8lg+7 = page lg/2, 16-byte piece lg&1 of each dim row
+      const unsigned char* vbase = sb + (lg >> 1) * SLOT + KBYTES;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        uint4 vf = *reinterpret_cast<const uint4*>(&vts[buf][16 * dt + lr][8 * lg]);
+        const int d = 16 * dt + lr;
+        uint4 vf = *reinterpret_cast<const uint4*>(vbase + d * VROW + (((lg & 1) ^ C::vswz(d)) * 16));
         vf.x &= keep[0];
         vf.y &= keep[1];
         vf.z &= keep[2];
@@ -258,9 +269,12 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
         const int k0 = 16 * t + 4 * lg;
         const bool ok0 = !edge || key_ok(cur, k0), ok1 = !edge || key_ok(cur, k0 + 1);
         const bool ok2 = !edge || key_ok(cur, k0 + 2), ok3 = !edge || key_ok(cur, k0 + 3);
+        // page t, 16-byte piece lg (keys 4lg..4lg+3) of each dim row
+        const unsigned char* vbase = sb + t * SLOT + KBYTES;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          uint4 vf = *reinterpret_cast<const uint4*>(&vts[buf][16 * dt + lr][k0]);
+          const int d = 16 * dt + lr;
+          uint4 vf = *reinterpret_cast<const uint4*>(vbase + d * VROW + ((lg ^ C::vswz(d)) * 16));
           vf.x = ok0 ? vf.x : 0u;
           vf.y = ok1 ? vf.y : 0u;
           vf.z = ok2 ? vf.z : 0u;
@@ -275,25 +289,19 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
       for (int i = 0; i < 4; ++i) oacc[dt][i] = oacc[dt][i] * corr + (double)ot[dt][i];
   };
 
-  // Pipeline: step st is in LDS buffer st & 1 while the cache reads of steps st + 1
-  // and st + 2 are in flight in two register stages used alternately.
-  Stage<NI> ra, rb;
-  if (n_steps > 0) {
-    fetch(0, ra);
-    if (n_steps > 1) fetch(1, rb);
-    stage(0, ra);
-  }
-  __syncthreads();
-  // body(st, nxt, fre): nxt holds step st + 1's reads; fre is free for step st + 2.
-  auto body = [&](int st, Stage<NI>& nxt, Stage<NI>& fre) {
-    if (st + 2 < n_steps) fetch(st + 2, fre);
-    compute(st);
-    if (st + 1 < n_steps) stage((st + 1) & 1, nxt);
-    __syncthreads();
-  };
-  for (int st = 0; st < n_steps; st += 2) {
-    body(st, rb, ra);
-    if (st + 1 < n_steps) body(st + 1, ra, rb);
+  // Batches of NBP / 2 steps: copy every page of the batch into LDS, wait, compute.
+  for (int b0 = 0; b0 < n_steps; b0 += NBP / 2) {
+    const int b1 = b0 + NBP / 2 < n_steps ? b0 + NBP / 2 : n_steps;
+    int seq = 0;
+    for (int st = b0; st < b1; ++st) {
+      const StepSrc src = source(st);
+      issue(src, 0, 2 * (st - b0), seq);
+      issue(src, 1, 2 * (st - b0) + 1, seq);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed in LDS
+    __syncthreads();                 // and every other wave's
+    for (int st = b0; st < b1; ++st) compute(st, lds + 2 * (st - b0) * SLOT);
+    __syncthreads();                 // the batch's slots are free again
   }
 
   double l_tot = l_run;
@@ -335,24 +343,40 @@ __global__ __launch_bounds__(64 * QT, (QT <= 4 ? 8 / QT : 1)) void k_attn(const 
         make_float4((float)oacc[dt][0], (float)oacc[dt][1], (float)oacc[dt][2], (float)oacc[dt][3]);
 }
 
-// Combine the chunks of one (stream, kv head, query tile, 16-dim slice) in chunk order.
-// A lane's query has its chunks' (max, sum) pairs contiguous.
+// Combine the chunks of one (stream, kv head, query tile, 16-dim slice): four waves
+// take contiguous quarters of the stream's own chunks (its count depends only on its
+// reach, so the grouping is the same in any batch), each summing its quarter in chunk
+// order, and the quarters are added in wave order. A lane's query has its chunks'
+// (max, sum) pairs contiguous.
+constexpr int kCombineWaves = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_attn_combine(const AttnParams p, int QT) {
-  constexpr int NDT = D / 16;
-  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+__global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnParams p, int QT) {
+  constexpr int NDT = D / 16, NW = kCombineWaves;
+  __shared__ float s_max[NW][16];
+  __shared__ double s_sum[NW][64][5];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int sh = blockIdx.x / QT, qt = blockIdx.x % QT, dt = blockIdx.y;
   const int s = sh / p.n_kv_heads, h = sh % p.n_kv_heads;
   const int qi = 16 * qt + lr;
-  if (qi >= p.group * p.B) return;
-  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + qi) * p.n_chunks;
+  const bool valid = qi < p.group * p.B;
+  int Cs = p.ctx_len[s];
+  Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
+  const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
+  const int n_own = attention_chunks(span_pages(lo, Cs));
+  const int c0 = (int)((int64_t)w * n_own / NW), c1 = (int)((int64_t)(w + 1) * n_own / NW);
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + (valid ? qi : 0)) * p.n_chunks;
   float M = -INFINITY;
-  for (int cc = 0; cc < p.n_chunks; ++cc) M = fmaxf(M, ml[cc].x);
+  for (int cc = c0; cc < c1; ++cc) M = fmaxf(M, ml[cc].x);
+  if (lg == 0) s_max[w][lr] = M;
+  __syncthreads();
+  M = s_max[0][lr];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_max[ww][lr]);
   double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
   const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
   const int64_t cstride = (int64_t)QT * NDT * (kWave * 4);
-#pragma unroll 8
-  for (int cc = 0; cc < p.n_chunks; ++cc) {
+#pragma unroll 4
+  for (int cc = c0; cc < c1; ++cc) {
     const float2 m = ml[cc];
     const float4 v = *reinterpret_cast<const float4*>(po + cc * cstride);
     const double f = (m.x == -INFINITY) ? 0.0 : exp2((double)m.x - (double)M);
@@ -361,6 +385,17 @@ __global__ __launch_bounds__(64) void k_attn_combine(const AttnParams p, int QT)
     o[1] += (double)v.y * f;
     o[2] += (double)v.z * f;
     o[3] += (double)v.w * f;
+  }
+  s_sum[w][lane][0] = L;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_sum[w][lane][1 + i] = o[i];
+  __syncthreads();
+  if (w != 0 || !valid) return;
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) {
+    L += s_sum[ww][lane][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += s_sum[ww][lane][1 + i];
   }
   const int hl = qi / p.B, jrow = qi % p.B;
   T* dst = static_cast<T*>(p.o) + (int64_t)(s * p.B + jrow) * (p.n_q_heads * D) + (h * p.group + hl) * D + 16 * dt + 4 * lg;
@@ -391,7 +426,7 @@ static hipError_t launch_td(const AttnParams& p, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
-  (void)launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64), st, p, qt);
+  (void)launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64 * kCombineWaves), st, p, qt);
   return hipGetLastError();
 }
 

@@ -1,18 +1,16 @@
 // Skinny MFMA GEMMs of the draft round with fused epilogues (gfx950).
 //
 // Y[M, N] = A[M, K] . W[N, K]^T with M small (block rows x streams) and W streamed
-// from HBM exactly once. A work item is a tile of 16*NT output columns for 16*MT
-// rows; a workgroup of 8 waves takes a contiguous run of work items (row groups of
-// one tile back to back, so a tile's weight rows are re-read from the same L2) and
-// its waves split K eight ways. Each wave streams its slice of the tile's weight
-// rows, every lane reading 64 contiguous bytes of a row per iteration; the loads of
-// the next iteration - also across work items - are in flight while the current
-// one is multiplied, so the next tile's reads overlap this tile's epilogue.
-// Every MFMA's partial (32 products per element for bf16) is added into a float64
-// accumulator and the eight wave partials are summed in wave order. No workgroup
-// ever waits for another: row statistics (sums of squares for the next RMSNorm)
-// leave as per-tile partials that the consuming kernel adds in tile order, so every
-// result is independent of scheduling and of the batch.
+// from HBM exactly once. A workgroup owns one work item: a tile of 16*NT output
+// columns for 16*MT rows over one of the GEMM's ksplit ranges of K. Its KW waves
+// split that range again; each wave streams its slice of the tile's weight rows,
+// every lane reading U*16 contiguous bytes of each row per iteration with the next
+// iteration's reads in flight. Every MFMA's partial (32 products per element for
+// bf16) is added into a float64 accumulator and the KW wave partials are summed in
+// wave order. With ksplit > 1 each range writes its own float64 partial and the
+// consuming kernel adds the ranges in order (see kernels.h), so no workgroup ever
+// waits for another and every result is independent of scheduling and of the
+// batch: ksplit, KW and U depend only on the weight's shape, never on M.
 #include "common.hpp"
 #include "kernels.h"
 
@@ -25,7 +23,6 @@ struct GemmTune {
   static constexpr int KW = KW_;
   static constexpr int U = U_;
 };
-using DefaultTune = GemmTune<8, 4>;
 
 template <typename T, typename Tune>
 struct GemmCfg {
@@ -69,7 +66,7 @@ __device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile, in
       const int l = n / (2 * p.nkv), rem = n % (2 * p.nkv);
       return static_cast<const T*>(rem < p.nkv ? p.wk_l[l] : p.wv_l[l]) + (int64_t)(rem % p.nkv) * p.K;
     }
-    if (n < p.nq) return static_cast<const T*>(p.w0) + (int64_t)n * p.K;
+    if (p.nq == 0 || n < p.nq) return static_cast<const T*>(p.w0) + (int64_t)n * p.K;   // one matrix, or wq
     if (n < p.nq + p.nkv) return static_cast<const T*>(p.w1) + (int64_t)(n - p.nq) * p.K;
     return static_cast<const T*>(p.w2) + (int64_t)(n - p.nq - p.nkv) * p.K;
   } else {
@@ -78,41 +75,35 @@ __device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile, in
   }
 }
 
-template <typename T, int MT, int NT, int EPI, typename Tune = DefaultTune>
+template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
 __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   using C = GemmCfg<T, Tune>;
-  constexpr int E = C::E, U = C::U, KI = C::KI, kKW = C::KW, kGemmThreads = C::THREADS;
-  constexpr int AM = EPI == EPI_FC ? A_TAPS : A_PLAIN;
+  constexpr int E = C::E, U = C::U, KI = C::KI, KW = C::KW, THREADS = C::THREADS;
   constexpr int ROWS = 16 * MT, COLS = 16 * NT;
-  __shared__ float red[kKW][ROWS][COLS + 1];
+  __shared__ float red[KW][ROWS][COLS + 1];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  // contiguous run of work items (tile-major, row group fastest)
-  const int G = gridDim.x, b = blockIdx.x;
-  const int q0 = (int)((int64_t)b * p.n_work / G), q1 = (int)((int64_t)(b + 1) * p.n_work / G);
-  if (q0 >= q1) return;
-
-  const int it0 = (int)((int64_t)w * p.iters / kKW), it1 = (int)((int64_t)(w + 1) * p.iters / kKW);
-  const bool has_k = it0 < it1;
+  // work item: (column tile, row group, K range), K range fastest
+  const int wi = blockIdx.x;
+  const int ks = wi % p.ksplit, rest = wi / p.ksplit;
+  const int tile = rest / p.mgroups, mg = rest % p.mgroups;
+  const int row0 = mg * ROWS;
+  const int kb = (int)((int64_t)ks * p.iters / p.ksplit), ke = (int)((int64_t)(ks + 1) * p.iters / p.ksplit);
+  const int it0 = kb + (int)((int64_t)w * (ke - kb) / KW), it1 = kb + (int)((int64_t)(w + 1) * (ke - kb) / KW);
   const int lane_k = lg * (U * E);
-  const T* abase = static_cast<const T*>(p.a);
 
-  // load cursor: work item, iteration and the item's row pointers
-  int l_wi = q0, l_it = it0;
   const T* brow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) brow[nt] = weight_row<T, NT, EPI>(p, tile, 16 * nt + lr);
   int64_t aoff[MT];
-  auto setup = [&](int wi) {
-    const int tile = wi / p.mgroups, mg = wi % p.mgroups;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) brow[nt] = weight_row<T, NT, EPI>(p, tile, 16 * nt + lr);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      int r = mg * ROWS + 16 * mt + lr;
-      r = r < p.M ? r : p.M - 1;
-      aoff[mt] = AM == A_TAPS ? (int64_t)r * p.tap_stride : (int64_t)r * p.lda;
-    }
-  };
+  for (int mt = 0; mt < MT; ++mt) {
+    int r = row0 + 16 * mt + lr;
+    r = r < p.M ? r : p.M - 1;
+    aoff[mt] = AM == A_TAPS ? (int64_t)r * p.tap_stride : (int64_t)r * p.lda;
+  }
+  const T* abase = static_cast<const T*>(p.a);
   auto load = [&](int it, uint4 (&a)[MT][U], uint4 (&bb)[NT][U]) {
     const int k = it * KI + lane_k;
 #pragma unroll
@@ -135,28 +126,21 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
     }
   };
 
-  setup(l_wi);
-  uint4 a_c[MT][U], b_c[NT][U];
-  if (has_k) load(l_it, a_c, b_c);
+  double acc[MT][NT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.0;
 
-  for (int wi = q0; wi < q1; ++wi) {
-    double acc[MT][NT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.0;
-
+  if (it0 < it1) {
+    uint4 a_c[MT][U], b_c[NT][U];
+    load(it0, a_c, b_c);
     for (int it = it0; it < it1; ++it) {
-      // advance the load cursor and start the next iteration's reads
-      if (++l_it == it1) {
-        l_it = it0;
-        if (++l_wi < q1) setup(l_wi);
-      }
       uint4 a_n[MT][U], b_n[NT][U];
-      const bool more = l_wi < q1;
-      if (more) load(l_it, a_n, b_n);
+      const bool more = it + 1 < it1;
+      if (more) load(it + 1, a_n, b_n);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -179,67 +163,48 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
         }
       }
     }
+  }
 
-    // ---- the eight K slices -> LDS, summed in wave order
-    const int tile = wi / p.mgroups, row0 = (wi % p.mgroups) * ROWS;
-    __syncthreads();   // the previous item's epilogue has read red
+  // ---- the KW K slices -> LDS, summed in wave order
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[w][16 * mt + 4 * lg + i][16 * nt + lr] = (float)acc[mt][nt][i];
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) red[w][16 * mt + 4 * lg + i][16 * nt + lr] = (float)acc[mt][nt][i];
+  __syncthreads();
 
-    // ---- epilogue: one element per thread and pass; COLS consecutive lanes per row
+  // ---- epilogue: one element per thread and pass; COLS consecutive lanes per row
 #pragma unroll
-    for (int e0 = 0; e0 < ROWS * COLS; e0 += kGemmThreads) {
-      const int e = e0 + tid;
-      if (e >= ROWS * COLS) break;   // whole waves (ROWS * COLS is a multiple of 64)
-      const int rl = e / COLS, c = e % COLS;
-      double vd = 0.0;
+  for (int e0 = 0; e0 < ROWS * COLS; e0 += THREADS) {
+    const int e = e0 + tid;
+    if (e >= ROWS * COLS) break;   // whole waves (ROWS * COLS is a multiple of 64)
+    const int rl = e / COLS, c = e % COLS;
+    double vd = 0.0;
 #pragma unroll
-      for (int ww = 0; ww < kKW; ++ww) vd += (double)red[ww][rl][c];
-      const float v = (float)vd;
-      const int r = row0 + rl;
-      const bool rv = r < p.M;
-      const int n = tile * COLS + c;
+    for (int ww = 0; ww < KW; ++ww) vd += (double)red[ww][rl][c];
+    const float v = (float)vd;
+    const int r = row0 + rl;
+    const bool rv = r < p.M;
+    const int n = tile * COLS + c;
 
-      if constexpr (EPI == EPI_FC) {
-        double ss = vd * vd;
-        for (int m = 1; m < COLS; m <<= 1) ss += __shfl_xor(ss, m, kWave);
-        if (rv) {
-          p.y_out[(int64_t)r * p.N + n] = vd;
-          if (c == 0) p.ssq_out[(int64_t)r * p.ssq_ld + tile] = ss;
-        }
-      } else if constexpr (EPI == EPI_RAW) {
-        if (rv) p.y_out[(int64_t)r * p.N + n] = vd;   // raw projections; norms and RoPE follow
-      } else if constexpr (EPI == EPI_RESID) {
-        float xn = 0.f;
-        if (rv) {
-          T* x = static_cast<T*>(p.x_io) + (int64_t)r * p.N + n;
-          xn = Elem<T>::round_d((double)Elem<T>::load1(x) + vd);
-          if constexpr (sizeof(T) == 2) *x = (T)f32_to_bf16(xn);
-          else *x = xn;
-        }
-        double ss = (double)xn * (double)xn;
-        for (int m = 1; m < COLS; m <<= 1) ss += __shfl_xor(ss, m, kWave);
-        if (rv && c == 0) p.ssq_out[(int64_t)r * p.ssq_ld + tile] = ss;
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        const double up = __shfl_xor(vd, 16, kWave);
-        if (rv && c < 16) {
-          T* dst = static_cast<T*>(p.m_out) + (int64_t)r * p.ld_out + tile * 16 + c;
-          Elem<T>::store_d(dst, vd / (1.0 + exp(-vd)) * up);
-        }
-      } else if constexpr (EPI == EPI_LMHEAD) {
-        const bool cv = n < p.N;
-        float v1 = cv ? v : -INFINITY, v2 = -INFINITY;
-        int i1 = cv ? n : 0x7fffffff;
-        if (rv && cv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
-        top_xor_merge(v1, i1, v2, COLS);
-        if (rv && c == 0)
-          reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + tile] = make_float4(v1, __int_as_float(i1), v2, 0.f);
+    if constexpr (EPI == EPI_RAW) {
+      // this K range's float64 partial; the consumer adds the ranges in order
+      if (rv) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = vd;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      const double up = __shfl_xor(vd, 16, kWave);
+      if (rv && c < 16) {
+        T* dst = static_cast<T*>(p.m_out) + (int64_t)r * p.ld_out + tile * 16 + c;
+        Elem<T>::store_d(dst, vd / (1.0 + exp(-vd)) * up);
       }
+    } else if constexpr (EPI == EPI_LMHEAD) {
+      const bool cv = n < p.N;
+      float v1 = cv ? v : -INFINITY, v2 = -INFINITY;
+      int i1 = cv ? n : 0x7fffffff;
+      if (rv && cv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
+      top_xor_merge(v1, i1, v2, COLS);
+      if (rv && c == 0)
+        reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + tile] = make_float4(v1, __int_as_float(i1), v2, 0.f);
     }
   }
 }
@@ -275,85 +240,65 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float4* tile_res, in
 
 // ------------------------------------------------------------------ host launchers
 
-// Persistent grid: as many workgroups as the device holds at once (its CU count times
-// the kernel's resident workgroups per CU), capped by the work items.
-template <typename T, int MT, int NT, int EPI, typename Tune>
-static int resident_grid(int n_work) {
-  constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  if (cached[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm<T, MT, NT, EPI, Tune>,
-                                                     GemmCfg<T, Tune>::THREADS, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    cached[dev] = cus * per_cu;
-  }
-  return n_work < cached[dev] ? n_work : cached[dev];
-}
-
 // Tuning per GEMM kind, from a sweep over (waves, bytes per lane per row and
-// iteration, grid) on the 9B round's shapes: the wide-N kinds run one workgroup per
-// tile with 32-byte reads per lane and row, the fc GEMM (N = hidden, K = taps x
-// hidden) keeps a resident grid with 128-byte reads when hidden allows it.
-enum TuneId { TUNE_W8_U2 = 0, TUNE_W4_U2 = 1, TUNE_W4_U8 = 2, TUNE_W8_U4 = 3 };
+// iteration, tile width, K ranges) on the 9B round's shapes: 32-column tiles
+// everywhere, 8 waves reading 32 bytes per lane and row, 4 waves for the LM head.
+enum TuneId { TUNE_W8_U2 = 0, TUNE_W4_U2 = 1 };
 
-static int tune_of(int epi, int K, int tap_h) {
-  if (epi == EPI_LMHEAD) return TUNE_W4_U2;
-  if (epi == EPI_FC) return tap_h % 256 == 0 && K % 256 == 0 ? TUNE_W4_U8 : TUNE_W8_U4;
-  return TUNE_W8_U2;
-}
+static int tune_of(int epi, int, int, int) { return epi == EPI_LMHEAD ? TUNE_W4_U2 : TUNE_W8_U2; }
 
-template <typename T, int MT, int NT, int EPI, typename Tune>
-static hipError_t launch_tuned(const GemmParams& p, bool persistent, hipStream_t st) {
-  const int grid = persistent ? resident_grid<T, MT, NT, EPI, Tune>(p.n_work) : p.n_work;
-  (void)launch_k(k_gemm<T, MT, NT, EPI, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
+template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
+static hipError_t launch_tuned(const GemmParams& p, hipStream_t st) {
+  (void)launch_k(k_gemm<T, MT, NT, EPI, AM, Tune>, dim3(p.n_work), dim3(GemmCfg<T, Tune>::THREADS), st, p);
   return hipGetLastError();
 }
 
-template <typename T, int MT, int NT, int EPI>
+template <typename T, int MT, int NT, int EPI, int AM>
 static hipError_t launch_t(const GemmParams& p, hipStream_t st) {
-  switch (tune_of(EPI, p.K, p.tap_h)) {
-    case TUNE_W4_U2: return launch_tuned<T, MT, NT, EPI, GemmTune<4, 2>>(p, false, st);
-    case TUNE_W4_U8: return launch_tuned<T, MT, NT, EPI, GemmTune<4, 8>>(p, true, st);
-    case TUNE_W8_U4: return launch_tuned<T, MT, NT, EPI, GemmTune<8, 4>>(p, true, st);
-    default: return launch_tuned<T, MT, NT, EPI, GemmTune<8, 2>>(p, false, st);
-  }
+  if (tune_of(EPI, AM, p.K, p.tap_h) == TUNE_W4_U2) return launch_tuned<T, MT, NT, EPI, AM, GemmTune<4, 2>>(p, st);
+  return launch_tuned<T, MT, NT, EPI, AM, GemmTune<8, 2>>(p, st);
 }
 
-template <typename T, int EPI, int NT>
+template <typename T, int EPI, int NT, int AM>
 static hipError_t launch_mt(const GemmParams& p, int mt, hipStream_t st) {
-  if (mt == 1) return launch_t<T, 1, NT, EPI>(p, st);
-  return launch_t<T, 2, NT, EPI>(p, st);
+  if (mt == 1) return launch_t<T, 1, NT, EPI, AM>(p, st);
+  return launch_t<T, 2, NT, EPI, AM>(p, st);
 }
 
 template <typename T>
-static hipError_t launch_epi(const GemmParams& p, int epi, int mt, hipStream_t st) {
+static hipError_t launch_epi(const GemmParams& p, int epi, int am, int mt, hipStream_t st) {
   switch (epi) {
-    case EPI_FC: return launch_mt<T, EPI_FC, 1>(p, mt, st);
-    case EPI_RAW: return launch_mt<T, EPI_RAW, 1>(p, mt, st);
-    case EPI_RESID: return launch_mt<T, EPI_RESID, 1>(p, mt, st);
-    case EPI_SWIGLU: return launch_mt<T, EPI_SWIGLU, 2>(p, mt, st);
-    default: return launch_mt<T, EPI_LMHEAD, 2>(p, mt, st);
+    case EPI_RAW:
+      return am == A_TAPS ? launch_mt<T, EPI_RAW, 2, A_TAPS>(p, mt, st) : launch_mt<T, EPI_RAW, 2, A_PLAIN>(p, mt, st);
+    case EPI_SWIGLU: return launch_mt<T, EPI_SWIGLU, 2, A_PLAIN>(p, mt, st);
+    default: return launch_mt<T, EPI_LMHEAD, 2, A_PLAIN>(p, mt, st);
   }
 }
 
-int gemm_k_per_iter(int dtype, int epi, int K, int tap_h) {
+int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h) {
   const int kf = dtype == 0 ? Elem<float>::KF : Elem<bf16_t>::KF;
-  switch (tune_of(epi, K, tap_h)) {
-    case TUNE_W4_U8: return 8 * kf;
-    case TUNE_W8_U4: return 4 * kf;
-    default: return 2 * kf;
-  }
+  (void)epi;
+  (void)am;
+  (void)K;
+  (void)tap_h;
+  return 2 * kf;   // U = 2 for every tuning in use
 }
 
-int gemm_tile_cols(int epi) { return (epi == EPI_SWIGLU || epi == EPI_LMHEAD) ? 32 : 16; }
+int gemm_tile_cols(int) { return 32; }
 
-hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStream_t st) {
-  if (dtype == 0) return launch_epi<float>(p, epi, mt, st);
-  return launch_epi<bf16_t>(p, epi, mt, st);
+// K ranges of a GEMM: about 512 work items (two workgroups per CU) while each range
+// keeps at least 16 iterations; a function of the weight's shape only.
+int gemm_ksplit(int epi, int n_tiles, int iters) {
+  if (epi != EPI_RAW) return 1;
+  int ks = (512 + n_tiles / 2) / n_tiles;
+  const int cap = iters / 16 > 1 ? iters / 16 : 1;
+  ks = ks < cap ? ks : cap;
+  return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+}
+
+hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st) {
+  if (dtype == 0) return launch_epi<float>(p, epi, am, mt, st);
+  return launch_epi<bf16_t>(p, epi, am, mt, st);
 }
 
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,

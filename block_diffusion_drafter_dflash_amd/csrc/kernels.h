@@ -9,7 +9,7 @@
 namespace dfl {
 
 enum AMode { A_PLAIN = 0, A_TAPS = 1 };
-enum Epi { EPI_FC = 0, EPI_RAW = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
+enum Epi { EPI_RAW = 1, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
 
 constexpr int kMaxLayers = 64;
 constexpr int kMaxTaps = 8;
@@ -17,12 +17,18 @@ constexpr int kBlockSlots = 32;   // block rows held by a stream's block K/V pag
 
 // One skinny GEMM launch: Y[M, N] = A[M, K] . W[N, K]^T. Every field not used by the
 // epilogue stays zero.
+//
+// Split K: EPI_RAW launches cut the reduction into ksplit ranges (a function of the
+// weight's shape only) and write one float64 partial per range,
+// y_out[ks][M][N]. Every consumer forms the full sum as ((P_0 + P_1) + P_2) + ...
+// in range order before using it, so results do not depend on scheduling.
 struct GemmParams {
   int M, N, K;          // rows, output columns (all segments), reduction length
   int n_tiles;          // column tiles (16 or 32 columns each)
   int mgroups;          // row groups of 16 * MT rows
   int iters;            // K / k-elements per iteration
-  int n_work;           // n_tiles * mgroups work items, dealt to the grid
+  int ksplit;           // K ranges (EPI_RAW only; 1 otherwise)
+  int n_work;           // n_tiles * mgroups * ksplit work items, one per workgroup
   // A operand
   const void* a;        // A_PLAIN: [M, lda]
   int64_t lda;
@@ -38,10 +44,7 @@ struct GemmParams {
   const void* wk_l[kMaxLayers];
   const void* wv_l[kMaxLayers];
   // epilogue outputs
-  double* y_out;        // EPI_FC: y [M, N]; EPI_RAW: projections [M, N] (float64)
-  double* ssq_out;      // EPI_FC / EPI_RESID: [M, ssq_ld] per-tile sums of squares
-  int ssq_ld;
-  void* x_io;           // EPI_RESID: residual stream [M, N], updated in place
+  double* y_out;        // EPI_RAW: float64 partials [ksplit, M, N]
   void* m_out;          // EPI_SWIGLU: [M, ld_out]
   int ld_out;
   float* logits_out;    // EPI_LMHEAD (nullable), fp32
@@ -71,7 +74,8 @@ struct AttnParams {
 // layouts the attention kernel reads.
 struct QkvFinishParams {
   int S, B, n_q_heads, n_kv_heads, head_dim;
-  const double* raw;    // [S*B, nq + 2 nkv]
+  const double* raw;    // partials [ksplit, S*B, nq + 2 nkv]
+  int ksplit;
   const int* ctx_len;
   int max_ctx;
   const void* q_norm;
@@ -84,7 +88,8 @@ struct QkvFinishParams {
 
 struct KvFinishParams {
   int R, n_layers, n_kv_heads, head_dim;
-  const double* raw;    // [R, n_layers * 2 * n_kv * d]: per layer k | v
+  const double* raw;    // partials [ksplit, R, n_layers * 2 * n_kv * d]: per layer k | v
+  int ksplit;
   const int* row_stream;
   const int* row_pos;
   const void* kn_l[kMaxLayers];
@@ -105,22 +110,24 @@ struct EmbedParams {
   void* a;              // [S*B, hidden] round(RMSNorm(x) * gain)
 };
 
-// a[r] = round(x[src(r)] / sqrt(mean(x^2) + eps) * gain); the row's sum of squares
-// is the in-order sum of ssq_parts per-tile partials. src(r) = r, or with rowmap_bm1
-// > 0 the r-th mask row: (r / bm1) * (bm1 + 1) + 1 + r % bm1.
+// Residual add and RMSNorm of one row: with partials,
+//   x[src] = round(x[src] + ((P_0 + P_1) + ...)[src])     (written back),
+// then a[r] = round(x[src] / sqrt(mean(x[src]^2) + eps) * gain). src(r) = r, or with
+// rowmap_bm1 > 0 the r-th mask row: (r / bm1) * (bm1 + 1) + 1 + r % bm1.
 struct NormParams {
-  int R, hidden, ssq_parts, ssq_ld, rowmap_bm1;
-  const void* x;
-  const double* ssq;
+  int R, hidden, rowmap_bm1;
+  void* x;              // [rows, hidden] residual stream
+  const double* parts;  // nullable: float64 partials [ksplit, rows, hidden] of the branch
+  int ksplit, part_rows;
   const void* gain;
   float eps;
-  void* a;
+  void* a;              // [R, hidden]
 };
 
+// Fused rows: y = (P_0 + P_1) + ... (the fc GEMM's partials), out = round(y / rms(y) * gain).
 struct RowNormParams {
-  int R, hidden, n_tiles;
-  const double* y;      // [R, hidden]
-  const double* ssq_part;  // [R, n_tiles]
+  int R, hidden, ksplit;
+  const double* parts;  // [ksplit, R, hidden]
   const void* gain;
   void* out;            // [R, hidden]
   float eps;
@@ -176,9 +183,10 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t st, Args
   return hipGetLastError();
 }
 
-int gemm_k_per_iter(int dtype, int epi, int K, int tap_h);
+int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h);
+int gemm_ksplit(int epi, int n_tiles, int iters);
 int gemm_tile_cols(int epi);
-hipError_t launch_gemm(int dtype, int epi, const GemmParams& p, int mt, hipStream_t st);
+hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st);
 hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st);

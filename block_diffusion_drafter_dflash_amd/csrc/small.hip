@@ -5,15 +5,39 @@
 
 namespace dfl {
 
-// Deterministic sum over a workgroup of 256 threads: butterfly inside each wave,
-// then the four wave sums in wave order.
-__device__ double block_sum_256(double v, double* red) {
+// Deterministic sum over a workgroup of NT threads: butterfly inside each wave,
+// then the wave sums in wave order.
+template <int NT>
+__device__ double block_sum(double v, double* red) {
   for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  double t = red[0];
+  for (int i = 1; i < NT / kWave; ++i) t += red[i];
+  return t;
+}
+__device__ double block_sum_256(double v, double* red) { return block_sum<256>(v, red); }
+
+// E consecutive float64 values, the in-order sum of ksplit partials [ks][rows][ld].
+template <int E>
+__device__ __forceinline__ void sum_parts(const double* parts, int ksplit, int64_t ks_stride, int64_t off,
+                                          double (&out)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; e += 2) {
+    const double2 v = *reinterpret_cast<const double2*>(parts + off + e);
+    out[e] = v.x;
+    out[e + 1] = v.y;
+  }
+  for (int ks = 1; ks < ksplit; ++ks) {
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const double2 v = *reinterpret_cast<const double2*>(parts + ks * ks_stride + off + e);
+      out[e] += v.x;
+      out[e + 1] += v.y;
+    }
+  }
 }
 
 // Block rows: X[s*B] = embed[anchor[s]], X[s*B + j] = embed[mask] for j >= 1, and the
@@ -51,25 +75,43 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedParams p) {
   }
 }
 
-// a[r] = round(x[src(r)] * inv_rms * gain), the row's sum of squares being the
-// per-tile partials of the kernel that wrote x, added in a fixed tree order.
+// One row of the residual stream: x = round(x + branch) when the branch's partials
+// are given, then a = round(x / sqrt(mean(x^2) + eps) * gain), the sum of squares
+// taken over the stored (rounded) x in a fixed tree order.
+constexpr int kNormThreads = 512;
 template <typename T>
-__global__ __launch_bounds__(256) void k_norm(const NormParams p) {
-  constexpr int E = Elem<T>::E;
-  __shared__ double red[4];
+__global__ __launch_bounds__(kNormThreads) void k_norm(const NormParams p) {
+  constexpr int E = Elem<T>::E, NT = kNormThreads;
+  __shared__ double red[NT / kWave];
   const int r = blockIdx.x;
   const int bm1 = p.rowmap_bm1;
   const int xr = bm1 > 0 ? (r / bm1) * (bm1 + 1) + 1 + r % bm1 : r;
+  T* x = static_cast<T*>(p.x) + (int64_t)xr * p.hidden;
+  const int64_t ks_stride = (int64_t)p.part_rows * p.hidden;
   double ss = 0.0;
-  for (int t = threadIdx.x; t < p.ssq_parts; t += 256) ss += p.ssq[(int64_t)xr * p.ssq_ld + t];
-  ss = block_sum_256(ss, red);
+  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
+    float f[E];
+    uint4 v = ldg16(x + c);
+    if (p.parts) {
+      double br[E], xn[E];
+      sum_parts<E>(p.parts, p.ksplit, ks_stride, (int64_t)xr * p.hidden + c, br);
+      unpack(v, f, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) xn[e] = (double)f[e] + br[e];
+      v = pack_d(xn, T());
+      stg16(x + c, v);
+    }
+    unpack(v, f, T());
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
+  }
+  ss = block_sum<NT>(ss, red);
   const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
-  const T* x = static_cast<const T*>(p.x) + (int64_t)xr * p.hidden;
   T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
-  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
+  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
     float f[E], gf[E];
     double y[E];
-    unpack(ldg16(x + c), f, T());
+    unpack(ldg16(x + c), f, T());   // this thread's own store above
     unpack(ldg16(static_cast<const T*>(p.gain) + c), gf, T());
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
@@ -102,7 +144,16 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
   const bool on = lane < D / 2;
   const double* src = p.raw + (int64_t)r * ld + (int64_t)hi * D;
-  const double x0 = on ? src[lane] : 0.0, x1 = on ? src[lane + D / 2] : 0.0;
+  const int64_t ks_stride = (int64_t)p.S * p.B * ld;
+  double x0 = 0.0, x1 = 0.0;
+  if (on) {
+    x0 = src[lane];
+    x1 = src[lane + D / 2];
+    for (int ks = 1; ks < p.ksplit; ++ks) {
+      x0 += src[ks * ks_stride + lane];
+      x1 += src[ks * ks_stride + lane + D / 2];
+    }
+  }
   if (hi >= p.n_q_heads + p.n_kv_heads) {
     const int vh = hi - p.n_q_heads - p.n_kv_heads;
     T* vb = static_cast<T*>(p.vblk) + ((int64_t)s * p.n_kv_heads + vh) * (D * kBlockSlots);
@@ -165,18 +216,13 @@ __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
   __syncthreads();
   constexpr int TPH = D / 8;
   const int nkvd = p.n_kv_heads * D;
-  const double* raw = p.raw + (int64_t)r * (p.n_layers * 2 * nkvd) + (int64_t)l * 2 * nkvd;
+  const double* raw = p.raw + (int64_t)r * (p.n_layers * 2 * nkvd) + (int64_t)l * 2 * nkvd;   // range 0
   const int items = 2 * p.n_kv_heads * TPH;
   for (int it = tid; it < items; it += 256) {
     const int kind = it / (p.n_kv_heads * TPH), rem = it % (p.n_kv_heads * TPH);
     const int head = rem / TPH, part = rem % TPH;
     double x[8];
-    const double* src = raw + kind * nkvd + head * D + part * 8;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const double2 v = *reinterpret_cast<const double2*>(src + i);
-      x[i] = v.x; x[i + 1] = v.y;
-    }
+    sum_parts<8>(raw, p.ksplit, (int64_t)p.R * p.n_layers * 2 * nkvd, (int64_t)kind * nkvd + head * D + part * 8, x);
     // norm and rotation are computed for every item (shuffles stay inside a head's
     // TPH lanes); only K items keep them
     double ss = 0.0;
@@ -210,30 +256,33 @@ __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
   }
 }
 
-// Fused rows: out[r] = y[r] / sqrt(mean(y[r]^2) + eps) * gain, with the squares summed
-// per column tile by the fc GEMM and here over tiles in order.
+// Fused rows: y = the fc GEMM's partials added in range order; out = round(y /
+// sqrt(mean(y^2) + eps) * gain), the squares summed in a fixed tree order.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rownorm(const RowNormParams p) {
-  constexpr int E = Elem<T>::E;
-  __shared__ double s_inv;
+__global__ __launch_bounds__(kNormThreads) void k_rownorm(const RowNormParams p) {
+  constexpr int E = Elem<T>::E, NT = kNormThreads;
+  __shared__ double red[NT / kWave];
   const int r = blockIdx.x;
-  if (threadIdx.x == 0) {
-    double ss = 0.0;
-    for (int t = 0; t < p.n_tiles; ++t) ss += p.ssq_part[(int64_t)r * p.n_tiles + t];
-    s_inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
+  const int64_t ks_stride = (int64_t)p.R * p.hidden, off = (int64_t)r * p.hidden;
+  double ss = 0.0;
+  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
+    double y[E];
+    sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y);
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += y[e] * y[e];
   }
-  __syncthreads();
-  const double inv = s_inv;
-  const double* y = p.y + (int64_t)r * p.hidden;
+  ss = block_sum<NT>(ss, red);
+  const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
   const T* gn = static_cast<const T*>(p.gain);
-  T* out = static_cast<T*>(p.out) + (int64_t)r * p.hidden;
-  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
+  T* out = static_cast<T*>(p.out) + off;
+  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
+    double y[E];
     float gf[E];
-    double f[E];
+    sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y);
     unpack(ldg16(gn + c), gf, T());
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = y[c + e] * inv * (double)gf[e];
-    stg16(out + c, pack_d(f, T()));
+    for (int e = 0; e < E; ++e) y[e] = y[e] * inv * (double)gf[e];
+    stg16(out + c, pack_d(y, T()));
   }
 }
 
@@ -283,8 +332,8 @@ hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st) 
 }
 
 hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st) {
-  if (dtype == 0) (void)launch_k(k_norm<float>, dim3(p.R), dim3(256), st, p);
-  else (void)launch_k(k_norm<bf16_t>, dim3(p.R), dim3(256), st, p);
+  if (dtype == 0) (void)launch_k(k_norm<float>, dim3(p.R), dim3(kNormThreads), st, p);
+  else (void)launch_k(k_norm<bf16_t>, dim3(p.R), dim3(kNormThreads), st, p);
   return hipGetLastError();
 }
 
@@ -301,8 +350,8 @@ hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st
 }
 
 hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st) {
-  if (dtype == 0) (void)launch_k(k_rownorm<float>, dim3(p.R), dim3(256), st, p);
-  else (void)launch_k(k_rownorm<bf16_t>, dim3(p.R), dim3(256), st, p);
+  if (dtype == 0) (void)launch_k(k_rownorm<float>, dim3(p.R), dim3(kNormThreads), st, p);
+  else (void)launch_k(k_rownorm<bf16_t>, dim3(p.R), dim3(kNormThreads), st, p);
   return hipGetLastError();
 }
 
