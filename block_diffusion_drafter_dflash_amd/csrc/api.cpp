@@ -100,7 +100,7 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h = 
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
   g.iters = K / gemm_k_per_iter(dtype, epi, am, K, tap_h);
-  g.ksplit = gemm_ksplit(epi, g.n_tiles, g.iters);
+  g.ksplit = gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
   return g;
 }

@@ -118,7 +118,16 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
   double l_run = 0.0;
 
   const int64_t kv_page = (int64_t)p.page_size * D;   // elements per (page, head)
-  auto source = [&](int step) {
+  // Page ids of the current batch: lane i of every wave holds the id of the batch's
+  // i-th page (one vector load per batch instead of a dependent read per step).
+  int batch_pid = -1;
+  auto load_batch_pids = [&](int b0) {
+    const int i = cp0 + 2 * b0 + lane;   // chunk-relative page index
+    batch_pid = -1;
+    if (lane < NBP && i < cp1) batch_pid = p.page_table[(int64_t)s * p.pages_per_stream + pg_lo + i];
+  };
+  // step's sources; `b0` is the first step of the batch whose page ids are loaded
+  auto source = [&](int step, int b0) {
     StepSrc src;
     if (step < n_ctx_steps) {
       const int pg = pg_lo + cp0 + 2 * step;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
         src.k[hf] = nullptr;
         src.v[hf] = nullptr;
         if (cp0 + 2 * step + hf < cp1) {
-          const int page = p.page_table[(int64_t)s * p.pages_per_stream + pg + hf];
+          const int page = __shfl(batch_pid, 2 * (step - b0) + hf, kWave);
           if (page >= 0 && page < p.pool_pages) {
             const int64_t off = ((int64_t)page * p.n_kv_heads + h) * kv_page;
             src.k[hf] = static_cast<const T*>(p.kpool) + off;
@@ -179,8 +188,8 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
     }
   };
 
-  auto compute = [&](int step, const unsigned char* sb) {
-    const StepSrc cur = source(step);
+  auto compute = [&](int step, int b0, const unsigned char* sb) {
+    const StepSrc cur = source(step, b0);
 
     // ---- S^T = K Q^T: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i)
     floatx4 sacc[2];
@@ -293,14 +302,15 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
   for (int b0 = 0; b0 < n_steps; b0 += NBP / 2) {
     const int b1 = b0 + NBP / 2 < n_steps ? b0 + NBP / 2 : n_steps;
     int seq = 0;
+    load_batch_pids(b0);
     for (int st = b0; st < b1; ++st) {
-      const StepSrc src = source(st);
+      const StepSrc src = source(st, b0);
       issue(src, 0, 2 * (st - b0), seq);
       issue(src, 1, 2 * (st - b0) + 1, seq);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed in LDS
     __syncthreads();                 // and every other wave's
-    for (int st = b0; st < b1; ++st) compute(st, lds + 2 * (st - b0) * SLOT);
+    for (int st = b0; st < b1; ++st) compute(st, b0, lds + 2 * (st - b0) * SLOT);
     __syncthreads();                 // the batch's slots are free again
   }
 
@@ -345,9 +355,11 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
 
 // Combine the chunks of one (stream, kv head, query tile, 16-dim slice): four waves
 // take contiguous quarters of the stream's own chunks (its count depends only on its
-// reach, so the grouping is the same in any batch), each summing its quarter in chunk
-// order, and the quarters are added in wave order. A lane's query has its chunks'
-// (max, sum) pairs contiguous.
+// reach, so the grouping is the same in any batch). The maximum over all chunks comes
+// first; then each wave sums its quarter in chunk order in float64, every chunk scaled
+// by 2^(m_c - M) (fp32 exp2, as precise as the fp32 chunk partials it scales, and
+// exactly 1 for the chunk holding the maximum), and the quarters are added in wave
+// order. A lane's query has its chunks' (max, sum) pairs contiguous.
 constexpr int kCombineWaves = 4;
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnParams p, int QT) {
@@ -379,7 +391,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnP
   for (int cc = c0; cc < c1; ++cc) {
     const float2 m = ml[cc];
     const float4 v = *reinterpret_cast<const float4*>(po + cc * cstride);
-    const double f = (m.x == -INFINITY) ? 0.0 : exp2((double)m.x - (double)M);
+    const double f = (m.x == -INFINITY) ? 0.0 : (double)exp2f(m.x - M);
     L += (double)m.y * f;
     o[0] += (double)v.x * f;
     o[1] += (double)v.y * f;

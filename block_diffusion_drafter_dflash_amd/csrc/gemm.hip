@@ -209,15 +209,21 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   }
 }
 
-// Final argmax over the LM head's column tiles: one workgroup per mask row.
-__global__ __launch_bounds__(256) void k_argmax_final(const float4* tile_res, int n_tiles, int* draft_out,
-                                                      float* top2_out) {
-  __shared__ float s1[4], s2[4];
-  __shared__ int si[4];
+// Final argmax over the LM head's column tiles: one workgroup of 1024 threads per
+// mask row. The (max, index, second max) merge is order-independent (largest value,
+// lowest index among equals, largest remaining value), so the split over threads
+// does not change the result.
+constexpr int kArgmaxThreads = 1024;
+__global__ __launch_bounds__(kArgmaxThreads) void k_argmax_final(const float4* tile_res, int n_tiles, int* draft_out,
+                                                                 float* top2_out) {
+  constexpr int NW = kArgmaxThreads / kWave;
+  __shared__ float s1[NW], s2[NW];
+  __shared__ int si[NW];
   const int r = blockIdx.x, tid = threadIdx.x;
   float v1 = -INFINITY, v2 = -INFINITY;
   int i1 = 0x7fffffff;
-  for (int t = tid; t < n_tiles; t += 256) {
+#pragma unroll 4
+  for (int t = tid; t < n_tiles; t += kArgmaxThreads) {
     const float4 x = tile_res[(int64_t)r * n_tiles + t];
     top_merge(v1, i1, v2, x.x, __float_as_int(x.y), x.z);
   }
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float4* tile_res, in
   }
   __syncthreads();
   if (tid == 0) {
-    for (int k = 1; k < 4; ++k) top_merge(v1, i1, v2, s1[k], si[k], s2[k]);
+    for (int k = 1; k < NW; ++k) top_merge(v1, i1, v2, s1[k], si[k], s2[k]);
     draft_out[r] = i1;
     if (top2_out) {
       top2_out[2 * r] = v1;
@@ -286,11 +292,12 @@ int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h) {
 
 int gemm_tile_cols(int) { return 32; }
 
-// K ranges of a GEMM: about 512 work items (two workgroups per CU) while each range
-// keeps at least 16 iterations; a function of the weight's shape only.
-int gemm_ksplit(int epi, int n_tiles, int iters) {
+// K ranges of a GEMM: about one workgroup per CU (two for K >= 16384) while each
+// range keeps at least 16 iterations; a function of the weight's shape only.
+int gemm_ksplit(int epi, int n_tiles, int iters, int K) {
   if (epi != EPI_RAW) return 1;
-  int ks = (512 + n_tiles / 2) / n_tiles;
+  const int target = K >= 16384 ? 512 : 256;
+  int ks = (target + n_tiles / 2) / n_tiles;
   const int cap = iters / 16 > 1 ? iters / 16 : 1;
   ks = ks < cap ? ks : cap;
   return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
@@ -303,7 +310,7 @@ hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, 
 
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
                                hipStream_t st) {
-  (void)launch_k(k_argmax_final, dim3(rows), dim3(256), st, reinterpret_cast<const float4*>(tile_res),
+  (void)launch_k(k_argmax_final, dim3(rows), dim3(kArgmaxThreads), st, reinterpret_cast<const float4*>(tile_res),
                      n_tiles, draft_out, top2_out);
   return hipGetLastError();
 }
