@@ -86,21 +86,23 @@ namespace {
 
 struct GemmPlan {
   int am, mt, mgroups, n_tiles, iters, ksplit, n_work;
+  bool tall;   // many rows: the tiled kernel
   size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * 8; }
 };
 
-// Rows are processed in groups of 16 * mt (mt = 1 or 2). The tiling of N, the K
+// Rows are processed in groups of 16 * mt (mt = 1, 2 or 4). The tiling of N, the K
 // ranges and the wave split of each range depend only on the weight's shape, so
 // the per-row arithmetic never depends on M.
 GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h = 0) {
   GemmPlan g;
   g.am = am;
-  g.mt = M <= 16 ? 1 : 2;
+  g.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   g.mgroups = (M + 16 * g.mt - 1) / (16 * g.mt);
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
   g.iters = K / gemm_k_per_iter(dtype, epi, am, K, tap_h);
-  g.ksplit = gemm_ksplit(epi, g.n_tiles, g.iters, K);
+  g.tall = dtype == DFLASH_BF16 && M >= kTallMinRows;
+  g.ksplit = g.tall ? gemm_tall_ksplit(epi, N, K) : gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
   return g;
 }
@@ -421,6 +423,11 @@ static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
 
 static_assert(sizeof(GemmParams) <= 4000, "kernel argument block too large");
 
+static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmParams& p, hipStream_t st) {
+  if (g.tall) return launch_gemm_tall(epi, g.am, p, st);
+  return launch_gemm(dtype, epi, g.am, p, g.mt, st);
+}
+
 int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row_stride, int32_t n_rows,
                      void* fused_out, void* ws, size_t ws_bytes, void* stream) {
   if (!h) return DFLASH_ERR_ARG;
@@ -447,7 +454,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   hipError_t e;
   {
     ProfScope ps(h, "fuse_fc_gemm", st);
-    e = launch_gemm(c.dtype, EPI_RAW, A_TAPS, p, L.g.mt, st);
+    e = run_gemm(c.dtype, L.g, EPI_RAW, p, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
   RowNormParams rn;
@@ -505,7 +512,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   hipError_t e;
   {
     ProfScope ps(h, "inject_kv_gemm", st);
-    e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.g.mt, st);
+    e = run_gemm(c.dtype, L.g, EPI_RAW, p, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
   KvFinishParams kf;
@@ -625,7 +632,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.y_out = qkv_raw;
     {
       ProfScope ps(h, "qkv_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.qkv.mt, st);
+      e = run_gemm(c.dtype, L.qkv, EPI_RAW, p, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv: %s", l, hipGetErrorString(e));
 
@@ -692,7 +699,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.y_out = o_parts;
     {
       ProfScope ps(h, "o_proj_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.o.mt, st);
+      e = run_gemm(c.dtype, L.o, EPI_RAW, p, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d o_proj: %s", l, hipGetErrorString(e));
 
@@ -709,7 +716,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.ld_out = c.intermediate;
     {
       ProfScope ps(h, "gate_up_gemm", st);
-      e = launch_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, p, L.gu.mt, st);
+      e = run_gemm(c.dtype, L.gu, EPI_SWIGLU, p, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d gate/up: %s", l, hipGetErrorString(e));
 
@@ -721,7 +728,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     p.y_out = d_parts;
     {
       ProfScope ps(h, "down_gemm", st);
-      e = launch_gemm(c.dtype, EPI_RAW, A_PLAIN, p, L.down.mt, st);
+      e = run_gemm(c.dtype, L.down, EPI_RAW, p, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d down: %s", l, hipGetErrorString(e));
   }
@@ -738,7 +745,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
   {
     ProfScope ps(h, "lm_head_gemm", st);
-    e = launch_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, p, L.lm.mt, st);
+    e = run_gemm(c.dtype, L.lm, EPI_LMHEAD, p, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "lm head: %s", hipGetErrorString(e));
   {

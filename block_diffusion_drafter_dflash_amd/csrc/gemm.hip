@@ -84,10 +84,13 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  // work item: (column tile, row group, K range), K range fastest
+  // Work item: a column (tile, K range) and a row group. Workgroups are dealt to the
+  // eight XCDs round-robin, so the row groups of one column are placed 8 apart: they
+  // land on the same XCD back to back and share the column's weights in its L2.
   const int wi = blockIdx.x;
-  const int ks = wi % p.ksplit, rest = wi / p.ksplit;
-  const int tile = rest / p.mgroups, mg = rest % p.mgroups;
+  const int col = (wi / (8 * p.mgroups)) * 8 + wi % 8, mg = (wi / 8) % p.mgroups;
+  if (col >= p.n_tiles * p.ksplit) return;
+  const int ks = col % p.ksplit, tile = col / p.ksplit;
   const int row0 = mg * ROWS;
   const int kb = (int)((int64_t)ks * p.iters / p.ksplit), ke = (int)((int64_t)(ks + 1) * p.iters / p.ksplit);
   const int it0 = kb + (int)((int64_t)w * (ke - kb) / KW), it1 = kb + (int)((int64_t)(w + 1) * (ke - kb) / KW);
@@ -142,17 +145,17 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
       const bool more = it + 1 < it1;
       if (more) load(it + 1, a_n, b_n);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < NT; ++nt) {
+          // an iteration's U MFMAs (U * KF products) are summed in fp32, then added
+          // into the float64 accumulator
+          floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            // each MFMA's partial (KF products) is added into the float64 accumulator
-            floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
-            mma_frag(part, a_c[mt][u], b_c[nt][u], T());
+          for (int u = 0; u < U; ++u) mma_frag(part, a_c[mt][u], b_c[nt][u], T());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][nt][i] += (double)part[i];
-          }
+          for (int i = 0; i < 4; ++i) acc[mt][nt][i] += (double)part[i];
+        }
       if (more) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -255,7 +258,9 @@ static int tune_of(int epi, int, int, int) { return epi == EPI_LMHEAD ? TUNE_W4_
 
 template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
 static hipError_t launch_tuned(const GemmParams& p, hipStream_t st) {
-  (void)launch_k(k_gemm<T, MT, NT, EPI, AM, Tune>, dim3(p.n_work), dim3(GemmCfg<T, Tune>::THREADS), st, p);
+  // columns padded to a multiple of 8 so that every column's row groups share an XCD
+  const int grid = (p.n_tiles * p.ksplit + 7) / 8 * 8 * p.mgroups;
+  (void)launch_k(k_gemm<T, MT, NT, EPI, AM, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
   return hipGetLastError();
 }
 
@@ -268,7 +273,8 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t st) {
 template <typename T, int EPI, int NT, int AM>
 static hipError_t launch_mt(const GemmParams& p, int mt, hipStream_t st) {
   if (mt == 1) return launch_t<T, 1, NT, EPI, AM>(p, st);
-  return launch_t<T, 2, NT, EPI, AM>(p, st);
+  if (mt == 2) return launch_t<T, 2, NT, EPI, AM>(p, st);
+  return launch_t<T, 4, NT, EPI, AM>(p, st);
 }
 
 template <typename T>

@@ -185,6 +185,10 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t st, Args
 
 int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h);
 int gemm_ksplit(int epi, int n_tiles, int iters, int K);
+// Tiled GEMM for many rows (bf16, M > kTallMinRows): same parameters and outputs.
+constexpr int kTallMinRows = 65;
+int gemm_tall_ksplit(int epi, int N, int K);
+hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st);
 int gemm_tile_cols(int epi);
 hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
