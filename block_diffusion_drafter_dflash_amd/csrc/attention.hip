@@ -5,23 +5,28 @@
 // context rows in the layer's reach, read from the paged cache, plus all B block
 // rows (added by the stream's last chunk). K pages are [16 keys][d] and V pages are
 // stored transposed, [d][16 keys], so both MFMA operands are contiguous along the
-// reduction. The chunk's pages are copied straight from HBM into LDS in batches
-// (global_load_lds, 16 bytes a lane, every read of a batch in flight at once and no
-// registers held), with an XOR swizzle of 16-byte pieces that keeps the fragment
-// reads free of bank conflicts; each wave then reads its fragments from LDS.
-// Scores are computed transposed (S^T = K Q^T) so that each lane owns one query:
-// the softmax statistics are lane-local plus two cross-lane-group shuffles, and the
-// probabilities feed the P.V MFMA without a transpose. P (fp32) enters the bf16
-// MFMA as three bf16 parts (hi, mid, lo) that hold all of its 24 bits, and the
-// running output and denominator are kept in float64.
+// reduction. A chunk's pages are copied straight from HBM into LDS in batches of
+// BP pages (global_load_lds, 16 bytes a lane, no registers held), into two LDS
+// buffers used alternately: batch b + 1 is in flight while the waves compute on
+// batch b. An XOR swizzle of 16-byte pieces keeps the fragment reads free of bank
+// conflicts. Scores are computed transposed (S^T = K Q^T) so that each lane owns
+// one query: the softmax statistics are lane-local plus two cross-lane-group
+// shuffles, and the probabilities feed the P.V MFMA without a transpose. The
+// running maximum moves once per batch; P (fp32) enters the bf16 MFMA as three bf16
+// parts (hi, mid, lo) that hold all of its 24 bits, and a batch's P.V accumulates
+// into the rescaled fp32 running output. Which keys
+// of a step are valid is one wave-uniform 32-bit mask, so steps without an edge
+// (reach boundary, missing page, block padding) take no masking work at all.
 // A stream whose reach spans several chunks leaves per-chunk partials (max, sum,
 // unnormalised output); k_attn_combine adds them in chunk order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.h"
 
 namespace dfl {
 
-constexpr int kAttnLdsBytes = 64 * 1024;   // one batch of pages
+constexpr int kAttnBufBytes = 32 * 1024;   // one LDS buffer: a batch of pages
 
 template <typename T, int D>
 struct AttnCfg {
@@ -35,15 +40,18 @@ struct AttnCfg {
   static constexpr int NCV = VROW / 16;
   static constexpr int KBYTES = 16 * KROW;               // K part of a page in LDS
   static constexpr int SLOT = KBYTES + D * VROW;         // one page (K and V^T) in LDS
-  static constexpr int NBP = kAttnLdsBytes / SLOT;       // pages per batch (even)
+  static constexpr int BP = kAttnBufBytes / SLOT >= 4 ? 4 : 2;   // pages per batch
+  static constexpr int NSB = BP / 2;                     // steps (two pages) per batch
   static constexpr int NKI = KBYTES / 1024;              // wave-wide 16-byte loads per page: K
   static constexpr int NVI = D * VROW / 1024;            //   and V^T
+  static_assert(BP * SLOT <= kAttnBufBytes, "a batch fits one buffer");
   // XOR swizzles of 16-byte pieces: 16 lanes reading the same piece of 16 key rows,
   // or of 16 value dims, touch 16 distinct bank groups.
   __device__ static __forceinline__ int kswz(int row) {
     return (KROW >= 256 ? row : row / (256 / KROW)) % NCK;
   }
   __device__ static __forceinline__ int vswz(int d) { return (d / (256 / VROW)) % NCV; }
+  static_assert(16 % (256 / VROW) == 0 && (16 / (256 / VROW)) % NCV == 0, "vswz(d + 16) == vswz(d)");
 };
 
 // Key (0..31 within the step's two pages) supplied as row r of S^T tile t. For bf16
@@ -54,29 +62,29 @@ __device__ __forceinline__ int key_of_row(int t, int r) {
   return BF ? 8 * (r >> 2) + 4 * t + (r & 3) : 16 * t + r;
 }
 
-struct StepSrc {
-  const void* k[2];     // K page base ([16][D]) of each half, or null (no keys there)
-  const void* v[2];     // V^T page base ([D][vld]) of each half, or null
-  int vld;              // V^T row stride (16 for cache pages, 32 for the block)
-  int key0;             // absolute position of the step's first key; -1 for the block
-};
-
 __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// Bits [a, e) of a 16-bit half (0 <= a, e <= 16).
+__device__ __forceinline__ uint32_t bit_range16(int a, int e) {
+  return e > a ? ((0xffffu >> (16 - (e - a))) << a) : 0u;
+}
+
 template <typename T, int D, int QT>
-__global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
+__device__ __forceinline__ void attn_body(const AttnParams& p) {
   using C = AttnCfg<T, D>;
   constexpr bool BF = C::BF;
-  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, NBP = C::NBP, SLOT = C::SLOT;
+  constexpr int E = C::E, NF = C::NF, NDT = C::NDT, BP = C::BP, NSB = C::NSB, SLOT = C::SLOT;
   constexpr int KROW = C::KROW, VROW = C::VROW, KBYTES = C::KBYTES, NKI = C::NKI, NVI = C::NVI;
-  static_assert(NBP >= 2 && NBP % 2 == 0, "a batch holds whole steps");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBP * SLOT];
+  // Two separate buffers: the compiler then sees that a batch's copies into one
+  // never alias the fragment reads of the other, and keeps them in flight.
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[BP * SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[BP * SLOT];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int g = p.group, B = p.B;
   const int nq_local = g * B;
@@ -90,10 +98,15 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
   const int n_own = attention_chunks(n_pages);
   const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages) : 0;
   const int cp0 = c * cpp;
-  const int cp1 = c < n_own ? ((c + 1) * cpp < n_pages ? (c + 1) * cpp : n_pages) : cp0;
+  int n_cp = c < n_own ? ((c + 1) * cpp < n_pages ? (c + 1) * cpp : n_pages) - cp0 : 0;
+  n_cp = n_cp > 0 ? n_cp : 0;   // the last chunks of a rounded-up split can be empty
   const bool has_block = (c == n_own - 1);
-  const int n_ctx_steps = cp1 > cp0 ? (cp1 - cp0 + 1) / 2 : 0;
-  const int n_steps = n_ctx_steps + (has_block ? 1 : 0);
+  const int nb_ctx = (n_cp + BP - 1) / BP;
+  const int nb = nb_ctx + (has_block ? 1 : 0);
+
+  // Page ids: lane i holds the id of the chunk's page i (a chunk has at most 64 pages).
+  int pid = -1;
+  if (lane < n_cp) pid = p.page_table[(int64_t)s * p.pages_per_stream + pg_lo + cp0 + lane];
 
   // Queries owned by this lane (column lr of wave w's MFMA tiles): dims
   // [lg*D/4, (lg+1)*D/4) of query row (hl, jrow), as NF 16-byte fragments.
@@ -109,139 +122,130 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
     for (int f = 0; f < NF; ++f) qf[f] = q_valid ? ldg16(qp + f * E) : make_uint4(0, 0, 0, 0);
   }
 
-  double oacc[NDT][4];
+  floatx4 orun[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[dt][i] = 0.0;
+  for (int dt = 0; dt < NDT; ++dt) orun[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   double l_run = 0.0;
 
   const int64_t kv_page = (int64_t)p.page_size * D;   // elements per (page, head)
-  // Page ids of the current batch: lane i of every wave holds the id of the batch's
-  // i-th page (one vector load per batch instead of a dependent read per step).
-  int batch_pid = -1;
-  auto load_batch_pids = [&](int b0) {
-    const int i = cp0 + 2 * b0 + lane;   // chunk-relative page index
-    batch_pid = -1;
-    if (lane < NBP && i < cp1) batch_pid = p.page_table[(int64_t)s * p.pages_per_stream + pg_lo + i];
+  const int64_t blk_off = ((int64_t)s * p.n_kv_heads + h) * (kBlockSlots * D);
+  const T* kblk = static_cast<const T*>(p.kblk) + blk_off;
+  const T* vblk = static_cast<const T*>(p.vblk) + blk_off;
+  // Chunk page i (uniform): its cache id, or -1 when absent or out of the pool.
+  auto page_id = [&](int i) {
+    const int page = __builtin_amdgcn_readlane(pid, i);
+    return (i < n_cp && page >= 0 && page < p.pool_pages) ? page : -1;
   };
-  // step's sources; `b0` is the first step of the batch whose page ids are loaded
-  auto source = [&](int step, int b0) {
-    StepSrc src;
-    if (step < n_ctx_steps) {
-      const int pg = pg_lo + cp0 + 2 * step;
-      src.vld = 16;
-      src.key0 = pg * 16;
+
+  // Copy batch b's pages into `buf`. Wave w issues the wave-wide 16-byte loads
+  // jj = w, w + QT, ... (< NKI + NVI) of every page of the batch: lane l of load jj
+  // fills bytes [jj*1024 + 16 l, + 16) of the page's slot (K part, then V^T part)
+  // from the piece that the swizzle puts there. The lane's source offset within a
+  // page does not depend on the page (K rows [16][D]; V^T dim rows of stride 16 in
+  // the cache, kBlockSlots in the block), so it is computed once.
+  constexpr int LPP = NKI + NVI;
+  constexpr int JW = (LPP + QT - 1) / QT;
+  int src_pg[JW], src_blk[JW];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        src.k[hf] = nullptr;
-        src.v[hf] = nullptr;
-        if (cp0 + 2 * step + hf < cp1) {
-          const int page = __shfl(batch_pid, 2 * (step - b0) + hf, kWave);
-          if (page >= 0 && page < p.pool_pages) {
-            const int64_t off = ((int64_t)page * p.n_kv_heads + h) * kv_page;
-            src.k[hf] = static_cast<const T*>(p.kpool) + off;
-            src.v[hf] = static_cast<const T*>(p.vpool) + off;
-          }
-        }
-      }
+  for (int k = 0; k < JW; ++k) {
+    const int jj = w + QT * k;
+    src_pg[k] = src_blk[k] = 0;
+    if (jj >= LPP) continue;
+    const int bo = (jj < NKI ? jj : jj - NKI) * 1024 + lane * 16;
+    if (jj < NKI) {
+      const int row = bo / KROW, pc = (bo % KROW) / 16;
+      src_pg[k] = src_blk[k] = row * D + (pc ^ C::kswz(row)) * (16 / (int)sizeof(T));
     } else {
-      const int64_t off = ((int64_t)s * p.n_kv_heads + h) * (kBlockSlots * D);
-      src.vld = kBlockSlots;
-      src.key0 = -1;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        src.k[hf] = static_cast<const T*>(p.kblk) + off + hf * 16 * D;
-        src.v[hf] = static_cast<const T*>(p.vblk) + off + hf * 16;
-      }
+      const int d = bo / VROW, ph = (bo % VROW) / 16;
+      const int piece = (ph ^ C::vswz(d)) * (16 / (int)sizeof(T));
+      src_pg[k] = d * 16 + piece;
+      src_blk[k] = d * kBlockSlots + piece;
     }
-    return src;
-  };
-  // A key's validity: on a page, and inside the reach (context) or a block row (block).
-  auto key_ok = [&](const StepSrc& src, int kk) {
-    if (!(kk < 16 ? src.k[0] : src.k[1])) return false;
-    if (src.key0 < 0) return kk < B;
-    const int pos = src.key0 + kk;
-    return pos >= lo && pos < Cs;
-  };
-  // Copy page hf of step `step` into LDS slot `slot`: the wave-wide loads of the slot
-  // are dealt to the workgroup's waves; lane l of load j fills bytes [j*1024 + 16 l,
-  // + 16) of the slot's K part (then V part) from the piece that the swizzle puts there.
-  auto issue = [&](const StepSrc& src, int hf, int slot, int& seq) {
-    const T* kp = static_cast<const T*>(hf ? src.k[1] : src.k[0]);
-    const T* vp = static_cast<const T*>(hf ? src.v[1] : src.v[0]);
-    unsigned char* base = lds + slot * SLOT;
-#pragma unroll
-    for (int j = 0; j < NKI + NVI; ++j, ++seq) {
-      if (seq % QT != w || !kp) continue;
-      const int b = (j < NKI ? j : j - NKI) * 1024 + lane * 16;
-      if (j < NKI) {
-        const int row = b / KROW, pc = (b % KROW) / 16;
-        const int piece = pc ^ C::kswz(row);
-        load_lds16(kp + row * D + piece * (16 / (int)sizeof(T)), base + j * 1024);
+  }
+  auto issue = [&](int b, unsigned char* buf) {
+    const bool blk = b >= nb_ctx;
+    const int np = blk ? 2 : (n_cp - b * BP < BP ? n_cp - b * BP : BP);
+    for (int pb = 0; pb < np; ++pb) {
+      const T* kp;
+      const T* vp;
+      if (blk) {
+        kp = kblk + pb * 16 * D;
+        vp = vblk + pb * 16;
       } else {
-        const int d = b / VROW, ph = (b % VROW) / 16;
-        const int piece = ph ^ C::vswz(d);
-        load_lds16(vp + (int64_t)d * src.vld + piece * (16 / (int)sizeof(T)), base + KBYTES + (j - NKI) * 1024);
+        const int page = page_id(b * BP + pb);
+        if (page < 0) continue;   // absent page: its keys are masked
+        const int64_t off = ((int64_t)page * p.n_kv_heads + h) * kv_page;
+        kp = static_cast<const T*>(p.kpool) + off;
+        vp = static_cast<const T*>(p.vpool) + off;
+      }
+      unsigned char* slot = buf + pb * SLOT;
+#pragma unroll
+      for (int k = 0; k < JW; ++k) {
+        const int jj = w + QT * k;
+        if (jj >= LPP) break;
+        const int so = blk ? src_blk[k] : src_pg[k];
+        if (jj < NKI) load_lds16(kp + so, slot + jj * 1024);
+        else load_lds16(vp + so, slot + KBYTES + (jj - NKI) * 1024);
       }
     }
   };
 
-  auto compute = [&](int step, int b0, const unsigned char* sb) {
-    const StepSrc cur = source(step, b0);
+  // Valid keys of step st of batch b as a uniform 32-bit mask (bit k = key k).
+  auto step_mask = [&](int b, int st) -> uint32_t {
+    if (b >= nb_ctx) return st == 0 ? (B >= 32 ? 0xffffffffu : (1u << B) - 1u) : 0u;
+    uint32_t m = 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int i = b * BP + 2 * st + hf;
+      if (i < n_cp && page_id(i) >= 0) {
+        const int pos0 = (pg_lo + cp0 + i) * 16;
+        const int a = lo - pos0 > 0 ? lo - pos0 : 0, e = Cs - pos0 < 16 ? Cs - pos0 : 16;
+        m |= bit_range16(a, e) << (16 * hf);
+      }
+    }
+    return m;
+  };
 
-    // ---- S^T = K Q^T: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i)
-    floatx4 sacc[2];
+  // Lane byte offsets of the fragments in a buffer (step 0; step st adds 2 st SLOT).
+  // K: tile t row r is key key_of_row(t, r), whose 16-byte piece 4 lg + f (dims
+  // [lg D/4 + f E, + E)) sits at the swizzled place. V^T: bf16 lane group lg reads
+  // keys 8lg..8lg+7 = page lg/2, piece lg&1 of dim row lr (+16 dt); fp32 lane group
+  // lg reads keys 4lg..4lg+3 = piece lg of page t. The swizzle of dim 16 dt + lr
+  // equals that of dim lr. Every LDS address is one buffer plus one offset, so the
+  // compiler can tell the two buffers apart.
+  int koff[2][NF], voff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int kk = key_of_row<BF>(t, lr), row = kk & 15;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int piece = (lg * (D / 4) + f * E) * (int)sizeof(T) / 16;
+      koff[t][f] = (kk >> 4) * SLOT + row * KROW + (piece ^ C::kswz(row)) * 16;
+    }
+    voff[t] = BF ? (lg >> 1) * SLOT + KBYTES + lr * VROW + (((lg & 1) ^ C::vswz(lr)) * 16)
+                 : t * SLOT + KBYTES + lr * VROW + ((lg ^ C::vswz(lr)) * 16);
+  }
+
+  // S^T tiles of step st: lane holds query lr; tile t row 4lg+i is key key_of_row(t, 4lg+i).
+  auto qk_step = [&](const unsigned char* buf, int st, floatx4 (&sacc)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int kk = key_of_row<BF>(t, lr), row = kk & 15;
-      const unsigned char* krow = sb + (kk >> 4) * SLOT + row * KROW;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int piece = (lg * (D / 4) + f * E) * (int)sizeof(T) / 16;
-        mma_frag(sacc[t], *reinterpret_cast<const uint4*>(krow + ((piece ^ C::kswz(row)) * 16)), qf[f], T());
-      }
+      for (int f = 0; f < NF; ++f)
+        mma_frag(sacc[t], *reinterpret_cast<const uint4*>(buf + (koff[t][f] + 2 * st * SLOT)), qf[f], T());
     }
-
-    // ---- online softmax (base 2); the denominator sums in float64
-    const bool edge = cur.key0 < 0 || !cur.k[0] || !cur.k[1] || cur.key0 < lo || cur.key0 + 32 > Cs;
-    float pf[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = !edge || key_ok(cur, key_of_row<BF>(t, 4 * lg + i));
-        pf[t][i] = ok ? sacc[t][i] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, pf[t][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const double corr = (m_new == -INFINITY) ? 1.0 : (double)exp2f(m_run - m_new);
-    double psum = 0.0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[t][i] = (pf[t][i] == -INFINITY) ? 0.f : exp2f(pf[t][i] - m_new);
-        psum += (double)pf[t][i];
-      }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-
-    // ---- this step's O^T = V^T P^T, added to the float64 running output. Values of
-    // keys outside the reach (or of pages never loaded) may be stale or non-finite:
-    // they are zeroed so that a zero probability times them cannot reach the output.
-    floatx4 ot[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) ot[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+  // O^T += V^T P^T of step st (probabilities pr). With MASKED, the values of invalid
+  // keys (outside the reach, absent pages, stale slots) are zeroed so that a zero
+  // probability times them cannot reach the output.
+  auto pv_step = [&](const unsigned char* buf, int st, const float (&pr)[2][4], uint32_t m, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     if constexpr (BF) {
       // P as hi + mid + lo bf16 parts (each remainder is exact in fp32): 24 bits.
-      const float pv[8] = {pf[0][0], pf[0][1], pf[0][2], pf[0][3], pf[1][0], pf[1][1], pf[1][2], pf[1][3]};
-      uint32_t hw[4], mw[4], lw[4], keep[4];
+      const float pv[8] = {pr[0][0], pr[0][1], pr[0][2], pr[0][3], pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
+      uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         hw[q] = f32x2_to_bf16x2(pv[2 * q], pv[2 * q + 1]);
@@ -249,69 +253,155 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
         const float r1 = pv[2 * q + 1] - bf16_to_f32(hw[q] >> 16);
         mw[q] = f32x2_to_bf16x2(r0, r1);
         lw[q] = f32x2_to_bf16x2(r0 - bf16_to_f32(mw[q] & 0xffffu), r1 - bf16_to_f32(mw[q] >> 16));
-        keep[q] = 0xffffffffu;
-        if (edge)
-          keep[q] = (key_ok(cur, 8 * lg + 2 * q) ? 0x0000ffffu : 0u) | (key_ok(cur, 8 * lg + 2 * q + 1) ? 0xffff0000u : 0u);
       }
       const uint4 bh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       const uint4 bm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       const uint4 bl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      // lane group lg: keys 8lg..8lg+7 = page lg/2, 16-byte piece lg&1 of each dim row
-      const unsigned char* vbase = sb + (lg >> 1) * SLOT + KBYTES;
+      uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
+      if constexpr (MASKED) {
+        // lane group lg holds keys 8lg..8lg+7, two to a 32-bit word
+        const uint32_t kb = m >> (8 * lg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          keep[q] = ((kb >> (2 * q)) & 1u ? 0x0000ffffu : 0u) | ((kb >> (2 * q + 1)) & 1u ? 0xffff0000u : 0u);
+      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 16 * dt + lr;
-        uint4 vf = *reinterpret_cast<const uint4*>(vbase + d * VROW + (((lg & 1) ^ C::vswz(d)) * 16));
-        vf.x &= keep[0];
-        vf.y &= keep[1];
-        vf.z &= keep[2];
-        vf.w &= keep[3];
-        mma_frag(ot[dt], vf, bh, T());
-        mma_frag(ot[dt], vf, bm, T());
-        mma_frag(ot[dt], vf, bl, T());
+        uint4 vf = *reinterpret_cast<const uint4*>(buf + (voff[0] + (2 * st * SLOT + dt * 16 * VROW)));
+        if constexpr (MASKED) {
+          vf.x &= keep[0];
+          vf.y &= keep[1];
+          vf.z &= keep[2];
+          vf.w &= keep[3];
+        }
+        mma_frag(orun[dt], vf, bh, T());
+        mma_frag(orun[dt], vf, bm, T());
+        mma_frag(orun[dt], vf, bl, T());
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint4 pb = make_uint4(__float_as_uint(pf[t][0]), __float_as_uint(pf[t][1]), __float_as_uint(pf[t][2]),
-                                    __float_as_uint(pf[t][3]));
-        const int k0 = 16 * t + 4 * lg;
-        const bool ok0 = !edge || key_ok(cur, k0), ok1 = !edge || key_ok(cur, k0 + 1);
-        const bool ok2 = !edge || key_ok(cur, k0 + 2), ok3 = !edge || key_ok(cur, k0 + 3);
-        // page t, 16-byte piece lg (keys 4lg..4lg+3) of each dim row
-        const unsigned char* vbase = sb + t * SLOT + KBYTES;
+        const uint4 pb = make_uint4(__float_as_uint(pr[t][0]), __float_as_uint(pr[t][1]), __float_as_uint(pr[t][2]),
+                                    __float_as_uint(pr[t][3]));
+        const uint32_t kb = m >> (16 * t + 4 * lg);   // page t, keys 4lg..4lg+3
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const int d = 16 * dt + lr;
-          uint4 vf = *reinterpret_cast<const uint4*>(vbase + d * VROW + ((lg ^ C::vswz(d)) * 16));
-          vf.x = ok0 ? vf.x : 0u;
-          vf.y = ok1 ? vf.y : 0u;
-          vf.z = ok2 ? vf.z : 0u;
-          vf.w = ok3 ? vf.w : 0u;
-          mma_frag(ot[dt], vf, pb, T());
+          uint4 vf = *reinterpret_cast<const uint4*>(buf + (voff[t] + (2 * st * SLOT + dt * 16 * VROW)));
+          if constexpr (MASKED) {
+            vf.x = (kb & 1u) ? vf.x : 0u;
+            vf.y = (kb & 2u) ? vf.y : 0u;
+            vf.z = (kb & 4u) ? vf.z : 0u;
+            vf.w = (kb & 8u) ? vf.w : 0u;
+          }
+          mma_frag(orun[dt], vf, pb, T());
         }
       }
     }
+  };
+
+  // One batch. A batch whose keys are all valid (the common case) runs straight-line
+  // code with no masking; otherwise steps without valid keys are skipped and edge
+  // steps are masked (steps whose keys are all valid still take no masking work).
+  auto compute = [&](int b, const unsigned char* buf) {
+    uint32_t msk[NSB];
+    bool full = true;
+#pragma unroll
+    for (int st = 0; st < NSB; ++st) {
+      msk[st] = step_mask(b, st);
+      full = full && msk[st] == 0xffffffffu;
+    }
+    // Workgroups of more than four waves must fit three waves per SIMD; their
+    // registers do not hold two steps' P.V in flight, so they go step by step.
+    if constexpr (QT > 4) full = false;
+
+    float sv[NSB][2][4];
+    {
+      floatx4 sacc[NSB][2];
+      if (full) {
+#pragma unroll
+        for (int st = 0; st < NSB; ++st) qk_step(buf, st, sacc[st]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NSB; ++st) {
+          if (msk[st]) qk_step(buf, st, sacc[st]);
+          else sacc[st][0] = sacc[st][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < NSB; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[st][t][i] = sacc[st][t][i] * p.scale_log2;
+    }
+    if (!full) {
+#pragma unroll
+      for (int st = 0; st < NSB; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((msk[st] >> key_of_row<BF>(t, 4 * lg + i)) & 1u)) sv[st][t][i] = -INFINITY;
+    }
+
+    // ---- the batch's maximum, probabilities (base 2) and their sum; the running
+    // output is rescaled to the new maximum before the batch's P.V accumulates.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NSB; ++st)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[st][t][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < NSB; ++st)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = sv[st][t][i];
+          sv[st][t][i] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m_new);
+          psum += sv[st][t][i];
+        }
+    l_run = l_run * (double)corr + (double)psum;
+    m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] = oacc[dt][i] * corr + (double)ot[dt][i];
+      for (int i = 0; i < 4; ++i) orun[dt][i] *= corr;
+
+    if (full) {
+#pragma unroll
+      for (int st = 0; st < NSB; ++st) pv_step(buf, st, sv[st], 0xffffffffu, std::false_type{});
+    } else {
+#pragma unroll
+      for (int st = 0; st < NSB; ++st) {
+        if (!msk[st]) continue;
+        if (msk[st] == 0xffffffffu) pv_step(buf, st, sv[st], msk[st], std::false_type{});
+        else pv_step(buf, st, sv[st], msk[st], std::true_type{});
+      }
+    }
   };
 
-  // Batches of NBP / 2 steps: copy every page of the batch into LDS, wait, compute.
-  for (int b0 = 0; b0 < n_steps; b0 += NBP / 2) {
-    const int b1 = b0 + NBP / 2 < n_steps ? b0 + NBP / 2 : n_steps;
-    int seq = 0;
-    load_batch_pids(b0);
-    for (int st = b0; st < b1; ++st) {
-      const StepSrc src = source(st, b0);
-      issue(src, 0, 2 * (st - b0), seq);
-      issue(src, 1, 2 * (st - b0) + 1, seq);
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed in LDS
-    __syncthreads();                 // and every other wave's
-    for (int st = b0; st < b1; ++st) compute(st, b0, lds + 2 * (st - b0) * SLOT);
-    __syncthreads();                 // the batch's slots are free again
+  // Pipeline: batch b + 1 is copied into the other buffer while batch b is computed.
+  // Each wait covers only the batch about to be used (the next one is issued after
+  // the barrier), and the barrier also frees the buffer that the next copy reuses.
+  if (nb > 0) issue(0, buf0);
+  for (int b = 0; b < nb; b += 2) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of batch b have landed
+    __syncthreads();                 // everyone's; and buf1 is no longer read
+    if (b + 1 < nb) issue(b + 1, buf1);
+    compute(b, buf0);
+    if (b + 1 >= nb) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (b + 2 < nb) issue(b + 2, buf0);
+    compute(b + 1, buf1);
   }
 
   double l_tot = l_run;
@@ -328,7 +418,7 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
       double v4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = (double)(float)oacc[dt][i] / L;
+      for (int i = 0; i < 4; ++i) v4[i] = (double)orun[dt][i] / L;
       T* dst = op + 16 * dt + 4 * lg;
       if constexpr (BF) {
         *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2(f32_round_odd(v4[0]), f32_round_odd(v4[1])),
@@ -349,60 +439,97 @@ __global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
   float* op = p.part_o + (((sh * p.n_chunks + c) * QT + w) * NDT) * (kWave * 4);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
-    *reinterpret_cast<float4*>(op + (dt * kWave + lane) * 4) =
-        make_float4((float)oacc[dt][0], (float)oacc[dt][1], (float)oacc[dt][2], (float)oacc[dt][3]);
+    *reinterpret_cast<float4*>(op + (dt * kWave + lane) * 4) = make_float4(orun[dt][0], orun[dt][1], orun[dt][2], orun[dt][3]);
 }
 
-// Combine the chunks of one (stream, kv head, query tile, 16-dim slice): four waves
-// take contiguous quarters of the stream's own chunks (its count depends only on its
-// reach, so the grouping is the same in any batch). The maximum over all chunks comes
-// first; then each wave sums its quarter in chunk order in float64, every chunk scaled
-// by 2^(m_c - M) (fp32 exp2, as precise as the fp32 chunk partials it scales, and
-// exactly 1 for the chunk holding the maximum), and the quarters are added in wave
-// order. A lane's query has its chunks' (max, sum) pairs contiguous.
-constexpr int kCombineWaves = 4;
+// Up to four waves a workgroup: two workgroups a CU (LDS-bound) hold two waves a SIMD.
+template <typename T, int D, int QT>
+__global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
+  attn_body<T, D, QT>(p);
+}
+// Five to eight waves: registers for three waves a SIMD.
+template <typename T, int D, int QT>
+__global__ __launch_bounds__(64 * QT, 3) void k_attn_wide(const AttnParams p) {
+  attn_body<T, D, QT>(p);
+}
+
+// Combine the chunks of one (stream, kv head, query tile, 16-dim output slice).
+// Only the stream's own chunks count (their number depends only on its reach, so
+// the result is the same in any batch). Every wave first finds each query's maximum
+// M over all chunk maxima. Then the four waves take contiguous quarters of the
+// chunks; lane (lg, lr) owns dims 16 dt + 4 lg .. + 3 of query lr and adds, in chunk
+// order in float64, each chunk's partial and sum scaled by 2^(m_c - M) (fp32 exp2,
+// as precise as the fp32 chunk partials it scales, and exactly 1 for the chunk
+// holding M); the quarters are added in wave order. Loads go in rounds of
+// kCombineRound chunks a wave, all in flight at once (indices past the range are
+// clamped to a valid chunk and their terms dropped).
+constexpr int kCombineWaves = 4, kCombineRound = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnParams p, int QT) {
-  constexpr int NDT = D / 16, NW = kCombineWaves;
-  __shared__ float s_max[NW][16];
+  constexpr int NDT = D / 16, NW = kCombineWaves, RC = kCombineRound;
   __shared__ double s_sum[NW][64][5];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int sh = blockIdx.x / QT, qt = blockIdx.x % QT, dt = blockIdx.y;
   const int s = sh / p.n_kv_heads, h = sh % p.n_kv_heads;
+  const int nq_local = p.group * p.B;
   const int qi = 16 * qt + lr;
-  const bool valid = qi < p.group * p.B;
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
-  const int n_own = attention_chunks(span_pages(lo, Cs));
-  const int c0 = (int)((int64_t)w * n_own / NW), c1 = (int)((int64_t)(w + 1) * n_own / NW);
-  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + (valid ? qi : 0)) * p.n_chunks;
-  float M = -INFINITY;
-  for (int cc = c0; cc < c1; ++cc) M = fmaxf(M, ml[cc].x);
-  if (lg == 0) s_max[w][lr] = M;
-  __syncthreads();
-  M = s_max[0][lr];
-#pragma unroll
-  for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_max[ww][lr]);
-  double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
+  const int n_own = attention_chunks(span_pages(lo, Cs));   // >= 1
+  // (max, sum) of query qi, chunk c: mq[c]
+  const float2* mq = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + (qi < nq_local ? qi : 0)) * p.n_chunks;
   const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
   const int64_t cstride = (int64_t)QT * NDT * (kWave * 4);
-#pragma unroll 4
-  for (int cc = c0; cc < c1; ++cc) {
-    const float2 m = ml[cc];
-    const float4 v = *reinterpret_cast<const float4*>(po + cc * cstride);
-    const double f = (m.x == -INFINITY) ? 0.0 : (double)exp2f(m.x - M);
-    L += (double)m.y * f;
-    o[0] += (double)v.x * f;
-    o[1] += (double)v.y * f;
-    o[2] += (double)v.z * f;
-    o[3] += (double)v.w * f;
+
+  // ---- M: lane group lg takes chunks lg, lg + 4, ...
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < n_own; c0 += 4 * RC) {
+    float m[RC];
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+      const int c = c0 + 4 * k + lg;
+      const float x = mq[c < n_own ? c : n_own - 1].x;
+      m[k] = c < n_own ? x : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < RC; ++k) M = fmaxf(M, m[k]);
+  }
+  M = fmaxf(M, __shfl_xor(M, 16, kWave));
+  M = fmaxf(M, __shfl_xor(M, 32, kWave));
+
+  // ---- this wave's quarter
+  const int cb = (int)((int64_t)w * n_own / NW), ce = (int)((int64_t)(w + 1) * n_own / NW);
+  double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int c0 = cb; c0 < ce; c0 += RC) {
+    float4 v[RC];
+    float2 ml[RC];
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+      const int c = c0 + k < ce ? c0 + k : ce - 1;
+      v[k] = *reinterpret_cast<const float4*>(po + c * cstride);
+      ml[k] = mq[c];
+    }
+#pragma unroll
+    for (int k = 0; k < RC; ++k) {
+      if (c0 + k < ce) {
+        const double f = (ml[k].x == -INFINITY) ? 0.0 : (double)exp2f(ml[k].x - M);
+        L += (double)ml[k].y * f;
+        o[0] += (double)v[k].x * f;
+        o[1] += (double)v[k].y * f;
+        o[2] += (double)v[k].z * f;
+        o[3] += (double)v[k].w * f;
+      }
+    }
   }
   s_sum[w][lane][0] = L;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_sum[w][lane][1 + i] = o[i];
   __syncthreads();
-  if (w != 0 || !valid) return;
+  if (w != 0 || qi >= nq_local) return;
+  L = s_sum[0][lane][0];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = s_sum[0][lane][1 + i];
 #pragma unroll
   for (int ww = 1; ww < NW; ++ww) {
     L += s_sum[ww][lane][0];
@@ -420,7 +547,8 @@ int attention_query_tiles(int group, int block) { return (group * block + 15) / 
 template <typename T, int D, int QT>
 static void launch_qt(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.n_chunks, p.n_kv_heads, p.S);
-  (void)launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
+  if constexpr (QT > 4) (void)launch_k((k_attn_wide<T, D, QT>), grid, dim3(64 * QT), st, p);
+  else (void)launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
 }
 
 template <typename T, int D>

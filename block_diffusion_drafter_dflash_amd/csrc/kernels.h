@@ -145,15 +145,17 @@ struct VerifyParams {
 
 // Context chunking, in pages of 16 keys, of one stream's reach: a function of that
 // reach alone, so a stream's result does not depend on the other streams of the batch.
-// Up to 256 pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 4096 pages
-// the chunk count stays at 256 / kChunkPagesShort; beyond, chunks hold 64 pages.
-// The count never decreases as the reach grows, so a grid sized for the longest
-// reach covers every stream.
+// Up to 256 pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 2048 pages
+// the chunk count stays at 256 / kChunkPagesShort; beyond, chunks hold at most 64
+// pages. No chunk ever exceeds 64 pages (the attention kernel keeps a chunk's page ids
+// one per lane), and the count never decreases as the reach grows, so a grid sized
+// for the longest reach covers every stream.
 constexpr int kChunkPagesShort = 8;
+constexpr int kChunkPagesMax = 64;
 __host__ __device__ inline int attention_chunks(int pages) {
   if (pages <= 256) return pages <= kChunkPagesShort ? 1 : (pages + kChunkPagesShort - 1) / kChunkPagesShort;
-  if (pages <= 256 / kChunkPagesShort * 64) return 256 / kChunkPagesShort;
-  return (pages + 63) / 64;
+  if (pages <= 256 / kChunkPagesShort * kChunkPagesMax) return 256 / kChunkPagesShort;
+  return (pages + kChunkPagesMax - 1) / kChunkPagesMax;
 }
 __host__ __device__ inline int attention_chunk_pages(int pages) {
   const int n = attention_chunks(pages);
