@@ -2,16 +2,24 @@
 //
 // Y[M, N] = A[M, K] . W[N, K]^T with the same epilogues and outputs as the skinny
 // kernel (float64 K-range partials, SwiGLU, LM-head logits and per-32-column top-2).
-// A workgroup of 4 waves owns a 128-row x 64-column output tile over one K range.
-// Chunks of 64 k are copied from global memory into LDS (A: 128 x 64, W: 64 x 64,
-// XOR-swizzled 16-byte pieces for conflict-free fragment reads), the next two
-// chunks' reads in flight in registers while the current chunk is multiplied. Each wave
-// computes 32 rows x 64 columns with v_mfma_f32_16x16x32_bf16; every two chunks
-// (128 products per element) the fp32 MFMA sums are added into float64
-// accumulators. The row tiles of one column share an XCD and run back to back, so a
-// weight tile read from HBM serves all of them from L2. The summation order differs
-// from the skinny kernel's (one K sweep per K range rather than eight wave slices),
-// so a batch on this path is not bitwise equal to the same streams drafted alone.
+// A workgroup of 8 waves owns a 128-row x 128-column output tile over one K range;
+// wave (wm, wn) computes a 64 x 32 piece as 4 x 2 v_mfma_f32_16x16x32_bf16 tiles.
+// K goes in chunks of 64: a chunk's A (128 x 64) and W (128 x 64) tiles are copied
+// straight from global memory into LDS (global_load_lds, 16 bytes a lane, XOR-swizzled
+// 16-byte pieces so that fragment reads are free of bank conflicts) through a ring of
+// kRing buffers, so that up to kRing - 1 chunks (48 KB of weights) are in flight
+// while one is multiplied: enough bytes per CU to stream the weights at HBM speed.
+// Each buffer is its own LDS object, so the compiler sees that copies into one never
+// alias the fragment reads of another. Every kFlushChunks chunks (256 products per
+// element) the fp32 MFMA sums are added into float64 accumulators. The row tiles of
+// one column share an XCD and run side by side, so a weight tile read from HBM serves
+// all of them from L2. The summation order differs from the skinny kernel's (one K
+// sweep per K range rather than eight wave slices), so a batch on this path is not
+// bitwise equal to the same streams drafted alone.
+//
+// Shapes: K is a multiple of 64 and every weight segment (q | k | v, a layer's k | v,
+// SwiGLU halves) a multiple of 16 rows; the configuration checks (hidden,
+// intermediate and head projections multiples of 128) guarantee both.
 #include "common.hpp"
 #include "kernels.h"
 
@@ -19,13 +27,38 @@ namespace dfl {
 
 namespace {
 
-constexpr int kTallThreads = 256;
-constexpr int BM = 128, BN = 64, BK = 64;
-constexpr int kFlushChunks = 2;
-constexpr int ROWB = BK * 2;           // bytes of one tile row in LDS (bf16)
-constexpr int NCH = ROWB / 16;         // 16-byte pieces per tile row
+constexpr int kWaves = 8, kTallThreads = 64 * kWaves;
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kRing = 4;                     // chunk buffers
+constexpr int kFlushChunks = 4;
+constexpr int ROWB = BK * 2;                 // bytes of one tile row in LDS (bf16)
+constexpr int TILEB = BM * ROWB;             // bytes of one operand tile (A or W)
+constexpr int LOADS = TILEB / 1024;          // wave-wide 16-byte loads per operand tile
+constexpr int QW = LOADS / kWaves;           // loads per wave per operand tile
+constexpr int LPW = 2 * QW;                  // loads per wave per chunk
+static_assert(BM == BN && LOADS % kWaves == 0, "both tiles split evenly over the waves");
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & (NCH - 1); }
+constexpr int NPC = ROWB / 16;               // 16-byte pieces per tile row
+constexpr int RPL = 1024 / ROWB;             // tile rows per wave-wide load
+// 16-byte piece p of tile row r sits at piece p ^ swz(r): the 16 rows one fragment
+// read touches (128 bytes apart) land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & (NPC - 1); }
+
+// Buffer resource over [base, base + 2 GiB): raw (stride 0) 32-bit accesses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// Copy 16 bytes a lane from rsrc + lane_off + uniform_off straight into LDS at
+// lds_wave_base + 16 lane (buffer_load ... lds: the lane offset register is not
+// rewritten per copy, the uniform offset is a scalar). The destination is passed as
+// a plain LDS address, so the copy carries no aliasing information and the compiler
+// adds no waits of its own for it: the ring's explicit waits order copies and reads.
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t uniform_off,
+                                               void* lds_wave_base) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds_wave_base);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(uintptr_t)dst, 16, lane_off, uniform_off, 0, 0);
+}
 
 __device__ __forceinline__ void tall_top_merge(float& v1, int& i1, float& v2, float bv1, int bi1, float bv2) {
   if (bv1 > v1 || (bv1 == v1 && bi1 < i1)) {
@@ -37,15 +70,16 @@ __device__ __forceinline__ void tall_top_merge(float& v1, int& i1, float& v2, fl
   }
 }
 
-// Weight row of local column c (0..63) of column tile t.
+// Weight row of tile row r (0..127) of column tile t. SwiGLU tile t: the 32 rows of
+// wave column h = r / 32 are gate rows 64 t + 16 h + 0..15, then the matching up rows.
 template <int EPI>
-__device__ __forceinline__ const bf16_t* tall_wrow(const GemmParams& p, int t, int c) {
+__device__ __forceinline__ const bf16_t* tall_wrow(const GemmParams& p, int t, int r) {
   if constexpr (EPI == EPI_SWIGLU) {
-    // tile t: columns 0..31 are gate rows 32t.., columns 32..63 the matching up rows
-    const int r = 32 * t + (c & 31);
-    return static_cast<const bf16_t*>(c < 32 ? p.w0 : p.w1) + (int64_t)r * p.K;
+    const int h = r >> 5, q = r & 31;
+    const int gr = 64 * t + 16 * h + (q & 15);
+    return static_cast<const bf16_t*>(q < 16 ? p.w0 : p.w1) + (int64_t)gr * p.K;
   } else if constexpr (EPI == EPI_RAW) {
-    const int n = t * BN + c;
+    const int n = t * BN + r;
     if (p.seg_layers > 0) {
       const int l = n / (2 * p.nkv), rem = n % (2 * p.nkv);
       return static_cast<const bf16_t*>(rem < p.nkv ? p.wk_l[l] : p.wv_l[l]) + (int64_t)(rem % p.nkv) * p.K;
@@ -54,21 +88,38 @@ __device__ __forceinline__ const bf16_t* tall_wrow(const GemmParams& p, int t, i
     if (n < p.nq + p.nkv) return static_cast<const bf16_t*>(p.w1) + (int64_t)(n - p.nq) * p.K;
     return static_cast<const bf16_t*>(p.w2) + (int64_t)(n - p.nq - p.nkv) * p.K;
   } else {
-    int n = t * BN + c;
-    n = n < p.N ? n : p.N - 1;   // ragged last tile: read a valid row, drop it later
-    return static_cast<const bf16_t*>(p.w0) + (int64_t)n * p.K;
+    return static_cast<const bf16_t*>(p.w0) + (int64_t)(t * BN + r) * p.K;
   }
+}
+
+// Workgroup barrier for the copy ring: s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding),
+// then s_barrier. __syncthreads() would also wait for every copy still in flight (its
+// fence must cover LDS writes, and the copies write LDS), which would drain the ring.
+// Here each wave has waited for its own copies of the chunk about to be read and for
+// its own fragment reads, so after the barrier that chunk is complete and the buffer
+// about to be refilled is no longer read. The asm's memory clobber keeps the compiler
+// from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
 }
 
 }  // namespace
 
 template <int EPI, int AM>
-__global__ __launch_bounds__(kTallThreads) void k_gemm_tall(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds_a[BM * ROWB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_b[BN * ROWB];
+__global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf2[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf3[2 * TILEB];
+  static_assert(kRing == 4, "four buffers");
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wm = w >> 2, wn = w & 3;   // rows 64 wm .., columns 32 wn ..
+
   const int n_ct = EPI == EPI_SWIGLU ? p.N / BN : (p.N + BN - 1) / BN;   // column tiles
   const int n_rt = (p.M + BM - 1) / BM;                                   // row tiles
   // (column tile, K range) columns; the row tiles of a column are 8 apart (one XCD)
@@ -79,87 +130,108 @@ __global__ __launch_bounds__(kTallThreads) void k_gemm_tall(const GemmParams p) 
   const int n_chunks = p.K / BK;
   const int kb = (int)((int64_t)ks * n_chunks / p.ksplit), ke = (int)((int64_t)(ks + 1) * n_chunks / p.ksplit);
 
-  // This thread's share of a chunk: A rows (tid >> 3) + 32 j, piece tid & 7; W rows
-  // (tid >> 3) + 32 j, same piece.
-  const int piece = tid & 7, trow = tid >> 3;
-  const bf16_t* arow[4];
+  // ---- copies: wave w issues loads q = QW w + k (k < QW) of the A tile and of the W
+  // tile. Lane l of load q fills bytes [1024 q + 16 l, + 16) of the tile: row
+  // RPL q + l / NPC, stored piece l % NPC, i.e. source piece (l % NPC) ^ swz(row). The
+  // uniform part of a source address (matrix, first row of the load, chunk) is a
+  // scalar, the lane adds a fixed offset. Rows past M (and LM-head rows past N) repeat
+  // the last row; their results are never stored.
+  const bf16_t* a_base[QW];
+  const bf16_t* w_base[QW];
+  int a_off[QW], w_off[QW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int r = rt * BM + trow + 32 * j;
-    r = r < p.M ? r : p.M - 1;
-    arow[j] = AM == A_TAPS ? nullptr : static_cast<const bf16_t*>(p.a) + (int64_t)r * p.lda;
+  for (int k = 0; k < QW; ++k) {
+    const int q = QW * w + k;
+    const int row = RPL * q + lane / NPC;
+    const int piece = (lane % NPC) ^ swz(row);
+    const int ar0 = min(rt * BM + RPL * q, p.M - 1), ar = min(rt * BM + row, p.M - 1);
+    if constexpr (AM == A_TAPS) {
+      a_base[k] = nullptr;
+      a_off[k] = (int)((int64_t)ar * p.tap_stride) + piece * 8;
+    } else {
+      a_base[k] = static_cast<const bf16_t*>(p.a) + (int64_t)ar0 * p.lda;
+      a_off[k] = (ar - ar0) * (int)p.lda + piece * 8;
+    }
+    if constexpr (EPI == EPI_SWIGLU) {
+      w_base[k] = tall_wrow<EPI>(p, ct, RPL * q);   // RPL consecutive gate or up rows
+      w_off[k] = (lane / NPC) * p.K + piece * 8;
+    } else {
+      const int n0 = min(ct * BN + RPL * q, p.N - 1), n = min(ct * BN + row, p.N - 1);
+      w_base[k] = tall_wrow<EPI>(p, ct, n0 - ct * BN);
+      w_off[k] = (n - n0) * p.K + piece * 8;
+    }
   }
-  const bf16_t* wrow[2];
+  __amdgpu_buffer_rsrc_t a_rsrc[QW], w_rsrc[QW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) wrow[j] = tall_wrow<EPI>(p, ct, trow + 32 * j);
-
-  auto fetch = [&](int ch, uint4 (&ra)[4], uint4 (&rb)[2]) {
-    const int k = ch * BK + piece * 8;
+  for (int k = 0; k < QW; ++k) {
+    if constexpr (AM != A_TAPS) a_rsrc[k] = rsrc_of(a_base[k]);
+    w_rsrc[k] = rsrc_of(w_base[k]);
+  }
+  auto issue = [&](int ch, unsigned char* buf) {
+    const int k0 = ch * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int k = 0; k < QW; ++k) {
+      const int q = QW * w + k;
       if constexpr (AM == A_TAPS) {
         // a chunk never straddles two planes (hidden % 64 == 0)
-        const int plane = (ch * BK) / p.tap_h;
-        int r = rt * BM + trow + 32 * j;
-        r = r < p.M ? r : p.M - 1;
-        ra[j] = ldg16(static_cast<const bf16_t*>(p.taps[plane]) + (int64_t)r * p.tap_stride + (k - plane * p.tap_h));
+        const int plane = k0 / p.tap_h;
+        buf_load_lds16(rsrc_of(static_cast<const bf16_t*>(p.taps[plane]) + (k0 - plane * p.tap_h)), 2u * (uint32_t)a_off[k],
+                       0u, buf + q * 1024);
       } else {
-        ra[j] = ldg16(arow[j] + k);
+        buf_load_lds16(a_rsrc[k], 2u * (uint32_t)a_off[k], 2u * (uint32_t)k0, buf + q * 1024);
       }
+      buf_load_lds16(w_rsrc[k], 2u * (uint32_t)w_off[k], 2u * (uint32_t)k0, buf + TILEB + q * 1024);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) rb[j] = ldg16(wrow[j] + k);
   };
-  auto stage = [&](const uint4 (&ra)[4], const uint4 (&rb)[2]) {
+
+  // ---- fragments: A rows 64 wm + 16 i + lr, W rows 32 wn + 16 j + lr; for k-step s
+  // of the chunk, lane group lg reads k = 32 s + 8 lg .. + 7 (piece 4 s + lg). One
+  // buffer plus one offset, so that every read stays attributed to its buffer.
+  constexpr int KS = BK / 32;
+  int aoff[KS][4], boff[KS][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = trow + 32 * j;
-      *reinterpret_cast<uint4*>(lds_a + r * ROWB + ((piece ^ swz(r)) * 16)) = ra[j];
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = 64 * wm + 16 * i + lr;
+      aoff[s][i] = ra * ROWB + (((4 * s + lg) ^ swz(ra)) * 16);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int r = trow + 32 * j;
-      *reinterpret_cast<uint4*>(lds_b + r * ROWB + ((piece ^ swz(r)) * 16)) = rb[j];
+      const int rb = 32 * wn + 16 * j + lr;
+      boff[s][j] = TILEB + rb * ROWB + (((4 * s + lg) ^ swz(rb)) * 16);
     }
-  };
+  }
 
-  // wave w: rows 32w..32w+31 of the tile (2 row tiles), all 64 columns (4 column tiles)
-  double acc[2][4][4];
-  floatx4 part[2][4];
+  double acc[4][2][4];
+  floatx4 part[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0;
     }
 
-  auto compute = [&](int ch) {
+  auto compute = [&](int ch, const unsigned char* buf) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int pc = sub * 4 + lg;
-      uint4 af[2], bf[4];
+    for (int s = 0; s < KS; ++s) {
+      uint4 af[4], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 32 * w + 16 * i + lr;
-        af[i] = *reinterpret_cast<const uint4*>(lds_a + r * ROWB + ((pc ^ swz(r)) * 16));
-      }
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(buf + aoff[s][i]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * j + lr;
-        bf[j] = *reinterpret_cast<const uint4*>(lds_b + r * ROWB + ((pc ^ swz(r)) * 16));
-      }
+      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(buf + boff[s][j]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma_frag(part[i][j], af[i], bf[j], bf16_t());
+        for (int j = 0; j < 2; ++j) mma_frag(part[i][j], af[i], bf[j], bf16_t());
     }
     if ((ch - kb) % kFlushChunks == kFlushChunks - 1 || ch + 1 == ke) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][j][e] += (double)part[i][j][e];
           part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -167,74 +239,74 @@ __global__ __launch_bounds__(kTallThreads) void k_gemm_tall(const GemmParams p) 
     }
   };
 
-  // Pipeline: chunk ch is in LDS while the reads of chunks ch + 1 and ch + 2 are in
-  // flight in two register sets used alternately.
+  // ---- pipeline over the ring: chunk c lives in buffer (c - kb) % kRing. Before
+  // chunk ch is multiplied, this wave's copies of it have landed (the kRing - 2 later
+  // chunks may still be in flight) and, after the barrier, everyone's; no wave reads
+  // the buffer of chunk ch - 1 any more, so chunk ch + kRing - 1 is copied into it.
+  // Copies past the range repeat its last chunk (never read), so that every step has
+  // the same number of copies in flight.
+  auto step = [&](int ch, const unsigned char* cur, unsigned char* nxt) {
+    ring_barrier<(kRing - 2) * LPW>();
+    issue(min(ch + kRing - 1, ke - 1), nxt);
+    compute(ch, cur);
+  };
   if (kb < ke) {
-    uint4 ra0[4], rb0[2], ra1[4], rb1[2];
-    fetch(kb, ra0, rb0);
-    if (kb + 1 < ke) fetch(kb + 1, ra1, rb1);
-    stage(ra0, rb0);
-    __syncthreads();
-    // body(ch, next, free): `next` holds chunk ch + 1's reads; `free` takes ch + 2's
-    auto body = [&](int ch, uint4 (&na)[4], uint4 (&nb)[2], uint4 (&fa)[4], uint4 (&fb)[2]) {
-      if (ch + 2 < ke) fetch(ch + 2, fa, fb);
-      compute(ch);
-      __syncthreads();
-      if (ch + 1 < ke) {
-        stage(na, nb);
-        __syncthreads();
-      }
-    };
-    for (int ch = kb; ch < ke; ch += 2) {
-      body(ch, ra1, rb1, ra0, rb0);
-      if (ch + 1 < ke) body(ch + 1, ra0, rb0, ra1, rb1);
+    issue(kb, buf0);
+    issue(min(kb + 1, ke - 1), buf1);
+    issue(min(kb + 2, ke - 1), buf2);
+    for (int ch = kb; ch < ke; ch += kRing) {
+      step(ch, buf0, buf3);
+      if (ch + 1 >= ke) break;
+      step(ch + 1, buf1, buf0);
+      if (ch + 2 >= ke) break;
+      step(ch + 2, buf2, buf1);
+      if (ch + 3 >= ke) break;
+      step(ch + 3, buf3, buf2);
     }
+    // the repeated copies must land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
-  // ---- epilogue: lane holds rows 32w + 16i + 4lg + e, columns 16j + lr
+  // ---- epilogue: lane holds rows 64 wm + 16 i + 4 lg + e, columns 32 wn + 16 j + lr
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = rt * BM + 32 * w + 16 * i + 4 * lg + e;
+      const int r = rt * BM + 64 * wm + 16 * i + 4 * lg + e;
       const bool rv = r < p.M;
       if constexpr (EPI == EPI_RAW) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = ct * BN + 16 * j + lr;
+        for (int j = 0; j < 2; ++j) {
+          const int n = ct * BN + 32 * wn + 16 * j + lr;
           if (rv && n < p.N) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = acc[i][j][e];
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
+        // column lr of tile j = 0 is gate row 64 ct + 16 wn + lr; tile j = 1 its up row
+        const double g = acc[i][0][e], u = acc[i][1][e];
+        if (rv)
+          Elem<bf16_t>::store_d(static_cast<bf16_t*>(p.m_out) + (int64_t)r * p.ld_out + 64 * ct + 16 * wn + lr,
+                                g / (1.0 + exp(-g)) * u);
+      } else {   // EPI_LMHEAD: fp32 logits and top-2 of the wave's 32-column group
+        float v1 = -INFINITY, v2 = -INFINITY;
+        int i1 = 0x7fffffff;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const double g = acc[i][j][e], u = acc[i][j + 2][e];
-          if (rv) Elem<bf16_t>::store_d(static_cast<bf16_t*>(p.m_out) + (int64_t)r * p.ld_out + 32 * ct + 16 * j + lr,
-                                       g / (1.0 + exp(-g)) * u);
-        }
-      } else {   // EPI_LMHEAD: fp32 logits and top-2 of each 32-column group
-#pragma unroll
-        for (int jg = 0; jg < 2; ++jg) {
-          float v1 = -INFINITY, v2 = -INFINITY;
-          int i1 = 0x7fffffff;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int n = ct * BN + 32 * jg + 16 * jj + lr;
-            const float v = (float)acc[i][2 * jg + jj][e];
-            if (n < p.N) {
-              if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
-              tall_top_merge(v1, i1, v2, v, n, -INFINITY);
-            }
+          const int n = ct * BN + 32 * wn + 16 * j + lr;
+          const float v = (float)acc[i][j][e];
+          if (n < p.N) {
+            if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
+            tall_top_merge(v1, i1, v2, v, n, -INFINITY);
           }
-          for (int m = 1; m < 16; m <<= 1) {
-            const float o1 = __shfl_xor(v1, m, kWave);
-            const int oi = __shfl_xor(i1, m, kWave);
-            const float o2 = __shfl_xor(v2, m, kWave);
-            tall_top_merge(v1, i1, v2, o1, oi, o2);
-          }
-          const int grp = 2 * ct + jg;
-          if (rv && lr == 0 && grp < p.n_tiles)
-            reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + grp] = make_float4(v1, __int_as_float(i1), v2, 0.f);
         }
+        for (int m = 1; m < 16; m <<= 1) {
+          const float o1 = __shfl_xor(v1, m, kWave);
+          const int oi = __shfl_xor(i1, m, kWave);
+          const float o2 = __shfl_xor(v2, m, kWave);
+          tall_top_merge(v1, i1, v2, o1, oi, o2);
+        }
+        const int grp = 4 * ct + wn;
+        if (rv && lr == 0 && grp < p.n_tiles)
+          reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + grp] = make_float4(v1, __int_as_float(i1), v2, 0.f);
       }
     }
 }
@@ -242,13 +314,13 @@ __global__ __launch_bounds__(kTallThreads) void k_gemm_tall(const GemmParams p) 
 int gemm_tall_column_tiles(int epi, int N) { return epi == EPI_SWIGLU ? N / BN : (N + BN - 1) / BN; }
 
 // K ranges of the tiled GEMM: about 256 (column tile, K range) pairs, each range at
-// least 8 chunks; a function of the weight's shape only, so that a row's arithmetic
+// least 16 chunks; a function of the weight's shape only, so that a row's arithmetic
 // does not depend on how many rows the batch has.
 int gemm_tall_ksplit(int epi, int N, int K) {
   if (epi != EPI_RAW) return 1;
   const int tiles = gemm_tall_column_tiles(epi, N);
   int ks = (256 + tiles / 2) / tiles;
-  const int cap = K / BK / 8 > 1 ? K / BK / 8 : 1;
+  const int cap = K / BK / 16 > 1 ? K / BK / 16 : 1;
   ks = ks < cap ? ks : cap;
   return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
 }
