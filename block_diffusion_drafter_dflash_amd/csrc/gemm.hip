@@ -298,15 +298,21 @@ int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h) {
 
 int gemm_tile_cols(int) { return 32; }
 
-// K ranges of a GEMM: about one workgroup per CU (two for K >= 16384) while each
-// range keeps at least 16 iterations; a function of the weight's shape only.
+// K ranges of a GEMM, a function of the weight's shape only. Preferred: the fewest
+// ranges that give at least one workgroup per CU (two for K >= 16384) and deal the
+// work items evenly over the MI355X's 256 CUs; otherwise about that many workgroups.
+// Every range keeps at least 16 iterations.
+constexpr int kCUs = 256;
 int gemm_ksplit(int epi, int n_tiles, int iters, int K) {
   if (epi != EPI_RAW) return 1;
-  const int target = K >= 16384 ? 512 : 256;
+  const int target = K >= 16384 ? 2 * kCUs : kCUs;
+  int cap = iters / 16 > 1 ? iters / 16 : 1;
+  cap = cap < 8 ? cap : 8;
+  for (int ks = 1; ks <= cap; ++ks)
+    if (n_tiles * ks >= target && (n_tiles * ks) % kCUs == 0) return ks;
   int ks = (target + n_tiles / 2) / n_tiles;
-  const int cap = iters / 16 > 1 ? iters / 16 : 1;
   ks = ks < cap ? ks : cap;
-  return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+  return ks < 1 ? 1 : ks;
 }
 
 hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st) {

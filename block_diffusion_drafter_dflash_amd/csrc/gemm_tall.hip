@@ -313,16 +313,27 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 
 int gemm_tall_column_tiles(int epi, int N) { return epi == EPI_SWIGLU ? N / BN : (N + BN - 1) / BN; }
 
-// K ranges of the tiled GEMM: about 256 (column tile, K range) pairs, each range at
-// least 16 chunks; a function of the weight's shape only, so that a row's arithmetic
-// does not depend on how many rows the batch has.
+// K ranges of the tiled GEMM, a function of the weight's shape only (so that a row's
+// arithmetic does not depend on how many rows the batch has). Sized for two row tiles
+// (up to 256 rows) on 256 CUs, one workgroup each: the split with the shortest
+// makespan, rounds(ks) / ks with rounds = ceil(2 * tiles * ks / 256), each extra range
+// charged a little for its float64 partial; every range at least 16 chunks.
 int gemm_tall_ksplit(int epi, int N, int K) {
   if (epi != EPI_RAW) return 1;
   const int tiles = gemm_tall_column_tiles(epi, N);
-  int ks = (256 + tiles / 2) / tiles;
-  const int cap = K / BK / 16 > 1 ? K / BK / 16 : 1;
-  ks = ks < cap ? ks : cap;
-  return ks < 1 ? 1 : (ks > 8 ? 8 : ks);
+  int cap = K / BK / 16 > 1 ? K / BK / 16 : 1;
+  cap = cap < 8 ? cap : 8;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int ks = 1; ks <= cap; ++ks) {
+    const int rounds = (2 * tiles * ks + 255) / 256;
+    const double cost = (double)rounds / ks + 0.02 * ks;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = ks;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st) {
