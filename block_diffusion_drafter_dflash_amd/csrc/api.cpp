@@ -241,6 +241,8 @@ static int validate(const dflash_config* c) {
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
     REFUSE("n_q_heads %d is not a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
   if (c->hidden < 128 || c->hidden % 128) REFUSE("hidden %d is not a positive multiple of 128", c->hidden);
+  if (c->hidden > (c->dtype == DFLASH_F32 ? 8192 : 16384))
+    REFUSE("hidden %d exceeds %d (the row kernels hold a row in registers)", c->hidden, c->dtype == DFLASH_F32 ? 8192 : 16384);
   if (c->intermediate < 128 || c->intermediate % 128) REFUSE("intermediate %d is not a positive multiple of 128", c->intermediate);
   if ((c->n_q_heads * c->head_dim) % 128 || (c->n_kv_heads * c->head_dim) % 128)
     REFUSE("head projections (n_q*d=%d, n_kv*d=%d) are not multiples of 128", c->n_q_heads * c->head_dim,

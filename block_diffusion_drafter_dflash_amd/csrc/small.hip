@@ -18,68 +18,99 @@ __device__ double block_sum(double v, double* red) {
   for (int i = 1; i < NT / kWave; ++i) t += red[i];
   return t;
 }
-__device__ double block_sum_256(double v, double* red) { return block_sum<256>(v, red); }
 
-// E consecutive float64 values, the in-order sum of ksplit partials [ks][rows][ld].
+// E consecutive float64 values, the in-order sum of ksplit partials [ks][rows][ld]:
+// ((P_0 + P_1) + P_2) + ..., the loads of up to four partials in flight at once.
 template <int E>
 __device__ __forceinline__ void sum_parts(const double* parts, int ksplit, int64_t ks_stride, int64_t off,
                                           double (&out)[E]) {
+  constexpr int KR = 4;
 #pragma unroll
-  for (int e = 0; e < E; e += 2) {
-    const double2 v = *reinterpret_cast<const double2*>(parts + off + e);
-    out[e] = v.x;
-    out[e + 1] = v.y;
-  }
-  for (int ks = 1; ks < ksplit; ++ks) {
+  for (int e = 0; e < E; ++e) out[e] = 0.0;
+  for (int k0 = 0; k0 < ksplit; k0 += KR) {
+    double2 v[KR][E / 2];
 #pragma unroll
-    for (int e = 0; e < E; e += 2) {
-      const double2 v = *reinterpret_cast<const double2*>(parts + ks * ks_stride + off + e);
-      out[e] += v.x;
-      out[e + 1] += v.y;
-    }
+    for (int k = 0; k < KR; ++k)
+      if (k0 + k < ksplit)
+#pragma unroll
+        for (int e = 0; e < E; e += 2) v[k][e / 2] = *reinterpret_cast<const double2*>(parts + (k0 + k) * ks_stride + off + e);
+#pragma unroll
+    for (int k = 0; k < KR; ++k)
+      if (k0 + k < ksplit)
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          if (k0 + k == 0) {
+            out[e] = v[k][e / 2].x;
+            out[e + 1] = v[k][e / 2].y;
+          } else {
+            out[e] += v[k][e / 2].x;
+            out[e + 1] += v[k][e / 2].y;
+          }
+        }
   }
 }
 
+// Row kernels: kNormThreads threads a row, thread t owning the CH groups of E
+// consecutive elements at (g * kNormThreads + t) * E, kept in registers between the
+// sum of squares and the scaling (hidden <= kNormThreads * E * CH).
+constexpr int kNormThreads = 512;
+
 // Block rows: X[s*B] = embed[anchor[s]], X[s*B + j] = embed[mask] for j >= 1, and the
 // first layer's normalised input a = round(X / sqrt(mean(X^2) + eps) * gain).
-template <typename T>
-__global__ __launch_bounds__(256) void k_embed(const EmbedParams p) {
-  constexpr int E = Elem<T>::E;
-  __shared__ double red[4];
+template <typename T, int CH>
+__global__ __launch_bounds__(kNormThreads) void k_embed(const EmbedParams p) {
+  constexpr int E = Elem<T>::E, NT = kNormThreads;
+  __shared__ double red[NT / kWave];
   const int r = blockIdx.x;
   const int s = r / p.B, j = r % p.B;
   int tok = j == 0 ? p.anchor[s] : p.mask_token;
   tok = tok < 0 ? 0 : (tok >= p.vocab ? p.vocab - 1 : tok);
   const T* src = static_cast<const T*>(p.embed) + (int64_t)tok * p.hidden;
   T* dst = static_cast<T*>(p.x) + (int64_t)r * p.hidden;
-  double ss = 0.0;
-  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
-    uint4 v = ldg16(src + c);
-    stg16(dst + c, v);
-    float f[E];
-    unpack(v, f, T());
-#pragma unroll
-    for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
-  }
-  ss = block_sum_256(ss, red);
-  const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
   T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
-  for (int c = threadIdx.x * E; c < p.hidden; c += 256 * E) {
-    float f[E], gf[E];
-    double y[E];
-    unpack(ldg16(src + c), f, T());
-    unpack(ldg16(static_cast<const T*>(p.gain) + c), gf, T());
+  const T* gn = static_cast<const T*>(p.gain);
+  uint4 v[CH], g[CH];
 #pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
-    stg16(a + c, pack_d(y, T()));
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      v[ch] = ldg16(src + c);
+      g[ch] = ldg16(gn + c);
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      stg16(dst + c, v[ch]);
+      float f[E];
+      unpack(v[ch], f, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
+    }
+  }
+  ss = block_sum<NT>(ss, red);
+  const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      float f[E], gf[E];
+      double y[E];
+      unpack(v[ch], f, T());
+      unpack(g[ch], gf, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
+      stg16(a + c, pack_d(y, T()));
+    }
   }
 }
 
 // One row of the residual stream: x = round(x + branch) when the branch's partials
 // are given, then a = round(x / sqrt(mean(x^2) + eps) * gain), the sum of squares
 // taken over the stored (rounded) x in a fixed tree order.
-constexpr int kNormThreads = 512;
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(kNormThreads) void k_norm(const NormParams p) {
   constexpr int E = Elem<T>::E, NT = kNormThreads;
   __shared__ double red[NT / kWave];
@@ -87,35 +118,52 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(const NormParams p) {
   const int bm1 = p.rowmap_bm1;
   const int xr = bm1 > 0 ? (r / bm1) * (bm1 + 1) + 1 + r % bm1 : r;
   T* x = static_cast<T*>(p.x) + (int64_t)xr * p.hidden;
+  const T* gn = static_cast<const T*>(p.gain);
   const int64_t ks_stride = (int64_t)p.part_rows * p.hidden;
-  double ss = 0.0;
-  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
-    float f[E];
-    uint4 v = ldg16(x + c);
-    if (p.parts) {
-      double br[E], xn[E];
-      sum_parts<E>(p.parts, p.ksplit, ks_stride, (int64_t)xr * p.hidden + c, br);
-      unpack(v, f, T());
+  uint4 v[CH], g[CH];
 #pragma unroll
-      for (int e = 0; e < E; ++e) xn[e] = (double)f[e] + br[e];
-      v = pack_d(xn, T());
-      stg16(x + c, v);
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      v[ch] = ldg16(x + c);
+      g[ch] = ldg16(gn + c);
     }
-    unpack(v, f, T());
+  }
+  double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      float f[E];
+      if (p.parts) {
+        double br[E], xn[E];
+        sum_parts<E>(p.parts, p.ksplit, ks_stride, (int64_t)xr * p.hidden + c, br);
+        unpack(v[ch], f, T());
+#pragma unroll
+        for (int e = 0; e < E; ++e) xn[e] = (double)f[e] + br[e];
+        v[ch] = pack_d(xn, T());
+        stg16(x + c, v[ch]);
+      }
+      unpack(v[ch], f, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += (double)f[e] * (double)f[e];
+    }
   }
   ss = block_sum<NT>(ss, red);
   const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
   T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
-  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
-    float f[E], gf[E];
-    double y[E];
-    unpack(ldg16(x + c), f, T());   // this thread's own store above
-    unpack(ldg16(static_cast<const T*>(p.gain) + c), gf, T());
 #pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
-    stg16(a + c, pack_d(y, T()));
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      float f[E], gf[E];
+      double y[E];
+      unpack(v[ch], f, T());
+      unpack(g[ch], gf, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = (double)f[e] * inv * (double)gf[e];
+      stg16(a + c, pack_d(y, T()));
+    }
   }
 }
 
@@ -147,11 +195,21 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   const int64_t ks_stride = (int64_t)p.S * p.B * ld;
   double x0 = 0.0, x1 = 0.0;
   if (on) {
-    x0 = src[lane];
-    x1 = src[lane + D / 2];
-    for (int ks = 1; ks < p.ksplit; ++ks) {
-      x0 += src[ks * ks_stride + lane];
-      x1 += src[ks * ks_stride + lane + D / 2];
+    // ((P_0 + P_1) + P_2) + ..., up to eight partials' loads in flight
+    for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
+      double v0[8], v1[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < p.ksplit) {
+          v0[k] = src[(k0 + k) * ks_stride + lane];
+          v1[k] = src[(k0 + k) * ks_stride + lane + D / 2];
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < p.ksplit) {
+          x0 = k0 + k == 0 ? v0[k] : x0 + v0[k];
+          x1 = k0 + k == 0 ? v1[k] : x1 + v1[k];
+        }
     }
   }
   if (hi >= p.n_q_heads + p.n_kv_heads) {
@@ -258,31 +316,40 @@ __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
 
 // Fused rows: y = the fc GEMM's partials added in range order; out = round(y /
 // sqrt(mean(y^2) + eps) * gain), the squares summed in a fixed tree order.
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(kNormThreads) void k_rownorm(const RowNormParams p) {
   constexpr int E = Elem<T>::E, NT = kNormThreads;
   __shared__ double red[NT / kWave];
   const int r = blockIdx.x;
   const int64_t ks_stride = (int64_t)p.R * p.hidden, off = (int64_t)r * p.hidden;
+  const T* gn = static_cast<const T*>(p.gain);
+  double y[CH][E];
+  uint4 g[CH];
   double ss = 0.0;
-  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
-    double y[E];
-    sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y);
 #pragma unroll
-    for (int e = 0; e < E; ++e) ss += y[e] * y[e];
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      g[ch] = ldg16(gn + c);
+      sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y[ch]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += y[ch][e] * y[ch][e];
+    }
   }
   ss = block_sum<NT>(ss, red);
   const double inv = 1.0 / sqrt(ss / (double)p.hidden + (double)p.eps);
-  const T* gn = static_cast<const T*>(p.gain);
   T* out = static_cast<T*>(p.out) + off;
-  for (int c = threadIdx.x * E; c < p.hidden; c += NT * E) {
-    double y[E];
-    float gf[E];
-    sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y);
-    unpack(ldg16(gn + c), gf, T());
 #pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = y[e] * inv * (double)gf[e];
-    stg16(out + c, pack_d(y, T()));
+  for (int ch = 0; ch < CH; ++ch) {
+    const int c = (ch * NT + threadIdx.x) * E;
+    if (c < p.hidden) {
+      float gf[E];
+      double o[E];
+      unpack(g[ch], gf, T());
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = y[ch][e] * inv * (double)gf[e];
+      stg16(out + c, pack_d(o, T()));
+    }
   }
 }
 
@@ -313,9 +380,24 @@ __global__ void k_fill_zero(int* p, int64_t n) {
     p[i] = 0;
 }
 
+// Groups of E elements a thread needs for `hidden`: 1, 2 or 4 (hidden <= 4 * 512 * E).
+static int row_groups(int dtype, int hidden) {
+  const int per = kNormThreads * (dtype == 0 ? Elem<float>::E : Elem<bf16_t>::E);
+  const int g = (hidden + per - 1) / per;
+  return g <= 1 ? 1 : (g <= 2 ? 2 : 4);
+}
+
 hipError_t launch_embed(int dtype, const EmbedParams& p, hipStream_t st) {
-  if (dtype == 0) (void)launch_k(k_embed<float>, dim3(p.S * p.B), dim3(256), st, p);
-  else (void)launch_k(k_embed<bf16_t>, dim3(p.S * p.B), dim3(256), st, p);
+  const int g = row_groups(dtype, p.hidden), rows = p.S * p.B;
+  if (dtype == 0) {
+    if (g == 1) (void)launch_k(k_embed<float, 1>, dim3(rows), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_embed<float, 2>, dim3(rows), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_embed<float, 4>, dim3(rows), dim3(kNormThreads), st, p);
+  } else {
+    if (g == 1) (void)launch_k(k_embed<bf16_t, 1>, dim3(rows), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_embed<bf16_t, 2>, dim3(rows), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_embed<bf16_t, 4>, dim3(rows), dim3(kNormThreads), st, p);
+  }
   return hipGetLastError();
 }
 
@@ -332,8 +414,16 @@ hipError_t launch_kv_finish(int dtype, const KvFinishParams& p, hipStream_t st) 
 }
 
 hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st) {
-  if (dtype == 0) (void)launch_k(k_norm<float>, dim3(p.R), dim3(kNormThreads), st, p);
-  else (void)launch_k(k_norm<bf16_t>, dim3(p.R), dim3(kNormThreads), st, p);
+  const int g = row_groups(dtype, p.hidden);
+  if (dtype == 0) {
+    if (g == 1) (void)launch_k(k_norm<float, 1>, dim3(p.R), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_norm<float, 2>, dim3(p.R), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_norm<float, 4>, dim3(p.R), dim3(kNormThreads), st, p);
+  } else {
+    if (g == 1) (void)launch_k(k_norm<bf16_t, 1>, dim3(p.R), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_norm<bf16_t, 2>, dim3(p.R), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_norm<bf16_t, 4>, dim3(p.R), dim3(kNormThreads), st, p);
+  }
   return hipGetLastError();
 }
 
@@ -350,8 +440,16 @@ hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st
 }
 
 hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st) {
-  if (dtype == 0) (void)launch_k(k_rownorm<float>, dim3(p.R), dim3(kNormThreads), st, p);
-  else (void)launch_k(k_rownorm<bf16_t>, dim3(p.R), dim3(kNormThreads), st, p);
+  const int g = row_groups(dtype, p.hidden);
+  if (dtype == 0) {
+    if (g == 1) (void)launch_k(k_rownorm<float, 1>, dim3(p.R), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_rownorm<float, 2>, dim3(p.R), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_rownorm<float, 4>, dim3(p.R), dim3(kNormThreads), st, p);
+  } else {
+    if (g == 1) (void)launch_k(k_rownorm<bf16_t, 1>, dim3(p.R), dim3(kNormThreads), st, p);
+    else if (g == 2) (void)launch_k(k_rownorm<bf16_t, 2>, dim3(p.R), dim3(kNormThreads), st, p);
+    else (void)launch_k(k_rownorm<bf16_t, 4>, dim3(p.R), dim3(kNormThreads), st, p);
+  }
   return hipGetLastError();
 }
 

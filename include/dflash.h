@@ -62,6 +62,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
  *   dtype is DFLASH_F32 or DFLASH_BF16;
  *   1 <= n_layers <= 64; head_dim is 64 or 128; n_q_heads % n_kv_heads == 0;
  *   hidden, intermediate, n_q_heads*head_dim, n_kv_heads*head_dim are multiples of 128;
+ *   hidden <= 16384 (bf16) or 8192 (f32);
  *   vocab >= 2; 1 <= n_taps <= 8; tap ids strictly ascending (so never repeated),
  *   each in [0, target_n_layers); 2 <= block_size <= 32; 0 <= mask_token_id < vocab;
  *   causal == 0; layer_window[l] >= 0 (0 = full attention) for l < n_layers;

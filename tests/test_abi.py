@@ -71,6 +71,7 @@ def test_presets_are_accepted(name):
     (dict(n_kv_heads=6), "multiple"),
     (dict(head_dim=96), "head_dim"),
     (dict(hidden=4000), "hidden"),
+    (dict(hidden=16384 + 128), "exceeds"),
     (dict(mask_token_id=151936), "mask_token_id"),
     (dict(layer_window=[0, 0, -1]), "window"),
     (dict(page_size=32), "page_size"),
