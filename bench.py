@@ -82,9 +82,10 @@ def kernel_costs(p, ctx, rows):
 
 # Source files whose kernels a committed traffic measurement covers, per kernel name.
 KERNEL_SOURCES = {
-    "gate_up_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
-    "lm_head_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
-    "down_gemm": ["gemm.hip", "common.hpp", "kernels.h"],
+    "gate_up_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
+    "lm_head_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
+    "down_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
+    "fuse_fc_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
     "attention_full": ["attention.hip", "common.hpp", "kernels.h"],
 }
 COPY_CALIBRATION_BYTES = 256 << 20

@@ -95,8 +95,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int pg_lo = lo / 16;
   const int n_pages = span_pages(lo, Cs);
   // This stream's own chunking; the grid's chunks past it are empty.
-  const int n_own = attention_chunks(n_pages);
-  const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages) : 0;
+  const int n_own = attention_chunks(n_pages, p.wide);
+  const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages, p.wide) : 0;
   const int cp0 = c * cpp;
   int n_cp = c < n_own ? ((c + 1) * cpp < n_pages ? (c + 1) * cpp : n_pages) - cp0 : 0;
   n_cp = n_cp > 0 ? n_cp : 0;   // the last chunks of a rounded-up split can be empty
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnP
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
-  const int n_own = attention_chunks(span_pages(lo, Cs));   // >= 1
+  const int n_own = attention_chunks(span_pages(lo, Cs), p.wide);   // >= 1
   // (max, sum) of query qi, chunk c: mq[c]
   const float2* mq = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + (qi < nq_local ? qi : 0)) * p.n_chunks;
   const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;

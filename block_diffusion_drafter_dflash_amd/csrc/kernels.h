@@ -54,7 +54,8 @@ struct GemmParams {
 struct AttnParams {
   int S, B, n_q_heads, n_kv_heads, head_dim, group;
   int window;           // 0 = full
-  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages)
+  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages, wide)
+  int wide;             // 1: the batch is wide (batch_is_wide), chunks of up to 64 pages
   int max_ctx;
   const int* ctx_len;
   const void* q;        // [S*B, n_q*d] rotated, normalised queries
@@ -144,21 +145,24 @@ struct VerifyParams {
 };
 
 // Context chunking, in pages of 16 keys, of one stream's reach: a function of that
-// reach alone, so a stream's result does not depend on the other streams of the batch.
-// Up to 256 pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 2048 pages
-// the chunk count stays at 256 / kChunkPagesShort; beyond, chunks hold at most 64
-// pages. No chunk ever exceeds 64 pages (the attention kernel keeps a chunk's page ids
-// one per lane), and the count never decreases as the reach grows, so a grid sized
-// for the longest reach covers every stream.
+// reach and of the batch's class (see batch_is_wide), so a stream's result does not
+// depend on the other streams of a batch of its class. Narrow batches: up to 256
+// pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 2048 pages the chunk
+// count stays at 256 / kChunkPagesShort; beyond, chunks hold at most 64 pages. Wide
+// batches (many streams fill the GPU by themselves): chunks of up to 64 pages, which
+// keeps the per-chunk partials few. No chunk ever exceeds 64 pages (the attention
+// kernel keeps a chunk's page ids one per lane), and the count never decreases as
+// the reach grows, so a grid sized for the longest reach covers every stream.
 constexpr int kChunkPagesShort = 8;
 constexpr int kChunkPagesMax = 64;
-__host__ __device__ inline int attention_chunks(int pages) {
+__host__ __device__ inline int attention_chunks(int pages, int wide) {
+  if (wide) return pages <= kChunkPagesMax ? 1 : (pages + kChunkPagesMax - 1) / kChunkPagesMax;
   if (pages <= 256) return pages <= kChunkPagesShort ? 1 : (pages + kChunkPagesShort - 1) / kChunkPagesShort;
   if (pages <= 256 / kChunkPagesShort * kChunkPagesMax) return 256 / kChunkPagesShort;
   return (pages + kChunkPagesMax - 1) / kChunkPagesMax;
 }
-__host__ __device__ inline int attention_chunk_pages(int pages) {
-  const int n = attention_chunks(pages);
+__host__ __device__ inline int attention_chunk_pages(int pages, int wide) {
+  const int n = attention_chunks(pages, wide);
   return (pages + n - 1) / n;
 }
 // Pages touched by the key range [lo, hi) (page-aligned span).
@@ -189,6 +193,10 @@ int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h);
 int gemm_ksplit(int epi, int n_tiles, int iters, int K);
 // Tiled GEMM for many rows (bf16, M > kTallMinRows): same parameters and outputs.
 constexpr int kTallMinRows = 65;
+// A batch of this many block rows (streams x block) is wide: its GEMMs take the tiled
+// kernel (bf16) and its attention the 64-page chunking. A stream's results are
+// bitwise the same in any batch of its class.
+inline bool batch_is_wide(int rows) { return rows >= kTallMinRows; }
 int gemm_tall_ksplit(int epi, int N, int K);
 hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st);
 int gemm_tile_cols(int epi);

@@ -414,6 +414,35 @@ def test_batched_equals_solo_bitwise():
         assert torch.equal(dr[0], case.draft[s])
 
 
+WIDE = small_variant(MID, name="wide_bf16", n_streams=6, ctx_spec=[300, 77, 1030, 0, 513, 4100], seed=2003)
+
+
+def test_wide_batch_class_is_invariant_to_stream_order_bitwise():
+    # 6 streams x block 16 = 96 rows: a wide batch (tiled GEMMs, 64-page attention
+    # chunks). A stream's result is bitwise the same in any batch of its class; here
+    # the same streams drafted in reverse order.
+    case = RoundCase(WIDE)
+    case.run_gpu()
+    batched, bdraft = case.logits.clone(), case.draft.clone()
+    S = WIDE.n_streams
+    perm = list(reversed(range(S)))
+    kv = SimpleNamespace(struct=D.KV())
+    for l in range(WIDE.n_layers):
+        kv.struct.k_pool[l] = case.kv.k[l].data_ptr()
+        kv.struct.v_pool[l] = case.kv.v[l].data_ptr()
+    pt = case.kv.page_table[perm].contiguous()
+    kv.struct.page_table = pt.data_ptr()
+    kv.struct.pages_per_stream = case.kv.pages_per_stream
+    out = torch.zeros_like(case.logits)
+    dr = torch.zeros_like(case.draft)
+    case.dr.dflash_draft_block(case.anchor[perm].contiguous(), case.ctx_len[perm].contiguous(), case.max_ctx, kv, dr,
+                               case.ws, logits_out=out)
+    torch.cuda.synchronize()
+    for i, s in enumerate(perm):
+        assert torch.equal(out[i].view(torch.int32), batched[s].view(torch.int32)), f"stream {s}"
+        assert torch.equal(dr[i], bdraft[s])
+
+
 def test_chunked_inject_equals_one_shot_and_page_order_is_invisible():
     a = RoundCase(MID, permute_pages=True)
     a.fuse()
