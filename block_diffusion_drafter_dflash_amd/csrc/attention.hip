@@ -72,19 +72,26 @@ __device__ __forceinline__ uint32_t bit_range16(int a, int e) {
   return e > a ? ((0xffffu >> (16 - (e - a))) << a) : 0u;
 }
 
-template <typename T, int D, int QT>
+template <typename T, int D, int QT, int KG>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using C = AttnCfg<T, D>;
   constexpr bool BF = C::BF;
   constexpr int E = C::E, NF = C::NF, NDT = C::NDT, BP = C::BP, NSB = C::NSB, SLOT = C::SLOT;
   constexpr int KROW = C::KROW, VROW = C::VROW, KBYTES = C::KBYTES, NKI = C::NKI, NVI = C::NVI;
+  constexpr int NW = KG * QT;          // waves: KG key groups of QT query waves
+  constexpr int NSG = NSB / KG;        // steps of a batch that one key group computes
+  static_assert(KG >= 1 && NSB % KG == 0, "a batch's steps split evenly over the key groups");
   // Two separate buffers: the compiler then sees that a batch's copies into one
   // never alias the fragment reads of the other, and keeps them in flight.
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[BP * SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[BP * SLOT];
+  // the second key group's (max, sum) handed to the first for the merge
+  __shared__ float s_m[KG > 1 ? QT : 1][64];
+  __shared__ double s_l[KG > 1 ? QT : 1][64];
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int kg = wv / QT, w = wv % QT;   // key group, query wave
   const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int g = p.group, B = p.B;
   const int nq_local = g * B;
@@ -138,18 +145,18 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     return (i < n_cp && page >= 0 && page < p.pool_pages) ? page : -1;
   };
 
-  // Copy batch b's pages into `buf`. Wave w issues the wave-wide 16-byte loads
-  // jj = w, w + QT, ... (< NKI + NVI) of every page of the batch: lane l of load jj
+  // Copy batch b's pages into `buf`. Wave wv issues the wave-wide 16-byte loads
+  // jj = wv, wv + NW, ... (< NKI + NVI) of every page of the batch: lane l of load jj
   // fills bytes [jj*1024 + 16 l, + 16) of the page's slot (K part, then V^T part)
   // from the piece that the swizzle puts there. The lane's source offset within a
   // page does not depend on the page (K rows [16][D]; V^T dim rows of stride 16 in
   // the cache, kBlockSlots in the block), so it is computed once.
   constexpr int LPP = NKI + NVI;
-  constexpr int JW = (LPP + QT - 1) / QT;
+  constexpr int JW = (LPP + NW - 1) / NW;
   int src_pg[JW], src_blk[JW];
 #pragma unroll
   for (int k = 0; k < JW; ++k) {
-    const int jj = w + QT * k;
+    const int jj = wv + NW * k;
     src_pg[k] = src_blk[k] = 0;
     if (jj >= LPP) continue;
     const int bo = (jj < NKI ? jj : jj - NKI) * 1024 + lane * 16;
@@ -182,7 +189,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       unsigned char* slot = buf + pb * SLOT;
 #pragma unroll
       for (int k = 0; k < JW; ++k) {
-        const int jj = w + QT * k;
+        const int jj = wv + NW * k;
         if (jj >= LPP) break;
         const int so = blk ? src_blk[k] : src_pg[k];
         if (jj < NKI) load_lds16(kp + so, slot + jj * 1024);
@@ -303,32 +310,33 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   // code with no masking; otherwise steps without valid keys are skipped and edge
   // steps are masked (steps whose keys are all valid still take no masking work).
   auto compute = [&](int b, const unsigned char* buf) {
-    uint32_t msk[NSB];
+    // this key group's steps of the batch: kg * NSG + i
+    uint32_t msk[NSG];
     bool full = true;
 #pragma unroll
-    for (int st = 0; st < NSB; ++st) {
-      msk[st] = step_mask(b, st);
-      full = full && msk[st] == 0xffffffffu;
+    for (int i = 0; i < NSG; ++i) {
+      msk[i] = step_mask(b, kg * NSG + i);
+      full = full && msk[i] == 0xffffffffu;
     }
-    // Workgroups of more than four waves must fit three waves per SIMD; their
+    // Workgroups of more than four query waves must fit three waves per SIMD; their
     // registers do not hold two steps' P.V in flight, so they go step by step.
-    if constexpr (QT > 4) full = false;
+    if constexpr (QT > 4 && NSG > 1) full = false;
 
-    float sv[NSB][2][4];
+    float sv[NSG][2][4];
     {
-      floatx4 sacc[NSB][2];
+      floatx4 sacc[NSG][2];
       if (full) {
 #pragma unroll
-        for (int st = 0; st < NSB; ++st) qk_step(buf, st, sacc[st]);
+        for (int st = 0; st < NSG; ++st) qk_step(buf, kg * NSG + st, sacc[st]);
       } else {
 #pragma unroll
-        for (int st = 0; st < NSB; ++st) {
-          if (msk[st]) qk_step(buf, st, sacc[st]);
+        for (int st = 0; st < NSG; ++st) {
+          if (msk[st]) qk_step(buf, kg * NSG + st, sacc[st]);
           else sacc[st][0] = sacc[st][1] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
       }
 #pragma unroll
-      for (int st = 0; st < NSB; ++st)
+      for (int st = 0; st < NSG; ++st)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -336,7 +344,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     }
     if (!full) {
 #pragma unroll
-      for (int st = 0; st < NSB; ++st)
+      for (int st = 0; st < NSG; ++st)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -348,7 +356,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     // output is rescaled to the new maximum before the batch's P.V accumulates.
     float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < NSB; ++st)
+    for (int st = 0; st < NSG; ++st)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -359,7 +367,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int st = 0; st < NSB; ++st)
+    for (int st = 0; st < NSG; ++st)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -377,13 +385,13 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
     if (full) {
 #pragma unroll
-      for (int st = 0; st < NSB; ++st) pv_step(buf, st, sv[st], 0xffffffffu, std::false_type{});
+      for (int st = 0; st < NSG; ++st) pv_step(buf, kg * NSG + st, sv[st], 0xffffffffu, std::false_type{});
     } else {
 #pragma unroll
-      for (int st = 0; st < NSB; ++st) {
+      for (int st = 0; st < NSG; ++st) {
         if (!msk[st]) continue;
-        if (msk[st] == 0xffffffffu) pv_step(buf, st, sv[st], msk[st], std::false_type{});
-        else pv_step(buf, st, sv[st], msk[st], std::true_type{});
+        if (msk[st] == 0xffffffffu) pv_step(buf, kg * NSG + st, sv[st], msk[st], std::false_type{});
+        else pv_step(buf, kg * NSG + st, sv[st], msk[st], std::true_type{});
       }
     }
   };
@@ -402,6 +410,40 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     __syncthreads();
     if (b + 2 < nb) issue(b + 2, buf0);
     compute(b + 1, buf1);
+  }
+
+  if constexpr (KG > 1) {
+    // The second key group hands its running state to the first, which merges:
+    // M = max(m0, m1), each side scaled by 2^(m_k - M) (exactly 1 for the side
+    // holding M). The batch buffers are free once every wave is past the loop.
+    __syncthreads();
+    float* so0 = reinterpret_cast<float*>(buf0);
+    float* so1 = reinterpret_cast<float*>(buf1);
+    constexpr int HALF = NDT / 2;   // dims tiles 0..HALF-1 go through buf0, the rest buf1
+    static_assert(QT * 64 * HALF * 4 * 4 <= BP * SLOT, "the hand-over fits the buffers");
+    if (kg == 1) {
+      s_m[w][lane] = m_run;
+      s_l[w][lane] = l_run;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        float* dst = (dt < HALF ? so0 : so1) + ((w * HALF + dt % HALF) * 64 + lane) * 4;
+        *reinterpret_cast<floatx4*>(dst) = orun[dt];
+      }
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m1 = s_m[w][lane];
+    const float M = fmaxf(m_run, m1);
+    const float f0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    l_run = l_run * (double)f0 + s_l[w][lane] * (double)f1;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const floatx4 o1 = *reinterpret_cast<const floatx4*>((dt < HALF ? so0 : so1) + ((w * HALF + dt % HALF) * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orun[dt][i] = orun[dt][i] * f0 + o1[i] * f1;
+    }
+    m_run = M;
   }
 
   double l_tot = l_run;
@@ -442,15 +484,15 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     *reinterpret_cast<float4*>(op + (dt * kWave + lane) * 4) = make_float4(orun[dt][0], orun[dt][1], orun[dt][2], orun[dt][3]);
 }
 
-// Up to four waves a workgroup: two workgroups a CU (LDS-bound) hold two waves a SIMD.
-template <typename T, int D, int QT>
-__global__ __launch_bounds__(64 * QT, 2) void k_attn(const AttnParams p) {
-  attn_body<T, D, QT>(p);
+// KG key groups of QT query waves. Up to four query waves: registers for two waves a
+// SIMD; more: three.
+template <typename T, int D, int QT, int KG>
+__global__ __launch_bounds__(64 * QT * KG, 2) void k_attn(const AttnParams p) {
+  attn_body<T, D, QT, KG>(p);
 }
-// Five to eight waves: registers for three waves a SIMD.
-template <typename T, int D, int QT>
-__global__ __launch_bounds__(64 * QT, 3) void k_attn_wide(const AttnParams p) {
-  attn_body<T, D, QT>(p);
+template <typename T, int D, int QT, int KG>
+__global__ __launch_bounds__(64 * QT * KG, 3) void k_attn_wide(const AttnParams p) {
+  attn_body<T, D, QT, KG>(p);
 }
 
 // Combine the chunks of one (stream, kv head, query tile, 16-dim output slice).
@@ -547,8 +589,13 @@ int attention_query_tiles(int group, int block) { return (group * block + 15) / 
 template <typename T, int D, int QT>
 static void launch_qt(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.n_chunks, p.n_kv_heads, p.S);
-  if constexpr (QT > 4) (void)launch_k((k_attn_wide<T, D, QT>), grid, dim3(64 * QT), st, p);
-  else (void)launch_k((k_attn<T, D, QT>), grid, dim3(64 * QT), st, p);
+  // Two key groups for five or six query waves: such workgroups run one to a CU (two
+  // would put four waves on a SIMD), so the second group doubles the waves a batch is
+  // computed with. Up to four query waves two workgroups share a CU already, each
+  // with its own copies in flight; the doubled workgroup would run alone.
+  constexpr int KG = (AttnCfg<T, D>::NSB % 2 == 0 && QT > 4 && QT <= 6) ? 2 : 1;
+  if constexpr (QT > 4) (void)launch_k((k_attn_wide<T, D, QT, KG>), grid, dim3(64 * QT * KG), st, p);
+  else (void)launch_k((k_attn<T, D, QT, KG>), grid, dim3(64 * QT * KG), st, p);
 }
 
 template <typename T, int D>
