@@ -2,23 +2,22 @@
 //
 // Y[M, N] = A[M, K] . W[N, K]^T with the same epilogues and outputs as the skinny
 // kernel (float64 K-range partials, SwiGLU, LM-head logits and per-32-column top-2).
-// A workgroup of 8 waves owns a 128-row x 128-column output tile over one K range;
-// wave (wm, wn) computes a 64 x 32 piece as 4 x 2 v_mfma_f32_16x16x32_bf16 tiles.
-// K goes in chunks of 64: a chunk's A (128 x 64) and W (128 x 64) tiles are copied
-// straight from global memory into LDS (global_load_lds, 16 bytes a lane, XOR-swizzled
-// 16-byte pieces so that fragment reads are free of bank conflicts) through a ring of
-// kRing buffers, so that up to kRing - 1 chunks (48 KB of weights) are in flight
-// while one is multiplied: enough bytes per CU to stream the weights at HBM speed.
-// Each buffer is its own LDS object, so the compiler sees that copies into one never
-// alias the fragment reads of another. Every kFlushChunks chunks (256 products per
-// element) the fp32 MFMA sums are added into float64 accumulators. The row tiles of
-// one column share an XCD and run side by side, so a weight tile read from HBM serves
-// all of them from L2. The summation order differs from the skinny kernel's (one K
-// sweep per K range rather than eight wave slices), so a batch on this path is not
-// bitwise equal to the same streams drafted alone.
+// A workgroup of 8 waves owns a 256-row x 128-column output tile over one K range, so
+// a batch of up to 256 rows reads every weight tile from HBM exactly once; wave
+// (wm, wn) computes a 64 x 64 piece as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles (the
+// largest piece whose accumulators fit, which keeps LDS reads at 0.5 per MFMA).
+// K goes in chunks of 64: a chunk's A (256 x 64) and W (128 x 64) tiles are copied
+// straight from global memory into LDS (buffer_load ... lds, XOR-swizzled 16-byte
+// pieces so that fragment reads are free of bank conflicts) through a ring of three
+// buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
+// object, so the compiler sees that copies into one never alias the fragment reads
+// of another. Every kFlushChunks chunks (256 products per element) the fp32 MFMA sums
+// are added into float64 accumulators. The summation order differs from the skinny
+// kernel's (one K sweep per K range rather than eight wave slices), so a batch on this
+// path is not bitwise equal to the same streams drafted alone.
 //
 // Shapes: K is a multiple of 64 and every weight segment (q | k | v, a layer's k | v,
-// SwiGLU halves) a multiple of 16 rows; the configuration checks (hidden,
+// SwiGLU halves) a multiple of 32 rows; the configuration checks (hidden,
 // intermediate and head projections multiples of 128) guarantee both.
 #include "common.hpp"
 #include "kernels.h"
@@ -28,18 +27,19 @@ namespace dfl {
 namespace {
 
 constexpr int kWaves = 8, kTallThreads = 64 * kWaves;
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kRing = 4;                     // chunk buffers
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int WM = 4, WN = 2;                // waves along M and N: 64 x 64 each
+constexpr int kRing = 3;                     // chunk buffers
 constexpr int kFlushChunks = 4;
 constexpr int ROWB = BK * 2;                 // bytes of one tile row in LDS (bf16)
-constexpr int TILEB = BM * ROWB;             // bytes of one operand tile (A or W)
-constexpr int LOADS = TILEB / 1024;          // wave-wide 16-byte loads per operand tile
-constexpr int QW = LOADS / kWaves;           // loads per wave per operand tile
-constexpr int LPW = 2 * QW;                  // loads per wave per chunk
-static_assert(BM == BN && LOADS % kWaves == 0, "both tiles split evenly over the waves");
-
+constexpr int ATILE = BM * ROWB, WTILE = BN * ROWB;
 constexpr int NPC = ROWB / 16;               // 16-byte pieces per tile row
 constexpr int RPL = 1024 / ROWB;             // tile rows per wave-wide load
+constexpr int QA = ATILE / 1024 / kWaves;    // A loads per wave per chunk
+constexpr int QB = WTILE / 1024 / kWaves;    // W loads per wave per chunk
+constexpr int LPW = QA + QB;                 // loads per wave per chunk
+static_assert(WM * WN == kWaves && WM * 64 == BM && WN * 64 == BN, "waves tile the output");
+static_assert(ATILE % (1024 * kWaves) == 0 && WTILE % (1024 * kWaves) == 0, "tiles split evenly over the waves");
 // 16-byte piece p of tile row r sits at piece p ^ swz(r): the 16 rows one fragment
 // read touches (128 bytes apart) land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & (NPC - 1); }
@@ -70,14 +70,14 @@ __device__ __forceinline__ void tall_top_merge(float& v1, int& i1, float& v2, fl
   }
 }
 
-// Weight row of tile row r (0..127) of column tile t. SwiGLU tile t: the 32 rows of
-// wave column h = r / 32 are gate rows 64 t + 16 h + 0..15, then the matching up rows.
+// Weight row of tile row r (0..127) of column tile t. SwiGLU tile t: the 64 rows of
+// wave column h = r / 64 are gate rows 64 t + 32 h + 0..31, then the matching up rows.
 template <int EPI>
 __device__ __forceinline__ const bf16_t* tall_wrow(const GemmParams& p, int t, int r) {
   if constexpr (EPI == EPI_SWIGLU) {
-    const int h = r >> 5, q = r & 31;
-    const int gr = 64 * t + 16 * h + (q & 15);
-    return static_cast<const bf16_t*>(q < 16 ? p.w0 : p.w1) + (int64_t)gr * p.K;
+    const int h = r >> 6, q = r & 63;
+    const int gr = 64 * t + 32 * h + (q & 31);
+    return static_cast<const bf16_t*>(q < 32 ? p.w0 : p.w1) + (int64_t)gr * p.K;
   } else if constexpr (EPI == EPI_RAW) {
     const int n = t * BN + r;
     if (p.seg_layers > 0) {
@@ -110,15 +110,14 @@ __device__ __forceinline__ void ring_barrier() {
 
 template <int EPI, int AM>
 __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf2[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf3[2 * TILEB];
-  static_assert(kRing == 4, "four buffers");
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[ATILE + WTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[ATILE + WTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf2[ATILE + WTILE];
+  static_assert(kRing == 3, "three buffers");
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int wm = w >> 2, wn = w & 3;   // rows 64 wm .., columns 32 wn ..
+  const int wm = w / WN, wn = w % WN;   // rows 64 wm .., columns 64 wn ..
 
   const int n_ct = EPI == EPI_SWIGLU ? p.N / BN : (p.N + BN - 1) / BN;   // column tiles
   const int n_rt = (p.M + BM - 1) / BM;                                   // row tiles
@@ -130,48 +129,46 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   const int n_chunks = p.K / BK;
   const int kb = (int)((int64_t)ks * n_chunks / p.ksplit), ke = (int)((int64_t)(ks + 1) * n_chunks / p.ksplit);
 
-  // ---- copies: wave w issues loads q = QW w + k (k < QW) of the A tile and of the W
-  // tile. Lane l of load q fills bytes [1024 q + 16 l, + 16) of the tile: row
-  // RPL q + l / NPC, stored piece l % NPC, i.e. source piece (l % NPC) ^ swz(row). The
-  // uniform part of a source address (matrix, first row of the load, chunk) is a
-  // scalar, the lane adds a fixed offset. Rows past M (and LM-head rows past N) repeat
-  // the last row; their results are never stored.
-  const bf16_t* a_base[QW];
-  const bf16_t* w_base[QW];
-  int a_off[QW], w_off[QW];
+  // ---- copies: wave w issues A loads q = QA w + k (k < QA) and W loads q = QB w + k.
+  // Lane l of load q fills bytes [1024 q + 16 l, + 16) of the tile: row RPL q + l / NPC,
+  // stored piece l % NPC, i.e. source piece (l % NPC) ^ swz(row). The uniform part of
+  // a source address (matrix, first row of the load, chunk) is a scalar, the lane adds
+  // a fixed offset. Rows past M (and LM-head rows past N) repeat the last row; their
+  // results are never stored.
+  int a_off[QA], w_off[QB];
+  __amdgpu_buffer_rsrc_t a_rsrc[QA], w_rsrc[QB];
 #pragma unroll
-  for (int k = 0; k < QW; ++k) {
-    const int q = QW * w + k;
+  for (int k = 0; k < QA; ++k) {
+    const int q = QA * w + k;
     const int row = RPL * q + lane / NPC;
     const int piece = (lane % NPC) ^ swz(row);
     const int ar0 = min(rt * BM + RPL * q, p.M - 1), ar = min(rt * BM + row, p.M - 1);
     if constexpr (AM == A_TAPS) {
-      a_base[k] = nullptr;
       a_off[k] = (int)((int64_t)ar * p.tap_stride) + piece * 8;
     } else {
-      a_base[k] = static_cast<const bf16_t*>(p.a) + (int64_t)ar0 * p.lda;
+      a_rsrc[k] = rsrc_of(static_cast<const bf16_t*>(p.a) + (int64_t)ar0 * p.lda);
       a_off[k] = (ar - ar0) * (int)p.lda + piece * 8;
     }
+  }
+#pragma unroll
+  for (int k = 0; k < QB; ++k) {
+    const int q = QB * w + k;
+    const int row = RPL * q + lane / NPC;
+    const int piece = (lane % NPC) ^ swz(row);
     if constexpr (EPI == EPI_SWIGLU) {
-      w_base[k] = tall_wrow<EPI>(p, ct, RPL * q);   // RPL consecutive gate or up rows
+      w_rsrc[k] = rsrc_of(tall_wrow<EPI>(p, ct, RPL * q));   // RPL consecutive gate or up rows
       w_off[k] = (lane / NPC) * p.K + piece * 8;
     } else {
       const int n0 = min(ct * BN + RPL * q, p.N - 1), n = min(ct * BN + row, p.N - 1);
-      w_base[k] = tall_wrow<EPI>(p, ct, n0 - ct * BN);
+      w_rsrc[k] = rsrc_of(tall_wrow<EPI>(p, ct, n0 - ct * BN));
       w_off[k] = (n - n0) * p.K + piece * 8;
     }
-  }
-  __amdgpu_buffer_rsrc_t a_rsrc[QW], w_rsrc[QW];
-#pragma unroll
-  for (int k = 0; k < QW; ++k) {
-    if constexpr (AM != A_TAPS) a_rsrc[k] = rsrc_of(a_base[k]);
-    w_rsrc[k] = rsrc_of(w_base[k]);
   }
   auto issue = [&](int ch, unsigned char* buf) {
     const int k0 = ch * BK;
 #pragma unroll
-    for (int k = 0; k < QW; ++k) {
-      const int q = QW * w + k;
+    for (int k = 0; k < QA; ++k) {
+      const int q = QA * w + k;
       if constexpr (AM == A_TAPS) {
         // a chunk never straddles two planes (hidden % 64 == 0)
         const int plane = k0 / p.tap_h;
@@ -180,35 +177,34 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       } else {
         buf_load_lds16(a_rsrc[k], 2u * (uint32_t)a_off[k], 2u * (uint32_t)k0, buf + q * 1024);
       }
-      buf_load_lds16(w_rsrc[k], 2u * (uint32_t)w_off[k], 2u * (uint32_t)k0, buf + TILEB + q * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < QB; ++k) {
+      const int q = QB * w + k;
+      buf_load_lds16(w_rsrc[k], 2u * (uint32_t)w_off[k], 2u * (uint32_t)k0, buf + ATILE + q * 1024);
     }
   };
 
-  // ---- fragments: A rows 64 wm + 16 i + lr, W rows 32 wn + 16 j + lr; for k-step s
+  // ---- fragments: A rows 64 wm + 16 i + lr, W rows 64 wn + 16 j + lr; for k-step s
   // of the chunk, lane group lg reads k = 32 s + 8 lg .. + 7 (piece 4 s + lg). One
   // buffer plus one offset, so that every read stays attributed to its buffer.
   constexpr int KS = BK / 32;
-  int aoff[KS][4], boff[KS][2];
+  int aoff[KS][4], boff[KS][4];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
+  for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ra = 64 * wm + 16 * i + lr;
+      const int ra = 64 * wm + 16 * i + lr, rb = 64 * wn + 16 * i + lr;
       aoff[s][i] = ra * ROWB + (((4 * s + lg) ^ swz(ra)) * 16);
+      boff[s][i] = ATILE + rb * ROWB + (((4 * s + lg) ^ swz(rb)) * 16);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rb = 32 * wn + 16 * j + lr;
-      boff[s][j] = TILEB + rb * ROWB + (((4 * s + lg) ^ swz(rb)) * 16);
-    }
-  }
 
-  double acc[4][2][4];
-  floatx4 part[4][2];
+  double acc[4][4][4];
+  floatx4 part[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0;
@@ -217,21 +213,21 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   auto compute = [&](int ch, const unsigned char* buf) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      uint4 af[4], bf[2];
+      uint4 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(buf + aoff[s][i]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const uint4*>(buf + boff[s][j]);
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(buf + boff[s][j]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma_frag(part[i][j], af[i], bf[j], bf16_t());
+        for (int j = 0; j < 4; ++j) mma_frag(part[i][j], af[i], bf[j], bf16_t());
     }
     if ((ch - kb) % kFlushChunks == kFlushChunks - 1 || ch + 1 == ke) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][j][e] += (double)part[i][j][e];
           part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -253,21 +249,18 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   if (kb < ke) {
     issue(kb, buf0);
     issue(min(kb + 1, ke - 1), buf1);
-    issue(min(kb + 2, ke - 1), buf2);
     for (int ch = kb; ch < ke; ch += kRing) {
-      step(ch, buf0, buf3);
+      step(ch, buf0, buf2);
       if (ch + 1 >= ke) break;
       step(ch + 1, buf1, buf0);
       if (ch + 2 >= ke) break;
       step(ch + 2, buf2, buf1);
-      if (ch + 3 >= ke) break;
-      step(ch + 3, buf3, buf2);
     }
     // the repeated copies must land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  // ---- epilogue: lane holds rows 64 wm + 16 i + 4 lg + e, columns 32 wn + 16 j + lr
+  // ---- epilogue: lane holds rows 64 wm + 16 i + 4 lg + e, columns 64 wn + 16 j + lr
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -276,37 +269,43 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       const bool rv = r < p.M;
       if constexpr (EPI == EPI_RAW) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = ct * BN + 32 * wn + 16 * j + lr;
+        for (int j = 0; j < 4; ++j) {
+          const int n = ct * BN + 64 * wn + 16 * j + lr;
           if (rv && n < p.N) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = acc[i][j][e];
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
-        // column lr of tile j = 0 is gate row 64 ct + 16 wn + lr; tile j = 1 its up row
-        const double g = acc[i][0][e], u = acc[i][1][e];
-        if (rv)
-          Elem<bf16_t>::store_d(static_cast<bf16_t*>(p.m_out) + (int64_t)r * p.ld_out + 64 * ct + 16 * wn + lr,
-                                g / (1.0 + exp(-g)) * u);
-      } else {   // EPI_LMHEAD: fp32 logits and top-2 of the wave's 32-column group
-        float v1 = -INFINITY, v2 = -INFINITY;
-        int i1 = 0x7fffffff;
+        // column 16 j + lr (j = 0, 1) is gate row 64 ct + 32 wn + 16 j + lr; j + 2 its up row
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = ct * BN + 32 * wn + 16 * j + lr;
-          const float v = (float)acc[i][j][e];
-          if (n < p.N) {
-            if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
-            tall_top_merge(v1, i1, v2, v, n, -INFINITY);
+          const double g = acc[i][j][e], u = acc[i][j + 2][e];
+          if (rv)
+            Elem<bf16_t>::store_d(static_cast<bf16_t*>(p.m_out) + (int64_t)r * p.ld_out + 64 * ct + 32 * wn + 16 * j + lr,
+                                  g / (1.0 + exp(-g)) * u);
+        }
+      } else {   // EPI_LMHEAD: fp32 logits and top-2 of each 32-column group
+#pragma unroll
+        for (int jg = 0; jg < 2; ++jg) {
+          float v1 = -INFINITY, v2 = -INFINITY;
+          int i1 = 0x7fffffff;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int n = ct * BN + 64 * wn + 32 * jg + 16 * jj + lr;
+            const float v = (float)acc[i][2 * jg + jj][e];
+            if (n < p.N) {
+              if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
+              tall_top_merge(v1, i1, v2, v, n, -INFINITY);
+            }
           }
+          for (int m = 1; m < 16; m <<= 1) {
+            const float o1 = __shfl_xor(v1, m, kWave);
+            const int oi = __shfl_xor(i1, m, kWave);
+            const float o2 = __shfl_xor(v2, m, kWave);
+            tall_top_merge(v1, i1, v2, o1, oi, o2);
+          }
+          const int grp = 4 * ct + 2 * wn + jg;
+          if (rv && lr == 0 && grp < p.n_tiles)
+            reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + grp] = make_float4(v1, __int_as_float(i1), v2, 0.f);
         }
-        for (int m = 1; m < 16; m <<= 1) {
-          const float o1 = __shfl_xor(v1, m, kWave);
-          const int oi = __shfl_xor(i1, m, kWave);
-          const float o2 = __shfl_xor(v2, m, kWave);
-          tall_top_merge(v1, i1, v2, o1, oi, o2);
-        }
-        const int grp = 4 * ct + wn;
-        if (rv && lr == 0 && grp < p.n_tiles)
-          reinterpret_cast<float4*>(p.tile_res)[(int64_t)r * p.n_tiles + grp] = make_float4(v1, __int_as_float(i1), v2, 0.f);
       }
     }
 }
@@ -314,9 +313,9 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 int gemm_tall_column_tiles(int epi, int N) { return epi == EPI_SWIGLU ? N / BN : (N + BN - 1) / BN; }
 
 // K ranges of the tiled GEMM, a function of the weight's shape only (so that a row's
-// arithmetic does not depend on how many rows the batch has). Sized for two row tiles
+// arithmetic does not depend on how many rows the batch has). Sized for one row tile
 // (up to 256 rows) on 256 CUs, one workgroup each: the split with the shortest
-// makespan, rounds(ks) / ks with rounds = ceil(2 * tiles * ks / 256), each extra range
+// makespan, rounds(ks) / ks with rounds = ceil(tiles * ks / 256), each extra range
 // charged a little for its float64 partial; every range at least 16 chunks.
 int gemm_tall_ksplit(int epi, int N, int K) {
   if (epi != EPI_RAW) return 1;
@@ -326,7 +325,7 @@ int gemm_tall_ksplit(int epi, int N, int K) {
   int best = 1;
   double best_cost = 1e30;
   for (int ks = 1; ks <= cap; ++ks) {
-    const int rounds = (2 * tiles * ks + 255) / 256;
+    const int rounds = (tiles * ks + 255) / 256;
     const double cost = (double)rounds / ks + 0.02 * ks;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
