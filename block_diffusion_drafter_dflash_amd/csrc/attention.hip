@@ -114,6 +114,16 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   // Page ids: lane i holds the id of the chunk's page i (a chunk has at most 64 pages).
   int pid = -1;
   if (lane < n_cp) pid = p.page_table[(int64_t)s * p.pages_per_stream + pg_lo + cp0 + lane];
+  // Per chunk page i (lane i), computed once: the (page, kv head) index its keys and
+  // values are copied from (a page that is absent, outside the pool or past the chunk
+  // is copied from pool page 0 instead, valid memory whose keys are masked), and
+  // whether all 16 of its keys are valid. A batch whose pages are all valid needs no
+  // mask; the per-batch work is then a few scalar operations per page.
+  const bool pg_ok = lane < n_cp && pid >= 0 && pid < p.pool_pages;
+  const uint32_t src_page = (uint32_t)((pg_ok ? pid : 0) * p.n_kv_heads + h);
+  const int pos_i = (pg_lo + cp0 + lane) * 16;
+  const uint64_t full_pages = __ballot(pg_ok && pos_i >= lo && pos_i + 16 <= Cs);
+  const uint64_t ok_pages = __ballot(pg_ok);
 
   // Queries owned by this lane (column lr of wave w's MFMA tiles): dims
   // [lg*D/4, (lg+1)*D/4) of query row (hl, jrow), as NF 16-byte fragments.
@@ -139,11 +149,6 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int64_t blk_off = ((int64_t)s * p.n_kv_heads + h) * (kBlockSlots * D);
   const T* kblk = static_cast<const T*>(p.kblk) + blk_off;
   const T* vblk = static_cast<const T*>(p.vblk) + blk_off;
-  // Chunk page i (uniform): its cache id, or -1 when absent or out of the pool.
-  auto page_id = [&](int i) {
-    const int page = __builtin_amdgcn_readlane(pid, i);
-    return (i < n_cp && page >= 0 && page < p.pool_pages) ? page : -1;
-  };
 
   // Copy batch b's pages into `buf`. Wave wv issues the wave-wide 16-byte loads
   // jj = wv, wv + NW, ... (< NKI + NVI) of every page of the batch: lane l of load jj
@@ -170,32 +175,46 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       src_blk[k] = d * kBlockSlots + piece;
     }
   }
+  // Context batches copy BP pages each (the chunk's pages past its end come from the
+  // stand-in page); the block batch copies the stream's two block pages.
+  const T* kpool = static_cast<const T*>(p.kpool);
+  const T* vpool = static_cast<const T*>(p.vpool);
   auto issue = [&](int b, unsigned char* buf) {
-    const bool blk = b >= nb_ctx;
-    const int np = blk ? 2 : (n_cp - b * BP < BP ? n_cp - b * BP : BP);
-    for (int pb = 0; pb < np; ++pb) {
-      const T* kp;
-      const T* vp;
-      if (blk) {
-        kp = kblk + pb * 16 * D;
-        vp = vblk + pb * 16;
-      } else {
-        const int page = page_id(b * BP + pb);
-        if (page < 0) continue;   // absent page: its keys are masked
-        const int64_t off = ((int64_t)page * p.n_kv_heads + h) * kv_page;
-        kp = static_cast<const T*>(p.kpool) + off;
-        vp = static_cast<const T*>(p.vpool) + off;
+    if (b >= nb_ctx) {
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        unsigned char* slot = buf + pb * SLOT;
+#pragma unroll
+        for (int k = 0; k < JW; ++k) {
+          const int jj = wv + NW * k;
+          if (jj >= LPP) break;
+          if (jj < NKI) load_lds16(kblk + pb * 16 * D + src_blk[k], slot + jj * 1024);
+          else load_lds16(vblk + pb * 16 + src_blk[k], slot + KBYTES + (jj - NKI) * 1024);
+        }
       }
+      return;
+    }
+#pragma unroll
+    for (int pb = 0; pb < BP; ++pb) {
+      // b * BP + pb <= 63: a chunk has at most 64 pages and 64 % BP == 0
+      const uint32_t sp = __builtin_amdgcn_readlane(src_page, b * BP + pb);
+      const int64_t off = (int64_t)sp * (16 * D);   // pages of 16 keys
+      const T* kp = kpool + off;
+      const T* vp = vpool + off;
       unsigned char* slot = buf + pb * SLOT;
 #pragma unroll
       for (int k = 0; k < JW; ++k) {
         const int jj = wv + NW * k;
         if (jj >= LPP) break;
-        const int so = blk ? src_blk[k] : src_pg[k];
-        if (jj < NKI) load_lds16(kp + so, slot + jj * 1024);
-        else load_lds16(vp + so, slot + KBYTES + (jj - NKI) * 1024);
+        if (jj < NKI) load_lds16(kp + src_pg[k], slot + jj * 1024);
+        else load_lds16(vp + src_pg[k], slot + KBYTES + (jj - NKI) * 1024);
       }
     }
+  };
+  // Context batch b has only valid keys.
+  auto batch_full = [&](int b) {
+    constexpr uint64_t all = (1ull << BP) - 1ull;
+    return b < nb_ctx && ((full_pages >> (b * BP)) & all) == all;
   };
 
   // Valid keys of step st of batch b as a uniform 32-bit mask (bit k = key k).
@@ -205,7 +224,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int i = b * BP + 2 * st + hf;
-      if (i < n_cp && page_id(i) >= 0) {
+      if ((ok_pages >> i) & 1ull) {
         const int pos0 = (pg_lo + cp0 + i) * 16;
         const int a = lo - pos0 > 0 ? lo - pos0 : 0, e = Cs - pos0 < 16 ? Cs - pos0 : 16;
         m |= bit_range16(a, e) << (16 * hf);
@@ -312,11 +331,17 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   auto compute = [&](int b, const unsigned char* buf) {
     // this key group's steps of the batch: kg * NSG + i
     uint32_t msk[NSG];
-    bool full = true;
+    bool full = batch_full(b);
 #pragma unroll
-    for (int i = 0; i < NSG; ++i) {
-      msk[i] = step_mask(b, kg * NSG + i);
-      full = full && msk[i] == 0xffffffffu;
+    for (int i = 0; i < NSG; ++i) msk[i] = 0xffffffffu;
+    if (!full) {
+      bool f = true;
+#pragma unroll
+      for (int i = 0; i < NSG; ++i) {
+        msk[i] = step_mask(b, kg * NSG + i);
+        f = f && msk[i] == 0xffffffffu;
+      }
+      full = f;
     }
     // Workgroups of more than four query waves must fit three waves per SIMD; their
     // registers do not hold two steps' P.V in flight, so they go step by step.
