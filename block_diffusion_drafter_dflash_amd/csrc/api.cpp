@@ -272,6 +272,8 @@ static int validate(const dflash_config* c) {
   if (c->max_streams < 1) REFUSE("max_streams %d < 1", c->max_streams);
   if (c->page_size != 16) REFUSE("page_size %d is not 16", c->page_size);
   if (c->pool_pages < 1) REFUSE("pool_pages %d < 1", c->pool_pages);
+  if ((int64_t)c->pool_pages * c->n_kv_heads > INT32_MAX)
+    REFUSE("pool_pages * n_kv_heads = %lld exceeds 2^31 - 1", (long long)c->pool_pages * c->n_kv_heads);
 #undef REFUSE
   return DFLASH_OK;
 }

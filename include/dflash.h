@@ -66,7 +66,8 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
  *   vocab >= 2; 1 <= n_taps <= 8; tap ids strictly ascending (so never repeated),
  *   each in [0, target_n_layers); 2 <= block_size <= 32; 0 <= mask_token_id < vocab;
  *   causal == 0; layer_window[l] >= 0 (0 = full attention) for l < n_layers;
- *   rope_theta > 0; rms_eps >= 0; max_streams >= 1; page_size == 16; pool_pages >= 1.
+ *   rope_theta > 0; rms_eps >= 0; max_streams >= 1; page_size == 16; pool_pages >= 1;
+ *   pool_pages * n_kv_heads <= 2^31 - 1 (a (page, kv head) pair is indexed in 32 bits).
  */
 typedef struct {
   int32_t dtype;

@@ -75,6 +75,7 @@ def test_presets_are_accepted(name):
     (dict(mask_token_id=151936), "mask_token_id"),
     (dict(layer_window=[0, 0, -1]), "window"),
     (dict(page_size=32), "page_size"),
+    (dict(pool_pages=1 << 28), "2^31"),
     (dict(dtype=7), "dtype"),
     (dict(max_streams=0), "max_streams"),
 ])
