@@ -67,6 +67,16 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups), with the
+// gfx950 lane-swap instructions: each swap leaves a lane holding its own value and its
+// partner's (lane ^ 32, then lane ^ 16) in its two results.
+__device__ __forceinline__ float xor_max_16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Bits [a, e) of a 16-bit half (0 <= a, e <= 16).
 __device__ __forceinline__ uint32_t bit_range16(int a, int e) {
   return e > a ? ((0xffffu >> (16 - (e - a))) << a) : 0u;
@@ -386,10 +396,12 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[st][t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = xor_max_16_32(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // A finite stand-in for the maximum: exp2(-inf - m_safe) is exactly 0, also while
+    // no valid key has been seen (m_new = -inf, where the running sums are still 0).
+    const float m_safe = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_safe);
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < NSG; ++st)
@@ -397,8 +409,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = sv[st][t][i];
-          sv[st][t][i] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m_new);
+          sv[st][t][i] = __builtin_amdgcn_exp2f(sv[st][t][i] - m_safe);
           psum += sv[st][t][i];
         }
     l_run = l_run * (double)corr + (double)psum;
@@ -609,6 +620,73 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnP
   for (int i = 0; i < 4; ++i) Elem<T>::store_d(dst + i, o[i] / L);
 }
 
+// The same combine for grids of at most kCombineShort chunks: one workgroup per
+// (stream, kv head, query tile), wave dt owning the 16-dim output slice dt. Each lane
+// loads every chunk of its query and slice at once and forms exactly the sums above
+// (the four quarters in chunk order, then added in quarter order), so the two kernels
+// give identical results.
+constexpr int kCombineShort = 8;
+template <typename T, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void k_attn_combine_short(const AttnParams p, int QT) {
+  constexpr int NDT = D / 16, RC = kCombineShort;
+  const int tid = threadIdx.x, dt = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int sh = blockIdx.x / QT, qt = blockIdx.x % QT;
+  const int s = sh / p.n_kv_heads, h = sh % p.n_kv_heads;
+  const int nq_local = p.group * p.B;
+  const int qi = 16 * qt + lr;
+  if (qi >= nq_local) return;   // whole lane groups of padding queries; no barrier follows
+  int Cs = p.ctx_len[s];
+  Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
+  const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
+  const int n_own = attention_chunks(span_pages(lo, Cs), p.wide);   // 1 <= n_own <= RC
+  const float2* mq = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + qi) * p.n_chunks;
+  const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
+  const int64_t cstride = (int64_t)QT * NDT * (kWave * 4);
+  float4 v[RC];
+  float2 ml[RC];
+#pragma unroll
+  for (int c = 0; c < RC; ++c) {
+    const int cc = c < n_own ? c : n_own - 1;
+    v[c] = *reinterpret_cast<const float4*>(po + cc * cstride);
+    ml[c] = mq[cc];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < RC; ++c)
+    if (c < n_own) M = fmaxf(M, ml[c].x);
+  // One pass in chunk order; the running quarter sum is added into the total where
+  // the next quarter starts (an empty quarter adds an exact zero).
+  double L = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0}, Lq = 0.0, oq[4] = {0.0, 0.0, 0.0, 0.0};
+  const int e1 = n_own / kCombineWaves, e2 = 2 * n_own / kCombineWaves, e3 = 3 * n_own / kCombineWaves;
+#pragma unroll
+  for (int c = 0; c < RC; ++c) {
+    if (c < n_own) {
+      if (c > 0 && (c == e1 || c == e2 || c == e3)) {
+        L += Lq;
+        Lq = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += oq[i];
+          oq[i] = 0.0;
+        }
+      }
+      const double f = (ml[c].x == -INFINITY) ? 0.0 : (double)exp2f(ml[c].x - M);
+      Lq += (double)ml[c].y * f;
+      oq[0] += (double)v[c].x * f;
+      oq[1] += (double)v[c].y * f;
+      oq[2] += (double)v[c].z * f;
+      oq[3] += (double)v[c].w * f;
+    }
+  }
+  L += Lq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] += oq[i];
+  const int hl = qi / p.B, jrow = qi % p.B;
+  T* dst = static_cast<T*>(p.o) + (int64_t)(s * p.B + jrow) * (p.n_q_heads * D) + (h * p.group + hl) * D + 16 * dt + 4 * lg;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Elem<T>::store_d(dst + i, o[i] / L);
+}
+
 int attention_query_tiles(int group, int block) { return (group * block + 15) / 16; }
 
 template <typename T, int D, int QT>
@@ -638,7 +716,10 @@ static hipError_t launch_td(const AttnParams& p, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_chunks == 1) return e;
-  (void)launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64 * kCombineWaves), st, p, qt);
+  if (p.n_chunks <= kCombineShort)
+    (void)launch_k((k_attn_combine_short<T, D>), dim3(p.S * p.n_kv_heads * qt), dim3(64 * (D / 16)), st, p, qt);
+  else
+    (void)launch_k((k_attn_combine<T, D>), dim3(p.S * p.n_kv_heads * qt, D / 16), dim3(64 * kCombineWaves), st, p, qt);
   return hipGetLastError();
 }
 
