@@ -87,6 +87,9 @@ namespace {
 struct GemmPlan {
   int am, mt, mgroups, n_tiles, iters, ksplit, n_work;
   bool tall;   // many rows: the tiled kernel
+  // Tiled SWIGLU whose last round of column tiles would be mostly idle: the tiled
+  // kernel takes gate/up rows [0, tail_from), the skinny kernel the rest (0: no split).
+  int tail_from;
   size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * 8; }
 };
 
@@ -105,6 +108,13 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
   g.tall = dtype == DFLASH_BF16 && wide;
   g.ksplit = g.tall ? gemm_tall_ksplit(epi, N, K) : gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
+  g.tail_from = 0;
+  if (g.tall && epi == EPI_SWIGLU) {
+    // One 128-column tile (64 gate + 64 up rows) per CU and round: a remainder of at
+    // most a quarter round goes to the skinny kernel, which spreads it over all CUs.
+    const int tiles = gemm_tall_column_tiles(epi, N), rem = tiles % kTallRoundTiles;
+    if (tiles > kTallRoundTiles && rem > 0 && rem <= kTallRoundTiles / 4) g.tail_from = (tiles - rem) * 64;
+  }
   return g;
 }
 
@@ -431,6 +441,28 @@ static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
 static_assert(sizeof(GemmParams) <= 4000, "kernel argument block too large");
 
 static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmParams& p, hipStream_t st) {
+  if (g.tall && g.tail_from > 0) {
+    // SWIGLU split by gate/up rows: [0, tail_from) tiled, the rest skinny (16 gate +
+    // 16 up rows a tile, every row group; the whole K in each workgroup).
+    const int half = p.N / 2, tail = half - g.tail_from;
+    GemmParams a = p;
+    a.N = 2 * g.tail_from;
+    hipError_t e = launch_gemm_tall(epi, g.am, a, st);
+    if (e != hipSuccess) return e;
+    GemmParams b = p;
+    const size_t esz = dtype == DFLASH_F32 ? 4 : 2;
+    b.N = 2 * tail;
+    b.w0 = static_cast<const char*>(p.w0) + (size_t)g.tail_from * p.K * esz;
+    b.w1 = static_cast<const char*>(p.w1) + (size_t)g.tail_from * p.K * esz;
+    b.m_out = static_cast<char*>(p.m_out) + (size_t)g.tail_from * esz;
+    const int mt = 4;
+    b.mgroups = (p.M + 16 * mt - 1) / (16 * mt);
+    b.n_tiles = (b.N + gemm_tile_cols(epi) - 1) / gemm_tile_cols(epi);
+    b.iters = p.K / gemm_k_per_iter(dtype, epi, g.am, p.K, 0);
+    b.ksplit = 1;
+    b.n_work = b.n_tiles * b.mgroups;
+    return launch_gemm(dtype, epi, g.am, b, mt, st);
+  }
   if (g.tall) return launch_gemm_tall(epi, g.am, p, st);
   return launch_gemm(dtype, epi, g.am, p, g.mt, st);
 }

@@ -198,6 +198,8 @@ constexpr int kTallMinRows = 65;
 // bitwise the same in any batch of its class.
 inline bool batch_is_wide(int rows) { return rows >= kTallMinRows; }
 int gemm_tall_ksplit(int epi, int N, int K);
+int gemm_tall_column_tiles(int epi, int N);
+constexpr int kTallRoundTiles = 256;   // column tiles of one round: one per CU
 hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st);
 int gemm_tile_cols(int epi);
 hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st);

@@ -334,6 +334,16 @@ def test_round_parity_mid_d64_two_row_groups():
     run_case(case, list(range(MID64.n_streams)))
 
 
+WIDE_TAIL = small_variant(MID, name="wide_tail_bf16", n_layers=2, layer_window=[0, 37], intermediate=17408,
+                          n_streams=6, ctx_spec=[300, 77, 1030, 0, 513, 64], seed=2004)
+
+
+def test_round_parity_wide_swiglu_tail():
+    # 96 rows (a wide batch) and 2 * 17408 gate/up rows: 272 tiled column tiles, of
+    # which the last 16 (a sixteenth of a round) are computed by the skinny kernel.
+    run_case(RoundCase(WIDE_TAIL), list(range(WIDE_TAIL.n_streams)))
+
+
 def test_round_parity_9b_ctx4k():
     run_case(RoundCase(wl.preset("9b_ctx4k")), [0], conditioning=True)
 
