@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--workload", default="9b_ctx4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="instead of the round: fuse + inject this many prompt rows of one stream")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the round shards by "
@@ -177,6 +179,9 @@ def main():
 
     torch.cuda.init()
     p = wl.preset(args.workload)
+    if args.prefill > 0:
+        prefill_main(args, p)
+        return
     print(f"[bench] workload {p.name}: setting up", file=sys.stderr, flush=True)
     case = RoundCase(p)
     S, B = p.n_streams, p.block_size
@@ -207,6 +212,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = e0.elapsed_time(e1) / args.steps
+
+    # distribution of single rounds (a separate pass; the timed region above is untouched)
+    qn = min(args.steps, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(qn)]
+    for a, b in evs:
+        a.record(st)
+        step()
+        b.record(st)
+    torch.cuda.synchronize()
+    per_round = sorted(a.elapsed_time(b) for a, b in evs)
+    quant = {q: round(per_round[min(qn - 1, int(f * (qn - 1) + 0.5))], 5)
+             for q, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
 
     # per-kernel pass: the library brackets each of its launches with events on this stream
     case.dr.set_profiling(True)
@@ -254,6 +271,9 @@ def main():
         "hbm_frac_of_peak": round(tot_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_frac_of_peak": round(tot_flops / (ms * 1e-3) / 1e12 / mfma_dtype_peak, 5),
         "round_bytes": tot_bytes, "round_flops": tot_flops, "wall_s_timed": round(wall, 4),
+        "round_ms_quantiles": quant,
+        "bytes_per_drafted_token": round(tot_bytes / drafted),
+        "bytes_per_accepted_token": round(tot_bytes / max(1, case.R)),
         "roofline": roof,
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_step"])},
@@ -264,6 +284,97 @@ def main():
         sample = [0] if S == 1 else [int(min(range(S), key=lambda s: case.ctx[s]))]
         cb, _ = cpu_baseline(case, sample)
         out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def prefill_main(args, p):
+    """Fuse + inject of `args.prefill` prompt rows of one stream at the workload's shapes
+    (the step before the round at prompt scale): rows/s, the fc GEMM against the MFMA
+    roofline, and the oracle on a few of the rows."""
+    import torch
+    import workloads as wl
+    from workloads.round_case import RoundCase, to_np
+
+    R = args.prefill
+    from workloads.presets import small_variant
+    q = small_variant(p, n_streams=1)
+    print(f"[bench] prefill: {R} rows at {p.name} shapes: setting up", file=sys.stderr, flush=True)
+    case = RoundCase(q, ctx=[max(R, 4096)], rows=[R])
+    st = torch.cuda.current_stream()
+
+    def step():
+        case.fuse()
+        case.inject()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    case.dr.set_profiling(True)
+    case.dr.profile_read()
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = case.dr.profile_read()
+    case.dr.set_profiling(False)
+
+    costs = kernel_costs(q, case.ctx, case.rows)
+    names = ("fuse_fc_gemm", "fuse_rownorm", "inject_kv_gemm", "inject_kv_finish")
+    tot_bytes = sum(costs[n]["bytes"] for n in names)
+    tot_flops = sum(costs[n]["flops"] for n in names)
+    kernels = {}
+    for name, (cnt, total) in prof.items():
+        per = total / cnt
+        c = costs.get(name, {"bytes": 0, "flops": 0})
+        kernels[name] = dict(launches_per_step=cnt / args.profile_steps, avg_ms=round(per, 5),
+                             gbps=round(c["bytes"] / (per * 1e-3) / 1e9, 1),
+                             tflops=round(c["flops"] / (per * 1e-3) / 1e12, 2))
+    dom = "fuse_fc_gemm"
+    peak = FP32_TFLOPS if q.dtype == "f32" else MFMA_BF16_TFLOPS
+    roof = dict(bound="mfma", achieved=kernels[dom]["tflops"], peak=peak, unit="TFLOP/s",
+                frac=round(kernels[dom]["tflops"] / peak, 4), kernel=dom,
+                bytes_per_launch=costs[dom]["bytes"], flops_per_launch=costs[dom]["flops"],
+                avg_launch_ms=kernels[dom]["avg_ms"], traffic=None)
+    out = {
+        "metric": "prefill-scale fuse + inject: prompt rows/s (fc GEMM + hidden norm + K/V of every layer)",
+        "value": round(R / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": q.dtype, "data": "synthetic",
+        "config": {"workload": f"fuse + inject of {R} prompt rows at {p.name} shapes", "preset": p.name,
+                   "rows": R, "hidden": q.hidden, "taps": q.n_taps, "layers": q.n_layers},
+        "mfma_frac_of_peak": round(tot_flops / (ms * 1e-3) / 1e12 / peak, 4),
+        "hbm_gbps": round(tot_bytes / (ms * 1e-3) / 1e9, 1), "step_bytes": tot_bytes, "step_flops": tot_flops,
+        "roofline": roof, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dflash_oracle as O
+        W = case.weights_np()
+        idx = list(range(0, R, max(1, R // 8)))[:8]
+        taps = [to_np(t[idx]) for t in case.taps]
+        reps, total = 0, 0.0
+        while total < 10.0:
+            t0 = time.perf_counter()
+            f = O.fuse_taps(q, taps, W)
+            O.inject_kv(q, f, [case.ctx[0] - R + i for i in idx], W)
+            total += time.perf_counter() - t0
+            reps += 1
+        per_row = total / reps / len(idx)
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = dict(value=round(1.0 / per_row, 2), unit="rows/s", cores=int(threads), kind="oracle",
+                                   sample=f"{reps} x fuse + inject of {len(idx)} of the {R} rows, float64 numpy",
+                                   seconds=round(total, 2))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

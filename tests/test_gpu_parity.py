@@ -297,6 +297,30 @@ def test_fuse_and_inject_parity(preset, rows):
         assert_close_storage(to_np(vg), kv[l][1], p.dtype, f"V layer {l}")
 
 
+def test_prefill_scale_fuse_and_inject_sampled_rows():
+    # 2048 prompt rows of one stream at the 9B shapes (fc K = 32768): eight row tiles of
+    # the tiled kernel. The oracle computes a sample of the rows (the steps act on each
+    # row alone); inject is checked on the GPU's own fused rows.
+    p = small_variant(wl.preset("9b_ctx4k"), n_streams=1)
+    R = 2048
+    case = RoundCase(p, ctx=[4096], rows=[R])
+    log(f"[fuse/inject] {p.name} prefill rows={R}")
+    case.fuse()
+    case.inject()
+    torch.cuda.synchronize()
+    idx = [0, 1, 255, 256, 1023, 1500, 2046, 2047]
+    W = case.weights_np()
+    fused = O.fuse_taps(p, [to_np(t[idx]) for t in case.taps], W)
+    assert_close_storage(to_np(case.fused[idx]), fused, p.dtype, "fused (sampled rows)")
+    pos = [case.ctx[0] - R + i for i in idx]
+    kv = O.inject_kv(p, to_np(case.fused[idx]), np.array(pos), W)
+    for l in range(p.n_layers):
+        for j, ps in enumerate(pos):
+            kg, vg = case.kv.read_rows(l, 0, ps, 1)
+            assert_close_storage(to_np(kg), kv[l][0][j:j + 1], p.dtype, f"K layer {l} pos {ps}")
+            assert_close_storage(to_np(vg), kv[l][1][j:j + 1], p.dtype, f"V layer {l} pos {ps}")
+
+
 def test_inject_skips_invalid_rows_and_touches_nothing_else():
     p = small_variant(MID, n_streams=2)
     case = RoundCase(p, ctx=[64, 64], rows=[0, 0])
