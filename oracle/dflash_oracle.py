@@ -26,6 +26,9 @@ What it computes (sources are the four pages on DFlash):
             section 4, "Greedy decoding"; "Port the DFlash2 protocol, not its
             checkpoint", "What is portable" and "Golden replay before
             training").
+  * sampling: inverse-CDF draws from tempered softmax rows, and speculative-
+            sampling acceptance with the residual max(p_target - p_draft, 0)
+            (explainer section 4, "Sampling decoding").
 
 Numerics: every product and reduction is float64. Values are rounded to the
 activation dtype (bf16 by round-to-nearest-even straight from float64, or
@@ -46,7 +49,10 @@ Readings taken where the pages are silent (each also listed in the design doc):
   row j at C+j; rotate-half RoPE over the whole head; a sliding layer with
   window W sees context rows [max(0, C-W), C) plus all B block rows; q head h
   reads kv head h // (n_q / n_kv); scale 1/sqrt(head_dim); mask row j predicts
-  the token at position C+j; argmax ties go to the lowest index.
+  the token at position C+j; argmax ties go to the lowest index; sampling
+  accepts d when u * p_draft(d) < p_target(d), draws by inverse CDF over token
+  ids in ascending order with one uniform per draw, and falls back to the
+  target's distribution when the residual has no mass.
 """
 import math
 
@@ -315,6 +321,69 @@ def verify_greedy(draft, target):
         committed[s, :a] = draft[s, :a]
         committed[s, a] = target[s, a]
     return accept, bonus, committed
+
+
+# --------------------------------------------------------------------------
+# Sampling (DFlash explainer, section 4, "Sampling decoding"): the standard
+# speculative-sampling rule the page names, with its residual distribution.
+
+
+def tempered_probs(logits, T):
+    """softmax(logits / T) over the last axis, float64 (T > 0)."""
+    return softmax(np.asarray(logits, dtype=np.float64) / float(T))
+
+
+def sample_index(p, u):
+    """Inverse-CDF draw from the weights p (not necessarily normalised) with one
+    uniform u in [0, 1): the smallest k with p_0 + ... + p_k > u * sum(p). A
+    zero weight is never drawn."""
+    p = np.asarray(p, dtype=np.float64)
+    c = np.cumsum(p)
+    k = int(np.searchsorted(c, u * c[-1], side="right"))
+    if k >= len(p):                      # u * sum landed on the total: the last nonzero weight
+        k = int(np.flatnonzero(p > 0)[-1])
+    return k
+
+
+def verify_sampling(draft, draft_logits, target_logits, T, u_accept, u_sample):
+    """Speculative-sampling acceptance per stream.
+
+    draft [S, B-1]: d_1..d_{B-1}, drawn from the draft's tempered distributions
+    p_j = softmax(draft_logits[s, j-1] / T); target_logits [S, B]: row i gives the
+    target's distribution q_i = softmax(target_logits[s, i] / T) for the token
+    after the anchor and d_1..d_i. Walking j = 1, 2, ..., d_j is accepted when
+    u_accept[s, j-1] * p_j(d_j) < q_{j-1}(d_j) (probability min(1, q/p)). At the
+    first rejection j the next token is drawn with u_sample[s] from the residual
+    max(q_{j-1} - p_j, 0) (renormalised; q_{j-1} itself if that residual has no
+    mass); when every d_j is accepted it is drawn from q_{B-1}. Returns the
+    accepted length a, that token, and committed = d_1..d_a, token (-1 padded),
+    as in verify_greedy.
+    """
+    draft = np.asarray(draft, dtype=np.int64)
+    S, Bm1 = draft.shape
+    accept = np.zeros(S, dtype=np.int64)
+    token = np.zeros(S, dtype=np.int64)
+    committed = np.full((S, Bm1 + 1), -1, dtype=np.int64)
+    for s in range(S):
+        a = 0
+        nxt = None
+        while a < Bm1:
+            p = tempered_probs(draft_logits[s, a], T)
+            q = tempered_probs(target_logits[s, a], T)
+            d = draft[s, a]
+            if u_accept[s, a] * p[d] < q[d]:
+                a += 1
+                continue
+            r = np.maximum(q - p, 0.0)
+            nxt = sample_index(r if r.sum() > 0 else q, u_sample[s])
+            break
+        if nxt is None:
+            nxt = sample_index(tempered_probs(target_logits[s, Bm1], T), u_sample[s])
+        accept[s] = a
+        token[s] = nxt
+        committed[s, :a] = draft[s, :a]
+        committed[s, a] = nxt
+    return accept, token, committed
 
 
 # --------------------------------------------------------------------------
