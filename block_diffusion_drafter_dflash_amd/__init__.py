@@ -80,6 +80,9 @@ def library():
         "dflash_inject_kv": (i32, [_VP, _VP, i32, _VP, _VP, ctypes.POINTER(KV), _VP, sz, _VP]),
         "dflash_draft_block": (i32, [_VP, i32, _VP, _VP, i32, ctypes.POINTER(KV), _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_greedy": (i32, [_VP, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP]),
+        "dflash_verify_sampling": (i32, [_VP, i32, _VP, _VP, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
+                                         _VP, _VP, sz, _VP]),
         "dflash_set_profiling": (i32, [_VP, i32]),
         "dflash_profile_read": (i32, [_VP, ctypes.c_char_p, sz]),
         "dflash_last_error": (ctypes.c_char_p, [_VP]),
@@ -97,6 +100,7 @@ def library():
 EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflash_bind_weights",
             "dflash_fused_row_bytes", "dflash_tap_row_bytes", "dflash_workspace_bytes", "dflash_workspace_init",
             "dflash_fuse_taps", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_greedy",
+            "dflash_sample_rows", "dflash_verify_sampling",
             "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
 
 
@@ -249,6 +253,20 @@ class Drafter:
         self._check(self.lib.dflash_verify_greedy(self.h, n_streams, _ptr(draft), _ptr(target), _ptr(accept_len),
                                                   _ptr(bonus), _ptr(committed), _ptr(ctx_len_inout),
                                                   _stream(stream)))
+
+    def dflash_sample_rows(self, logits, temperature, u, token_out, prob_out=None, n_rows=None, stream=None):
+        n_rows = logits.shape[0] if n_rows is None else n_rows
+        self._check(self.lib.dflash_sample_rows(self.h, n_rows, _ptr(logits), logits.stride(0), float(temperature),
+                                                _ptr(u), _ptr(token_out), _ptr(prob_out), _stream(stream)))
+
+    def dflash_verify_sampling(self, draft, draft_logits, target_logits, temperature, u_accept, u_sample,
+                               accept_len, token, committed, ws, ctx_len_inout=None, n_streams=None, stream=None):
+        n_streams = draft.shape[0] if n_streams is None else n_streams
+        self._check(self.lib.dflash_verify_sampling(self.h, n_streams, _ptr(draft), _ptr(draft_logits),
+                                                    _ptr(target_logits), draft_logits.stride(-2),
+                                                    float(temperature), _ptr(u_accept), _ptr(u_sample),
+                                                    _ptr(accept_len), _ptr(token), _ptr(committed),
+                                                    _ptr(ctx_len_inout), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 class PagedKV:

@@ -222,6 +222,22 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   return L;
 }
 
+// Speculative-sampling verify: per-row (max, total weight) of the draft's S (B - 1)
+// and the target's S B rows.
+struct VerifyLayout {
+  size_t draft_stats, target_stats, end;
+};
+VerifyLayout layout_verify(const dflash& h, int S) {
+  VerifyLayout L;
+  const int B = h.cfg.block_size;
+  Region r;
+  r.take(kCounterInts * 4);
+  L.draft_stats = r.take((size_t)S * (B - 1) * 16);
+  L.target_stats = r.take((size_t)S * B * 16);
+  L.end = r.off;
+  return L;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -361,6 +377,7 @@ size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_strea
     b = std::max(b, layout_inject(*h, max_rows).end);
   }
   b = std::max(b, layout_draft(*h, n_streams, max_ctx).end);
+  b = std::max(b, layout_verify(*h, n_streams).end);
   return b;
 }
 
@@ -818,6 +835,84 @@ int dflash_verify_greedy(dflash* h, int32_t n_streams, const int32_t* draft, con
     e = launch_verify(vp, (hipStream_t)stream);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "verify: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+int dflash_sample_rows(dflash* h, int32_t n_rows, const float* logits, int64_t row_stride, float temperature,
+                       const float* u, int32_t* token_out, float* prob_out, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (n_rows < 0) return fail(h, DFLASH_ERR_ARG, "n_rows %d < 0", n_rows);
+  if (n_rows == 0) return DFLASH_OK;
+  if (!logits || !u || !token_out) return fail(h, DFLASH_ERR_ARG, "a sampling pointer is NULL");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(h, DFLASH_ERR_ARG, "temperature must be positive and finite");
+  if (row_stride < h->cfg.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
+  SampleParams sp;
+  sp.rows = n_rows;
+  sp.V = h->cfg.vocab;
+  sp.ld = row_stride;
+  sp.logits = logits;
+  sp.scale = (float)(1.4426950408889634 / (double)temperature);
+  sp.u = u;
+  sp.token_out = token_out;
+  sp.prob_out = prob_out;
+  hipError_t e;
+  {
+    ProfScope ps(h, "sample_rows", (hipStream_t)stream);
+    e = launch_sample_rows(sp, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "sample rows: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+int dflash_verify_sampling(dflash* h, int32_t n_streams, const int32_t* draft, const float* draft_logits,
+                           const float* target_logits, int64_t row_stride, float temperature, const float* u_accept,
+                           const float* u_sample, int32_t* accept_len, int32_t* token, int32_t* committed,
+                           int32_t* ctx_len_inout, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const auto& c = h->cfg;
+  if (n_streams < 1 || n_streams > c.max_streams)
+    return fail(h, DFLASH_ERR_ARG, "n_streams %d outside [1, %d]", n_streams, c.max_streams);
+  if (!draft || !draft_logits || !target_logits || !u_accept || !u_sample || !accept_len || !token || !committed)
+    return fail(h, DFLASH_ERR_ARG, "a verify pointer is NULL");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(h, DFLASH_ERR_ARG, "temperature must be positive and finite");
+  if (row_stride < c.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
+  const VerifyLayout L = layout_verify(*h, n_streams);
+  int rc = check_ws(h, ws, ws_bytes, L.end);
+  if (rc != DFLASH_OK) return rc;
+  char* W = static_cast<char*>(ws);
+  const int B = c.block_size;
+  const float scale = (float)(1.4426950408889634 / (double)temperature);
+  SpecVerifyParams vp;
+  vp.S = n_streams;
+  vp.B = B;
+  vp.V = c.vocab;
+  vp.ld = row_stride;
+  vp.draft = draft;
+  vp.draft_logits = draft_logits;
+  vp.target_logits = target_logits;
+  vp.draft_stats = reinterpret_cast<const double*>(W + L.draft_stats);
+  vp.target_stats = reinterpret_cast<const double*>(W + L.target_stats);
+  vp.scale = scale;
+  vp.u_accept = u_accept;
+  vp.u_sample = u_sample;
+  vp.accept = accept_len;
+  vp.token = token;
+  vp.committed = committed;
+  vp.ctx_len = ctx_len_inout;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  {
+    ProfScope ps(h, "verify_sampling", st);
+    e = launch_row_stats(draft_logits, n_streams * (B - 1), c.vocab, row_stride, scale,
+                         reinterpret_cast<double*>(W + L.draft_stats), st);
+    if (e == hipSuccess)
+      e = launch_row_stats(target_logits, n_streams * B, c.vocab, row_stride, scale,
+                           reinterpret_cast<double*>(W + L.target_stats), st);
+    if (e == hipSuccess) e = launch_verify_sampling(vp, st);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "verify sampling: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 

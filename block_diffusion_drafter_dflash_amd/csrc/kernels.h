@@ -144,6 +144,38 @@ struct VerifyParams {
   int* ctx_len;
 };
 
+// Draws from tempered softmax rows: token_out[r] ~ softmax(logits[r] / T) by inverse
+// CDF with uniform u[r]; prob_out (nullable) gets the drawn token's probability.
+struct SampleParams {
+  int rows, V;
+  int64_t ld;           // row stride of logits, in floats
+  const float* logits;
+  float scale;          // log2(e) / T
+  const float* u;
+  int* token_out;
+  float* prob_out;
+};
+
+// Speculative-sampling acceptance (one workgroup a stream). Rows of draft_logits
+// [S, B-1] and target_logits [S, B] share the stride ld; their (max, total weight)
+// come from k_row_stats.
+struct SpecVerifyParams {
+  int S, B, V;
+  int64_t ld;
+  const int* draft;
+  const float* draft_logits;
+  const float* target_logits;
+  const double* draft_stats;    // [S * (B - 1)][2]
+  const double* target_stats;   // [S * B][2]
+  float scale;                  // log2(e) / T
+  const float* u_accept;        // [S, B - 1]
+  const float* u_sample;        // [S]
+  int* accept;
+  int* token;
+  int* committed;               // [S, B], -1 padded
+  int* ctx_len;                 // nullable: += accept + 1
+};
+
 // Context chunking, in pages of 16 keys, of one stream's reach: a function of that
 // reach and of the batch's class (see batch_is_wide), so a stream's result does not
 // depend on the other streams of a batch of its class. Narrow batches: up to 256
@@ -214,5 +246,9 @@ hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st);
 hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st);
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
 hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st);
+hipError_t launch_row_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
+                            hipStream_t st);
+hipError_t launch_sample_rows(const SampleParams& p, hipStream_t st);
+hipError_t launch_verify_sampling(const SpecVerifyParams& p, hipStream_t st);
 
 }  // namespace dfl

@@ -6,6 +6,8 @@
  *   dflash_inject_kv      fused rows -> k and v of every draft layer, written into a paged cache
  *   dflash_draft_block    one non-causal forward over anchor + (B-1) mask rows, LM-head argmax
  *   dflash_verify_greedy  longest prefix equal to the target's argmax, plus the bonus token
+ *   dflash_sample_rows    inverse-CDF draws from tempered softmax rows
+ *   dflash_verify_sampling speculative-sampling acceptance with the residual draw
  *
  * The round is the one described by TensorFold pull request #1851 ("What this
  * changes", items 1-4), the DFlash explainer (sections 3 and 4) and "Port the
@@ -227,6 +229,52 @@ int dflash_draft_block(dflash *h, int32_t n_streams, const int32_t *anchor,
 int dflash_verify_greedy(dflash *h, int32_t n_streams, const int32_t *draft,
                          const int32_t *target_argmax, int32_t *accept_len, int32_t *bonus,
                          int32_t *committed, int32_t *ctx_len_inout, void *stream);
+
+/*
+ * Sampling (DFlash explainer section 4, "Sampling decoding"). Draws from tempered
+ * softmax rows: token_out[r] is drawn from softmax(logits[r, :vocab] / temperature)
+ * by inverse CDF over token ids in ascending order with the caller's uniform u[r] in
+ * [0, 1): the smallest id whose running probability exceeds u[r]; an id of zero
+ * probability is never drawn.
+ *   logits:    device float [n_rows, row_stride] (row_stride >= vocab), e.g. the
+ *              logits_out of dflash_draft_block;
+ *   u:         device float [n_rows];
+ *   token_out: device int32 [n_rows];
+ *   prob_out:  NULL, or device float [n_rows]: the drawn token's probability.
+ * temperature must be positive and finite. n_rows == 0 is a no-op. Probabilities are
+ * fp32 exponentials summed in float64. Works without bound weights.
+ */
+int dflash_sample_rows(dflash *h, int32_t n_rows, const float *logits, int64_t row_stride,
+                       float temperature, const float *u, int32_t *token_out, float *prob_out,
+                       void *stream);
+
+/*
+ * Speculative-sampling verify (DFlash explainer section 4, "Sampling decoding": the
+ * standard acceptance rule and the residual max(p_target - p_draft, 0)). Per stream,
+ * with draft d_1..d_{B-1} (device int32 [n_streams, B-1]) drawn from the draft's
+ * tempered distributions p_j = softmax(draft_logits[s, j-1] / T) (device float
+ * [n_streams, B-1, row_stride]) and the target's q_i = softmax(target_logits[s, i] / T)
+ * (device float [n_streams, B, row_stride]; row i: the token after the anchor and
+ * d_1..d_i):
+ *   d_j is accepted, for j = 1, 2, ..., while u_accept[s, j-1] * p_j(d_j) < q_{j-1}(d_j)
+ *   (an id outside [0, vocab) is rejected);
+ *   accept_len[s] = a, the number accepted;
+ *   token[s] = a draw with u_sample[s] (inverse CDF, as dflash_sample_rows) from the
+ *   residual max(q_a - p_{a+1}, 0) renormalised (q_a when the residual has no mass)
+ *   if a < B-1, else from q_{B-1};
+ *   committed[s] = d_1..d_a, token[s], then -1 up to B entries (device int32 [n_streams, B]);
+ *   ctx_len_inout[s] += a + 1 when ctx_len_inout is not NULL.
+ * u_accept: device float [n_streams, B-1]; u_sample: device float [n_streams]; all
+ * uniforms in [0, 1). ws: a workspace initialised with dflash_workspace_init for at
+ * least n_streams streams (it holds each row's max and total weight). temperature must
+ * be positive and finite. Works without bound weights.
+ */
+int dflash_verify_sampling(dflash *h, int32_t n_streams, const int32_t *draft,
+                           const float *draft_logits, const float *target_logits,
+                           int64_t row_stride, float temperature, const float *u_accept,
+                           const float *u_sample, int32_t *accept_len, int32_t *token,
+                           int32_t *committed, int32_t *ctx_len_inout, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /*
  * Instrumentation (not part of the round). With profiling enabled, every kernel the
