@@ -31,7 +31,7 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16
 FP32_TFLOPS = 157.3
 
 
-def kernel_costs(p, ctx, rows):
+def kernel_costs(p, ctx, rows, sampling=False):
     """Algorithmic bytes and FLOPs per launch of each kernel of one round.
 
     Bytes are what the method itself must move: each weight once per call that reads
@@ -70,9 +70,15 @@ def kernel_costs(p, ctx, rows):
     k["o_proj_gemm"] = dict(bytes=(h * nq + M * nq) * es, flops=2 * M * nq * h)
     k["gate_up_gemm"] = dict(bytes=(2 * I * h + M * h + M * I) * es, flops=4 * M * h * I)
     k["down_gemm"] = dict(bytes=(h * I + M * I) * es, flops=2 * M * I * h)
-    k["lm_head_gemm"] = dict(bytes=(V * h + Mm * h) * es, flops=2 * Mm * h * V)
+    # the sampled round also writes the fp32 logits the draws read
+    k["lm_head_gemm"] = dict(bytes=(V * h + Mm * h) * es + (Mm * V * 4 if sampling else 0), flops=2 * Mm * h * V)
     k["argmax_final"] = dict(bytes=Mm * 4, flops=0)
-    k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
+    if sampling:
+        # draws: each draft logit row read once; verify: every draft and target row read once
+        k["sample_rows"] = dict(bytes=Mm * V * 4 + Mm * 8, flops=0)
+        k["verify_sampling"] = dict(bytes=(Mm + M) * V * 4 + (2 * Mm + 3 * S + S * B) * 4, flops=0)
+    else:
+        k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
     for name in ("qkv_gemm", "qkv_finish", "o_proj_gemm", "gate_up_gemm", "down_gemm"):
         k[name]["launches"] = L
     for name, v in k.items():
@@ -167,6 +173,9 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--prefill", type=int, default=0,
                     help="instead of the round: fuse + inject this many prompt rows of one stream")
+    ap.add_argument("--sampling", type=float, default=0.0,
+                    help="temperature T > 0: the round drafts by sampling and verifies by speculative sampling "
+                         "(draft logits written, tempered draws, synthetic target logits)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the round shards by "
@@ -191,11 +200,32 @@ def main():
     case.set_target_from(case.draft.cpu().numpy())
     torch.cuda.synchronize()
 
-    def step():
-        case.fuse()
-        case.inject()
-        case.draft_block(logits=False, top2=False)
-        case.verify()
+    if args.sampling > 0:
+        # sampled round: the draft's logits are written, each mask row is drawn from its
+        # tempered softmax, and the block is verified by speculative sampling against
+        # seeded target logits (what a target model would return for the block)
+        T = args.sampling
+        g = torch.Generator(device="cuda").manual_seed(p.seed + 17)
+        target_logits = torch.randn((S, B, p.vocab), generator=g, device="cuda") * 2.0
+        u_draw = torch.rand(S * (B - 1), generator=g, device="cuda")
+        u_acc = torch.rand((S, B - 1), generator=g, device="cuda")
+        u_smp = torch.rand(S, generator=g, device="cuda")
+        s_draft = torch.zeros(S * (B - 1), dtype=torch.int32, device="cuda")
+        s_token = torch.zeros(S, dtype=torch.int32, device="cuda")
+
+        def step():
+            case.fuse()
+            case.inject()
+            case.draft_block(logits=True, top2=False)
+            case.dr.dflash_sample_rows(case.logits.view(S * (B - 1), p.vocab), T, u_draw, s_draft)
+            case.dr.dflash_verify_sampling(s_draft.view(S, B - 1), case.logits, target_logits, T, u_acc, u_smp,
+                                           case.accept, s_token, case.committed, case.ws)
+    else:
+        def step():
+            case.fuse()
+            case.inject()
+            case.draft_block(logits=False, top2=False)
+            case.verify()
 
     for _ in range(args.warmup):
         step()
@@ -235,7 +265,7 @@ def main():
     case.dr.set_profiling(False)
     print(f"[bench] timed {ms:.4f} ms/step; per-kernel pass done", file=sys.stderr, flush=True)
 
-    costs = kernel_costs(p, case.ctx, case.rows)
+    costs = kernel_costs(p, case.ctx, case.rows, sampling=args.sampling > 0)
     tot_bytes, tot_flops = round_totals(costs)
     drafted = S * (B - 1)
     value = drafted / (ms * 1e-3)
@@ -264,7 +294,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "drafted tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": p.note or p.name, "preset": p.name, "streams": S, "block": B,
+        "config": {"workload": (p.note or p.name) + (f", sampled at T={args.sampling}" if args.sampling > 0 else ""),
+                   "preset": p.name, "streams": S, "block": B,
                    "context": case.ctx if S > 1 else case.ctx[0], "rows_fused": case.R,
                    "hidden": p.hidden, "layers": p.n_layers, "vocab": p.vocab},
         "hbm_gbps": round(tot_bytes / (ms * 1e-3) / 1e9, 1),

@@ -847,6 +847,8 @@ int dflash_sample_rows(dflash* h, int32_t n_rows, const float* logits, int64_t r
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(h, DFLASH_ERR_ARG, "temperature must be positive and finite");
   if (row_stride < h->cfg.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
+  if (h->cfg.vocab > kSampleVocabMax)
+    return fail(h, DFLASH_ERR_CONFIG, "sampling takes a vocabulary of at most %d ids", kSampleVocabMax);
   SampleParams sp;
   sp.rows = n_rows;
   sp.V = h->cfg.vocab;
@@ -878,6 +880,8 @@ int dflash_verify_sampling(dflash* h, int32_t n_streams, const int32_t* draft, c
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(h, DFLASH_ERR_ARG, "temperature must be positive and finite");
   if (row_stride < c.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
+  if (c.vocab > kSampleVocabMax)
+    return fail(h, DFLASH_ERR_CONFIG, "sampling takes a vocabulary of at most %d ids", kSampleVocabMax);
   const VerifyLayout L = layout_verify(*h, n_streams);
   int rc = check_ws(h, ws, ws_bytes, L.end);
   if (rc != DFLASH_OK) return rc;

@@ -144,6 +144,9 @@ struct VerifyParams {
   int* ctx_len;
 };
 
+// Largest vocabulary the sampling kernels take (their per-row segment sums live in LDS).
+constexpr int kSampleVocabMax = 262144;
+
 // Draws from tempered softmax rows: token_out[r] ~ softmax(logits[r] / T) by inverse
 // CDF with uniform u[r]; prob_out (nullable) gets the drawn token's probability.
 struct SampleParams {

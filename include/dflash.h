@@ -241,8 +241,9 @@ int dflash_verify_greedy(dflash *h, int32_t n_streams, const int32_t *draft,
  *   u:         device float [n_rows];
  *   token_out: device int32 [n_rows];
  *   prob_out:  NULL, or device float [n_rows]: the drawn token's probability.
- * temperature must be positive and finite. n_rows == 0 is a no-op. Probabilities are
- * fp32 exponentials summed in float64. Works without bound weights.
+ * temperature must be positive and finite; vocab at most 262144 (DFLASH_ERR_CONFIG
+ * otherwise). n_rows == 0 is a no-op. Probabilities are fp32 exponentials summed in
+ * float64. Works without bound weights.
  */
 int dflash_sample_rows(dflash *h, int32_t n_rows, const float *logits, int64_t row_stride,
                        float temperature, const float *u, int32_t *token_out, float *prob_out,
@@ -267,7 +268,7 @@ int dflash_sample_rows(dflash *h, int32_t n_rows, const float *logits, int64_t r
  * u_accept: device float [n_streams, B-1]; u_sample: device float [n_streams]; all
  * uniforms in [0, 1). ws: a workspace initialised with dflash_workspace_init for at
  * least n_streams streams (it holds each row's max and total weight). temperature must
- * be positive and finite. Works without bound weights.
+ * be positive and finite; vocab at most 262144. Works without bound weights.
  */
 int dflash_verify_sampling(dflash *h, int32_t n_streams, const int32_t *draft,
                            const float *draft_logits, const float *target_logits,

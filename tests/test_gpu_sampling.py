@@ -178,3 +178,7 @@ def test_sampling_calls_refuse_bad_arguments():
     narrow = torch.zeros((2, 500), device="cuda")
     with pytest.raises(D.DFlashError):
         dr.dflash_sample_rows(narrow, 1.0, u, t)    # row stride below the vocabulary
+    big, _ = drafter(262144 + 256, block=8)        # past the kernels' vocabulary bound (host refusal)
+    wide = torch.zeros((2, 262144 + 256), device="cuda")
+    with pytest.raises(D.DFlashError):
+        big.dflash_sample_rows(wide, 1.0, u, t)
