@@ -217,7 +217,7 @@ def main():
             case.fuse()
             case.inject()
             case.draft_block(logits=True, top2=False)
-            case.dr.dflash_sample_rows(case.logits.view(S * (B - 1), p.vocab), T, u_draw, s_draft)
+            case.dr.dflash_sample_rows(case.logits.view(S * (B - 1), p.vocab), T, u_draw, s_draft, case.ws)
             case.dr.dflash_verify_sampling(s_draft.view(S, B - 1), case.logits, target_logits, T, u_acc, u_smp,
                                            case.accept, s_token, case.committed, case.ws)
     else:

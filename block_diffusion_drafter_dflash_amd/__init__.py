@@ -80,7 +80,7 @@ def library():
         "dflash_inject_kv": (i32, [_VP, _VP, i32, _VP, _VP, ctypes.POINTER(KV), _VP, sz, _VP]),
         "dflash_draft_block": (i32, [_VP, i32, _VP, _VP, i32, ctypes.POINTER(KV), _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_greedy": (i32, [_VP, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
-        "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP]),
+        "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_sampling": (i32, [_VP, i32, _VP, _VP, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
                                          _VP, _VP, sz, _VP]),
         "dflash_set_profiling": (i32, [_VP, i32]),
@@ -254,10 +254,11 @@ class Drafter:
                                                   _ptr(bonus), _ptr(committed), _ptr(ctx_len_inout),
                                                   _stream(stream)))
 
-    def dflash_sample_rows(self, logits, temperature, u, token_out, prob_out=None, n_rows=None, stream=None):
+    def dflash_sample_rows(self, logits, temperature, u, token_out, ws, prob_out=None, n_rows=None, stream=None):
         n_rows = logits.shape[0] if n_rows is None else n_rows
         self._check(self.lib.dflash_sample_rows(self.h, n_rows, _ptr(logits), logits.stride(0), float(temperature),
-                                                _ptr(u), _ptr(token_out), _ptr(prob_out), _stream(stream)))
+                                                _ptr(u), _ptr(token_out), _ptr(prob_out), _ptr(ws), ws.numel(),
+                                                _stream(stream)))
 
     def dflash_verify_sampling(self, draft, draft_logits, target_logits, temperature, u_accept, u_sample,
                                accept_len, token, committed, ws, ctx_len_inout=None, n_streams=None, stream=None):

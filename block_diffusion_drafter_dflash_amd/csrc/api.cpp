@@ -222,18 +222,31 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   return L;
 }
 
-// Speculative-sampling verify: per-row (max, total weight) of the draft's S (B - 1)
-// and the target's S B rows.
+// Sampling: each row's per-slice (max, weight sum); for verify also each stream's
+// draw rows (max, total) and per-slice residual and target sums.
+struct SampleLayout {
+  size_t stats, end;
+};
+SampleLayout layout_sample(int rows) {
+  SampleLayout L;
+  Region r;
+  r.take(kCounterInts * 4);
+  L.stats = r.take((size_t)rows * kSlices * 16);
+  L.end = r.off;
+  return L;
+}
 struct VerifyLayout {
-  size_t draft_stats, target_stats, end;
+  size_t draft_stats, target_stats, row_info, slice_sums, end;
 };
 VerifyLayout layout_verify(const dflash& h, int S) {
   VerifyLayout L;
   const int B = h.cfg.block_size;
   Region r;
   r.take(kCounterInts * 4);
-  L.draft_stats = r.take((size_t)S * (B - 1) * 16);
-  L.target_stats = r.take((size_t)S * B * 16);
+  L.draft_stats = r.take((size_t)S * (B - 1) * kSlices * 16);
+  L.target_stats = r.take((size_t)S * B * kSlices * 16);
+  L.row_info = r.take((size_t)S * 4 * 8);
+  L.slice_sums = r.take((size_t)S * kSlices * 16);
   L.end = r.off;
   return L;
 }
@@ -378,6 +391,7 @@ size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_strea
   }
   b = std::max(b, layout_draft(*h, n_streams, max_ctx).end);
   b = std::max(b, layout_verify(*h, n_streams).end);
+  b = std::max(b, layout_sample(std::max(max_rows, n_streams * h->cfg.block_size)).end);
   return b;
 }
 
@@ -839,7 +853,8 @@ int dflash_verify_greedy(dflash* h, int32_t n_streams, const int32_t* draft, con
 }
 
 int dflash_sample_rows(dflash* h, int32_t n_rows, const float* logits, int64_t row_stride, float temperature,
-                       const float* u, int32_t* token_out, float* prob_out, void* stream) {
+                       const float* u, int32_t* token_out, float* prob_out, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!h) return DFLASH_ERR_ARG;
   if (n_rows < 0) return fail(h, DFLASH_ERR_ARG, "n_rows %d < 0", n_rows);
   if (n_rows == 0) return DFLASH_OK;
@@ -849,6 +864,9 @@ int dflash_sample_rows(dflash* h, int32_t n_rows, const float* logits, int64_t r
   if (row_stride < h->cfg.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
   if (h->cfg.vocab > kSampleVocabMax)
     return fail(h, DFLASH_ERR_CONFIG, "sampling takes a vocabulary of at most %d ids", kSampleVocabMax);
+  const SampleLayout L = layout_sample(n_rows);
+  int rc = check_ws(h, ws, ws_bytes, L.end);
+  if (rc != DFLASH_OK) return rc;
   SampleParams sp;
   sp.rows = n_rows;
   sp.V = h->cfg.vocab;
@@ -858,6 +876,7 @@ int dflash_sample_rows(dflash* h, int32_t n_rows, const float* logits, int64_t r
   sp.u = u;
   sp.token_out = token_out;
   sp.prob_out = prob_out;
+  sp.slice_stats = reinterpret_cast<double*>(static_cast<char*>(ws) + L.stats);
   hipError_t e;
   {
     ProfScope ps(h, "sample_rows", (hipStream_t)stream);
@@ -896,8 +915,10 @@ int dflash_verify_sampling(dflash* h, int32_t n_streams, const int32_t* draft, c
   vp.draft = draft;
   vp.draft_logits = draft_logits;
   vp.target_logits = target_logits;
-  vp.draft_stats = reinterpret_cast<const double*>(W + L.draft_stats);
-  vp.target_stats = reinterpret_cast<const double*>(W + L.target_stats);
+  vp.draft_stats = reinterpret_cast<double*>(W + L.draft_stats);
+  vp.target_stats = reinterpret_cast<double*>(W + L.target_stats);
+  vp.row_info = reinterpret_cast<double*>(W + L.row_info);
+  vp.slice_sums = reinterpret_cast<double*>(W + L.slice_sums);
   vp.scale = scale;
   vp.u_accept = u_accept;
   vp.u_sample = u_sample;
@@ -909,12 +930,7 @@ int dflash_verify_sampling(dflash* h, int32_t n_streams, const int32_t* draft, c
   hipError_t e;
   {
     ProfScope ps(h, "verify_sampling", st);
-    e = launch_row_stats(draft_logits, n_streams * (B - 1), c.vocab, row_stride, scale,
-                         reinterpret_cast<double*>(W + L.draft_stats), st);
-    if (e == hipSuccess)
-      e = launch_row_stats(target_logits, n_streams * B, c.vocab, row_stride, scale,
-                           reinterpret_cast<double*>(W + L.target_stats), st);
-    if (e == hipSuccess) e = launch_verify_sampling(vp, st);
+    e = launch_verify_sampling(vp, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "verify sampling: %s", hipGetErrorString(e));
   return DFLASH_OK;

@@ -144,8 +144,10 @@ struct VerifyParams {
   int* ctx_len;
 };
 
-// Largest vocabulary the sampling kernels take (their per-row segment sums live in LDS).
+// Largest vocabulary the sampling kernels take (a slice's segment sums live in LDS),
+// and the slices a row is cut into for its reductions.
 constexpr int kSampleVocabMax = 262144;
+constexpr int kSlices = 32;
 
 // Draws from tempered softmax rows: token_out[r] ~ softmax(logits[r] / T) by inverse
 // CDF with uniform u[r]; prob_out (nullable) gets the drawn token's probability.
@@ -157,19 +159,21 @@ struct SampleParams {
   const float* u;
   int* token_out;
   float* prob_out;
+  double* slice_stats;  // workspace [rows][kSlices][2]: each slice's (max, weight sum)
 };
 
-// Speculative-sampling acceptance (one workgroup a stream). Rows of draft_logits
-// [S, B-1] and target_logits [S, B] share the stride ld; their (max, total weight)
-// come from k_row_stats.
+// Speculative-sampling acceptance. Rows of draft_logits [S, B-1] and target_logits
+// [S, B] share the stride ld.
 struct SpecVerifyParams {
   int S, B, V;
   int64_t ld;
   const int* draft;
   const float* draft_logits;
   const float* target_logits;
-  const double* draft_stats;    // [S * (B - 1)][2]
-  const double* target_stats;   // [S * B][2]
+  double* draft_stats;          // workspace [S * (B - 1)][kSlices][2]
+  double* target_stats;         // workspace [S * B][kSlices][2]
+  double* row_info;             // workspace [S][4]: target row a (max, total), draft row a (max, total)
+  double* slice_sums;           // workspace [S][kSlices][2]: residual and target sums of each slice
   float scale;                  // log2(e) / T
   const float* u_accept;        // [S, B - 1]
   const float* u_sample;        // [S]
@@ -249,8 +253,8 @@ hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st);
 hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st);
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
 hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st);
-hipError_t launch_row_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
-                            hipStream_t st);
+hipError_t launch_slice_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
+                              hipStream_t st);
 hipError_t launch_sample_rows(const SampleParams& p, hipStream_t st);
 hipError_t launch_verify_sampling(const SpecVerifyParams& p, hipStream_t st);
 

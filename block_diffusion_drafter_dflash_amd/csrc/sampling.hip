@@ -2,57 +2,42 @@
 // draws from tempered softmax rows, and speculative-sampling acceptance of a drafted
 // block with the residual max(p_target - p_draft, 0) at the first rejection.
 //
-// A row of V logits is handled by one workgroup of kRowThreads threads. The weight of
-// id k is w_k = exp2((l_k - max) * log2(e) / T) in fp32 (for the residual, the
-// difference of two normalised weights, in float64). Ids are cut into segments of
-// kSeg consecutive ids; each wave sums batches of kBatch consecutive segments, all
-// their loads in flight at once (lane l reads ids l, l + 64, ..., so every load is one
-// contiguous 256-byte run), in float64, and the segment sums are kept in LDS. A draw with uniform u scans the segment sums in id
-// order, picks the segment where the running total first exceeds u times the row
-// total, and one wave scans that segment's ids in order: the smallest id whose
-// running sum exceeds the target, never an id of zero weight. Every reduction has a
-// fixed order, so results are deterministic.
+// A row of V logits is cut into kSlices slices of whole segments (kSeg consecutive
+// ids). The weight of id k is exp2((l_k - max) * log2(e) / T) in fp32; sums are
+// float64. A first kernel gives every (row, slice) its max and its weight sum
+// relative to that max, one workgroup each, so that a row's reductions spread over
+// many CUs. A row's total is the slices' sums rescaled to the row max and added in
+// slice order. A draw with uniform u takes the first slice whose running total
+// exceeds u times the row total; inside it one workgroup sums the slice's segments
+// (each wave a batch of consecutive segments, every load in flight, lane l reading
+// ids l, l + 64, ...: contiguous 256-byte runs), scans the segment sums, binary-
+// searches them and scans one segment with a wave: the smallest id whose running
+// sum exceeds the target, never an id of zero weight (rounding that leaves the
+// crossing past a slice or segment falls back to its last id of positive weight).
+// Every reduction has a fixed order, so results are deterministic.
 #include "common.hpp"
 #include "kernels.h"
 
 namespace dfl {
 
-constexpr int kRowThreads = 1024;
-constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kSegPer = 4;                     // wave loads a segment
-constexpr int kSeg = kSegPer * kWave;          // ids a segment
-constexpr int kMaxSegs = kSampleVocabMax / kSeg;
+constexpr int kDrawThreads = 1024;                 // the draw: one workgroup a row
+constexpr int kDrawWaves = kDrawThreads / kWave;
+constexpr int kSliceThreads = 256;                 // the per-slice kernels
+constexpr int kSegPer = 4;                         // wave loads a segment
+constexpr int kSeg = kSegPer * kWave;              // ids a segment
+constexpr int kBatch = 8;                          // loads in flight a thread
+constexpr int kMaxSliceSegs = (kSampleVocabMax / kSlices + kSeg - 1) / kSeg;
 
 namespace {
 
-// Workgroup maximum of one float per thread (every thread gets it).
-__device__ __forceinline__ float block_max(float v, float* sh) {
-  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-  for (int i = 1; i < kRowWaves; ++i) r = fmaxf(r, sh[i]);
-  return r;
-}
-
-// Loads of a strided pass go in batches of kBatch per thread, all in flight at once.
-constexpr int kBatch = 8;
-
-__device__ __forceinline__ float row_max(const float* row, int V, float* sh) {
-  float m = -INFINITY;
-  for (int k0 = threadIdx.x; k0 < V; k0 += kBatch * kRowThreads) {
-    float x[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int k = k0 + b * kRowThreads;
-      x[b] = k < V ? row[k] : -INFINITY;
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) m = fmaxf(m, x[b]);
-  }
-  return block_max(m, sh);
+// Slice s of a row of V ids: [lo, hi), whole segments (the last slices may be empty).
+struct Slice {
+  int lo, hi;
+};
+__device__ __forceinline__ Slice slice_of(int V, int s) {
+  const int per = ((V + kSlices - 1) / kSlices + kSeg - 1) / kSeg * kSeg;
+  const int lo = min(s * per, V);
+  return {lo, min(lo + per, V)};
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -60,22 +45,100 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Segment sums of the weights w(k) (0 past V) into seg[0 .. n_seg), then, in place,
-// their exclusive prefix in id order; returns the row total (every thread).
+// Workgroup max / sum (every thread gets the result).
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, sh[i]);
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int i = 0; i < NW; ++i) r += sh[i];
+  return r;
+}
+
+// Sum over ids [lo, hi) of w(k), strided over the workgroup, kBatch loads in flight.
+template <int NT, typename Wf>
+__device__ __forceinline__ double strided_sum(const Wf& w, int lo, int hi) {
+  double x = 0.0;
+  for (int k0 = lo + threadIdx.x; k0 < hi; k0 += kBatch * NT) {
+    double v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int k = k0 + b * NT;
+      v[b] = k < hi ? w(k) : 0.0;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) x += v[b];
+  }
+  return x;
+}
+
+// A row's (max, total) from its slices' (max, sum): the total rescales each slice's
+// sum to the row max (exp2 in fp32) and adds them in slice order. y[s] gets the
+// rescaled slice sums when y is given.
+__device__ __forceinline__ void combine_slices(const double* st, float scale, float& M, double& total, double* y) {
+  float m = -INFINITY;
+  for (int s = 0; s < kSlices; ++s) m = fmaxf(m, (float)st[2 * s]);
+  double t = 0.0;
+  for (int s = 0; s < kSlices; ++s) {
+    const float ms = (float)st[2 * s];
+    const double v = ms == -INFINITY ? 0.0 : st[2 * s + 1] * (double)exp2f((ms - m) * scale);
+    if (y) y[s] = v;
+    t += v;
+  }
+  M = m;
+  total = t;
+}
+
+// The first slice whose running total exceeds target (the last slice of positive
+// sum when rounding leaves none); base gets the running total before it.
+__device__ __forceinline__ int pick_slice(const double* y, double target, double& base) {
+  double run = 0.0;
+  int last = -1;
+  double last_base = 0.0;
+  for (int s = 0; s < kSlices; ++s) {
+    if (y[s] > 0.0) {
+      if (run + y[s] > target) {
+        base = run;
+        return s;
+      }
+      last = s;
+      last_base = run;
+    }
+    run += y[s];
+  }
+  base = last_base;
+  return last;
+}
+
+// The draw inside ids [lo, hi) (one workgroup of kDrawThreads): the smallest id whose
+// running sum of w exceeds target (relative to lo), falling back to the range's last
+// id of positive weight. seg: LDS for the range's segment sums. Returns the id on
+// every thread.
 template <typename Wf>
-__device__ double segment_prefix(const Wf& w, int V, double* seg, double* sh) {
-  const int n_seg = (V + kSeg - 1) / kSeg;
+__device__ int draw_in_range(const Wf& w, int lo, int hi, double target, double* seg, int* sh_tok) {
+  const int n_seg = (hi - lo + kSeg - 1) / kSeg;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // wave wv sums segments wv * kBatch .. + kBatch - 1, then the next kRowWaves * kBatch
-  for (int sg0 = wv * kBatch; sg0 < n_seg; sg0 += kRowWaves * kBatch) {
+  for (int sg0 = wv * kBatch; sg0 < n_seg; sg0 += kDrawWaves * kBatch) {
     double x[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       x[b] = 0.0;
 #pragma unroll
       for (int i = 0; i < kSegPer; ++i) {
-        const int k = (sg0 + b) * kSeg + i * kWave + lane;
-        if (k < V) x[b] += w(k);
+        const int k = lo + (sg0 + b) * kSeg + i * kWave + lane;
+        if (k < hi) x[b] += w(k);
       }
     }
 #pragma unroll
@@ -88,62 +151,32 @@ __device__ double segment_prefix(const Wf& w, int V, double* seg, double* sh) {
         if (sg0 + b < n_seg) seg[sg0 + b] = x[b];
   }
   __syncthreads();
-  // exclusive prefix: thread t owns segments [t * per, (t + 1) * per)
-  const int per = (n_seg + kRowThreads - 1) / kRowThreads;
-  const int s0 = min((int)threadIdx.x * per, n_seg), s1 = min(s0 + per, n_seg);
-  double own = 0.0;
-  for (int sg = s0; sg < s1; ++sg) own += seg[sg];
-  double incl = own;
-  for (int m = 1; m < kWave; m <<= 1) {
-    const double o = __shfl_up(incl, m, kWave);
-    if (lane >= m) incl += o;
-  }
-  if (lane == kWave - 1) sh[wv] = incl;
-  __syncthreads();
-  double base = 0.0, total = 0.0;
-  for (int i = 0; i < kRowWaves; ++i) {
-    if (i < wv) base += sh[i];
-    total += sh[i];
-  }
-  double run = base + incl - own;
-  __syncthreads();   // every segment sum is read before it is overwritten
-  for (int sg = s0; sg < s1; ++sg) {
-    const double x = seg[sg];
-    seg[sg] = run;
-    run += x;
-  }
-  __syncthreads();
-  return total;
-}
-
-// The draw with uniform u over the weights whose segment prefixes segment_prefix left
-// in seg (total: the row total). Returns the id on every thread.
-template <typename Wf>
-__device__ int segment_draw(const Wf& w, int V, const double* seg, double total, double u, int* sh_tok) {
-  const int n_seg = (V + kSeg - 1) / kSeg;
-  const double target = u * total;
   if (threadIdx.x == 0) {
-    // the last segment whose prefix is <= target (segments of zero mass share the
-    // prefix of the next one and are skipped by taking the last)
-    int lo = 0, hi = n_seg - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seg[mid] <= target) lo = mid;
-      else hi = mid - 1;
+    // exclusive prefix in place, then the last segment whose prefix is <= target
+    double run = 0.0;
+    for (int sg = 0; sg < n_seg; ++sg) {
+      const double v = seg[sg];
+      seg[sg] = run;
+      run += v;
     }
-    *sh_tok = lo;
+    int a = 0, b = n_seg - 1;
+    while (a < b) {
+      const int mid = (a + b + 1) >> 1;
+      if (seg[mid] <= target) a = mid;
+      else b = mid - 1;
+    }
+    *sh_tok = a;
   }
   __syncthreads();
   const int sg = *sh_tok;
   __syncthreads();
   if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
     double run = seg[sg];
     int tok = -1, last = -1;
 #pragma unroll
     for (int i = 0; i < kSegPer; ++i) {
-      const int k = sg * kSeg + i * kWave + lane;
-      const double x = k < V ? w(k) : 0.0;
+      const int k = lo + sg * kSeg + i * kWave + lane;
+      const double x = k < hi ? w(k) : 0.0;
       double incl = x;
       for (int m = 1; m < kWave; m <<= 1) {
         const double o = __shfl_up(incl, m, kWave);
@@ -151,27 +184,24 @@ __device__ int segment_draw(const Wf& w, int V, const double* seg, double total,
       }
       const unsigned long long hit = __ballot(x > 0.0 && run + incl > target);
       const unsigned long long pos = __ballot(x > 0.0);
-      if (tok < 0 && hit) tok = sg * kSeg + i * kWave + __builtin_ctzll(hit);
-      if (pos) last = sg * kSeg + i * kWave + 63 - __builtin_clzll(pos);
+      if (tok < 0 && hit) tok = lo + sg * kSeg + i * kWave + __builtin_ctzll(hit);
+      if (pos) last = lo + sg * kSeg + i * kWave + 63 - __builtin_clzll(pos);
       run += __shfl(incl, kWave - 1, kWave);
     }
-    // rounding left the crossing past this segment: its last id of positive weight
     if (lane == 0) *sh_tok = tok >= 0 ? tok : last;
   }
   __syncthreads();
   int tok = *sh_tok;
   if (tok < 0) {
-    // a segment without mass (target at or past the total): the row's last id of
-    // positive weight
+    // the chosen segment has no mass: the range's last id of positive weight
     __syncthreads();
     if (threadIdx.x == 0) {
       int t = -1;
-      for (int s = n_seg - 1; s >= 0 && t < 0; --s)
-        for (int k = min(V, (s + 1) * kSeg) - 1; k >= s * kSeg; --k)
-          if (w(k) > 0.0) {
-            t = k;
-            break;
-          }
+      for (int k = hi - 1; k >= lo; --k)
+        if (w(k) > 0.0) {
+          t = k;
+          break;
+        }
       *sh_tok = t;
     }
     __syncthreads();
@@ -182,132 +212,205 @@ __device__ int segment_draw(const Wf& w, int V, const double* seg, double total,
 
 }  // namespace
 
-// One tempered softmax row: (max, total weight) as two doubles.
-__global__ __launch_bounds__(kRowThreads) void k_row_stats(const float* logits, int V, int64_t ld, float scale,
-                                                           double* stats) {
-  __shared__ float shf[kRowWaves];
-  __shared__ double shd[kRowWaves];
-  const float* row = logits + (int64_t)blockIdx.x * ld;
-  const float m = row_max(row, V, shf);
-  double x = 0.0;
-  for (int k0 = threadIdx.x; k0 < V; k0 += kBatch * kRowThreads) {
+// (max, weight sum relative to that max) of slice blockIdx.x of row blockIdx.y.
+__global__ __launch_bounds__(kSliceThreads) void k_slice_stats(const float* logits, int V, int64_t ld, float scale,
+                                                               double* stats) {
+  __shared__ float shf[kSliceThreads / kWave];
+  __shared__ double shd[kSliceThreads / kWave];
+  const float* row = logits + (int64_t)blockIdx.y * ld;
+  const Slice sl = slice_of(V, blockIdx.x);
+  float m = -INFINITY;
+  for (int k0 = sl.lo + threadIdx.x; k0 < sl.hi; k0 += kBatch * kSliceThreads) {
     float v[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const int k = k0 + b * kRowThreads;
-      v[b] = k < V ? row[k] : -INFINITY;
+      const int k = k0 + b * kSliceThreads;
+      v[b] = k < sl.hi ? row[k] : -INFINITY;
     }
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) x += (double)exp2f((v[b] - m) * scale);
+    for (int b = 0; b < kBatch; ++b) m = fmaxf(m, v[b]);
   }
-  x = wave_sum(x);
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) shd[wv] = x;
-  __syncthreads();
+  m = block_max<kSliceThreads / kWave>(m, shf);
+  double z = 0.0;
+  if (m != -INFINITY)   // uniform: every thread holds the slice max
+    z = block_sum<kSliceThreads / kWave>(
+        strided_sum<kSliceThreads>([&](int k) { return (double)exp2f((row[k] - m) * scale); }, sl.lo, sl.hi), shd);
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int i = 0; i < kRowWaves; ++i) t += shd[i];
-    stats[2 * blockIdx.x] = (double)m;
-    stats[2 * blockIdx.x + 1] = t;
+    double* o = stats + ((int64_t)blockIdx.y * kSlices + blockIdx.x) * 2;
+    o[0] = (double)m;
+    o[1] = z;
   }
 }
 
 // One draw per row from softmax(row / T) with uniform u[row].
-__global__ __launch_bounds__(kRowThreads) void k_sample_rows(const SampleParams p) {
-  __shared__ float shf[kRowWaves];
-  __shared__ double shd[kRowWaves];
-  __shared__ double seg[kMaxSegs];
-  __shared__ int sh_tok;
+__global__ __launch_bounds__(kDrawThreads) void k_sample_rows(const SampleParams p) {
+  __shared__ double seg[kMaxSliceSegs];
+  __shared__ double y[kSlices];
+  __shared__ float sh_m;
+  __shared__ double sh_total, sh_base;
+  __shared__ int sh_slice, sh_tok;
   const float* row = p.logits + (int64_t)blockIdx.x * p.ld;
-  const float m = row_max(row, p.V, shf);
+  const double* st = p.slice_stats + (int64_t)blockIdx.x * kSlices * 2;
+  const double u = (double)p.u[blockIdx.x];
+  if (threadIdx.x == 0) {
+    float M;
+    double total, base;
+    combine_slices(st, p.scale, M, total, y);
+    sh_slice = pick_slice(y, u * total, base);
+    sh_m = M;
+    sh_total = total;
+    sh_base = base;
+  }
+  __syncthreads();
+  const float M = sh_m;
+  const double total = sh_total;
   const float sc = p.scale;
-  auto w = [&](int k) { return (double)exp2f((row[k] - m) * sc); };
-  const double total = segment_prefix(w, p.V, seg, shd);
-  const int tok = segment_draw(w, p.V, seg, total, (double)p.u[blockIdx.x], &sh_tok);
+  auto w = [&](int k) { return (double)exp2f((row[k] - M) * sc); };
+  const Slice sl = slice_of(p.V, sh_slice);
+  const int tok = draw_in_range(w, sl.lo, sl.hi, u * total - sh_base, seg, &sh_tok);
   if (threadIdx.x == 0) {
     p.token_out[blockIdx.x] = tok;
     if (p.prob_out) p.prob_out[blockIdx.x] = (float)(w(tok) / total);
   }
 }
 
-// Speculative-sampling acceptance of one stream's drafted block (one workgroup).
-__global__ __launch_bounds__(kRowThreads) void k_verify_sampling(const SpecVerifyParams p) {
-  __shared__ double shd[kRowWaves];
-  __shared__ double seg[kMaxSegs];
-  __shared__ int sh_tok, sh_a;
+// Speculative-sampling acceptance walk (one thread a stream): the accepted length
+// and, for the draw that follows, the row max and total of the target row a and (on
+// a rejection) of the draft row a.
+__global__ __launch_bounds__(kWave) void k_spec_accept(const SpecVerifyParams p) {
   const int s = blockIdx.x, B = p.B, V = p.V;
+  if (threadIdx.x != 0) return;
   const float sc = p.scale;
   const int* d = p.draft + (int64_t)s * (B - 1);
-  const float* dl = p.draft_logits + (int64_t)s * (B - 1) * p.ld;
-  const float* tl = p.target_logits + (int64_t)s * B * p.ld;
-  const double* ds = p.draft_stats + (int64_t)s * (B - 1) * 2;
-  const double* ts = p.target_stats + (int64_t)s * B * 2;
+  int a = 0;
+  float tm = 0.f, dm = 0.f;
+  double tz = 1.0, dz = 1.0;
+  while (true) {
+    combine_slices(p.target_stats + ((int64_t)s * B + a) * kSlices * 2, sc, tm, tz, nullptr);
+    if (a == B - 1) break;
+    combine_slices(p.draft_stats + ((int64_t)s * (B - 1) + a) * kSlices * 2, sc, dm, dz, nullptr);
+    const int tok = d[a];
+    if (tok < 0 || tok >= V) break;   // an id outside the vocabulary is rejected
+    const float* drow = p.draft_logits + ((int64_t)s * (B - 1) + a) * p.ld;
+    const float* trow = p.target_logits + ((int64_t)s * B + a) * p.ld;
+    const double pd = (double)exp2f((drow[tok] - dm) * sc) / dz;
+    const double pt = (double)exp2f((trow[tok] - tm) * sc) / tz;
+    if (!((double)p.u_accept[(int64_t)s * (B - 1) + a] * pd < pt)) break;
+    ++a;
+  }
+  p.accept[s] = a;
+  double* r = p.row_info + (int64_t)s * 4;
+  r[0] = tm;
+  r[1] = tz;
+  r[2] = dm;
+  r[3] = dz;
+}
 
-  // accepted length: d_{j+1} is kept while u * p_draft(d) < p_target(d)
+// Per (slice, stream): the slice's sums of the residual max(q - p, 0) at the rejected
+// position and of q itself (q alone after a full acceptance, at row B - 1).
+__global__ __launch_bounds__(kSliceThreads) void k_spec_slices(const SpecVerifyParams p) {
+  __shared__ double shd[kSliceThreads / kWave];
+  const int s = blockIdx.y, B = p.B;
+  const int a = p.accept[s];
+  const double* ri = p.row_info + (int64_t)s * 4;
+  const float tm = (float)ri[0], dm = (float)ri[2];
+  const double tz = ri[1], dz = ri[3];
+  const float sc = p.scale;
+  const float* trow = p.target_logits + ((int64_t)s * B + a) * p.ld;
+  const Slice sl = slice_of(p.V, blockIdx.x);
+  auto wt = [&](int k) { return (double)exp2f((trow[k] - tm) * sc) / tz; };
+  double rsum = 0.0;
+  if (a < B - 1) {   // uniform over the workgroup
+    const float* drow = p.draft_logits + ((int64_t)s * (B - 1) + a) * p.ld;
+    auto wr = [&](int k) {
+      const double v = wt(k) - (double)exp2f((drow[k] - dm) * sc) / dz;
+      return v > 0.0 ? v : 0.0;
+    };
+    rsum = block_sum<kSliceThreads / kWave>(strided_sum<kSliceThreads>(wr, sl.lo, sl.hi), shd);
+  }
+  const double qsum = block_sum<kSliceThreads / kWave>(strided_sum<kSliceThreads>(wt, sl.lo, sl.hi), shd);
   if (threadIdx.x == 0) {
-    int a = 0;
-    while (a < B - 1) {
-      const int tok = d[a];
-      if (tok < 0 || tok >= V) break;   // an id outside the vocabulary is rejected
-      const float* drow = dl + (int64_t)a * p.ld;
-      const float* trow = tl + (int64_t)a * p.ld;
-      const double pd = (double)exp2f((drow[tok] - (float)ds[2 * a]) * sc) / ds[2 * a + 1];
-      const double pt = (double)exp2f((trow[tok] - (float)ts[2 * a]) * sc) / ts[2 * a + 1];
-      if (!((double)p.u_accept[(int64_t)s * (B - 1) + a] * pd < pt)) break;
-      ++a;
+    double* o = p.slice_sums + ((int64_t)s * kSlices + blockIdx.x) * 2;
+    o[0] = rsum;
+    o[1] = qsum;
+  }
+}
+
+// The draw that ends the stream's block (one workgroup a stream), and the outputs.
+__global__ __launch_bounds__(kDrawThreads) void k_spec_draw(const SpecVerifyParams p) {
+  __shared__ double seg[kMaxSliceSegs];
+  __shared__ double y[kSlices];
+  __shared__ double sh_target;
+  __shared__ int sh_slice, sh_resid, sh_tok;
+  const int s = blockIdx.x, B = p.B;
+  const int a = p.accept[s];
+  const double* ri = p.row_info + (int64_t)s * 4;
+  const float tm = (float)ri[0], dm = (float)ri[2];
+  const double tz = ri[1], dz = ri[3];
+  const float sc = p.scale;
+  const double u = (double)p.u_sample[s];
+  if (threadIdx.x == 0) {
+    const double* ss = p.slice_sums + (int64_t)s * kSlices * 2;
+    double rt = 0.0;
+    for (int i = 0; i < kSlices; ++i) rt += ss[2 * i];
+    const int resid = a < B - 1 && rt > 0.0;   // else the target's own distribution
+    double total = 0.0;
+    for (int i = 0; i < kSlices; ++i) {
+      y[i] = ss[2 * i + (resid ? 0 : 1)];
+      total += y[i];
     }
-    sh_a = a;
+    double base;
+    sh_slice = pick_slice(y, u * total, base);
+    sh_target = u * total - base;
+    sh_resid = resid;
   }
   __syncthreads();
-  const int a = sh_a;
-  const double u = (double)p.u_sample[s];
-  const float* trow = tl + (int64_t)a * p.ld;
-  const float tm = (float)ts[2 * a];
-  const double tz = ts[2 * a + 1];
+  const float* trow = p.target_logits + ((int64_t)s * B + a) * p.ld;
   auto wt = [&](int k) { return (double)exp2f((trow[k] - tm) * sc) / tz; };
-  int tok = -1;
-  bool from_target = a == B - 1;
-  if (!from_target) {
-    // residual max(q - p, 0) at the rejected position; q itself if it has no mass
-    const float* drow = dl + (int64_t)a * p.ld;
-    const float dm = (float)ds[2 * a];
-    const double dz = ds[2 * a + 1];
+  const Slice sl = slice_of(p.V, sh_slice);
+  int tok;
+  if (sh_resid) {
+    const float* drow = p.draft_logits + ((int64_t)s * (B - 1) + a) * p.ld;
     auto wr = [&](int k) {
-      const double r = wt(k) - (double)exp2f((drow[k] - dm) * sc) / dz;
-      return r > 0.0 ? r : 0.0;
+      const double v = wt(k) - (double)exp2f((drow[k] - dm) * sc) / dz;
+      return v > 0.0 ? v : 0.0;
     };
-    const double total = segment_prefix(wr, V, seg, shd);
-    if (total > 0.0) tok = segment_draw(wr, V, seg, total, u, &sh_tok);
-    else from_target = true;
+    tok = draw_in_range(wr, sl.lo, sl.hi, sh_target, seg, &sh_tok);
+  } else {
+    tok = draw_in_range(wt, sl.lo, sl.hi, sh_target, seg, &sh_tok);
   }
-  if (from_target) {
-    const double total = segment_prefix(wt, V, seg, shd);
-    tok = segment_draw(wt, V, seg, total, u, &sh_tok);
-  }
+  const int* d = p.draft + (int64_t)s * (B - 1);
   if ((int)threadIdx.x < B) {
     const int j = threadIdx.x;
     p.committed[(int64_t)s * B + j] = j < a ? d[j] : (j == a ? tok : -1);
   }
   if (threadIdx.x == 0) {
-    p.accept[s] = a;
     p.token[s] = tok;
     if (p.ctx_len) p.ctx_len[s] += a + 1;
   }
 }
 
-hipError_t launch_row_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
-                            hipStream_t st) {
-  (void)launch_k(k_row_stats, dim3(rows), dim3(kRowThreads), st, logits, V, ld, scale, stats);
+hipError_t launch_slice_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
+                              hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  (void)launch_k(k_slice_stats, dim3(kSlices, rows), dim3(kSliceThreads), st, logits, V, ld, scale, stats);
   return hipGetLastError();
 }
 
 hipError_t launch_sample_rows(const SampleParams& p, hipStream_t st) {
-  (void)launch_k(k_sample_rows, dim3(p.rows), dim3(kRowThreads), st, p);
+  hipError_t e = launch_slice_stats(p.logits, p.rows, p.V, p.ld, p.scale, p.slice_stats, st);
+  if (e != hipSuccess) return e;
+  (void)launch_k(k_sample_rows, dim3(p.rows), dim3(kDrawThreads), st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_verify_sampling(const SpecVerifyParams& p, hipStream_t st) {
-  (void)launch_k(k_verify_sampling, dim3(p.S), dim3(kRowThreads), st, p);
+  hipError_t e = launch_slice_stats(p.draft_logits, p.S * (p.B - 1), p.V, p.ld, p.scale, p.draft_stats, st);
+  if (e == hipSuccess) e = launch_slice_stats(p.target_logits, p.S * p.B, p.V, p.ld, p.scale, p.target_stats, st);
+  if (e != hipSuccess) return e;
+  (void)launch_k(k_spec_accept, dim3(p.S), dim3(kWave), st, p);
+  (void)launch_k(k_spec_slices, dim3(kSlices, p.S), dim3(kSliceThreads), st, p);
+  (void)launch_k(k_spec_draw, dim3(p.S), dim3(kDrawThreads), st, p);
   return hipGetLastError();
 }
 

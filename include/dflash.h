@@ -241,13 +241,16 @@ int dflash_verify_greedy(dflash *h, int32_t n_streams, const int32_t *draft,
  *   u:         device float [n_rows];
  *   token_out: device int32 [n_rows];
  *   prob_out:  NULL, or device float [n_rows]: the drawn token's probability.
+ *   ws:        a workspace initialised with dflash_workspace_init whose
+ *              dflash_workspace_bytes covered n_rows (max_rows, or n_streams * block_size,
+ *              at least n_rows); it holds each row's per-slice max and weight sum.
  * temperature must be positive and finite; vocab at most 262144 (DFLASH_ERR_CONFIG
  * otherwise). n_rows == 0 is a no-op. Probabilities are fp32 exponentials summed in
  * float64. Works without bound weights.
  */
 int dflash_sample_rows(dflash *h, int32_t n_rows, const float *logits, int64_t row_stride,
                        float temperature, const float *u, int32_t *token_out, float *prob_out,
-                       void *stream);
+                       void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Speculative-sampling verify (DFlash explainer section 4, "Sampling decoding": the
@@ -267,7 +270,8 @@ int dflash_sample_rows(dflash *h, int32_t n_rows, const float *logits, int64_t r
  *   ctx_len_inout[s] += a + 1 when ctx_len_inout is not NULL.
  * u_accept: device float [n_streams, B-1]; u_sample: device float [n_streams]; all
  * uniforms in [0, 1). ws: a workspace initialised with dflash_workspace_init for at
- * least n_streams streams (it holds each row's max and total weight). temperature must
+ * least n_streams streams (it holds every row's per-slice max and weight sum and the
+ * draw's per-slice sums). temperature must
  * be positive and finite; vocab at most 262144. Works without bound weights.
  */
 int dflash_verify_sampling(dflash *h, int32_t n_streams, const int32_t *draft,

@@ -48,6 +48,7 @@ def check_draw(tok, probs, u, what):
 def test_sample_rows_parity(vocab, T):
     dr, _ = drafter(vocab)
     rows = 37
+    ws = dr.new_workspace(rows, 1, 64)
     g = torch.Generator(device="cuda").manual_seed(vocab + int(T * 100))
     logits = torch.randn((rows, vocab), generator=g, device="cuda", dtype=torch.float32) * 3.0
     logits[5, ::3] = float("-inf")          # a row with masked ids
@@ -56,7 +57,7 @@ def test_sample_rows_parity(vocab, T):
     tok = torch.zeros(rows, dtype=torch.int32, device="cuda")
     prob = torch.zeros(rows, dtype=torch.float32, device="cuda")
     log(f"[sample_rows] V={vocab} T={T} rows={rows}")
-    dr.dflash_sample_rows(logits, T, u, tok, prob)
+    dr.dflash_sample_rows(logits, T, u, tok, ws, prob_out=prob)
     torch.cuda.synchronize()
     L, U, K, P = logits.cpu().numpy().astype(np.float64), u.cpu().numpy(), tok.cpu().numpy(), prob.cpu().numpy()
     near = 0
@@ -68,7 +69,7 @@ def test_sample_rows_parity(vocab, T):
     log(f"  near-boundary draws: {near}")
     # deterministic
     tok2 = torch.zeros_like(tok)
-    dr.dflash_sample_rows(logits, T, u, tok2)
+    dr.dflash_sample_rows(logits, T, u, tok2, ws)
     torch.cuda.synchronize()
     assert torch.equal(tok, tok2)
 
@@ -120,7 +121,7 @@ def test_verify_sampling_parity(vocab, S, T):
     dlog = (tlog[:, :B - 1] + 0.6 * torch.randn((S, B - 1, vocab), generator=g, device="cuda")).contiguous()
     u_draw = torch.rand((S * (B - 1),), generator=g, device="cuda")
     draft = torch.zeros(S * (B - 1), dtype=torch.int32, device="cuda")
-    dr.dflash_sample_rows(dlog.view(S * (B - 1), vocab), T, u_draw, draft)
+    dr.dflash_sample_rows(dlog.view(S * (B - 1), vocab), T, u_draw, draft, ws)
     draft = draft.view(S, B - 1)
     ua = torch.rand((S, B - 1), generator=g, device="cuda")
     us = torch.rand(S, generator=g, device="cuda")
@@ -174,11 +175,11 @@ def test_sampling_calls_refuse_bad_arguments():
     t = torch.zeros(2, dtype=torch.int32, device="cuda")
     for T in (0.0, -1.0, float("inf"), float("nan")):
         with pytest.raises(D.DFlashError):
-            dr.dflash_sample_rows(x, T, u, t)
+            dr.dflash_sample_rows(x, T, u, t, ws)
     narrow = torch.zeros((2, 500), device="cuda")
     with pytest.raises(D.DFlashError):
-        dr.dflash_sample_rows(narrow, 1.0, u, t)    # row stride below the vocabulary
+        dr.dflash_sample_rows(narrow, 1.0, u, t, ws)    # row stride below the vocabulary
     big, _ = drafter(262144 + 256, block=8)        # past the kernels' vocabulary bound (host refusal)
     wide = torch.zeros((2, 262144 + 256), device="cuda")
     with pytest.raises(D.DFlashError):
-        big.dflash_sample_rows(wide, 1.0, u, t)
+        big.dflash_sample_rows(wide, 1.0, u, t, ws)
