@@ -94,10 +94,10 @@ struct GemmPlan {
 };
 
 // Rows are processed in groups of 16 * mt (mt = 1, 2 or 4), or by the tiled kernel
-// when the batch is wide. The tiling of N, the K ranges and the wave split of each
-// range depend only on the weight's shape, so a row's arithmetic depends on M only
-// through the batch's class.
-GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, bool wide) {
+// when `tiled` (bf16 batches of kTallMinRows rows or more). The tiling of N, the K
+// ranges and the wave split of each range depend only on the weight's shape, so a
+// row's arithmetic depends on M only through the batch's class.
+GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, bool tiled) {
   GemmPlan g;
   g.am = am;
   g.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -105,7 +105,7 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
   const int cols = gemm_tile_cols(epi);
   g.n_tiles = (N + cols - 1) / cols;
   g.iters = K / gemm_k_per_iter(dtype, epi, am, K, tap_h);
-  g.tall = dtype == DFLASH_BF16 && wide;
+  g.tall = dtype == DFLASH_BF16 && tiled;
   g.ksplit = g.tall ? gemm_tall_ksplit(epi, N, K) : gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
   g.tail_from = 0;
@@ -132,7 +132,7 @@ int max_reach_pages(int max_ctx, int window) {
 
 AttnPlan plan_attn(const dflash_config& c, int S, int max_ctx, int window) {
   AttnPlan a;
-  a.wide = batch_is_wide(S * c.block_size) ? 1 : 0;
+  a.wide = attn_is_wide(S * c.block_size) ? 1 : 0;
   a.n_chunks = attention_chunks(max_reach_pages(max_ctx, window), a.wide);
   a.qt = attention_query_tiles(c.n_q_heads / c.n_kv_heads, c.block_size);
   const size_t sh = (size_t)S * c.n_kv_heads * a.n_chunks;
@@ -157,7 +157,7 @@ struct FuseLayout {
 FuseLayout layout_fuse(const dflash& h, int R) {
   FuseLayout L;
   const auto& c = h.cfg;
-  L.g = plan_gemm(c.dtype, EPI_RAW, A_TAPS, R, c.hidden, c.n_taps * c.hidden, c.hidden, batch_is_wide(R));
+  L.g = plan_gemm(c.dtype, EPI_RAW, A_TAPS, R, c.hidden, c.n_taps * c.hidden, c.hidden, gemm_is_tiled(R));
   Region r;
   r.take(kCounterInts * 4);
   L.y = r.take(L.g.part_bytes(R, c.hidden));
@@ -173,7 +173,7 @@ InjectLayout layout_inject(const dflash& h, int R) {
   InjectLayout L;
   const auto& c = h.cfg;
   const int N = c.n_layers * 2 * h.nkv();
-  L.g = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, R, N, c.hidden, 0, batch_is_wide(R));
+  L.g = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, R, N, c.hidden, 0, gemm_is_tiled(R));
   Region r;
   r.take(kCounterInts * 4);
   L.raw = r.take(L.g.part_bytes(R, N));
@@ -191,12 +191,12 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   const auto& c = h.cfg;
   const int M = S * c.block_size, Mm = S * (c.block_size - 1);
   const int es = h.esize();
-  const bool wide = batch_is_wide(M);   // the batch's class decides every path of the round
-  L.qkv = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, h.nq() + 2 * h.nkv(), c.hidden, 0, wide);
-  L.o = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, h.nq(), 0, wide);
-  L.gu = plan_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, M, 2 * c.intermediate, c.hidden, 0, wide);
-  L.down = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, c.intermediate, 0, wide);
-  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, Mm, c.vocab, c.hidden, 0, wide);
+  const bool tiled = gemm_is_tiled(M);   // the batch's class decides every GEMM path of the round
+  L.qkv = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, h.nq() + 2 * h.nkv(), c.hidden, 0, tiled);
+  L.o = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, h.nq(), 0, tiled);
+  L.gu = plan_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, M, 2 * c.intermediate, c.hidden, 0, tiled);
+  L.down = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, c.intermediate, 0, tiled);
+  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, Mm, c.vocab, c.hidden, 0, tiled);
   size_t po = 0, pml = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     L.attn.push_back(plan_attn(c, S, max_ctx, c.layer_window[l]));

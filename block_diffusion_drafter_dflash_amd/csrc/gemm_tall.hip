@@ -1,4 +1,4 @@
-// Tiled MFMA GEMM of the draft round for many rows (M > 64: batched streams), gfx950.
+// Tiled MFMA GEMM of the draft round for many rows (M > 32: batched streams), gfx950.
 //
 // Y[M, N] = A[M, K] . W[N, K]^T with the same epilogues and outputs as the skinny
 // kernel (float64 K-range partials, SwiGLU, LM-head logits and per-32-column top-2).
@@ -12,7 +12,9 @@
 // buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
 // object, so the compiler sees that copies into one never alias the fragment reads
 // of another. Every kFlushChunks chunks (256 products per element) the fp32 MFMA sums
-// are added into float64 accumulators. The summation order differs from the skinny
+// are added into float64 accumulators. Waves whose 64 rows lie past the batch (a batch
+// of 33..64 rows uses one of the four row groups) copy their share of the tiles but
+// skip the fragment reads and MFMAs; their results are never stored. The summation order differs from the skinny
 // kernel's (one K sweep per K range rather than eight wave slices), so a batch on this
 // path is not bitwise equal to the same streams drafted alone.
 //
@@ -210,7 +212,9 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0;
     }
 
+  const bool rows_live = 64 * wm < p.M - rt * BM;   // this wave's 64 rows hold any of the batch's
   auto compute = [&](int ch, const unsigned char* buf) {
+    if (!rows_live) return;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 af[4], bf[4];

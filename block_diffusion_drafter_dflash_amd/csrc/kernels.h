@@ -55,7 +55,7 @@ struct AttnParams {
   int S, B, n_q_heads, n_kv_heads, head_dim, group;
   int window;           // 0 = full
   int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages, wide)
-  int wide;             // 1: the batch is wide (batch_is_wide), chunks of up to 64 pages
+  int wide;             // 1: the batch is wide (attn_is_wide), chunks of up to 64 pages
   int max_ctx;
   const int* ctx_len;
   const void* q;        // [S*B, n_q*d] rotated, normalised queries
@@ -184,7 +184,7 @@ struct SpecVerifyParams {
 };
 
 // Context chunking, in pages of 16 keys, of one stream's reach: a function of that
-// reach and of the batch's class (see batch_is_wide), so a stream's result does not
+// reach and of the batch's class (see attn_is_wide), so a stream's result does not
 // depend on the other streams of a batch of its class. Narrow batches: up to 256
 // pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 2048 pages the chunk
 // count stays at 256 / kChunkPagesShort; beyond, chunks hold at most 64 pages. Wide
@@ -230,12 +230,19 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t st, Args
 
 int gemm_k_per_iter(int dtype, int epi, int am, int K, int tap_h);
 int gemm_ksplit(int epi, int n_tiles, int iters, int K);
-// Tiled GEMM for many rows (bf16, M > kTallMinRows): same parameters and outputs.
-constexpr int kTallMinRows = 65;
-// A batch of this many block rows (streams x block) is wide: its GEMMs take the tiled
-// kernel (bf16) and its attention the 64-page chunking. A stream's results are
-// bitwise the same in any batch of its class.
-inline bool batch_is_wide(int rows) { return rows >= kTallMinRows; }
+// Batch classes, fixed functions of a batch's block rows (streams x block); a stream's
+// results are bitwise the same in any batch of its class.
+//  - From kTallMinRows rows on, the GEMMs (bf16) take the tiled kernel (same
+//    parameters and outputs as the skinny one). The skinny kernel re-reads a work
+//    item's A rows for every 32-column tile, so its L2 traffic grows with the row
+//    groups; the tiled kernel copies each weight tile once for up to 256 rows and
+//    skips the MFMAs of 64-row groups past the batch.
+//  - From kAttnWideMinRows rows on, attention takes the 64-page chunking (enough
+//    streams fill the GPU by themselves); fewer rows keep the finer narrow chunking.
+constexpr int kTallMinRows = 33;
+constexpr int kAttnWideMinRows = 65;
+inline bool gemm_is_tiled(int rows) { return rows >= kTallMinRows; }
+inline bool attn_is_wide(int rows) { return rows >= kAttnWideMinRows; }
 int gemm_tall_ksplit(int epi, int N, int K);
 int gemm_tall_column_tiles(int epi, int N);
 constexpr int kTallRoundTiles = 256;   // column tiles of one round: one per CU

@@ -352,6 +352,12 @@ def test_round_parity_mid_ragged():
     run_case(RoundCase(MID), [0, 1, 2, 3])
 
 
+def test_round_parity_48_rows_partial_row_group():
+    # 3 streams x 16 = 48 rows: tiled GEMMs whose one live row group is part padding
+    p = small_variant(MID, name="mid3_bf16", n_streams=3, ctx_spec=[300, 1030, 77], seed=2006)
+    run_case(RoundCase(p), [0, 1, 2])
+
+
 def test_round_parity_mid_d64_two_row_groups():
     case = RoundCase(MID64)
     assert case.p.n_streams * case.p.block_size > 64      # more than one 64-row group
@@ -427,20 +433,25 @@ def test_run_to_run_bit_identity_and_reset_rerun():
     assert torch.equal(case.draft, d)
 
 
+# 2 streams x block 16 = 32 rows: a narrow batch (skinny GEMMs, narrow attention chunks),
+# whose streams draft exactly what they draft alone (16 rows, the same class).
+NARROW2 = small_variant(MID, name="narrow2_bf16", n_streams=2, ctx_spec=[300, 1030], seed=2005)
+
+
 def test_batched_equals_solo_bitwise():
-    case = RoundCase(MID)
+    case = RoundCase(NARROW2)
     case.run_gpu()
     batched = case.logits.clone()
-    for s in range(MID.n_streams):
+    for s in range(NARROW2.n_streams):
         kv1 = SimpleNamespace(struct=D.KV())
-        for l in range(MID.n_layers):
+        for l in range(NARROW2.n_layers):
             kv1.struct.k_pool[l] = case.kv.k[l].data_ptr()
             kv1.struct.v_pool[l] = case.kv.v[l].data_ptr()
         pt = case.kv.page_table[s:s + 1].contiguous()
         kv1.struct.page_table = pt.data_ptr()
         kv1.struct.pages_per_stream = case.kv.pages_per_stream
-        out = torch.zeros((1, MID.block_size - 1, MID.vocab), dtype=torch.float32, device="cuda")
-        dr = torch.zeros((1, MID.block_size - 1), dtype=torch.int32, device="cuda")
+        out = torch.zeros((1, NARROW2.block_size - 1, NARROW2.vocab), dtype=torch.float32, device="cuda")
+        dr = torch.zeros((1, NARROW2.block_size - 1), dtype=torch.int32, device="cuda")
         case.dr.dflash_draft_block(case.anchor[s:s + 1].contiguous(), case.ctx_len[s:s + 1].contiguous(),
                                    case.max_ctx, kv1, dr, case.ws, logits_out=out)
         torch.cuda.synchronize()
@@ -451,17 +462,19 @@ def test_batched_equals_solo_bitwise():
 WIDE = small_variant(MID, name="wide_bf16", n_streams=6, ctx_spec=[300, 77, 1030, 0, 513, 4100], seed=2003)
 
 
-def test_wide_batch_class_is_invariant_to_stream_order_bitwise():
-    # 6 streams x block 16 = 96 rows: a wide batch (tiled GEMMs, 64-page attention
-    # chunks). A stream's result is bitwise the same in any batch of its class; here
-    # the same streams drafted in reverse order.
-    case = RoundCase(WIDE)
+@pytest.mark.parametrize("preset", [MID, WIDE], ids=["64_rows", "96_rows"])
+def test_tiled_batch_classes_are_invariant_to_stream_order_bitwise(preset):
+    # 4 streams x block 16 = 64 rows (tiled GEMMs with one live row group, narrow
+    # attention chunks) and 6 x 16 = 96 rows (tiled GEMMs, 64-page attention chunks).
+    # A stream's result is bitwise the same in any batch of its class; here the same
+    # streams drafted in reverse order.
+    case = RoundCase(preset)
     case.run_gpu()
     batched, bdraft = case.logits.clone(), case.draft.clone()
-    S = WIDE.n_streams
+    S = preset.n_streams
     perm = list(reversed(range(S)))
     kv = SimpleNamespace(struct=D.KV())
-    for l in range(WIDE.n_layers):
+    for l in range(preset.n_layers):
         kv.struct.k_pool[l] = case.kv.k[l].data_ptr()
         kv.struct.v_pool[l] = case.kv.v[l].data_ptr()
     pt = case.kv.page_table[perm].contiguous()
