@@ -11,10 +11,10 @@
 // pieces so that fragment reads are free of bank conflicts) through a ring of three
 // buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
 // object, so the compiler sees that copies into one never alias the fragment reads
-// of another. Every kFlushChunks chunks (256 products per element) the fp32 MFMA sums
-// are added into float64 accumulators. Waves whose 64 rows lie past the batch (a batch
-// of 33..64 rows uses one of the four row groups) copy their share of the tiles but
-// skip the fragment reads and MFMAs; their results are never stored. The summation order differs from the skinny
+// of another. The MFMAs accumulate in fp32 over the whole K range (a K range's result
+// is stored as a float64 partial, as the skinny kernel's). Waves whose 64 rows lie past
+// the batch (a batch of 33..64 rows uses one of the four row groups) copy their share
+// of the tiles but skip the fragment reads and MFMAs; their results are never stored. The summation order differs from the skinny
 // kernel's (one K sweep per K range rather than eight wave slices), so a batch on this
 // path is not bitwise equal to the same streams drafted alone.
 //
@@ -32,7 +32,6 @@ constexpr int kWaves = 8, kTallThreads = 64 * kWaves;
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int WM = 4, WN = 2;                // waves along M and N: 64 x 64 each
 constexpr int kRing = 3;                     // chunk buffers
-constexpr int kFlushChunks = 4;
 constexpr int ROWB = BK * 2;                 // bytes of one tile row in LDS (bf16)
 constexpr int ATILE = BM * ROWB, WTILE = BN * ROWB;
 constexpr int NPC = ROWB / 16;               // 16-byte pieces per tile row
@@ -201,42 +200,36 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       boff[s][i] = ATILE + rb * ROWB + (((4 * s + lg) ^ swz(rb)) * 16);
     }
 
-  double acc[4][4][4];
-  floatx4 part[4][4];
+  floatx4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0;
-    }
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // A chunk's 16 fragments are read before its MFMAs; the schedule groups put the
+  // second k-step's reads behind the first four MFMAs, so they overlap.
   const bool rows_live = 64 * wm < p.M - rt * BM;   // this wave's 64 rows hold any of the batch's
-  auto compute = [&](int ch, const unsigned char* buf) {
+  auto compute = [&](const unsigned char* buf) {
     if (!rows_live) return;
+    uint4 af[KS][4], bf[KS][4];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      uint4 af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(buf + aoff[s][i]);
+      for (int i = 0; i < 4; ++i) af[s][i] = *reinterpret_cast<const uint4*>(buf + aoff[s][i]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(buf + boff[s][j]);
+      for (int j = 0; j < 4; ++j) bf[s][j] = *reinterpret_cast<const uint4*>(buf + boff[s][j]);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma_frag(part[i][j], af[i], bf[j], bf16_t());
-    }
-    if ((ch - kb) % kFlushChunks == kFlushChunks - 1 || ch + 1 == ke) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] += (double)part[i][j][e];
-          part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
+        for (int j = 0; j < 4; ++j) mma_frag(acc[i][j], af[s][i], bf[s][j], bf16_t());
+    static_assert(KS == 2, "the schedule groups below assume two k-steps a chunk");
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS reads of k-step 0
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS reads of k-step 1
+    __builtin_amdgcn_sched_group_barrier(0x008, 28, 0);   // the remaining MFMAs
   };
 
   // ---- pipeline over the ring: chunk c lives in buffer (c - kb) % kRing. Before
@@ -248,7 +241,7 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   auto step = [&](int ch, const unsigned char* cur, unsigned char* nxt) {
     ring_barrier<(kRing - 2) * LPW>();
     issue(min(ch + kRing - 1, ke - 1), nxt);
-    compute(ch, cur);
+    compute(cur);
   };
   if (kb < ke) {
     issue(kb, buf0);
@@ -275,7 +268,7 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = ct * BN + 64 * wn + 16 * j + lr;
-          if (rv && n < p.N) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = acc[i][j][e];
+          if (rv && n < p.N) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = (double)acc[i][j][e];
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
         // column 16 j + lr (j = 0, 1) is gate row 64 ct + 32 wn + 16 j + lr; j + 2 its up row
@@ -294,7 +287,7 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int n = ct * BN + 64 * wn + 32 * jg + 16 * jj + lr;
-            const float v = (float)acc[i][2 * jg + jj][e];
+            const float v = acc[i][2 * jg + jj][e];
             if (n < p.N) {
               if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
               tall_top_merge(v1, i1, v2, v, n, -INFINITY);
