@@ -90,7 +90,8 @@ struct GemmPlan {
   // Tiled SWIGLU whose last round of column tiles would be mostly idle: the tiled
   // kernel takes gate/up rows [0, tail_from), the skinny kernel the rest (0: no split).
   int tail_from;
-  size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * 8; }
+  // K-range partials: float64 from the skinny kernel, float32 from the tiled one
+  size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * (tall ? 4 : 8); }
 };
 
 // Rows are processed in groups of 16 * mt (mt = 1, 2 or 4), or by the tiled kernel
@@ -532,6 +533,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   rn.hidden = c.hidden;
   rn.ksplit = L.g.ksplit;
   rn.parts = p.y_out;
+  rn.parts_f32 = L.g.tall ? 1 : 0;   // the tiled kernel's partials are float32
   rn.gain = h->w.hidden_norm;
   rn.out = fused_out;
   rn.eps = c.rms_eps;
@@ -593,6 +595,7 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   kf.head_dim = c.head_dim;
   kf.raw = p.y_out;
   kf.ksplit = L.g.ksplit;
+  kf.raw_f32 = L.g.tall ? 1 : 0;
   kf.row_stream = row_stream;
   kf.row_pos = row_pos;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -667,14 +670,16 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
 
   // x = round(x + branch) (the branch's K-range partials added in order), then the
   // next normalised input a = round(RMSNorm(x) * gain)
-  auto norm = [&](const char* name, const double* parts, int ksplit, const void* gain, int rows, int rowmap_bm1) {
+  auto norm = [&](const char* name, const double* parts, const GemmPlan& g, const void* gain, int rows,
+                  int rowmap_bm1) {
     NormParams np;
     np.R = rows;
     np.hidden = c.hidden;
     np.rowmap_bm1 = rowmap_bm1;
     np.x = X;
     np.parts = parts;
-    np.ksplit = ksplit;
+    np.ksplit = g.ksplit;
+    np.parts_f32 = g.tall ? 1 : 0;
     np.part_rows = M;
     np.gain = gain;
     np.eps = c.rms_eps;
@@ -687,7 +692,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     // X += w_down . m of the previous layer (residual add 2); a = round(RMSNorm(X) * in_norm)
     // (layer 0: a is written by embed)
     if (l > 0) {
-      e = norm("norm_in", d_parts, L.down.ksplit, h->w.in_norm[l], M, 0);
+      e = norm("norm_in", d_parts, L.down, h->w.in_norm[l], M, 0);
       if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d input norm: %s", l, hipGetErrorString(e));
     }
     // raw q | k | v = a . [wq | wk | wv]^T
@@ -715,6 +720,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     qf.head_dim = c.head_dim;
     qf.raw = qkv_raw;
     qf.ksplit = L.qkv.ksplit;
+    qf.raw_f32 = L.qkv.tall ? 1 : 0;
     qf.ctx_len = ctx_len;
     qf.max_ctx = max_ctx_len;
     qf.q_norm = h->w.q_norm[l];
@@ -776,7 +782,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
 
     // X += wo . o (residual add 1); a = round(RMSNorm(X) * post_norm);
     // m = round(silu(w_gate . a) * (w_up . a))
-    e = norm("norm_post", o_parts, L.o.ksplit, h->w.post_norm[l], M, 0);
+    e = norm("norm_post", o_parts, L.o, h->w.post_norm[l], M, 0);
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d post norm: %s", l, hipGetErrorString(e));
     p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden);
     p.a = A;
@@ -806,7 +812,7 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
 
   // Last residual add and final norm of the mask rows (compacted), LM head, argmax
   // (lowest index on a tie).
-  e = norm("norm_final", d_parts, L.down.ksplit, h->w.norm, Mm, B - 1);
+  e = norm("norm_final", d_parts, L.down, h->w.norm, Mm, B - 1);
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "final norm: %s", hipGetErrorString(e));
   GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden);
   p.a = A;

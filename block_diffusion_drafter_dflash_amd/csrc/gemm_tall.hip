@@ -11,8 +11,8 @@
 // pieces so that fragment reads are free of bank conflicts) through a ring of three
 // buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
 // object, so the compiler sees that copies into one never alias the fragment reads
-// of another. The MFMAs accumulate in fp32 over the whole K range (a K range's result
-// is stored as a float64 partial, as the skinny kernel's). Waves whose 64 rows lie past
+// of another. The MFMAs accumulate in fp32 over the whole K range, and a K range's
+// result is stored as a float32 partial (the consumers add the ranges in float64). Waves whose 64 rows lie past
 // the batch (a batch of 33..64 rows uses one of the four row groups) copy their share
 // of the tiles but skip the fragment reads and MFMAs; their results are never stored. The summation order differs from the skinny
 // kernel's (one K sweep per K range rather than eight wave slices), so a batch on this
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = ct * BN + 64 * wn + 16 * j + lr;
-          if (rv && n < p.N) p.y_out[((int64_t)ks * p.M + r) * p.N + n] = (double)acc[i][j][e];
+          if (rv && n < p.N) reinterpret_cast<float*>(p.y_out)[((int64_t)ks * p.M + r) * p.N + n] = acc[i][j][e];
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
         // column 16 j + lr (j = 0, 1) is gate row 64 ct + 32 wn + 16 j + lr; j + 2 its up row

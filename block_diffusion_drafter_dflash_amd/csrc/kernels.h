@@ -44,7 +44,8 @@ struct GemmParams {
   const void* wk_l[kMaxLayers];
   const void* wv_l[kMaxLayers];
   // epilogue outputs
-  double* y_out;        // EPI_RAW: float64 partials [ksplit, M, N]
+  double* y_out;        // EPI_RAW: partials [ksplit, M, N], float64 (skinny kernel) or
+                        // float32 (tiled kernel, whose sums are fp32) in the same buffer
   void* m_out;          // EPI_SWIGLU: [M, ld_out]
   int ld_out;
   float* logits_out;    // EPI_LMHEAD (nullable), fp32
@@ -75,8 +76,9 @@ struct AttnParams {
 // layouts the attention kernel reads.
 struct QkvFinishParams {
   int S, B, n_q_heads, n_kv_heads, head_dim;
-  const double* raw;    // partials [ksplit, S*B, nq + 2 nkv]
+  const void* raw;      // partials [ksplit, S*B, nq + 2 nkv]
   int ksplit;
+  int raw_f32;          // 1: the partials are float32 (tiled GEMM), 0: float64
   const int* ctx_len;
   int max_ctx;
   const void* q_norm;
@@ -89,8 +91,9 @@ struct QkvFinishParams {
 
 struct KvFinishParams {
   int R, n_layers, n_kv_heads, head_dim;
-  const double* raw;    // partials [ksplit, R, n_layers * 2 * n_kv * d]: per layer k | v
+  const void* raw;      // partials [ksplit, R, n_layers * 2 * n_kv * d]: per layer k | v
   int ksplit;
+  int raw_f32;          // 1: the partials are float32 (tiled GEMM), 0: float64
   const int* row_stream;
   const int* row_pos;
   const void* kn_l[kMaxLayers];
@@ -118,8 +121,9 @@ struct EmbedParams {
 struct NormParams {
   int R, hidden, rowmap_bm1;
   void* x;              // [rows, hidden] residual stream
-  const double* parts;  // nullable: float64 partials [ksplit, rows, hidden] of the branch
+  const void* parts;    // nullable: partials [ksplit, rows, hidden] of the branch
   int ksplit, part_rows;
+  int parts_f32;        // 1: the partials are float32 (tiled GEMM), 0: float64
   const void* gain;
   float eps;
   void* a;              // [R, hidden]
@@ -128,7 +132,8 @@ struct NormParams {
 // Fused rows: y = (P_0 + P_1) + ... (the fc GEMM's partials), out = round(y / rms(y) * gain).
 struct RowNormParams {
   int R, hidden, ksplit;
-  const double* parts;  // [ksplit, R, hidden]
+  const void* parts;    // [ksplit, R, hidden]
+  int parts_f32;        // 1: the partials are float32 (tiled GEMM), 0: float64
   const void* gain;
   void* out;            // [R, hidden]
   float eps;

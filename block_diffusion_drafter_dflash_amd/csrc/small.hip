@@ -1,5 +1,7 @@
 // Small kernels of the draft round (gfx950): block input gather, row RMSNorms, the
 // block heads' norm + RoPE, injected K/V placement, greedy verify, workspace clearing.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.h"
 
@@ -19,35 +21,44 @@ __device__ double block_sum(double v, double* red) {
   return t;
 }
 
-// E consecutive float64 values, the in-order sum of ksplit partials [ks][rows][ld]:
-// ((P_0 + P_1) + P_2) + ..., the loads of up to four partials in flight at once.
-template <int E>
-__device__ __forceinline__ void sum_parts(const double* parts, int ksplit, int64_t ks_stride, int64_t off,
-                                          double (&out)[E]) {
+// E consecutive values, the in-order float64 sum of ksplit partials [ks][rows][ld]:
+// ((P_0 + P_1) + P_2) + ..., the loads of up to four partials in flight at once. The
+// partials are float64 (skinny GEMM) or float32 (tiled GEMM, whose sums are fp32 and
+// convert to float64 exactly).
+template <typename P, int E>
+__device__ __forceinline__ void sum_parts_t(const P* parts, int ksplit, int64_t ks_stride, int64_t off,
+                                            double (&out)[E]) {
   constexpr int KR = 4;
+  using P2 = typename std::conditional<sizeof(P) == 8, double2, float2>::type;
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = 0.0;
   for (int k0 = 0; k0 < ksplit; k0 += KR) {
-    double2 v[KR][E / 2];
+    P2 v[KR][E / 2];
 #pragma unroll
     for (int k = 0; k < KR; ++k)
       if (k0 + k < ksplit)
 #pragma unroll
-        for (int e = 0; e < E; e += 2) v[k][e / 2] = *reinterpret_cast<const double2*>(parts + (k0 + k) * ks_stride + off + e);
+        for (int e = 0; e < E; e += 2) v[k][e / 2] = *reinterpret_cast<const P2*>(parts + (k0 + k) * ks_stride + off + e);
 #pragma unroll
     for (int k = 0; k < KR; ++k)
       if (k0 + k < ksplit)
 #pragma unroll
         for (int e = 0; e < E; e += 2) {
           if (k0 + k == 0) {
-            out[e] = v[k][e / 2].x;
-            out[e + 1] = v[k][e / 2].y;
+            out[e] = (double)v[k][e / 2].x;
+            out[e + 1] = (double)v[k][e / 2].y;
           } else {
-            out[e] += v[k][e / 2].x;
-            out[e + 1] += v[k][e / 2].y;
+            out[e] += (double)v[k][e / 2].x;
+            out[e + 1] += (double)v[k][e / 2].y;
           }
         }
   }
+}
+template <int E>
+__device__ __forceinline__ void sum_parts(const void* parts, int f32, int ksplit, int64_t ks_stride, int64_t off,
+                                          double (&out)[E]) {
+  if (f32) sum_parts_t<float, E>(static_cast<const float*>(parts), ksplit, ks_stride, off, out);
+  else sum_parts_t<double, E>(static_cast<const double*>(parts), ksplit, ks_stride, off, out);
 }
 
 // Row kernels: kNormThreads threads a row, thread t owning the CH groups of E
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(const NormParams p) {
       float f[E];
       if (p.parts) {
         double br[E], xn[E];
-        sum_parts<E>(p.parts, p.ksplit, ks_stride, (int64_t)xr * p.hidden + c, br);
+        sum_parts<E>(p.parts, p.parts_f32, p.ksplit, ks_stride, (int64_t)xr * p.hidden + c, br);
         unpack(v[ch], f, T());
 #pragma unroll
         for (int e = 0; e < E; ++e) xn[e] = (double)f[e] + br[e];
@@ -191,7 +202,9 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   if (hi >= n_heads) return;
   const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
   const bool on = lane < D / 2;
-  const double* src = p.raw + (int64_t)r * ld + (int64_t)hi * D;
+  const int64_t src_off = (int64_t)r * ld + (int64_t)hi * D;
+  const double* src = static_cast<const double*>(p.raw) + src_off;
+  const float* srcf = static_cast<const float*>(p.raw) + src_off;
   const int64_t ks_stride = (int64_t)p.S * p.B * ld;
   double x0 = 0.0, x1 = 0.0;
   if (on) {
@@ -201,8 +214,9 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k0 + k < p.ksplit) {
-          v0[k] = src[(k0 + k) * ks_stride + lane];
-          v1[k] = src[(k0 + k) * ks_stride + lane + D / 2];
+          const int64_t o = (k0 + k) * ks_stride + lane;
+          v0[k] = p.raw_f32 ? (double)srcf[o] : src[o];
+          v1[k] = p.raw_f32 ? (double)srcf[o + D / 2] : src[o + D / 2];
         }
 #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -274,13 +288,14 @@ __global__ __launch_bounds__(256) void k_kv_finish(const KvFinishParams p) {
   __syncthreads();
   constexpr int TPH = D / 8;
   const int nkvd = p.n_kv_heads * D;
-  const double* raw = p.raw + (int64_t)r * (p.n_layers * 2 * nkvd) + (int64_t)l * 2 * nkvd;   // range 0
+  const int64_t raw_off = (int64_t)r * (p.n_layers * 2 * nkvd) + (int64_t)l * 2 * nkvd;   // range 0
   const int items = 2 * p.n_kv_heads * TPH;
   for (int it = tid; it < items; it += 256) {
     const int kind = it / (p.n_kv_heads * TPH), rem = it % (p.n_kv_heads * TPH);
     const int head = rem / TPH, part = rem % TPH;
     double x[8];
-    sum_parts<8>(raw, p.ksplit, (int64_t)p.R * p.n_layers * 2 * nkvd, (int64_t)kind * nkvd + head * D + part * 8, x);
+    sum_parts<8>(p.raw, p.raw_f32, p.ksplit, (int64_t)p.R * p.n_layers * 2 * nkvd,
+                 raw_off + (int64_t)kind * nkvd + head * D + part * 8, x);
     // norm and rotation are computed for every item (shuffles stay inside a head's
     // TPH lanes); only K items keep them
     double ss = 0.0;
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(kNormThreads) void k_rownorm(const RowNormParams p)
     const int c = (ch * NT + threadIdx.x) * E;
     if (c < p.hidden) {
       g[ch] = ldg16(gn + c);
-      sum_parts<E>(p.parts, p.ksplit, ks_stride, off + c, y[ch]);
+      sum_parts<E>(p.parts, p.parts_f32, p.ksplit, ks_stride, off + c, y[ch]);
 #pragma unroll
       for (int e = 0; e < E; ++e) ss += y[ch][e] * y[ch][e];
     }
