@@ -187,6 +187,27 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   __shared__ double2 tab[D / 2];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int s = r / p.B, j = r % p.B;
+  const int n_heads = p.n_q_heads + 2 * p.n_kv_heads;
+  const int hi = blockIdx.y * 4 + (tid >> 6);
+  const bool head_ok = hi < n_heads;
+  const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
+  const bool on = head_ok && lane < D / 2;
+  // The first eight partials' loads go out before the rotary table is computed, so
+  // their latency overlaps the table's float64 sincos.
+  const int64_t src_off = (int64_t)r * ld + (int64_t)(head_ok ? hi : 0) * D;
+  const double* src = static_cast<const double*>(p.raw) + src_off;
+  const float* srcf = static_cast<const float*>(p.raw) + src_off;
+  const int64_t ks_stride = (int64_t)p.S * p.B * ld;
+  double v0[8], v1[8];
+  if (on) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < p.ksplit) {
+        const int64_t o = k * ks_stride + lane;
+        v0[k] = p.raw_f32 ? (double)srcf[o] : src[o];
+        v1[k] = p.raw_f32 ? (double)srcf[o + D / 2] : src[o + D / 2];
+      }
+  }
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int pos = Cs + j;
@@ -197,27 +218,20 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
     tab[i] = make_double2(cs, sn);
   }
   __syncthreads();
-  const int n_heads = p.n_q_heads + 2 * p.n_kv_heads;
-  const int hi = blockIdx.y * 4 + (tid >> 6);
-  if (hi >= n_heads) return;
-  const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
-  const bool on = lane < D / 2;
-  const int64_t src_off = (int64_t)r * ld + (int64_t)hi * D;
-  const double* src = static_cast<const double*>(p.raw) + src_off;
-  const float* srcf = static_cast<const float*>(p.raw) + src_off;
-  const int64_t ks_stride = (int64_t)p.S * p.B * ld;
+  if (!head_ok) return;
   double x0 = 0.0, x1 = 0.0;
   if (on) {
-    // ((P_0 + P_1) + P_2) + ..., up to eight partials' loads in flight
+    // ((P_0 + P_1) + P_2) + ...: the first eight from registers, the rest eight at a time
     for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
-      double v0[8], v1[8];
+      if (k0 > 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (k0 + k < p.ksplit) {
-          const int64_t o = (k0 + k) * ks_stride + lane;
-          v0[k] = p.raw_f32 ? (double)srcf[o] : src[o];
-          v1[k] = p.raw_f32 ? (double)srcf[o + D / 2] : src[o + D / 2];
-        }
+        for (int k = 0; k < 8; ++k)
+          if (k0 + k < p.ksplit) {
+            const int64_t o = (k0 + k) * ks_stride + lane;
+            v0[k] = p.raw_f32 ? (double)srcf[o] : src[o];
+            v1[k] = p.raw_f32 ? (double)srcf[o + D / 2] : src[o + D / 2];
+          }
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         if (k0 + k < p.ksplit) {
