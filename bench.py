@@ -163,6 +163,34 @@ def cpu_baseline(case, sample_streams, min_seconds=10.0):
                        f"{dt:.2f} s per round", seconds=round(total, 2)), out
 
 
+def graph_replay(torch, step, st, steps):
+    """ms per round when one round is captured into a HIP graph and replayed `steps`
+    times on stream `st` (the library allocates nothing and clears with kernels, so
+    a round captures as it runs). A capture failure is reported, not raised."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            step()
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return {"ms_per_step": round(e0.elapsed_time(e1) / steps, 5), "replays": steps}
+    except RuntimeError as exc:
+        return {"error": str(exc)[:200]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +293,10 @@ def main():
     case.dr.set_profiling(False)
     print(f"[bench] timed {ms:.4f} ms/step; per-kernel pass done", file=sys.stderr, flush=True)
 
+    # the same round captured once as a HIP graph and replayed (reported beside the
+    # eager figure, which stays the headline)
+    graph = graph_replay(torch, step, st, args.steps)
+
     costs = kernel_costs(p, case.ctx, case.rows, sampling=args.sampling > 0)
     tot_bytes, tot_flops = round_totals(costs)
     drafted = S * (B - 1)
@@ -303,6 +335,7 @@ def main():
         "mfma_frac_of_peak": round(tot_flops / (ms * 1e-3) / 1e12 / mfma_dtype_peak, 5),
         "round_bytes": tot_bytes, "round_flops": tot_flops, "wall_s_timed": round(wall, 4),
         "round_ms_quantiles": quant,
+        "graph_replay": graph,
         "bytes_per_drafted_token": round(tot_bytes / drafted),
         "bytes_per_accepted_token": round(tot_bytes / max(1, case.R)),
         "roofline": roof,

@@ -490,6 +490,45 @@ def test_tiled_batch_classes_are_invariant_to_stream_order_bitwise(preset):
         assert torch.equal(dr[i], bdraft[s])
 
 
+def test_graph_replay_of_a_round_matches_eager_bitwise():
+    # One round (fuse, inject, draft, verify) captured as a HIP graph: every replay,
+    # with eager rounds and synchronisations between them, writes the eager round's bits.
+    case = RoundCase(MID)
+    case.run_gpu()
+    case.set_target_from(case.draft.cpu().numpy())
+
+    def step():
+        case.fuse()
+        case.inject()
+        case.draft_block(logits=True, top2=False)
+        case.verify()
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (case.logits, case.draft, case.accept, case.bonus, case.committed)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (case.logits, case.draft, case.accept, case.bonus, case.committed):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        outs = (case.logits, case.draft, case.accept, case.bonus, case.committed)
+        for name, a, b in zip(("logits", "draft", "accept", "bonus", "committed"), outs, ref):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {rep}: {name}"
+        step()                       # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_chunked_inject_equals_one_shot_and_page_order_is_invisible():
     a = RoundCase(MID, permute_pages=True)
     a.fuse()
