@@ -199,6 +199,7 @@ def main():
     ap.add_argument("--workload", default="9b_ctx4k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass")
     ap.add_argument("--prefill", type=int, default=0,
                     help="instead of the round: fuse + inject this many prompt rows of one stream")
     ap.add_argument("--sampling", type=float, default=0.0,
@@ -295,7 +296,7 @@ def main():
 
     # the same round captured once as a HIP graph and replayed (reported beside the
     # eager figure, which stays the headline)
-    graph = graph_replay(torch, step, st, args.steps)
+    graph = None if args.no_graph else graph_replay(torch, step, st, args.steps)
 
     costs = kernel_costs(p, case.ctx, case.rows, sampling=args.sampling > 0)
     tot_bytes, tot_flops = round_totals(costs)
