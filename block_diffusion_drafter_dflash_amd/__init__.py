@@ -78,6 +78,9 @@ def library():
         "dflash_workspace_init": (i32, [_VP, _VP, sz, _VP]),
         "dflash_fuse_taps": (i32, [_VP, ctypes.POINTER(_VP), i64, i32, _VP, _VP, sz, _VP]),
         "dflash_inject_kv": (i32, [_VP, _VP, i32, _VP, _VP, ctypes.POINTER(KV), _VP, sz, _VP]),
+        "dflash_inject_kv_layers": (i32, [_VP, _VP, i32, _VP, _VP, ctypes.POINTER(KV), ctypes.c_uint64, _VP, sz,
+                                          _VP]),
+        "dflash_layers_reading": (ctypes.c_uint64, [_VP, i32, i32]),
         "dflash_draft_block": (i32, [_VP, i32, _VP, _VP, i32, ctypes.POINTER(KV), _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_greedy": (i32, [_VP, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, sz, _VP]),
@@ -99,7 +102,8 @@ def library():
 
 EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflash_bind_weights",
             "dflash_fused_row_bytes", "dflash_tap_row_bytes", "dflash_workspace_bytes", "dflash_workspace_init",
-            "dflash_fuse_taps", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_greedy",
+            "dflash_fuse_taps", "dflash_inject_kv", "dflash_inject_kv_layers", "dflash_layers_reading",
+            "dflash_draft_block", "dflash_verify_greedy",
             "dflash_sample_rows", "dflash_verify_sampling",
             "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
 
@@ -239,6 +243,16 @@ class Drafter:
         n_rows = fused.shape[0] if n_rows is None else n_rows
         self._check(self.lib.dflash_inject_kv(self.h, _ptr(fused), n_rows, _ptr(row_stream), _ptr(row_pos),
                                               ctypes.byref(kv.struct), _ptr(ws), ws.numel(), _stream(stream)))
+
+    def dflash_inject_kv_layers(self, fused, row_stream, row_pos, kv, layer_mask, ws, n_rows=None, stream=None):
+        n_rows = fused.shape[0] if n_rows is None else n_rows
+        self._check(self.lib.dflash_inject_kv_layers(self.h, _ptr(fused), n_rows, _ptr(row_stream), _ptr(row_pos),
+                                                     ctypes.byref(kv.struct), ctypes.c_uint64(layer_mask), _ptr(ws),
+                                                     ws.numel(), _stream(stream)))
+
+    def dflash_layers_reading(self, pos, ctx_len):
+        """Bit mask of the layers that read context position `pos` at context length `ctx_len`."""
+        return int(self.lib.dflash_layers_reading(self.h, int(pos), int(ctx_len)))
 
     def dflash_draft_block(self, anchor, ctx_len, max_ctx_len, kv, draft_out, ws, logits_out=None, top2_out=None,
                            n_streams=None, stream=None):

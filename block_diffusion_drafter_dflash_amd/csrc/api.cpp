@@ -555,13 +555,23 @@ static int check_kv(dflash* h, const dflash_kv* kv) {
   return DFLASH_OK;
 }
 
-int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t* row_stream,
-                     const int32_t* row_pos, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+// Injected K/V of the layers in layer_mask. The GEMM's K split is the one of the
+// all-layer inject (a function of the weight's full shape), so a selected layer's
+// K/V are bitwise those of an inject of every layer.
+static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32_t* row_stream,
+                       const int32_t* row_pos, const dflash_kv* kv, uint64_t layer_mask, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!h) return DFLASH_ERR_ARG;
   const auto& c = h->cfg;
   if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
   if (n_rows < 0) return fail(h, DFLASH_ERR_ARG, "n_rows %d < 0", n_rows);
-  if (n_rows == 0) return DFLASH_OK;
+  if (c.n_layers < 64 && (layer_mask >> c.n_layers) != 0)
+    return fail(h, DFLASH_ERR_ARG, "layer_mask names a layer past n_layers (%d)", c.n_layers);
+  int sel[DFLASH_MAX_LAYERS];
+  int n_sel = 0;
+  for (int l = 0; l < c.n_layers; ++l)
+    if ((layer_mask >> l) & 1ull) sel[n_sel++] = l;
+  if (n_rows == 0 || n_sel == 0) return DFLASH_OK;
   if (!fused || !aligned16(fused) || !row_stream || !row_pos) return fail(h, DFLASH_ERR_ARG, "fused, row_stream or row_pos invalid");
   int rc = check_kv(h, kv);
   if (rc) return rc;
@@ -570,38 +580,42 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   if (rc) return rc;
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
-  const int N = c.n_layers * 2 * h->nkv();
-  GemmParams p = gemm_base(L.g, n_rows, N, c.hidden);
+  // the selected layers' [wk | wv] segments side by side; tiles of the all-layer plan
+  GemmPlan g = L.g;
+  const int N = n_sel * 2 * h->nkv();
+  g.n_tiles = (N + gemm_tile_cols(EPI_RAW) - 1) / gemm_tile_cols(EPI_RAW);
+  g.n_work = g.n_tiles * g.mgroups * g.ksplit;
+  GemmParams p = gemm_base(g, n_rows, N, c.hidden);
   p.a = fused;
   p.lda = c.hidden;
   p.nkv = h->nkv();
-  p.seg_layers = c.n_layers;
-  for (int l = 0; l < c.n_layers; ++l) {
-    p.wk_l[l] = h->w.wk[l];
-    p.wv_l[l] = h->w.wv[l];
+  p.seg_layers = n_sel;
+  for (int i = 0; i < n_sel; ++i) {
+    p.wk_l[i] = h->w.wk[sel[i]];
+    p.wv_l[i] = h->w.wv[sel[i]];
   }
   p.y_out = reinterpret_cast<double*>(W + L.raw);
   hipError_t e;
   {
     ProfScope ps(h, "inject_kv_gemm", st);
-    e = run_gemm(c.dtype, L.g, EPI_RAW, p, st);
+    e = run_gemm(c.dtype, g, EPI_RAW, p, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
   KvFinishParams kf;
   std::memset(&kf, 0, sizeof kf);
   kf.R = n_rows;
-  kf.n_layers = c.n_layers;
+  kf.n_layers = n_sel;
   kf.n_kv_heads = c.n_kv_heads;
   kf.head_dim = c.head_dim;
   kf.raw = p.y_out;
-  kf.ksplit = L.g.ksplit;
-  kf.raw_f32 = L.g.tall ? 1 : 0;
+  kf.ksplit = g.ksplit;
+  kf.raw_f32 = g.tall ? 1 : 0;
   kf.row_stream = row_stream;
   kf.row_pos = row_pos;
-  for (int l = 0; l < c.n_layers; ++l) {
-    kf.kn_l[l] = h->w.k_norm[l];
-    kf.kpool_l[l] = kv->k_pool[l];
-    kf.vpool_l[l] = kv->v_pool[l];
+  for (int i = 0; i < n_sel; ++i) {
+    kf.kn_l[i] = h->w.k_norm[sel[i]];
+    kf.kpool_l[i] = kv->k_pool[sel[i]];
+    kf.vpool_l[i] = kv->v_pool[sel[i]];
   }
   kf.page_table = kv->page_table;
   kf.pages_per_stream = kv->pages_per_stream;
@@ -616,6 +630,32 @@ int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject finish: %s", hipGetErrorString(e));
   return DFLASH_OK;
+}
+
+int dflash_inject_kv(dflash* h, const void* fused, int32_t n_rows, const int32_t* row_stream,
+                     const int32_t* row_pos, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const int nl = h->cfg.n_layers;
+  const uint64_t all = nl >= 64 ? ~0ull : ((1ull << nl) - 1ull);
+  return inject_impl(h, fused, n_rows, row_stream, row_pos, kv, all, ws, ws_bytes, stream);
+}
+
+int dflash_inject_kv_layers(dflash* h, const void* fused, int32_t n_rows, const int32_t* row_stream,
+                            const int32_t* row_pos, const dflash_kv* kv, uint64_t layer_mask, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return inject_impl(h, fused, n_rows, row_stream, row_pos, kv, layer_mask, ws, ws_bytes, stream);
+}
+
+uint64_t dflash_layers_reading(const dflash* h, int32_t pos, int32_t ctx_len) {
+  if (!h || pos < 0 || pos >= ctx_len) return 0;
+  const auto& c = h->cfg;
+  uint64_t m = 0;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const int w = c.layer_window[l];
+    const int lo = w > 0 ? (ctx_len - w > 0 ? ctx_len - w : 0) : 0;
+    if (pos >= lo) m |= 1ull << l;
+  }
+  return m;
 }
 
 int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,

@@ -189,6 +189,28 @@ int dflash_inject_kv(dflash *h, const void *fused, int32_t n_rows, const int32_t
                      void *stream);
 
 /*
+ * Inject for the layers in layer_mask only (bit l = layer l; a bit at or past n_layers
+ * -> DFLASH_ERR_ARG; an empty mask is a no-op): the prompt-side inject limited to the
+ * layers that will read a row (TensorFold #1851, cold prefill with the drafter attached:
+ * doing that work only for rows the drafter reads is the follow-up it names). A
+ * selected layer's K/V are bitwise those dflash_inject_kv writes; the other layers'
+ * pool slots are not touched. Arguments and errors otherwise as dflash_inject_kv.
+ */
+int dflash_inject_kv_layers(dflash *h, const void *fused, int32_t n_rows, const int32_t *row_stream,
+                            const int32_t *row_pos, const dflash_kv *kv, uint64_t layer_mask, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * The layers that read context position pos in a round at context length ctx_len:
+ * layer l when max(0, ctx_len - W_l) <= pos < ctx_len (W_l = layer_window[l]; every
+ * position below ctx_len when W_l == 0), as in dflash_draft_block. A stream's committed
+ * context never shrinks below its prompt, so with ctx_len = the prompt length this is
+ * every layer that will ever read a prompt row at pos: the mask for
+ * dflash_inject_kv_layers. 0 when pos is outside [0, ctx_len) or h is NULL. Host only.
+ */
+uint64_t dflash_layers_reading(const dflash *h, int32_t pos, int32_t ctx_len);
+
+/*
  * Draft one block per stream. Stream s's block is [anchor[s], mask x (B-1)] at
  * positions C_s .. C_s+B-1 with C_s = ctx_len[s]; one non-causal forward of the qwen3
  * body (two residual adds a layer); layer l attends the context positions

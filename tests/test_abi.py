@@ -167,8 +167,14 @@ def test_round_calls_refuse_on_the_host_before_any_enqueue():
     assert rc == -4 and "span" in dr.last_error()
     rc = lib.dflash_draft_block(dr.h, 2, fake, fake, 64, ctypes.byref(kv), fake, None, None, fake, 1 << 20, None)
     assert rc == -4 and "n_streams" in dr.last_error()
+    # a layer mask naming a layer past n_layers; an empty mask is a no-op
+    rc = lib.dflash_inject_kv_layers(dr.h, fake, 4, fake, fake, ctypes.byref(kv), 1 << p.n_layers, fake, 1 << 20, None)
+    assert rc == -1 and "layer_mask" in dr.last_error()
+    assert lib.dflash_inject_kv_layers(dr.h, fake, 4, fake, fake, ctypes.byref(kv), 0, fake, 1 << 20, None) == 0
     kv.k_pool[1] = 0
     rc = lib.dflash_inject_kv(dr.h, fake, 4, fake, fake, ctypes.byref(kv), fake, 1 << 20, None)
+    assert rc == -1 and "pool" in dr.last_error()
+    rc = lib.dflash_inject_kv_layers(dr.h, fake, 4, fake, fake, ctypes.byref(kv), 0b10, fake, 1 << 20, None)
     assert rc == -1 and "pool" in dr.last_error()
     assert lib.dflash_verify_greedy(dr.h, 0, fake, fake, fake, fake, fake, None, None) == -1
 
@@ -180,3 +186,22 @@ def test_workspace_sizes_grow_with_the_request():
     assert 0 < a < b
     assert dr.workspace_bytes(16, 5, 4096) == 0      # more streams than max_streams
     assert dr.workspace_bytes(-1, 1, 4096) == 0
+
+
+def test_layers_reading_follows_each_layers_reach():
+    # A layer reads position pos at context C when pos lies in its reach, as the oracle
+    # defines it ([max(0, C - W), C), all of [0, C) for a full layer).
+    from oracle import dflash_oracle as O
+    p = wl.preset("9b_long_x4")            # five sliding layers (W = 4096) and one full
+    dr = D.Drafter(cfg_of("9b_long_x4"))
+    for C in (0, 1, 100, 4096, 4097, 32768):
+        for pos in sorted({-1, 0, 1, C - 4097, C - 4096, C - 4095, C - 1, C, C + 5}):
+            want = 0
+            for l in range(p.n_layers):
+                lo, hi = O.context_reach(C, p.layer_window[l])
+                if lo <= pos < hi:
+                    want |= 1 << l
+            assert dr.dflash_layers_reading(pos, C) == want, (pos, C)
+    # a prompt row older than every window is read by the full layer alone
+    assert dr.dflash_layers_reading(0, 32768) == 1 << 5
+    assert D.library().dflash_layers_reading(None, 0, 10) == 0

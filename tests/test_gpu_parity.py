@@ -529,6 +529,47 @@ def test_graph_replay_of_a_round_matches_eager_bitwise():
         torch.cuda.synchronize()
 
 
+def test_deferred_inject_writes_the_layers_that_read_each_row():
+    # Prompt rows injected only into the layers that will read them (the mask of
+    # dflash_layers_reading at the prompt length): every selected (layer, row) holds the
+    # all-layer inject's bits, every other slot stays untouched, and a round drafted over
+    # the deferred cache writes the bits of the round over the full one.
+    P = 1030
+    p = small_variant(MID, name="defer_bf16", n_streams=1, ctx_spec=[P])   # windows 100, full, 37
+    case = RoundCase(p, ctx=[P], rows=[P])
+    case.fuse()
+    case.inject()
+    case.draft_block(logits=True, top2=False)
+    torch.cuda.synchronize()
+    full = [tuple(t.clone() for t in case.kv.read_rows(l, 0, 0, P)) for l in range(p.n_layers)]
+    ref_logits, ref_draft = case.logits.clone(), case.draft.clone()
+    for l in range(p.n_layers):
+        case.kv.k[l].zero_()
+        case.kv.v[l].zero_()
+    pos = case.row_pos.cpu().tolist()
+    masks = [case.dr.dflash_layers_reading(x, P) for x in pos]
+    groups = sorted(set(masks))
+    assert groups == [0b010, 0b011, 0b111]      # windows 100 and 37 split the prompt in three
+    for m in groups:
+        idx = torch.tensor([i for i, mm in enumerate(masks) if mm == m], device="cuda")
+        log(f"[defer] mask {m:03b}: {idx.numel()} rows")
+        case.dr.dflash_inject_kv_layers(case.fused[idx].contiguous(), case.row_stream[idx].contiguous(),
+                                        case.row_pos[idx].contiguous(), case.kv, m, case.ws)
+    torch.cuda.synchronize()
+    for l in range(p.n_layers):
+        k, v = case.kv.read_rows(l, 0, 0, P)
+        sel = torch.tensor([(m >> l) & 1 == 1 for m in masks], device="cuda")
+        assert torch.equal(k[sel].view(torch.int16), full[l][0][sel].view(torch.int16)), f"layer {l} K"
+        assert torch.equal(v[sel].view(torch.int16), full[l][1][sel].view(torch.int16)), f"layer {l} V"
+        assert not k[~sel].any() and not v[~sel].any(), f"layer {l}: an unselected slot was written"
+    case.logits.zero_()
+    case.draft.zero_()
+    case.draft_block(logits=True, top2=False)
+    torch.cuda.synchronize()
+    assert torch.equal(case.logits.view(torch.int32), ref_logits.view(torch.int32))
+    assert torch.equal(case.draft, ref_draft)
+
+
 def test_chunked_inject_equals_one_shot_and_page_order_is_invisible():
     a = RoundCase(MID, permute_pages=True)
     a.fuse()
