@@ -274,36 +274,43 @@ __global__ __launch_bounds__(kDrawThreads) void k_sample_rows(const SampleParams
   }
 }
 
-// Speculative-sampling acceptance walk (one thread a stream): the accepted length
-// and, for the draw that follows, the row max and total of the target row a and (on
-// a rejection) of the draft row a.
+// Speculative-sampling acceptance (one wave a stream): lane j evaluates the test at
+// position j (j < B - 1) and the (max, total) of target row j (j < B) in parallel; the
+// accepted length is the first failing position (B - 1 when none fails), so the
+// decisions are those of a walk that stops at the first rejection. For the draw that
+// follows: the row max and total of the target row a and (on a rejection) of the
+// draft row a.
 __global__ __launch_bounds__(kWave) void k_spec_accept(const SpecVerifyParams p) {
-  const int s = blockIdx.x, B = p.B, V = p.V;
-  if (threadIdx.x != 0) return;
+  const int s = blockIdx.x, B = p.B, V = p.V, j = threadIdx.x;
   const float sc = p.scale;
-  const int* d = p.draft + (int64_t)s * (B - 1);
-  int a = 0;
   float tm = 0.f, dm = 0.f;
   double tz = 1.0, dz = 1.0;
-  while (true) {
-    combine_slices(p.target_stats + ((int64_t)s * B + a) * kSlices * 2, sc, tm, tz, nullptr);
-    if (a == B - 1) break;
-    combine_slices(p.draft_stats + ((int64_t)s * (B - 1) + a) * kSlices * 2, sc, dm, dz, nullptr);
-    const int tok = d[a];
-    if (tok < 0 || tok >= V) break;   // an id outside the vocabulary is rejected
-    const float* drow = p.draft_logits + ((int64_t)s * (B - 1) + a) * p.ld;
-    const float* trow = p.target_logits + ((int64_t)s * B + a) * p.ld;
-    const double pd = (double)exp2f((drow[tok] - dm) * sc) / dz;
-    const double pt = (double)exp2f((trow[tok] - tm) * sc) / tz;
-    if (!((double)p.u_accept[(int64_t)s * (B - 1) + a] * pd < pt)) break;
-    ++a;
+  bool ok = false;   // the draft token at position j passes its test
+  if (j < B) combine_slices(p.target_stats + ((int64_t)s * B + j) * kSlices * 2, sc, tm, tz, nullptr);
+  if (j < B - 1) {
+    combine_slices(p.draft_stats + ((int64_t)s * (B - 1) + j) * kSlices * 2, sc, dm, dz, nullptr);
+    const int tok = p.draft[(int64_t)s * (B - 1) + j];
+    if (tok >= 0 && tok < V) {   // an id outside the vocabulary is rejected
+      const float* drow = p.draft_logits + ((int64_t)s * (B - 1) + j) * p.ld;
+      const float* trow = p.target_logits + ((int64_t)s * B + j) * p.ld;
+      const double pd = (double)exp2f((drow[tok] - dm) * sc) / dz;
+      const double pt = (double)exp2f((trow[tok] - tm) * sc) / tz;
+      ok = (double)p.u_accept[(int64_t)s * (B - 1) + j] * pd < pt;
+    }
   }
-  p.accept[s] = a;
-  double* r = p.row_info + (int64_t)s * 4;
-  r[0] = tm;
-  r[1] = tz;
-  r[2] = dm;
-  r[3] = dz;
+  const uint64_t rejected = __ballot(j < B - 1 && !ok);
+  const int a = rejected ? (int)__builtin_ctzll(rejected) : B - 1;
+  const int ad = a < B - 1 ? a : B - 2;   // the draft row's values only matter on a rejection
+  const float tma = __shfl(tm, a, kWave), dma = __shfl(dm, ad, kWave);
+  const double tza = __shfl(tz, a, kWave), dza = __shfl(dz, ad, kWave);
+  if (j == 0) {
+    p.accept[s] = a;
+    double* r = p.row_info + (int64_t)s * 4;
+    r[0] = tma;
+    r[1] = tza;
+    r[2] = dma;
+    r[3] = dza;
+  }
 }
 
 // Per (slice, stream): the slice's sums of the residual max(q - p, 0) at the rejected
