@@ -213,11 +213,16 @@ __device__ int draw_in_range(const Wf& w, int lo, int hi, double target, double*
 }  // namespace
 
 // (max, weight sum relative to that max) of slice blockIdx.x of row blockIdx.y.
+// Rows [0, rows1) come from (logits, stats), the grid's rows past them from
+// (logits2, stats2): one launch for the draft and the target rows of a verify.
 __global__ __launch_bounds__(kSliceThreads) void k_slice_stats(const float* logits, int V, int64_t ld, float scale,
-                                                               double* stats) {
+                                                               double* stats, int rows1, const float* logits2,
+                                                               double* stats2) {
   __shared__ float shf[kSliceThreads / kWave];
   __shared__ double shd[kSliceThreads / kWave];
-  const float* row = logits + (int64_t)blockIdx.y * ld;
+  const bool second = (int)blockIdx.y >= rows1;
+  const int ry = second ? (int)blockIdx.y - rows1 : (int)blockIdx.y;
+  const float* row = (second ? logits2 : logits) + (int64_t)ry * ld;
   const Slice sl = slice_of(V, blockIdx.x);
   float m = -INFINITY;
   for (int k0 = sl.lo + threadIdx.x; k0 < sl.hi; k0 += kBatch * kSliceThreads) {
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(kSliceThreads) void k_slice_stats(const float* logi
     z = block_sum<kSliceThreads / kWave>(
         strided_sum<kSliceThreads>([&](int k) { return (double)exp2f((row[k] - m) * scale); }, sl.lo, sl.hi), shd);
   if (threadIdx.x == 0) {
-    double* o = stats + ((int64_t)blockIdx.y * kSlices + blockIdx.x) * 2;
+    double* o = (second ? stats2 : stats) + ((int64_t)ry * kSlices + blockIdx.x) * 2;
     o[0] = (double)m;
     o[1] = z;
   }
@@ -400,7 +405,8 @@ __global__ __launch_bounds__(kDrawThreads) void k_spec_draw(const SpecVerifyPara
 hipError_t launch_slice_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
                               hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  (void)launch_k(k_slice_stats, dim3(kSlices, rows), dim3(kSliceThreads), st, logits, V, ld, scale, stats);
+  (void)launch_k(k_slice_stats, dim3(kSlices, rows), dim3(kSliceThreads), st, logits, V, ld, scale, stats, rows,
+                 static_cast<const float*>(nullptr), static_cast<double*>(nullptr));
   return hipGetLastError();
 }
 
@@ -412,8 +418,10 @@ hipError_t launch_sample_rows(const SampleParams& p, hipStream_t st) {
 }
 
 hipError_t launch_verify_sampling(const SpecVerifyParams& p, hipStream_t st) {
-  hipError_t e = launch_slice_stats(p.draft_logits, p.S * (p.B - 1), p.V, p.ld, p.scale, p.draft_stats, st);
-  if (e == hipSuccess) e = launch_slice_stats(p.target_logits, p.S * p.B, p.V, p.ld, p.scale, p.target_stats, st);
+  const int rd = p.S * (p.B - 1), rt = p.S * p.B;   // draft rows, then target rows
+  (void)launch_k(k_slice_stats, dim3(kSlices, rd + rt), dim3(kSliceThreads), st, p.draft_logits, p.V, p.ld, p.scale,
+                 p.draft_stats, rd, p.target_logits, p.target_stats);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   (void)launch_k(k_spec_accept, dim3(p.S), dim3(kWave), st, p);
   (void)launch_k(k_spec_slices, dim3(kSlices, p.S), dim3(kSliceThreads), st, p);
