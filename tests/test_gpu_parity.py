@@ -352,6 +352,13 @@ def test_round_parity_mid_ragged():
     run_case(RoundCase(MID), [0, 1, 2, 3])
 
 
+def test_round_parity_33_rows_first_tiled_batch():
+    # 3 streams x block 11 = 33 rows, the smallest batch on the tiled GEMMs (its LM head
+    # sees 30 mask rows); against the oracle like every other class
+    p = small_variant(MID, name="mid33_bf16", n_streams=3, block_size=11, ctx_spec=[300, 1030, 77], seed=2007)
+    run_case(RoundCase(p), [0, 1, 2])
+
+
 def test_round_parity_48_rows_partial_row_group():
     # 3 streams x 16 = 48 rows: tiled GEMMs whose one live row group is part padding
     p = small_variant(MID, name="mid3_bf16", n_streams=3, ctx_spec=[300, 1030, 77], seed=2006)
