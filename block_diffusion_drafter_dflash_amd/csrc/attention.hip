@@ -155,7 +155,6 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   float m_run = -INFINITY;
   double l_run = 0.0;
 
-  const int64_t kv_page = (int64_t)p.page_size * D;   // elements per (page, head)
   const int64_t blk_off = ((int64_t)s * p.n_kv_heads + h) * (kBlockSlots * D);
   const T* kblk = static_cast<const T*>(p.kblk) + blk_off;
   const T* vblk = static_cast<const T*>(p.vblk) + blk_off;
