@@ -165,10 +165,15 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       w_off[k] = (n - n0) * p.K + piece * 8;
     }
   }
+  // Wave w copies A tile rows [RPL QA w, + RPL QA); when they all lie past the batch it
+  // copies only its W share (their LDS rows are read by no live wave), and its ring
+  // waits count only those copies.
+  const bool a_live = RPL * QA * w < p.M - rt * BM;
   auto issue = [&](int ch, unsigned char* buf) {
     const int k0 = ch * BK;
 #pragma unroll
     for (int k = 0; k < QA; ++k) {
+      if (!a_live) break;
       const int q = QA * w + k;
       if constexpr (AM == A_TAPS) {
         // a chunk never straddles two planes (hidden % 64 == 0)
@@ -239,7 +244,8 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   // Copies past the range repeat its last chunk (never read), so that every step has
   // the same number of copies in flight.
   auto step = [&](int ch, const unsigned char* cur, unsigned char* nxt) {
-    ring_barrier<(kRing - 2) * LPW>();
+    if (a_live) ring_barrier<(kRing - 2) * LPW>();
+    else ring_barrier<(kRing - 2) * QB>();
     issue(min(ch + kRing - 1, ke - 1), nxt);
     compute(cur);
   };
