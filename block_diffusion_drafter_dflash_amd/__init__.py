@@ -86,6 +86,8 @@ def library():
         "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_sampling": (i32, [_VP, i32, _VP, _VP, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
                                          _VP, _VP, sz, _VP]),
+        "dflash_trace_bytes": (sz, [_VP, i32]),
+        "dflash_set_trace": (i32, [_VP, _VP, sz]),
         "dflash_set_profiling": (i32, [_VP, i32]),
         "dflash_profile_read": (i32, [_VP, ctypes.c_char_p, sz]),
         "dflash_last_error": (ctypes.c_char_p, [_VP]),
@@ -105,7 +107,7 @@ EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflas
             "dflash_fuse_taps", "dflash_inject_kv", "dflash_inject_kv_layers", "dflash_layers_reading",
             "dflash_draft_block", "dflash_verify_greedy",
             "dflash_sample_rows", "dflash_verify_sampling",
-            "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
+            "dflash_trace_bytes", "dflash_set_trace", "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
 
 
 def make_config(hidden, n_layers, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, tap_layer_ids,
@@ -181,6 +183,14 @@ class Drafter:
         return self.lib.dflash_last_error(self.h).decode()
 
     # -- instrumentation
+    def trace_bytes(self, n_streams):
+        return int(self.lib.dflash_trace_bytes(self.h, n_streams))
+
+    def set_trace(self, buf):
+        """Copy every stored tensor of each dflash_draft_block into `buf` (a device
+        tensor of at least trace_bytes(n_streams) bytes); None turns it off."""
+        self._check(self.lib.dflash_set_trace(self.h, _ptr(buf), 0 if buf is None else buf.numel() * buf.element_size()))
+
     def set_profiling(self, enable=True):
         self._check(self.lib.dflash_set_profiling(self.h, 1 if enable else 0))
 

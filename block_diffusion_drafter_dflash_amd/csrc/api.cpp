@@ -44,6 +44,8 @@ struct dflash {
   std::vector<std::pair<const void*, size_t>> ws_ready;
   bool profiling = false;
   std::vector<ProfRec> prof;
+  void* trace = nullptr;        // stage copies of dflash_draft_block (instrumentation)
+  size_t trace_cap = 0;
   std::vector<hipEvent_t> event_pool;
 
   ~dflash() {
@@ -151,6 +153,21 @@ struct Region {
   }
 };
 
+// Rows of one fuse or inject pass. A call of more than kRowPass rows runs as equal
+// passes of at most kRowPass rows (each well above the tiled GEMM's first row count,
+// whose per-row arithmetic depends only on the weight's shape), so the K-range
+// partials stay bounded at any prompt length and a row's result is bitwise that of
+// any other call of the tiled class.
+constexpr int kRowPass = 8192;
+int row_pass(int R) {
+  if (R <= kRowPass) return R;
+  const int n = (R + kRowPass - 1) / kRowPass;
+  return (R + n - 1) / n;
+}
+// The largest tap-plane row stride (elements): the tiled kernel's lane offsets span up
+// to seven row strides inside a 31-bit buffer range.
+constexpr int64_t kMaxPlaneStride = int64_t(1) << 27;
+
 struct FuseLayout {
   GemmPlan g;
   size_t y, end;
@@ -250,6 +267,33 @@ VerifyLayout layout_verify(const dflash& h, int S) {
   L.slice_sums = r.take((size_t)S * kSlices * 16);
   L.end = r.off;
   return L;
+}
+
+// Stage copies of a draft (instrumentation): per layer x_in, a, q, block K, block V^T,
+// o, x_attn, b, m; then the last residual stream and the final-normed mask rows.
+// Offsets in elements of the activation dtype.
+struct TraceLayout {
+  size_t x_in, a, q, kblk, vblk, o, x_attn, b, m, per_layer, x_last, z, end;
+};
+TraceLayout layout_trace(const dflash& h, int S) {
+  const auto& c = h.cfg;
+  const size_t M = (size_t)S * c.block_size, Mm = (size_t)S * (c.block_size - 1), H = c.hidden;
+  const size_t blk = (size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim;
+  TraceLayout t;
+  t.x_in = 0;
+  t.a = t.x_in + M * H;
+  t.q = t.a + M * H;
+  t.kblk = t.q + M * h.nq();
+  t.vblk = t.kblk + blk;
+  t.o = t.vblk + blk;
+  t.x_attn = t.o + M * h.nq();
+  t.b = t.x_attn + M * H;
+  t.m = t.b + M * H;
+  t.per_layer = t.m + M * c.intermediate;
+  t.x_last = (size_t)c.n_layers * t.per_layer;
+  t.z = t.x_last + M * H;
+  t.end = t.z + Mm * H;
+  return t;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -387,8 +431,12 @@ size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_strea
   if (!h || max_rows < 0 || n_streams < 1 || n_streams > h->cfg.max_streams || max_ctx < 0) return 0;
   size_t b = align_up(kCounterInts * 4);
   if (max_rows > 0) {
-    b = std::max(b, layout_fuse(*h, max_rows).end);
-    b = std::max(b, layout_inject(*h, max_rows).end);
+    // a call of up to max_rows rows runs passes of at most min(max_rows, kRowPass)
+    // rows, on the skinny kernel (float64 partials) up to 32 rows, tiled from 33
+    for (int r : {std::min(max_rows, kTallMinRows - 1), std::min(max_rows, kRowPass)}) {
+      b = std::max(b, layout_fuse(*h, r).end);
+      b = std::max(b, layout_inject(*h, r).end);
+    }
   }
   b = std::max(b, layout_draft(*h, n_streams, max_ctx).end);
   b = std::max(b, layout_verify(*h, n_streams).end);
@@ -509,39 +557,46 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   if (!tap_planes || !fused_out || !aligned16(fused_out)) return fail(h, DFLASH_ERR_ARG, "tap_planes or fused_out invalid");
   for (int t = 0; t < c.n_taps; ++t)
     if (!tap_planes[t] || !aligned16(tap_planes[t])) return fail(h, DFLASH_ERR_ARG, "tap plane %d is NULL or misaligned", t);
-  if (plane_row_stride < c.hidden || plane_row_stride % 8)
-    return fail(h, DFLASH_ERR_ARG, "plane_row_stride %lld must be >= hidden and a multiple of 8", (long long)plane_row_stride);
-  FuseLayout L = layout_fuse(*h, n_rows);
-  int rc = check_ws(h, ws, ws_bytes, L.end);
+  if (plane_row_stride < c.hidden || plane_row_stride % 8 || plane_row_stride > kMaxPlaneStride)
+    return fail(h, DFLASH_ERR_ARG, "plane_row_stride %lld must be >= hidden, <= 2^27 and a multiple of 8",
+                (long long)plane_row_stride);
+  const int pass = row_pass(n_rows);
+  int rc = check_ws(h, ws, ws_bytes, layout_fuse(*h, pass).end);
   if (rc) return rc;
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
-  GemmParams p = gemm_base(L.g, n_rows, c.hidden, c.n_taps * c.hidden);
-  for (int t = 0; t < c.n_taps; ++t) p.taps[t] = tap_planes[t];
-  p.tap_h = c.hidden;
-  p.tap_stride = plane_row_stride;
-  p.w0 = h->w.fc;
-  p.y_out = reinterpret_cast<double*>(W + L.y);
-  hipError_t e;
-  {
-    ProfScope ps(h, "fuse_fc_gemm", st);
-    e = run_gemm(c.dtype, L.g, EPI_RAW, p, st);
+  const size_t es = h->esize();
+  for (int r0 = 0; r0 < n_rows; r0 += pass) {
+    const int rows = std::min(pass, n_rows - r0);
+    const FuseLayout L = layout_fuse(*h, rows);
+    GemmParams p = gemm_base(L.g, rows, c.hidden, c.n_taps * c.hidden);
+    for (int t = 0; t < c.n_taps; ++t)
+      p.taps[t] = static_cast<const char*>(tap_planes[t]) + (size_t)r0 * plane_row_stride * es;
+    p.tap_h = c.hidden;
+    p.tap_stride = plane_row_stride;
+    p.w0 = h->w.fc;
+    p.y_out = reinterpret_cast<double*>(W + L.y);
+    hipError_t e;
+    {
+      ProfScope ps(h, "fuse_fc_gemm", st);
+      e = run_gemm(c.dtype, L.g, EPI_RAW, p, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
+    RowNormParams rn;
+    rn.R = rows;
+    rn.hidden = c.hidden;
+    rn.ksplit = L.g.ksplit;
+    rn.parts = p.y_out;
+    rn.parts_f32 = L.g.tall ? 1 : 0;   // the tiled kernel's partials are float32
+    rn.gain = h->w.hidden_norm;
+    rn.out = static_cast<char*>(fused_out) + (size_t)r0 * c.hidden * es;
+    rn.eps = c.rms_eps;
+    {
+      ProfScope ps(h, "fuse_rownorm", st);
+      e = launch_rownorm(c.dtype, rn, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse norm: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse fc: %s", hipGetErrorString(e));
-  RowNormParams rn;
-  rn.R = n_rows;
-  rn.hidden = c.hidden;
-  rn.ksplit = L.g.ksplit;
-  rn.parts = p.y_out;
-  rn.parts_f32 = L.g.tall ? 1 : 0;   // the tiled kernel's partials are float32
-  rn.gain = h->w.hidden_norm;
-  rn.out = fused_out;
-  rn.eps = c.rms_eps;
-  {
-    ProfScope ps(h, "fuse_rownorm", st);
-    e = launch_rownorm(c.dtype, rn, st);
-  }
-  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "fuse norm: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 
@@ -575,60 +630,64 @@ static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32
   if (!fused || !aligned16(fused) || !row_stream || !row_pos) return fail(h, DFLASH_ERR_ARG, "fused, row_stream or row_pos invalid");
   int rc = check_kv(h, kv);
   if (rc) return rc;
-  InjectLayout L = layout_inject(*h, n_rows);
-  rc = check_ws(h, ws, ws_bytes, L.end);
+  const int pass = row_pass(n_rows);
+  rc = check_ws(h, ws, ws_bytes, layout_inject(*h, pass).end);
   if (rc) return rc;
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
-  // the selected layers' [wk | wv] segments side by side; tiles of the all-layer plan
-  GemmPlan g = L.g;
-  const int N = n_sel * 2 * h->nkv();
-  g.n_tiles = (N + gemm_tile_cols(EPI_RAW) - 1) / gemm_tile_cols(EPI_RAW);
-  g.n_work = g.n_tiles * g.mgroups * g.ksplit;
-  GemmParams p = gemm_base(g, n_rows, N, c.hidden);
-  p.a = fused;
-  p.lda = c.hidden;
-  p.nkv = h->nkv();
-  p.seg_layers = n_sel;
-  for (int i = 0; i < n_sel; ++i) {
-    p.wk_l[i] = h->w.wk[sel[i]];
-    p.wv_l[i] = h->w.wv[sel[i]];
+  for (int r0 = 0; r0 < n_rows; r0 += pass) {
+    const int rows = std::min(pass, n_rows - r0);
+    const InjectLayout L = layout_inject(*h, rows);
+    // the selected layers' [wk | wv] segments side by side; tiles of the all-layer plan
+    GemmPlan g = L.g;
+    const int N = n_sel * 2 * h->nkv();
+    g.n_tiles = (N + gemm_tile_cols(EPI_RAW) - 1) / gemm_tile_cols(EPI_RAW);
+    g.n_work = g.n_tiles * g.mgroups * g.ksplit;
+    GemmParams p = gemm_base(g, rows, N, c.hidden);
+    p.a = static_cast<const char*>(fused) + (size_t)r0 * c.hidden * h->esize();
+    p.lda = c.hidden;
+    p.nkv = h->nkv();
+    p.seg_layers = n_sel;
+    for (int i = 0; i < n_sel; ++i) {
+      p.wk_l[i] = h->w.wk[sel[i]];
+      p.wv_l[i] = h->w.wv[sel[i]];
+    }
+    p.y_out = reinterpret_cast<double*>(W + L.raw);
+    hipError_t e;
+    {
+      ProfScope ps(h, "inject_kv_gemm", st);
+      e = run_gemm(c.dtype, g, EPI_RAW, p, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
+    KvFinishParams kf;
+    std::memset(&kf, 0, sizeof kf);
+    kf.R = rows;
+    kf.n_layers = n_sel;
+    kf.n_kv_heads = c.n_kv_heads;
+    kf.head_dim = c.head_dim;
+    kf.raw = p.y_out;
+    kf.ksplit = g.ksplit;
+    kf.raw_f32 = g.tall ? 1 : 0;
+    kf.row_stream = row_stream + r0;
+    kf.row_pos = row_pos + r0;
+    for (int i = 0; i < n_sel; ++i) {
+      kf.kn_l[i] = h->w.k_norm[sel[i]];
+      kf.kpool_l[i] = kv->k_pool[sel[i]];
+      kf.vpool_l[i] = kv->v_pool[sel[i]];
+    }
+    kf.page_table = kv->page_table;
+    kf.pages_per_stream = kv->pages_per_stream;
+    kf.page_size = c.page_size;
+    kf.pool_pages = c.pool_pages;
+    kf.max_streams = c.max_streams;
+    kf.theta = c.rope_theta;
+    kf.eps = c.rms_eps;
+    {
+      ProfScope ps(h, "inject_kv_finish", st);
+      e = launch_kv_finish(c.dtype, kf, st);
+    }
+    if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject finish: %s", hipGetErrorString(e));
   }
-  p.y_out = reinterpret_cast<double*>(W + L.raw);
-  hipError_t e;
-  {
-    ProfScope ps(h, "inject_kv_gemm", st);
-    e = run_gemm(c.dtype, g, EPI_RAW, p, st);
-  }
-  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject: %s", hipGetErrorString(e));
-  KvFinishParams kf;
-  std::memset(&kf, 0, sizeof kf);
-  kf.R = n_rows;
-  kf.n_layers = n_sel;
-  kf.n_kv_heads = c.n_kv_heads;
-  kf.head_dim = c.head_dim;
-  kf.raw = p.y_out;
-  kf.ksplit = g.ksplit;
-  kf.raw_f32 = g.tall ? 1 : 0;
-  kf.row_stream = row_stream;
-  kf.row_pos = row_pos;
-  for (int i = 0; i < n_sel; ++i) {
-    kf.kn_l[i] = h->w.k_norm[sel[i]];
-    kf.kpool_l[i] = kv->k_pool[sel[i]];
-    kf.vpool_l[i] = kv->v_pool[sel[i]];
-  }
-  kf.page_table = kv->page_table;
-  kf.pages_per_stream = kv->pages_per_stream;
-  kf.page_size = c.page_size;
-  kf.pool_pages = c.pool_pages;
-  kf.max_streams = c.max_streams;
-  kf.theta = c.rope_theta;
-  kf.eps = c.rms_eps;
-  {
-    ProfScope ps(h, "inject_kv_finish", st);
-    e = launch_kv_finish(c.dtype, kf, st);
-  }
-  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "inject finish: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 
@@ -683,6 +742,16 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
+  const TraceLayout T = layout_trace(*h, n_streams);
+  const size_t es = h->esize();
+  if (h->trace && h->trace_cap < T.end * es)
+    return fail(h, DFLASH_ERR_CAPACITY, "trace buffer holds %zu bytes, this draft needs %zu", h->trace_cap, T.end * es);
+  // instrumentation: copy a stored tensor into the trace (no-op when tracing is off)
+  auto trace = [&](size_t off, const void* src, size_t elems) -> hipError_t {
+    if (!h->trace) return hipSuccess;
+    return hipMemcpyAsync(static_cast<char*>(h->trace) + off * es, src, elems * es, hipMemcpyDeviceToDevice, st);
+  };
+  const size_t MH = (size_t)M * c.hidden, blk = (size_t)n_streams * c.n_kv_heads * kBlockSlots * c.head_dim;
   void* X = W + L.x;
   void* A = W + L.a;
   double* o_parts = reinterpret_cast<double*>(W + L.o_parts);   // wo . o, per K range
@@ -735,6 +804,9 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
       e = norm("norm_in", d_parts, L.down, h->w.in_norm[l], M, 0);
       if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d input norm: %s", l, hipGetErrorString(e));
     }
+    const size_t tl = (size_t)l * T.per_layer;
+    if ((e = trace(tl + T.x_in, X, MH)) != hipSuccess || (e = trace(tl + T.a, A, MH)) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
     // raw q | k | v = a . [wq | wk | wv]^T
     GemmParams p = gemm_base(L.qkv, M, h->nq() + 2 * h->nkv(), c.hidden);
     p.a = A;
@@ -775,6 +847,9 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
       e = launch_qkv_finish(c.dtype, qf, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d qkv finish: %s", l, hipGetErrorString(e));
+    if ((e = trace(tl + T.q, W + L.q, (size_t)M * h->nq())) != hipSuccess ||
+        (e = trace(tl + T.kblk, W + L.kblk, blk)) != hipSuccess || (e = trace(tl + T.vblk, W + L.vblk, blk)) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
 
     AttnParams ap;
     std::memset(&ap, 0, sizeof ap);
@@ -807,6 +882,8 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
       e = launch_attention(c.dtype, ap, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d attention: %s", l, hipGetErrorString(e));
+    if ((e = trace(tl + T.o, W + L.o_buf, (size_t)M * h->nq())) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
 
     // wo . o, per K range
     p = gemm_base(L.o, M, c.hidden, h->nq());
@@ -824,6 +901,8 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     // m = round(silu(w_gate . a) * (w_up . a))
     e = norm("norm_post", o_parts, L.o, h->w.post_norm[l], M, 0);
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d post norm: %s", l, hipGetErrorString(e));
+    if ((e = trace(tl + T.x_attn, X, MH)) != hipSuccess || (e = trace(tl + T.b, A, MH)) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
     p = gemm_base(L.gu, M, 2 * c.intermediate, c.hidden);
     p.a = A;
     p.lda = c.hidden;
@@ -836,6 +915,8 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
       e = run_gemm(c.dtype, L.gu, EPI_SWIGLU, p, st);
     }
     if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "layer %d gate/up: %s", l, hipGetErrorString(e));
+    if ((e = trace(tl + T.m, W + L.m, (size_t)M * c.intermediate)) != hipSuccess)
+      return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
 
     // w_down . m, per K range (added to X by the next norm: residual add 2)
     p = gemm_base(L.down, M, c.hidden, c.intermediate);
@@ -854,6 +935,8 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   // (lowest index on a tie).
   e = norm("norm_final", d_parts, L.down, h->w.norm, Mm, B - 1);
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "final norm: %s", hipGetErrorString(e));
+  if ((e = trace(T.x_last, X, MH)) != hipSuccess || (e = trace(T.z, A, (size_t)Mm * c.hidden)) != hipSuccess)
+    return fail(h, DFLASH_ERR_DEVICE, "trace: %s", hipGetErrorString(e));
   GemmParams p = gemm_base(L.lm, Mm, c.vocab, c.hidden);
   p.a = A;
   p.lda = c.hidden;
@@ -979,6 +1062,19 @@ int dflash_verify_sampling(dflash* h, int32_t n_streams, const int32_t* draft, c
     e = launch_verify_sampling(vp, st);
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "verify sampling: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+size_t dflash_trace_bytes(const dflash* h, int32_t n_streams) {
+  if (!h || n_streams < 1 || n_streams > h->cfg.max_streams) return 0;
+  return layout_trace(*h, n_streams).end * h->esize();
+}
+
+int dflash_set_trace(dflash* h, void* buf, size_t bytes) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (buf && !aligned16(buf)) return fail(h, DFLASH_ERR_ARG, "trace buffer misaligned");
+  h->trace = bytes ? buf : nullptr;
+  h->trace_cap = buf ? bytes : 0;
   return DFLASH_OK;
 }
 

@@ -136,7 +136,11 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   // a source address (matrix, first row of the load, chunk) is a scalar, the lane adds
   // a fixed offset. Rows past M (and LM-head rows past N) repeat the last row; their
   // results are never stored.
+  // Each load's resource starts at its first row (a 64-bit base), so a lane's offset
+  // spans at most RPL - 1 row strides: the host bounds the tap planes' row stride so
+  // that this stays inside the resource's 31-bit range for any row count.
   int a_off[QA], w_off[QB];
+  int64_t a_row0[QA];
   __amdgpu_buffer_rsrc_t a_rsrc[QA], w_rsrc[QB];
 #pragma unroll
   for (int k = 0; k < QA; ++k) {
@@ -145,7 +149,8 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
     const int piece = (lane % NPC) ^ swz(row);
     const int ar0 = min(rt * BM + RPL * q, p.M - 1), ar = min(rt * BM + row, p.M - 1);
     if constexpr (AM == A_TAPS) {
-      a_off[k] = (int)((int64_t)ar * p.tap_stride) + piece * 8;
+      a_row0[k] = (int64_t)ar0 * p.tap_stride;
+      a_off[k] = (int)((int64_t)(ar - ar0) * p.tap_stride) + piece * 8;
     } else {
       a_rsrc[k] = rsrc_of(static_cast<const bf16_t*>(p.a) + (int64_t)ar0 * p.lda);
       a_off[k] = (ar - ar0) * (int)p.lda + piece * 8;
@@ -178,8 +183,8 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       if constexpr (AM == A_TAPS) {
         // a chunk never straddles two planes (hidden % 64 == 0)
         const int plane = k0 / p.tap_h;
-        buf_load_lds16(rsrc_of(static_cast<const bf16_t*>(p.taps[plane]) + (k0 - plane * p.tap_h)), 2u * (uint32_t)a_off[k],
-                       0u, buf + q * 1024);
+        buf_load_lds16(rsrc_of(static_cast<const bf16_t*>(p.taps[plane]) + a_row0[k] + (k0 - plane * p.tap_h)),
+                       2u * (uint32_t)a_off[k], 0u, buf + q * 1024);
       } else {
         buf_load_lds16(a_rsrc[k], 2u * (uint32_t)a_off[k], 2u * (uint32_t)k0, buf + q * 1024);
       }

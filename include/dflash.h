@@ -167,9 +167,13 @@ int dflash_workspace_init(dflash *h, void *ws, size_t ws_bytes, void *stream);
  * * hidden_norm, stored in the dtype (TensorFold #1851, items 3 and 4: the taps pass runs
  * fc and hidden_norm once a row's planes are complete).
  *   tap_planes: host array of n_taps device pointers; plane t is [n_rows, hidden] with
- *               a row stride of plane_row_stride elements (>= hidden, multiple of 8).
+ *               a row stride of plane_row_stride elements (>= hidden, <= 2^27, multiple
+ *               of 8; else DFLASH_ERR_ARG).
  *   fused_out:  device [n_rows, hidden].
- * n_rows == 0 is a no-op. n_rows beyond the workspace's max_rows -> DFLASH_ERR_CAPACITY.
+ * n_rows == 0 is a no-op. A workspace sized for fewer rows -> DFLASH_ERR_CAPACITY. Calls
+ * of more than 8192 rows (prompt scale) run as equal passes of at most 8192 rows, so the
+ * workspace needed stops growing there; a row's result is the same bits in any call of
+ * 33 rows or more.
  */
 int dflash_fuse_taps(dflash *h, const void *const *tap_planes, int64_t plane_row_stride,
                      int32_t n_rows, void *fused_out, void *ws, size_t ws_bytes, void *stream);
@@ -182,7 +186,8 @@ int dflash_fuse_taps(dflash *h, const void *const *tap_planes, int64_t plane_row
  * TensorFold #1851 item 4; DFlash explainer section 3, KV injection into every layer).
  * row_stream / row_pos are device int32 [n_rows]; rows with a stream outside
  * [0, max_streams), a position outside [0, pages_per_stream * page_size) or an invalid
- * page are skipped. n_rows == 0 is a no-op.
+ * page are skipped. n_rows == 0 is a no-op. Like dflash_fuse_taps, calls of more than
+ * 8192 rows run in equal passes of at most 8192 rows.
  */
 int dflash_inject_kv(dflash *h, const void *fused, int32_t n_rows, const int32_t *row_stream,
                      const int32_t *row_pos, const dflash_kv *kv, void *ws, size_t ws_bytes,
@@ -312,6 +317,31 @@ int dflash_verify_sampling(dflash *h, int32_t n_streams, const int32_t *draft,
  */
 int dflash_set_profiling(dflash *h, int32_t enable);
 int dflash_profile_read(dflash *h, char *buf, size_t len);
+
+/*
+ * Stage trace (instrumentation for parity tests; not part of the round). With a trace
+ * buffer set, dflash_draft_block also copies every tensor it stores into the buffer,
+ * on its stream, so each step can be checked on exactly the inputs it read. Layout, in
+ * elements of the activation dtype, with M = n_streams * B, Mm = n_streams * (B - 1):
+ * for each layer l, one record of
+ *   x_in [M, hidden]          the layer's input residual stream (the embedding rows
+ *                             for layer 0; after residual add 2 of layer l - 1)
+ *   a [M, hidden]             round(RMSNorm(x_in) * in_norm)
+ *   q [M, n_q * d]            normalised, rotated queries
+ *   k [n_streams, n_kv, 32, d]    block keys (rows >= B unused)
+ *   v [n_streams, n_kv, d, 32]    block values, transposed (columns >= B unused)
+ *   o [M, n_q * d]            attention output
+ *   x_attn [M, hidden]        after residual add 1
+ *   b [M, hidden]             round(RMSNorm(x_attn) * post_norm)
+ *   m [M, intermediate]       SwiGLU product
+ * then x_last [M, hidden] (after the last layer's add 2; only the mask rows are
+ * updated) and z [Mm, hidden] (the final-normed mask rows, stream-major).
+ * dflash_trace_bytes gives the size for n_streams (0 when out of range). A draft whose
+ * trace would not fit the buffer is refused (DFLASH_ERR_CAPACITY). buf == NULL or
+ * bytes == 0 turns the trace off. The buffer is caller-owned device memory.
+ */
+size_t dflash_trace_bytes(const dflash *h, int32_t n_streams);
+int dflash_set_trace(dflash *h, void *buf, size_t bytes);
 
 /* The last error message of a handle (or of dflash_create when h is NULL). Never NULL. */
 const char *dflash_last_error(const dflash *h);

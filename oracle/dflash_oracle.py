@@ -219,31 +219,43 @@ def context_reach(C, window):
     return (0 if window == 0 else max(0, C - window)), C
 
 
-def draft_layer(cfg, l, X, W, k_ctx, v_ctx, C, trace=None):
-    """One qwen3 layer over the block rows X [B, h] (two residual adds)."""
+def draft_layer(cfg, l, X, W, k_ctx, v_ctx, C, trace=None, given=None):
+    """One qwen3 layer over the block rows X [B, h] (two residual adds).
+
+    `given` (parity tests only): stored tensors of another implementation of this
+    layer (any of a, q, k, v, o, x_attn, b, m; q [B, n_q, d], k and v [B, n_kv, d],
+    the others [B, width]). A step whose input is given reads it instead of this
+    function's own previous step, so every step is computed on exactly the inputs the
+    other implementation used; the trace still records this function's own results.
+    """
     pre = f"layers.{l}."
     dt, eps = cfg.dtype, cfg.rms_eps
     B = X.shape[0]
     nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     pos = C + np.arange(B)
+    g = {} if given is None else given
+    use = lambda name, own: as_f64(g[name]) if name in g else own
 
     a = round_to(rms_norm(X, as_f64(W[pre + "in_norm"]), eps), dt)                    # R3
-    q = rms_norm(linear(a, W[pre + "wq"]).reshape(B, nq, d), as_f64(W[pre + "q_norm"]), eps)
-    k = rms_norm(linear(a, W[pre + "wk"]).reshape(B, nkv, d), as_f64(W[pre + "k_norm"]), eps)
-    v = linear(a, W[pre + "wv"]).reshape(B, nkv, d)
+    a_in = use("a", a)
+    q = rms_norm(linear(a_in, W[pre + "wq"]).reshape(B, nq, d), as_f64(W[pre + "q_norm"]), eps)
+    k = rms_norm(linear(a_in, W[pre + "wk"]).reshape(B, nkv, d), as_f64(W[pre + "k_norm"]), eps)
+    v = linear(a_in, W[pre + "wv"]).reshape(B, nkv, d)
     q = round_to(rope(q, pos[:, None], cfg.rope_theta), dt)                           # R4
     k = round_to(rope(k, pos[:, None], cfg.rope_theta), dt)
     v = round_to(v, dt)
 
     lo, hi = context_reach(C, cfg.layer_window[l])
-    keys = np.concatenate([as_f64(k_ctx[lo:hi]), k], axis=0)
-    vals = np.concatenate([as_f64(v_ctx[lo:hi]), v], axis=0)
-    o = round_to(block_attention(q, keys, vals, nkv).reshape(B, nq * d), dt)          # R5
+    keys = np.concatenate([as_f64(k_ctx[lo:hi]), use("k", k)], axis=0)
+    vals = np.concatenate([as_f64(v_ctx[lo:hi]), use("v", v)], axis=0)
+    o = round_to(block_attention(use("q", q), keys, vals, nkv).reshape(B, nq * d), dt)  # R5
 
-    X1 = round_to(X + linear(o, W[pre + "wo"]), dt)                                   # R6: add #1
-    b = round_to(rms_norm(X1, as_f64(W[pre + "post_norm"]), eps), dt)                 # R3
-    m = round_to(silu(linear(b, W[pre + "w_gate"])) * linear(b, W[pre + "w_up"]), dt)  # R7
-    X2 = round_to(X1 + linear(m, W[pre + "w_down"]), dt)                              # R8: add #2
+    X1 = round_to(X + linear(use("o", o), W[pre + "wo"]), dt)                         # R6: add #1
+    X1_in = use("x_attn", X1)
+    b = round_to(rms_norm(X1_in, as_f64(W[pre + "post_norm"]), eps), dt)              # R3
+    b_in = use("b", b)
+    m = round_to(silu(linear(b_in, W[pre + "w_gate"])) * linear(b_in, W[pre + "w_up"]), dt)  # R7
+    X2 = round_to(X1_in + linear(use("m", m), W[pre + "w_down"]), dt)                 # R8: add #2
     if trace is not None:
         trace.setdefault("layers", []).append(
             dict(a=a, q=q, k=k, v=v, o=o, x_attn=X1, b=b, m=m, x_out=X2, reach=(lo, hi)))

@@ -153,8 +153,11 @@ def test_round_calls_refuse_on_the_host_before_any_enqueue():
     planes = (ctypes.c_void_p * 3)(1 << 24, 1 << 25, 1 << 26)
     rc = lib.dflash_fuse_taps(dr.h, planes, 256, 4, fake, fake, 1 << 20, None)
     assert rc == -5 and "initialised" in dr.last_error()
-    # bad stride, zero rows is a no-op
+    # bad stride (below hidden, not a multiple of 8, past 2^27), zero rows is a no-op
     assert lib.dflash_fuse_taps(dr.h, planes, 100, 4, fake, fake, 1 << 20, None) == -1
+    assert lib.dflash_fuse_taps(dr.h, planes, 260, 4, fake, fake, 1 << 20, None) == -1
+    assert lib.dflash_fuse_taps(dr.h, planes, (1 << 27) + 8, 4, fake, fake, 1 << 20, None) == -1
+    assert "2^27" in dr.last_error()
     assert lib.dflash_fuse_taps(dr.h, planes, 256, 0, fake, fake, 1 << 20, None) == 0
     # a request past the cache span is refused
     kv = D.KV()
@@ -205,3 +208,14 @@ def test_layers_reading_follows_each_layers_reach():
     # a prompt row older than every window is read by the full layer alone
     assert dr.dflash_layers_reading(0, 32768) == 1 << 5
     assert D.library().dflash_layers_reading(None, 0, 10) == 0
+
+
+def test_prompt_scale_calls_need_a_bounded_workspace():
+    # fuse and inject run calls of more than 8192 rows as passes of at most 8192 rows,
+    # so the workspace for a 65536-row prompt is the one for 8192 rows; calls of up to
+    # 32 rows (float64 partials) are covered by any larger request too
+    dr = D.Drafter(cfg_of("9b_ctx4k"))
+    a = dr.workspace_bytes(8192, 1, 4096)
+    assert dr.workspace_bytes(65536, 1, 4096) == a
+    assert dr.workspace_bytes(40, 1, 4096) >= dr.workspace_bytes(32, 1, 4096)
+    assert dr.workspace_bytes(2048, 1, 4096) < a

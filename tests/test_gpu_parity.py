@@ -297,28 +297,82 @@ def test_fuse_and_inject_parity(preset, rows):
         assert_close_storage(to_np(vg), kv[l][1], p.dtype, f"V layer {l}")
 
 
-def test_prefill_scale_fuse_and_inject_sampled_rows():
-    # 2048 prompt rows of one stream at the 9B shapes (fc K = 32768): eight row tiles of
-    # the tiled kernel. The oracle computes a sample of the rows (the steps act on each
-    # row alone); inject is checked on the GPU's own fused rows.
-    p = small_variant(wl.preset("9b_ctx4k"), n_streams=1)
-    R = 2048
-    case = RoundCase(p, ctx=[4096], rows=[R])
-    log(f"[fuse/inject] {p.name} prefill rows={R}")
+def _prompt_case(preset, R, interleave):
+    """One stream's R prompt rows at the preset's shapes; with interleave the tap planes
+    are views of one [R, n_taps, hidden] buffer (row stride n_taps * hidden)."""
+    p = small_variant(wl.preset(preset), n_streams=1)
+    case = RoundCase(p, ctx=[R], rows=[R])
+    if interleave:
+        buf = torch.stack(case.taps, dim=1)
+        case.taps = [buf[:, t, :] for t in range(p.n_taps)]
+        assert case.taps[0].stride(0) == p.n_taps * p.hidden
+    return p, case
+
+
+@pytest.mark.parametrize("R,interleave", [(100, True), (8192, False), (65536, True)])
+def test_prompt_scale_fuse_and_inject_sampled_rows(R, interleave):
+    # Prompt-scale fuse + inject at the 9B shapes (fc K = 32768): 100 rows (one row tile),
+    # 8192 rows (one pass of the tiled kernel) and 65536 rows (eight passes). Interleaved
+    # planes put row r of plane t at element (r * 8 + t) * 4096: past row 32767 its byte
+    # offset exceeds 2^31, which the tiled kernel's per-load resource base must absorb.
+    # Sampled rows (pass and row-tile edges, both sides of 2^31 bytes) against the
+    # oracle; inject on the GPU's own fused rows.
+    p, case = _prompt_case("9b_ctx4k", R, interleave)
+    log(f"[fuse/inject] {p.name} prompt rows={R} interleaved={interleave}")
     case.fuse()
     case.inject()
     torch.cuda.synchronize()
-    idx = [0, 1, 255, 256, 1023, 1500, 2046, 2047]
+    idx = sorted({i for i in (0, 1, 255, 256, 8191, 8192, 16383, 32767, 32768, 40000, 57344, R - 2, R - 1) if i < R})
     W = case.weights_np()
     fused = O.fuse_taps(p, [to_np(t[idx]) for t in case.taps], W)
     assert_close_storage(to_np(case.fused[idx]), fused, p.dtype, "fused (sampled rows)")
-    pos = [case.ctx[0] - R + i for i in idx]
-    kv = O.inject_kv(p, to_np(case.fused[idx]), np.array(pos), W)
+    pos = np.array(idx)
+    kv = O.inject_kv(p, to_np(case.fused[idx]), pos, W)
     for l in range(p.n_layers):
-        for j, ps in enumerate(pos):
+        for j, ps in enumerate(idx):
             kg, vg = case.kv.read_rows(l, 0, ps, 1)
             assert_close_storage(to_np(kg), kv[l][0][j:j + 1], p.dtype, f"K layer {l} pos {ps}")
             assert_close_storage(to_np(vg), kv[l][1][j:j + 1], p.dtype, f"V layer {l} pos {ps}")
+    if R == 100:
+        # the interleaved planes give the bits of the same rows given as separate planes
+        sep = [t.contiguous() for t in case.taps]
+        out = torch.zeros_like(case.fused)
+        case.dr.dflash_fuse_taps(sep, out, case.ws, n_rows=R)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), case.fused.view(torch.int16))
+
+
+def test_prompt_scale_deferred_inject_65536_rows():
+    # 65536 prompt rows at the 32k-span shapes (five sliding layers of 4096, one full):
+    # rows older than P - 4096 are injected into the full layer alone, the rest into all
+    # six, each group in passes of 8192 rows. Sampled slots hold the bits of the
+    # all-layer inject; unselected slots stay untouched.
+    p, case = _prompt_case("9b_ctx32k", 65536, False)
+    P = 65536
+    case.fuse()
+    case.inject()
+    torch.cuda.synchronize()
+    idx = [0, 8191, 8192, 32768, P - 4097, P - 4096, P - 1]
+    full = [[tuple(t.clone() for t in case.kv.read_rows(l, 0, i, 1)) for i in idx] for l in range(p.n_layers)]
+    for l in range(p.n_layers):
+        case.kv.k[l].zero_()
+        case.kv.v[l].zero_()
+    masks = [case.dr.dflash_layers_reading(i, P) for i in (0, P - 4096)]
+    assert masks == [1 << 5, 0b111111]
+    cut = P - 4096
+    case.dr.dflash_inject_kv_layers(case.fused[:cut], case.row_stream[:cut], case.row_pos[:cut], case.kv, masks[0],
+                                    case.ws)
+    case.dr.dflash_inject_kv_layers(case.fused[cut:], case.row_stream[cut:], case.row_pos[cut:], case.kv, masks[1],
+                                    case.ws)
+    torch.cuda.synchronize()
+    for l in range(p.n_layers):
+        for j, i in enumerate(idx):
+            k, v = case.kv.read_rows(l, 0, i, 1)
+            if (masks[0 if i < cut else 1] >> l) & 1:
+                assert torch.equal(k.view(torch.int16), full[l][j][0].view(torch.int16)), f"layer {l} row {i} K"
+                assert torch.equal(v.view(torch.int16), full[l][j][1].view(torch.int16)), f"layer {l} row {i} V"
+            else:
+                assert not k.any() and not v.any(), f"layer {l} row {i}: an unselected slot was written"
 
 
 def test_inject_skips_invalid_rows_and_touches_nothing_else():

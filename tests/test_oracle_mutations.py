@@ -21,24 +21,26 @@ ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 MUTATIONS = [
     # layer wiring (TensorFold #1851 item 1: plain qwen3 body, two residual adds)
     ("in_norm and post_norm gains trade places",
-     ['rms_norm(X, as_f64(W[pre + "in_norm"]), eps)', 'rms_norm(X1, as_f64(W[pre + "post_norm"]), eps)'],
-     ['rms_norm(X, as_f64(W[pre + "post_norm"]), eps)', 'rms_norm(X1, as_f64(W[pre + "in_norm"]), eps)']),
+     ['rms_norm(X, as_f64(W[pre + "in_norm"]), eps)', 'rms_norm(X1_in, as_f64(W[pre + "post_norm"]), eps)'],
+     ['rms_norm(X, as_f64(W[pre + "post_norm"]), eps)', 'rms_norm(X1_in, as_f64(W[pre + "in_norm"]), eps)']),
     ("norm gains swapped: post_norm before attention",
      'rms_norm(X, as_f64(W[pre + "in_norm"]), eps)', 'rms_norm(X, as_f64(W[pre + "post_norm"]), eps)'),
     ("norm gains swapped: in_norm before the MLP",
-     'rms_norm(X1, as_f64(W[pre + "post_norm"]), eps)', 'rms_norm(X1, as_f64(W[pre + "in_norm"]), eps)'),
+     'rms_norm(X1_in, as_f64(W[pre + "post_norm"]), eps)', 'rms_norm(X1_in, as_f64(W[pre + "in_norm"]), eps)'),
     ("add 2 onto the layer input, dropping add 1 from the stream",
-     'X2 = round_to(X1 + linear(m, W[pre + "w_down"]), dt)', 'X2 = round_to(X + linear(m, W[pre + "w_down"]), dt)'),
-    ("add 1 dropped", 'X1 = round_to(X + linear(o, W[pre + "wo"]), dt)', 'X1 = round_to(linear(o, W[pre + "wo"]), dt)'),
-    ("add 2 dropped", 'X2 = round_to(X1 + linear(m, W[pre + "w_down"]), dt)',
-     'X2 = round_to(linear(m, W[pre + "w_down"]), dt)'),
+     'X2 = round_to(X1_in + linear(use("m", m), W[pre + "w_down"]), dt)',
+     'X2 = round_to(X + linear(use("m", m), W[pre + "w_down"]), dt)'),
+    ("add 1 dropped", 'X1 = round_to(X + linear(use("o", o), W[pre + "wo"]), dt)',
+     'X1 = round_to(linear(use("o", o), W[pre + "wo"]), dt)'),
+    ("add 2 dropped", 'X2 = round_to(X1_in + linear(use("m", m), W[pre + "w_down"]), dt)',
+     'X2 = round_to(linear(use("m", m), W[pre + "w_down"]), dt)'),
     ("MLP normalises the layer input instead of add 1's sum",
-     'b = round_to(rms_norm(X1,', 'b = round_to(rms_norm(X,'),
-    ("SiLU on the up branch", 'silu(linear(b, W[pre + "w_gate"])) * linear(b, W[pre + "w_up"])',
-     'linear(b, W[pre + "w_gate"]) * silu(linear(b, W[pre + "w_up"]))'),
+     'b = round_to(rms_norm(X1_in,', 'b = round_to(rms_norm(X,'),
+    ("SiLU on the up branch", 'silu(linear(b_in, W[pre + "w_gate"])) * linear(b_in, W[pre + "w_up"])',
+     'linear(b_in, W[pre + "w_gate"]) * silu(linear(b_in, W[pre + "w_up"]))'),
     ("q normalised with k_norm's gain", 'as_f64(W[pre + "q_norm"]), eps)', 'as_f64(W[pre + "k_norm"]), eps)'),
-    ("block values taken from wk", 'v = linear(a, W[pre + "wv"]).reshape(B, nkv, d)',
-     'v = linear(a, W[pre + "wk"]).reshape(B, nkv, d)'),
+    ("block values taken from wk", 'v = linear(a_in, W[pre + "wv"]).reshape(B, nkv, d)',
+     'v = linear(a_in, W[pre + "wk"]).reshape(B, nkv, d)'),
     # storage points R1..R9
     ("R1 fused row not rounded", 'return round_to(rms_norm(y, as_f64(W["hidden_norm"]), cfg.rms_eps), cfg.dtype)',
      'return rms_norm(y, as_f64(W["hidden_norm"]), cfg.rms_eps)'),
@@ -47,14 +49,16 @@ MUTATIONS = [
     ("R3 layer input not rounded", 'a = round_to(rms_norm(X, as_f64(W[pre + "in_norm"]), eps), dt)',
      'a = rms_norm(X, as_f64(W[pre + "in_norm"]), eps)'),
     ("R4 block v not rounded", "v = round_to(v, dt)", "v = v"),
-    ("R5 attention output not rounded", "o = round_to(block_attention(q, keys, vals, nkv).reshape(B, nq * d), dt)",
-     "o = block_attention(q, keys, vals, nkv).reshape(B, nq * d)"),
-    ("R6 add 1 not rounded", 'X1 = round_to(X + linear(o, W[pre + "wo"]), dt)', 'X1 = X + linear(o, W[pre + "wo"])'),
+    ("R5 attention output not rounded",
+     'o = round_to(block_attention(use("q", q), keys, vals, nkv).reshape(B, nq * d), dt)',
+     'o = block_attention(use("q", q), keys, vals, nkv).reshape(B, nq * d)'),
+    ("R6 add 1 not rounded", 'X1 = round_to(X + linear(use("o", o), W[pre + "wo"]), dt)',
+     'X1 = X + linear(use("o", o), W[pre + "wo"])'),
     ("R7 SwiGLU product not rounded",
-     'm = round_to(silu(linear(b, W[pre + "w_gate"])) * linear(b, W[pre + "w_up"]), dt)',
-     'm = silu(linear(b, W[pre + "w_gate"])) * linear(b, W[pre + "w_up"])'),
-    ("R8 add 2 not rounded", 'X2 = round_to(X1 + linear(m, W[pre + "w_down"]), dt)',
-     'X2 = X1 + linear(m, W[pre + "w_down"])'),
+     'm = round_to(silu(linear(b_in, W[pre + "w_gate"])) * linear(b_in, W[pre + "w_up"]), dt)',
+     'm = silu(linear(b_in, W[pre + "w_gate"])) * linear(b_in, W[pre + "w_up"])'),
+    ("R8 add 2 not rounded", 'X2 = round_to(X1_in + linear(use("m", m), W[pre + "w_down"]), dt)',
+     'X2 = X1_in + linear(use("m", m), W[pre + "w_down"])'),
     ("R9 final-normed rows not rounded", 'z = round_to(rms_norm(X[1:], as_f64(W["norm"]), cfg.rms_eps), cfg.dtype)',
      'z = rms_norm(X[1:], as_f64(W["norm"]), cfg.rms_eps)'),
     ("bf16 rounding through an fp32 stage", "y = np.ldexp(np.rint(np.ldexp(x, -q)), q)",
@@ -77,7 +81,8 @@ MUTATIONS = [
     ("sliding reach one row short", "return (0 if window == 0 else max(0, C - window)), C",
      "return (0 if window == 0 else max(0, C - window + 1)), C"),
     ("block rows one position early", "pos = C + np.arange(B)", "pos = C - 1 + np.arange(B)"),
-    ("block keys left out", "keys = np.concatenate([as_f64(k_ctx[lo:hi]), k], axis=0)\n    vals = np.concatenate([as_f64(v_ctx[lo:hi]), v], axis=0)",
+    ("block keys left out",
+     'keys = np.concatenate([as_f64(k_ctx[lo:hi]), use("k", k)], axis=0)\n    vals = np.concatenate([as_f64(v_ctx[lo:hi]), use("v", v)], axis=0)',
      "keys = as_f64(k_ctx[lo:hi]) if hi > lo else k\n    vals = as_f64(v_ctx[lo:hi]) if hi > lo else v"),
     # head and verify (explainer sections 4-5)
     ("logits from the rows before the masks", 'z = round_to(rms_norm(X[1:],', 'z = round_to(rms_norm(X[:-1],'),
