@@ -12,9 +12,9 @@
 // conflicts. Scores are computed transposed (S^T = K Q^T) so that each lane owns
 // one query: the softmax statistics are lane-local plus two cross-lane-group
 // shuffles, and the probabilities feed the P.V MFMA without a transpose. The
-// running maximum moves once per batch; P (fp32) enters the bf16 MFMA as two bf16
-// parts (hi, lo: within 2^-18 of P, relative), and a batch's P.V accumulates
-// into the rescaled fp32 running output. Which keys
+// running maximum moves once per batch; P (fp32) enters the bf16 MFMA as three bf16
+// parts that sum to it exactly, and a batch's P.V accumulates into the rescaled fp32
+// running output. Which keys
 // of a step are valid is one wave-uniform 32-bit mask, so steps without an edge
 // (reach boundary, missing page, block padding) take no masking work at all.
 // A stream whose reach spans several chunks leaves per-chunk partials (max, sum,
@@ -278,19 +278,23 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   auto pv_step = [&](const unsigned char* buf, int st, const float (&pr)[2][4], uint32_t m, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     if constexpr (BF) {
-      // P as hi + lo bf16 parts: hi = bf16(P) is within 2^-9 of P, the remainder P - hi
-      // is exact in fp32 and lo = bf16(P - hi) within 2^-9 of it, so hi + lo is within
-      // 2^-18 of P (relative), far below the bf16 rounding of the stored output.
+      // P as three bf16 parts that sum to it exactly: hi = bf16(P); the remainder
+      // P - hi is exact in fp32 and keeps at most 16 significant bits, mid = bf16 of
+      // it; what is left, at most 8 bits, is exact in bf16 (lo). Two parts would leave
+      // P off by up to 2^-18 (relative) per key, which alone moves about 2e-3 of the
+      // stored bf16 outputs by one ulp; with three, only P's own fp32 rounding remains.
       const float pv[8] = {pr[0][0], pr[0][1], pr[0][2], pr[0][3], pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
-      uint32_t hw[4], lw[4];
+      uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         hw[q] = f32x2_to_bf16x2(pv[2 * q], pv[2 * q + 1]);
         const float r0 = pv[2 * q] - bf16_to_f32(hw[q] & 0xffffu);
         const float r1 = pv[2 * q + 1] - bf16_to_f32(hw[q] >> 16);
-        lw[q] = f32x2_to_bf16x2(r0, r1);
+        mw[q] = f32x2_to_bf16x2(r0, r1);
+        lw[q] = f32x2_to_bf16x2(r0 - bf16_to_f32(mw[q] & 0xffffu), r1 - bf16_to_f32(mw[q] >> 16));
       }
       const uint4 bh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      const uint4 bm = make_uint4(mw[0], mw[1], mw[2], mw[3]);
       const uint4 bl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       uint32_t keep[4] = {~0u, ~0u, ~0u, ~0u};
       if constexpr (MASKED) {
@@ -310,6 +314,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
           vf.w &= keep[3];
         }
         mma_frag(orun[dt], vf, bh, T());
+        mma_frag(orun[dt], vf, bm, T());
         mma_frag(orun[dt], vf, bl, T());
       }
     } else {

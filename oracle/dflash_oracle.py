@@ -73,7 +73,7 @@ def as_f64(a):
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return bf16_bits_to_f64(a)
-    return a.astype(np.float64)
+    return a.astype(np.float64, copy=False)
 
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
