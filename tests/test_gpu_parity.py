@@ -9,14 +9,15 @@ Bars (the oracle keeps float64; the GPU sums in fp32):
     2e-2 of the float64 oracle logits (fp32 presets: 1e-4);
   * logits of the 9B- and DFlash2-shaped presets, whole rounds and each layer run
     alone as a one-layer model: their random-weight float64 models move by more than
-    2e-2 (one layer: ~1e-2..2e-2, five or six layers: ~8e-2) when one stored element in
-    10^4 is rounded the other way, so no fp32-accumulating implementation can be held
-    to 2e-2 there. Their bar is tol = max(2e-2, 2 x the oracle's own max logit movement
-    under seeded 1-ulp flips at a rate of 1e-4 per stored element), and mean |d| <= 2 x
-    its mean movement. (Stage by stage on one layer the GPU's q, k, v differ from the
-    oracle's in ~1e-5 of the elements and the attention output in ~4e-4, from the fp32
-    sums inside the P.V MFMA; the MLP's roundings then carry those few flips into a
-    large share of the layer's output.)
+    2e-2 when a fraction 1e-4 of their stored elements is rounded the other way (a
+    one-layer model of the 9B width already moves ~0.027), and fp32 sums alone flip
+    more than 1e-4 of a projection's outputs, so no fp32-summing implementation can be
+    held to 2e-2 there. Their bar is tol = max(2e-2, FACTOR x the oracle's own max logit
+    movement at RATE) and mean |d| <= FACTOR x its mean movement, with RATE = 1e-4 and
+    FACTOR = 2 pinned on the CPU by tests/test_oracle_conditioning.py. Every step of
+    those rounds is held to 1 ulp on identical inputs by tests/test_gpu_stages.py.
+    Each comparison also logs the benchmark spec's own figures: the max-abs against 2e-2
+    and the drafted tokens that differ where the oracle's top-2 gap exceeds 2e-2;
   * drafted tokens: equal to the oracle's wherever the oracle's top-2 gap exceeds
     the logit tolerance, elsewhere the GPU token's oracle logit lies within the
     tolerance of the maximum;
@@ -31,6 +32,7 @@ import pytest
 import torch
 
 import block_diffusion_drafter_dflash_amd as D
+import conditioning as CD
 import workloads as wl
 from oracle import dflash_oracle as O
 from workloads.presets import small_variant
@@ -120,6 +122,11 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
                         problems.append(f"stream {s} {nm} layer {l}: {n} elements past the propagated bar (worst {ex:.3g})")
         d = float(np.max(np.abs(logits[s] - o["logits"])))
         worst = max(worst, d)
+        srt = np.sort(o["logits"], axis=-1)
+        sure = (srt[:, -1] - srt[:, -2]) > 2e-2
+        ns_off = int(np.sum(toks[s][sure] != O.argmax_lowest(o["logits"])[sure]))
+        log(f"[northstar] {p.name} stream {s}: logits max-abs {d:.4g} vs 2e-2 ({'met' if d <= 2e-2 else 'not met'}); "
+            f"tokens differing where the gap > 2e-2: {ns_off} of {int(sure.sum())}")
         t1, t2 = O.top2(o["logits"])
         dt = float(max(np.max(np.abs(top2[s, :, 0] - t1)), np.max(np.abs(top2[s, :, 1] - t2))))
         dm = float(np.mean(np.abs(logits[s] - o["logits"])))
@@ -141,40 +148,21 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
     return worst
 
 
-def oracle_flip_movement(case, streams, rate=1e-4, seed=12345):
-    """How far the oracle's own logits move when a seeded fraction `rate` of its
-    stored (rounded) elements are moved by one ulp: the conditioning of the round."""
-    base = {}
-    orig = O.round_to
-    rng = np.random.default_rng(seed)
-
-    def flippy(x, dtype):
-        y = orig(x, dtype)
-        if dtype != "bf16":
-            return y
-        m = rng.random(np.shape(y)) < rate
-        ulp = ulp_bf16(y)
-        return np.where(m, y + np.where(x >= y, 1.0, -1.0) * ulp, y)
-
-    O.round_to = flippy
-    try:
-        pert = O.run_round(case.p, case.weights_np(), case.oracle_streams(streams))
-    finally:
-        O.round_to = orig
-    return pert
-
-
-def run_case(case, streams, conditioning=False):
+def run_case(case, streams, conditioning=False, flip_streams=None):
     log(f"[case] {case.p.name} S={case.p.n_streams} ctx={case.ctx} rows={case.rows} streams={streams}")
     case.run_gpu()
-    orc = O.run_round(case.p, case.weights_np(), case.oracle_streams(streams))
+    W = {k: O.as_f64(v) for k, v in case.weights_np().items()}     # float64 once, for every oracle call
+    orc = O.run_round(case.p, W, case.oracle_streams(streams))
     tol = mean_tol = None
     if conditioning:
-        pert = oracle_flip_movement(case, streams)
-        mx = max(float(np.max(np.abs(a["logits"] - b["logits"]))) for a, b in zip(orc, pert))
-        mn = max(float(np.mean(np.abs(a["logits"] - b["logits"]))) for a, b in zip(orc, pert))
-        tol, mean_tol = max(LOGIT_TOL[case.p.dtype], 2 * mx), 2 * mn
-        log(f"[case] oracle movement under 1e-4 one-ulp flips: max {mx:.4g} mean {mn:.3g} -> tolerance {tol:.3g}")
+        fs = streams if flip_streams is None else flip_streams
+        base = [orc[streams.index(s)]["logits"] for s in fs]
+        pert = CD.with_flips(lambda: O.run_round(case.p, W, case.oracle_streams(fs)), CD.RATE, 12345)
+        mx, mn = CD.movement(base, [o["logits"] for o in pert])
+        tol, mean_tol = max(LOGIT_TOL[case.p.dtype], CD.FACTOR * mx), CD.FACTOR * mn
+        log(f"[case] oracle movement under {CD.RATE:g} one-ulp flips (streams {fs}): max {mx:.4g} mean {mn:.3g} "
+            f"-> tolerance {tol:.3g}")
+    del W
     worst = compare_round(case, streams, orc, tol, mean_tol)
     # verify against a synthetic target built from the oracle's tokens
     S = case.p.n_streams
@@ -443,19 +431,15 @@ def test_round_parity_9b_ctx32k():
     run_case(RoundCase(wl.preset("9b_ctx32k")), [0], conditioning=True)
 
 
-def test_round_parity_dflash2_x16_sampled_streams():
-    run_case(RoundCase(wl.preset("dflash2_x16")), [8], conditioning=True)
+def test_round_parity_dflash2_x16_every_stream():
+    run_case(RoundCase(wl.preset("dflash2_x16")), list(range(16)), conditioning=True, flip_streams=[0, 8])
 
 
-def test_round_parity_9b_long_x4_short_stream():
-    run_case(RoundCase(wl.preset("9b_long_x4")), [3], conditioning=True)
+def test_round_parity_9b_long_x4_every_stream():
+    run_case(RoundCase(wl.preset("9b_long_x4")), [0, 1, 2, 3], conditioning=True)
 
 
-def test_round_parity_9b_long_x4_longest_stream():
-    run_case(RoundCase(wl.preset("9b_long_x4")), [0], conditioning=True)
-
-
-# ------------------------------------------------------------------ every layer as a one-layer model (2e-2 bar)
+# ------------------------------------------------------------------ every layer as a one-layer model
 
 def one_layer_case(base, layer, ctx, rows, n_streams=1):
     """A one-layer drafter whose only layer is layer `layer` of the preset's weights."""
