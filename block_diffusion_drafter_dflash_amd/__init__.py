@@ -82,6 +82,7 @@ def library():
                                           _VP]),
         "dflash_layers_reading": (ctypes.c_uint64, [_VP, i32, i32]),
         "dflash_draft_block": (i32, [_VP, i32, _VP, _VP, i32, ctypes.POINTER(KV), _VP, _VP, _VP, _VP, sz, _VP]),
+        "dflash_draft_block_noalloc": (i32, [_VP, i32, _VP, _VP, i32, ctypes.POINTER(KV), _VP, _VP, _VP, _VP]),
         "dflash_verify_greedy": (i32, [_VP, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
         "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_sampling": (i32, [_VP, i32, _VP, _VP, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
@@ -105,7 +106,7 @@ def library():
 EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflash_bind_weights",
             "dflash_fused_row_bytes", "dflash_tap_row_bytes", "dflash_workspace_bytes", "dflash_workspace_init",
             "dflash_fuse_taps", "dflash_inject_kv", "dflash_inject_kv_layers", "dflash_layers_reading",
-            "dflash_draft_block", "dflash_verify_greedy",
+            "dflash_draft_block", "dflash_draft_block_noalloc", "dflash_verify_greedy",
             "dflash_sample_rows", "dflash_verify_sampling",
             "dflash_trace_bytes", "dflash_set_trace", "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
 
@@ -270,6 +271,13 @@ class Drafter:
         self._check(self.lib.dflash_draft_block(self.h, n_streams, _ptr(anchor), _ptr(ctx_len), int(max_ctx_len),
                                                 ctypes.byref(kv.struct), _ptr(draft_out), _ptr(logits_out),
                                                 _ptr(top2_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+    def dflash_draft_block_noalloc(self, anchor, ctx_len, max_ctx_len, kv, draft_out, logits_out=None, top2_out=None,
+                                   n_streams=None, stream=None):
+        n_streams = anchor.shape[0] if n_streams is None else n_streams
+        self._check(self.lib.dflash_draft_block_noalloc(self.h, n_streams, _ptr(anchor), _ptr(ctx_len),
+                                                        int(max_ctx_len), ctypes.byref(kv.struct), _ptr(draft_out),
+                                                        _ptr(logits_out), _ptr(top2_out), _stream(stream)))
 
     def dflash_verify_greedy(self, draft, target, accept_len, bonus, committed, ctx_len_inout=None,
                              n_streams=None, stream=None):

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -299,6 +300,39 @@ TraceLayout layout_trace(const dflash& h, int S) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
+
+// ------------------------------------------------------------------ device scratch
+
+// Scratch for dflash_draft_block_noalloc: one file-scope array on every device the
+// library runs on (each device holds its own copy until the process ends). Host code
+// never passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch_addr;   // (device, address of its scratch)
+}  // namespace
+
+static int scratch_of_current_device(dflash* h, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "scratch: hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (auto& d : g_scratch_addr)
+    if (d.first == dev) {
+      *out = d.second;
+      return DFLASH_OK;
+    }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(h, DFLASH_ERR_DEVICE, "scratch: hipGetSymbolAddress on device %d: %s", dev, hipGetErrorString(e));
+  g_scratch_addr.push_back({dev, ptr});
+  *out = ptr;
+  return DFLASH_OK;
+}
 
 // ------------------------------------------------------------------ C-ABI
 
@@ -717,9 +751,11 @@ uint64_t dflash_layers_reading(const dflash* h, int32_t pos, int32_t ctx_len) {
   return m;
 }
 
-int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,
-                       int32_t max_ctx_len, const dflash_kv* kv, int32_t* draft_out, void* logits_out,
-                       float* top2_out, void* ws, size_t ws_bytes, void* stream) {
+// The draft with its workspace given by the caller (dflash_draft_block), or with the
+// device's own file-scope scratch array (in_scratch: dflash_draft_block_noalloc).
+static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,
+                      int32_t max_ctx_len, const dflash_kv* kv, int32_t* draft_out, void* logits_out,
+                      float* top2_out, void* ws, size_t ws_bytes, void* stream, bool in_scratch) {
   if (!h) return DFLASH_ERR_ARG;
   const auto& c = h->cfg;
   if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
@@ -735,8 +771,14 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
     return fail(h, DFLASH_ERR_CAPACITY, "max_ctx_len %d is past the cache span of %d tokens", max_ctx_len,
                 kv->pages_per_stream * c.page_size);
   DraftLayout L = layout_draft(*h, n_streams, max_ctx_len);
-  rc = check_ws(h, ws, ws_bytes, L.end);
-  if (rc) return rc;
+  if (in_scratch) {
+    if (L.end > ws_bytes)
+      return fail(h, DFLASH_ERR_CAPACITY, "this draft needs %zu bytes of scratch, the device array holds %zu", L.end,
+                  ws_bytes);
+  } else {
+    rc = check_ws(h, ws, ws_bytes, L.end);
+    if (rc) return rc;
+  }
   if ((int64_t)n_streams * c.n_kv_heads > kCounterInts) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
 
   const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
@@ -954,6 +996,29 @@ int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, cons
   }
   if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "argmax: %s", hipGetErrorString(e));
   return DFLASH_OK;
+}
+
+int dflash_draft_block(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,
+                       int32_t max_ctx_len, const dflash_kv* kv, int32_t* draft_out, void* logits_out,
+                       float* top2_out, void* ws, size_t ws_bytes, void* stream) {
+  return draft_impl(h, n_streams, anchor, ctx_len, max_ctx_len, kv, draft_out, logits_out, top2_out, ws, ws_bytes,
+                    stream, false);
+}
+
+int dflash_draft_block_noalloc(dflash* h, int32_t n_streams, const int32_t* anchor, const int32_t* ctx_len,
+                               int32_t max_ctx_len, const dflash_kv* kv, int32_t* draft_out, void* logits_out,
+                               float* top2_out, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  void* ws = nullptr;
+  const int rc = scratch_of_current_device(h, &ws);
+  if (rc != DFLASH_OK) return rc;
+  // no profiling events either: the call creates nothing
+  const bool prof = h->profiling;
+  h->profiling = false;
+  const int out = draft_impl(h, n_streams, anchor, ctx_len, max_ctx_len, kv, draft_out, logits_out, top2_out, ws,
+                             kScratchBytes, stream, true);
+  h->profiling = prof;
+  return out;
 }
 
 int dflash_verify_greedy(dflash* h, int32_t n_streams, const int32_t* draft, const int32_t* target_argmax,

@@ -243,6 +243,26 @@ int dflash_draft_block(dflash *h, int32_t n_streams, const int32_t *anchor,
                        size_t ws_bytes, void *stream);
 
 /*
+ * dflash_draft_block for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * computation and kernels, bit for bit, with the workspace taken from a file-scope
+ * device array of 32 MiB that each device holds from the library's load until the
+ * process ends; the call itself calls no hipMalloc, hipFree or allocating routine,
+ * creates no events (profiling is suspended inside it) and needs no
+ * dflash_workspace_init. Its device address is looked up once per device, on the first
+ * call with that device current. A draft whose workspace would exceed the array (more
+ * than 32 MiB: dflash_workspace_bytes(h, 0, n_streams, max_ctx_len) tells; one stream
+ * at the 9B shapes needs about 16 MiB) is refused with DFLASH_ERR_CAPACITY before
+ * anything is enqueued. Nothing in the array must start at zero. Every call on one
+ * device shares that device's array: calls that overlap on one device (other streams,
+ * other threads, other handles) race and must be serialised by the caller. Arguments,
+ * outputs and other errors as dflash_draft_block.
+ */
+int dflash_draft_block_noalloc(dflash *h, int32_t n_streams, const int32_t *anchor,
+                               const int32_t *ctx_len, int32_t max_ctx_len, const dflash_kv *kv,
+                               int32_t *draft_out, void *logits_out, float *top2_out, void *stream);
+
+/*
  * Greedy verify (DFlash explainer section 4, greedy decoding; "Port the DFlash2
  * protocol", golden replay items 4-5). For each stream, with draft d_1..d_{B-1}
  * (device int32 [n_streams, B-1]) and target argmax t_0..t_{B-1} (device int32
