@@ -47,6 +47,12 @@ struct dflash {
   std::vector<ProfRec> prof;
   void* trace = nullptr;        // stage copies of dflash_draft_block (instrumentation)
   size_t trace_cap = 0;
+  // the skinny GEMMs' weights in their packed layout (dflash_pack_weights)
+  bool packed = false;
+  struct {
+    const void *fc, *lm;
+    const void *qkv[DFLASH_MAX_LAYERS], *o[DFLASH_MAX_LAYERS], *gu[DFLASH_MAX_LAYERS], *down[DFLASH_MAX_LAYERS];
+  } pk;
   std::vector<hipEvent_t> event_pool;
 
   ~dflash() {
@@ -299,6 +305,28 @@ TraceLayout layout_trace(const dflash& h, int S) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// The packed copies of the GEMM weights, one after another: fc, LM head, then per layer
+// [wq | wk | wv], wo, [w_gate | w_up] (16 + 16 rows a tile), w_down.
+struct PackLayout {
+  size_t fc, lm, qkv[DFLASH_MAX_LAYERS], o[DFLASH_MAX_LAYERS], gu[DFLASH_MAX_LAYERS], down[DFLASH_MAX_LAYERS], end;
+};
+PackLayout layout_pack(const dflash& h) {
+  const auto& c = h.cfg;
+  const int es = h.esize(), H = c.hidden;
+  PackLayout L;
+  Region r;
+  L.fc = r.take(packed_bytes(H, c.n_taps * H, es));
+  L.lm = r.take(packed_bytes(c.vocab, H, es));
+  for (int l = 0; l < c.n_layers; ++l) {
+    L.qkv[l] = r.take(packed_bytes(h.nq() + 2 * h.nkv(), H, es));
+    L.o[l] = r.take(packed_bytes(H, h.nq(), es));
+    L.gu[l] = r.take(packed_bytes(2 * c.intermediate, H, es));
+    L.down[l] = r.take(packed_bytes(H, c.intermediate, es));
+  }
+  L.end = r.off;
+  return L;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ device scratch
@@ -458,6 +486,56 @@ int dflash_bind_weights(dflash* h, const dflash_weights* w, const int64_t* shape
   }
   h->w = *w;
   h->bound = true;
+  h->packed = false;
+  return DFLASH_OK;
+}
+
+size_t dflash_packed_weight_bytes(const dflash* h) { return h ? layout_pack(*h).end : 0; }
+
+int dflash_pack_weights(dflash* h, void* buf, size_t bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
+  if (!buf || ((uintptr_t)buf & 255)) return fail(h, DFLASH_ERR_ARG, "packed weight buffer is NULL or not 256-byte aligned");
+  const PackLayout L = layout_pack(*h);
+  if (bytes < L.end) return fail(h, DFLASH_ERR_CAPACITY, "packed weights need %zu bytes, the buffer holds %zu", L.end, bytes);
+  const auto& c = h->cfg;
+  const int es = h->esize(), H = c.hidden;
+  char* B = static_cast<char*>(buf);
+  hipStream_t st = (hipStream_t)stream;
+  h->packed = false;
+  auto job = [&](int kind, int N, int K, const void* w0, const void* w1, const void* w2, size_t off) {
+    PackJob j;
+    std::memset(&j, 0, sizeof j);
+    j.kind = kind;
+    j.N = N;
+    j.K = K;
+    j.esize = es;
+    j.nq = h->nq();
+    j.nkv = h->nkv();
+    j.w0 = w0;
+    j.w1 = w1;
+    j.w2 = w2;
+    j.dst = B + off;
+    return launch_pack(j, st);
+  };
+  hipError_t e = job(PACK_PLAIN, H, c.n_taps * H, h->w.fc, nullptr, nullptr, L.fc);
+  if (e == hipSuccess) e = job(PACK_PLAIN, c.vocab, H, h->w.lm_head, nullptr, nullptr, L.lm);
+  for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+    e = job(PACK_QKV, h->nq() + 2 * h->nkv(), H, h->w.wq[l], h->w.wk[l], h->w.wv[l], L.qkv[l]);
+    if (e == hipSuccess) e = job(PACK_PLAIN, H, h->nq(), h->w.wo[l], nullptr, nullptr, L.o[l]);
+    if (e == hipSuccess) e = job(PACK_SWIGLU, 2 * c.intermediate, H, h->w.w_gate[l], h->w.w_up[l], nullptr, L.gu[l]);
+    if (e == hipSuccess) e = job(PACK_PLAIN, H, c.intermediate, h->w.w_down[l], nullptr, nullptr, L.down[l]);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "pack weights: %s", hipGetErrorString(e));
+  h->pk.fc = B + L.fc;
+  h->pk.lm = B + L.lm;
+  for (int l = 0; l < c.n_layers; ++l) {
+    h->pk.qkv[l] = B + L.qkv[l];
+    h->pk.o[l] = B + L.o[l];
+    h->pk.gu[l] = B + L.gu[l];
+    h->pk.down[l] = B + L.down[l];
+  }
+  h->packed = true;
   return DFLASH_OK;
 }
 
@@ -568,6 +646,8 @@ static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmPara
     b.N = 2 * tail;
     b.w0 = static_cast<const char*>(p.w0) + (size_t)g.tail_from * p.K * esz;
     b.w1 = static_cast<const char*>(p.w1) + (size_t)g.tail_from * p.K * esz;
+    // packed tiles hold 16 gate and 16 up rows each: skip the tiled kernel's rows
+    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / 16) * kPackTileRows * p.K * esz;
     b.m_out = static_cast<char*>(p.m_out) + (size_t)g.tail_from * esz;
     const int mt = 4;
     b.mgroups = (p.M + 16 * mt - 1) / (16 * mt);
@@ -597,6 +677,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   const int pass = row_pass(n_rows);
   int rc = check_ws(h, ws, ws_bytes, layout_fuse(*h, pass).end);
   if (rc) return rc;
+  if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   const size_t es = h->esize();
@@ -609,6 +690,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
     p.tap_h = c.hidden;
     p.tap_stride = plane_row_stride;
     p.w0 = h->w.fc;
+    p.wp = h->pk.fc;
     p.y_out = reinterpret_cast<double*>(W + L.y);
     hipError_t e;
     {
@@ -667,6 +749,7 @@ static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32
   const int pass = row_pass(n_rows);
   rc = check_ws(h, ws, ws_bytes, layout_inject(*h, pass).end);
   if (rc) return rc;
+  if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   for (int r0 = 0; r0 < n_rows; r0 += pass) {
@@ -682,9 +765,12 @@ static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32
     p.lda = c.hidden;
     p.nkv = h->nkv();
     p.seg_layers = n_sel;
+    p.wp_seg_tiles = 2 * h->nkv() / kPackTileRows;
     for (int i = 0; i < n_sel; ++i) {
       p.wk_l[i] = h->w.wk[sel[i]];
       p.wv_l[i] = h->w.wv[sel[i]];
+      // a layer's [wk | wv] tiles follow its wq tiles in the packed [wq | wk | wv]
+      p.wp_l[i] = static_cast<const char*>(h->pk.qkv[sel[i]]) + (size_t)h->nq() * c.hidden * h->esize();
     }
     p.y_out = reinterpret_cast<double*>(W + L.raw);
     hipError_t e;
@@ -780,6 +866,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     if (rc) return rc;
   }
   if ((int64_t)n_streams * c.n_kv_heads > kCounterInts) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
+  if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
 
   const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
   char* W = static_cast<char*>(ws);
@@ -856,6 +943,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.w0 = h->w.wq[l];
     p.w1 = h->w.wk[l];
     p.w2 = h->w.wv[l];
+    p.wp = h->pk.qkv[l];
     p.nq = h->nq();
     p.nkv = h->nkv();
     p.y_out = qkv_raw;
@@ -932,6 +1020,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.a = W + L.o_buf;
     p.lda = h->nq();
     p.w0 = h->w.wo[l];
+    p.wp = h->pk.o[l];
     p.y_out = o_parts;
     {
       ProfScope ps(h, "o_proj_gemm", st);
@@ -950,6 +1039,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.lda = c.hidden;
     p.w0 = h->w.w_gate[l];
     p.w1 = h->w.w_up[l];
+    p.wp = h->pk.gu[l];
     p.m_out = W + L.m;
     p.ld_out = c.intermediate;
     {
@@ -965,6 +1055,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.a = W + L.m;
     p.lda = c.intermediate;
     p.w0 = h->w.w_down[l];
+    p.wp = h->pk.down[l];
     p.y_out = d_parts;
     {
       ProfScope ps(h, "down_gemm", st);
@@ -983,6 +1074,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
   p.a = A;
   p.lda = c.hidden;
   p.w0 = h->w.lm_head;
+  p.wp = h->pk.lm;
   p.logits_out = static_cast<float*>(logits_out);
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
   {

@@ -1,11 +1,14 @@
 // Skinny MFMA GEMMs of the draft round with fused epilogues (gfx950).
 //
 // Y[M, N] = A[M, K] . W[N, K]^T with M small (block rows x streams) and W streamed
-// from HBM exactly once. A workgroup owns one work item: a tile of 16*NT output
-// columns for 16*MT rows over one of the GEMM's ksplit ranges of K. Its KW waves
-// split that range again; each wave streams its slice of the tile's weight rows,
-// every lane reading U*16 contiguous bytes of each row per iteration with the next
-// iteration's reads in flight. Every MFMA's partial (32 products per element for
+// from HBM exactly once. A workgroup owns one work item: a tile of 32 output columns
+// for 16*MT rows over one of the GEMM's ksplit ranges of K. W comes in the packed
+// layout (dflash_pack_weights): the tile's rows as consecutive 4 KB chunks of 32 rows
+// x 128 bytes, so a K range of a tile is one contiguous region. The KW waves take the
+// range's chunks in turn, so the workgroup streams KW consecutive chunks at a time (a
+// pattern that reads HBM at 6.0 TB/s where 32 rows read side by side, 2 K bytes
+// apart, reach 5.1); each lane reads U*16 bytes of each of its rows per chunk, with
+// the wave's next chunk in flight. Every MFMA's partial (32 products per element for
 // bf16) is added into a float64 accumulator and the KW wave partials are summed in
 // wave order. With ksplit > 1 each range writes its own float64 partial and the
 // consuming kernel adds the ranges in order (see kernels.h), so no workgroup ever
@@ -53,26 +56,13 @@ __device__ __forceinline__ void top_xor_merge(float& v1, int& i1, float& v2, int
   }
 }
 
-// Weight row of output column tile * (16 * NT) + c.
-template <typename T, int NT, int EPI>
-__device__ __forceinline__ const T* weight_row(const GemmParams& p, int tile, int c) {
-  const int n = tile * (16 * NT) + c;
-  if constexpr (EPI == EPI_SWIGLU) {
-    // tile t: columns 0..15 are gate rows 16t.., columns 16..31 the matching up rows
-    const int r = tile * 16 + (c & 15);
-    return static_cast<const T*>(c < 16 ? p.w0 : p.w1) + (int64_t)r * p.K;
-  } else if constexpr (EPI == EPI_RAW) {
-    if (p.seg_layers > 0) {   // per layer [wk | wv]
-      const int l = n / (2 * p.nkv), rem = n % (2 * p.nkv);
-      return static_cast<const T*>(rem < p.nkv ? p.wk_l[l] : p.wv_l[l]) + (int64_t)(rem % p.nkv) * p.K;
-    }
-    if (p.nq == 0 || n < p.nq) return static_cast<const T*>(p.w0) + (int64_t)n * p.K;   // one matrix, or wq
-    if (n < p.nq + p.nkv) return static_cast<const T*>(p.w1) + (int64_t)(n - p.nq) * p.K;
-    return static_cast<const T*>(p.w2) + (int64_t)(n - p.nq - p.nkv) * p.K;
-  } else {
-    const int nn = n < p.N ? n : p.N - 1;   // ragged last tile: read a valid row, drop it later
-    return static_cast<const T*>(p.w0) + (int64_t)nn * p.K;
-  }
+// First element of packed tile `tile` (see GemmParams::wp): K elements a row, 32 rows.
+template <typename T>
+__device__ __forceinline__ const T* packed_tile(const GemmParams& p, int tile) {
+  const int64_t tile_elems = (int64_t)kPackTileRows * p.K;
+  if (p.wp_seg_tiles > 0)
+    return static_cast<const T*>(p.wp_l[tile / p.wp_seg_tiles]) + (int64_t)(tile % p.wp_seg_tiles) * tile_elems;
+  return static_cast<const T*>(p.wp) + (int64_t)tile * tile_elems;
 }
 
 template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
@@ -93,12 +83,17 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   const int ks = col % p.ksplit, tile = col / p.ksplit;
   const int row0 = mg * ROWS;
   const int kb = (int)((int64_t)ks * p.iters / p.ksplit), ke = (int)((int64_t)(ks + 1) * p.iters / p.ksplit);
-  const int it0 = kb + (int)((int64_t)w * (ke - kb) / KW), it1 = kb + (int)((int64_t)(w + 1) * (ke - kb) / KW);
   const int lane_k = lg * (U * E);
+  static_assert(16 * NT == kPackTileRows && KI * (int)sizeof(T) == 128, "a packed chunk is 32 rows of 128 bytes");
 
-  const T* brow[NT];
+  // Packed weights: iteration `it` of this tile is the chunk at tw + it * 32 * KI, rows
+  // 16 nt + lr of it at KI elements apart. The KW waves take the range's chunks in
+  // turn (wave w: kb + w, kb + w + KW, ...), so at any time the workgroup streams KW
+  // consecutive 4 KB chunks of one contiguous region.
+  const T* tw = packed_tile<T>(p, tile);
+  int boff[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) brow[nt] = weight_row<T, NT, EPI>(p, tile, 16 * nt + lr);
+  for (int nt = 0; nt < NT; ++nt) boff[nt] = (16 * nt + lr) * KI + lane_k;
   int64_t aoff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -112,7 +107,7 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int u = 0; u < U; ++u) bb[nt][u] = ldg16(brow[nt] + k + u * E);
+      for (int u = 0; u < U; ++u) bb[nt][u] = ldg16(tw + (int64_t)it * (kPackTileRows * KI) + boff[nt] + u * E);
     if constexpr (AM == A_TAPS) {
       // An iteration's KI columns never straddle two planes (hidden % KI == 0).
       const int plane = (it * KI) / p.tap_h;
@@ -137,13 +132,13 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mt][nt][i] = 0.0;
 
-  if (it0 < it1) {
+  if (kb + w < ke) {
     uint4 a_c[MT][U], b_c[NT][U];
-    load(it0, a_c, b_c);
-    for (int it = it0; it < it1; ++it) {
+    load(kb + w, a_c, b_c);
+    for (int it = kb + w; it < ke; it += KW) {
       uint4 a_n[MT][U], b_n[NT][U];
-      const bool more = it + 1 < it1;
-      if (more) load(it + 1, a_n, b_n);
+      const bool more = it + KW < ke;
+      if (more) load(it + KW, a_n, b_n);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -35,7 +35,14 @@ struct GemmParams {
   const void* taps[kMaxTaps];   // A_TAPS: plane t holds columns [t * tap_h, (t + 1) * tap_h)
   int tap_h;
   int64_t tap_stride;
-  // B operand: one matrix, or segments picked by column
+  // B operand of the skinny kernel: the packed weights. Tile t (32 output columns) is
+  // K / KI consecutive chunks of [32 rows][KI] elements (KI = 128 bytes of a row), so
+  // a tile over a K range is one contiguous region; wp_seg_tiles > 0 splits the tiles
+  // into per-layer segments with their own bases (inject).
+  const void* wp;
+  int wp_seg_tiles;
+  const void* wp_l[kMaxLayers];
+  // B operand of the tiled kernel: one matrix, or segments picked by column
   const void* w0;       // single matrix; or wq / w_gate
   const void* w1;       // wk / w_up
   const void* w2;       // wv
@@ -138,6 +145,24 @@ struct RowNormParams {
   void* out;            // [R, hidden]
   float eps;
 };
+
+// One weight matrix copied into the skinny kernel's packed layout (see GemmParams::wp):
+// tile t holds output columns 32 t .. 32 t + 31 (zero rows past N), each as K / KI
+// chunks of 128 bytes a row. Kinds pick the source row of output column n.
+enum PackKind { PACK_PLAIN = 0, PACK_QKV = 1, PACK_SWIGLU = 2 };
+struct PackJob {
+  int kind, N, K, esize;
+  int nq, nkv;          // PACK_QKV: columns [0, nq) from w0, [nq, nq + nkv) from w1, the rest w2
+  const void* w0;       // PACK_PLAIN: the matrix; PACK_SWIGLU: gate rows (tile t: 16 t ..)
+  const void* w1;       //   and up rows (the tile's columns 16..31)
+  const void* w2;
+  void* dst;
+};
+constexpr int kPackTileRows = 32;
+inline size_t packed_bytes(int N, int K, int esize) {
+  return (size_t)((N + kPackTileRows - 1) / kPackTileRows) * kPackTileRows * (size_t)K * esize;
+}
+hipError_t launch_pack(const PackJob& j, hipStream_t st);
 
 struct VerifyParams {
   int S, B;

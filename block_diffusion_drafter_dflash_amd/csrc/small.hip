@@ -404,6 +404,42 @@ __global__ __launch_bounds__(64) void k_verify(const VerifyParams p) {
   }
 }
 
+// Weights into the skinny GEMM's packed layout: one thread a 16-byte piece. Packed
+// piece i is piece i % 8 of row (i / 8) % 32 of chunk (i / 256) % chunks of tile
+// i / (256 chunks); its source is the same 16 bytes of output column 32 tile + row's
+// weight row (zero past N).
+__global__ __launch_bounds__(256) void k_pack(const PackJob j) {
+  const int64_t chunks = (int64_t)j.K * j.esize / 128;
+  const int64_t tiles = (j.N + kPackTileRows - 1) / kPackTileRows;
+  const int64_t total = tiles * chunks * (kPackTileRows * 8);
+  const int64_t row_bytes = (int64_t)j.K * j.esize;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int piece = (int)(i % 8), row = (int)((i / 8) % kPackTileRows);
+    const int64_t chunk = (i / (8 * kPackTileRows)) % chunks, tile = i / (8 * kPackTileRows * chunks);
+    const int64_t n = tile * kPackTileRows + row;
+    const char* src = nullptr;
+    if (n < j.N) {
+      if (j.kind == PACK_SWIGLU) {
+        const int64_t r = tile * 16 + (row & 15);
+        src = static_cast<const char*>(row < 16 ? j.w0 : j.w1) + r * row_bytes;
+      } else if (j.kind == PACK_QKV) {
+        src = n < j.nq ? static_cast<const char*>(j.w0) + n * row_bytes
+                       : (n < j.nq + j.nkv ? static_cast<const char*>(j.w1) + (n - j.nq) * row_bytes
+                                           : static_cast<const char*>(j.w2) + (n - j.nq - j.nkv) * row_bytes);
+      } else {
+        src = static_cast<const char*>(j.w0) + n * row_bytes;
+      }
+    }
+    const uint4 v = src ? ldg16(src + chunk * 128 + piece * 16) : make_uint4(0, 0, 0, 0);
+    stg16(static_cast<char*>(j.dst) + i * 16, v);
+  }
+}
+
+hipError_t launch_pack(const PackJob& j, hipStream_t st) {
+  (void)launch_k(k_pack, dim3(4096), dim3(256), st, j);
+  return hipGetLastError();
+}
+
 __global__ void k_fill_zero(int* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0;

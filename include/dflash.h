@@ -148,6 +148,22 @@ int64_t dflash_fused_row_bytes(const dflash_config *cfg);
 int64_t dflash_tap_row_bytes(const dflash_config *cfg, int32_t fusing);
 
 /*
+ * The skinny GEMMs' weights in their packed layout. dflash_pack_weights copies the
+ * bound fc, LM head and every layer's [wq | wk | wv], wo, [w_gate | w_up] and w_down
+ * into `buf` (caller-owned device memory of at least dflash_packed_weight_bytes bytes,
+ * 256-byte aligned; else DFLASH_ERR_ARG / DFLASH_ERR_CAPACITY), on `stream`. In the
+ * packed layout the 32 output columns a workgroup computes are K / KI consecutive
+ * chunks of 32 rows x 128 bytes, so each workgroup streams one contiguous region of
+ * HBM instead of 32 rows 2 K bytes apart; the values are the bound weights' own. The
+ * tiled kernels (33 or more block rows) keep reading the bound weights, which must
+ * stay valid too. Required once after dflash_bind_weights, before the first fuse,
+ * inject or draft (else DFLASH_ERR_STATE); binding again drops the packing. The buffer
+ * must outlive its use; the library never frees it.
+ */
+size_t dflash_packed_weight_bytes(const dflash *h);
+int dflash_pack_weights(dflash *h, void *buf, size_t bytes, void *stream);
+
+/*
  * Workspace bytes for calls with at most `max_rows` fused/injected rows, `n_streams`
  * streams in a draft, and context length at most `max_ctx`. The workspace holds split-K
  * partials, block activations, attention partials and self-resetting counters.

@@ -219,3 +219,24 @@ def test_prompt_scale_calls_need_a_bounded_workspace():
     assert dr.workspace_bytes(65536, 1, 4096) == a
     assert dr.workspace_bytes(40, 1, 4096) >= dr.workspace_bytes(32, 1, 4096)
     assert dr.workspace_bytes(2048, 1, 4096) < a
+
+
+def test_packed_weight_bytes_closed_form():
+    # every GEMM weight once, its output columns padded to tiles of 32 rows: fc, LM head,
+    # and per layer [wq | wk | wv], wo, [w_gate | w_up], w_down (each 256-byte aligned)
+    def tile32(n):
+        return (n + 31) // 32 * 32
+
+    def align(b):
+        return (b + 255) // 256 * 256
+
+    for name in ("9b_ctx4k", "dflash2_x16", "tiny_f32"):
+        p = wl.preset(name)
+        es = 4 if p.dtype == "f32" else 2
+        h, nq, nkv, I = p.hidden, p.n_q_heads * p.head_dim, p.n_kv_heads * p.head_dim, p.intermediate
+        want = align(tile32(h) * p.n_taps * h * es) + align(tile32(p.vocab) * h * es)
+        want += p.n_layers * (align(tile32(nq + 2 * nkv) * h * es) + align(tile32(h) * nq * es) +
+                              align(tile32(2 * I) * h * es) + align(tile32(h) * I * es))
+        assert D.Drafter(cfg_of(name)).packed_weight_bytes() == want, name
+    dr = D.Drafter(cfg_of("tiny_f32"))
+    assert D.library().dflash_pack_weights(dr.h, None, 0, None) == -5      # nothing bound yet

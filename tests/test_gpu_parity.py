@@ -693,3 +693,30 @@ def test_zero_rows_are_a_no_op():
     case.dr.dflash_inject_kv(case.fused, case.row_stream, case.row_pos, case.kv, case.ws, n_rows=0)
     torch.cuda.synchronize()
     assert torch.equal(before, case.fused)
+
+
+def test_unpacked_weights_are_refused_and_rebinding_drops_the_packing():
+    case = RoundCase(NARROW2)          # 32 block rows: the skinny GEMMs, which read the packing
+    case.run_gpu()
+    ref_logits, ref_draft = case.logits.clone(), case.draft.clone()
+    dr = D.Drafter(case.cfg)
+    dr.dflash_bind_weights(case.W)
+    ws = dr.new_workspace(max(case.R, 1), NARROW2.n_streams, case.max_ctx)
+
+    def refused(fn):
+        with pytest.raises(D.DFlashError) as e:
+            fn()
+        assert e.value.code == -5 and "packed" in str(e.value), str(e.value)
+
+    out = torch.zeros_like(case.logits)
+    drafted = torch.zeros_like(case.draft)
+    draft = lambda: dr.dflash_draft_block(case.anchor, case.ctx_len, case.max_ctx, case.kv, drafted, ws, logits_out=out)
+    refused(lambda: dr.dflash_fuse_taps(case.taps, case.fused, ws, n_rows=case.R))
+    refused(lambda: dr.dflash_inject_kv(case.fused, case.row_stream, case.row_pos, case.kv, ws, n_rows=case.R))
+    refused(draft)
+    dr.new_packed_weights()
+    draft()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref_logits.view(torch.int32)) and torch.equal(drafted, ref_draft)
+    dr.dflash_bind_weights(case.W)
+    refused(draft)

@@ -62,6 +62,7 @@ class RoundCase:
                     self.kv.write_rows(l, s, 0, k, v)
         self.dr = D.Drafter(self.cfg)
         self.dr.dflash_bind_weights(self.W)
+        self.dr.new_packed_weights(device=device)
         self.ws = self.dr.new_workspace(max(R, 1), S, self.max_ctx, device=device)
         self.fused = torch.zeros((max(R, 1), p.hidden), dtype=self.dtype, device=device)
         self.draft = torch.zeros((S, B - 1), dtype=torch.int32, device=device)
