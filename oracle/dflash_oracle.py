@@ -29,6 +29,9 @@ What it computes (sources are the four pages on DFlash):
   * sampling: inverse-CDF draws from tempered softmax rows, and speculative-
             sampling acceptance with the residual max(p_target - p_draft, 0)
             (explainer section 4, "Sampling decoding").
+  * 4-bit weights: affine quantization in groups of 64 along each weight row,
+            and the dequantized weights used exactly (explainer section 8; TensorFold
+            #1851, "Exactness", Precision).
 
 Numerics: every product and reduction is float64. Values are rounded to the
 activation dtype (bf16 by round-to-nearest-even straight from float64, or
@@ -52,7 +55,10 @@ Readings taken where the pages are silent (each also listed in the design doc):
   the token at position C+j; argmax ties go to the lowest index; sampling
   accepts d when u * p_draft(d) < p_target(d), draws by inverse CDF over token
   ids in ascending order with one uniform per draw, and falls back to the
-  target's distribution when the residual has no mass.
+  target's distribution when the residual has no mass; a 4-bit group's bias is its
+  smallest weight and its scale (max - min) / 15 rounded once to bf16, codes round to
+  nearest even, and the LM head and fc are quantized with the layers (the embedding is
+  not).
 """
 import math
 
@@ -422,6 +428,63 @@ def tap_row_bytes(n_taps, hidden, fusing, elem_bytes=2):
     if fusing:
         return (2 * n_taps + 2) * hidden * elem_bytes
     return n_taps * hidden * elem_bytes
+
+
+# --------------------------------------------------------------------------
+# 4-bit drafter weights (DFlash explainer, section 8: the drafter's layers are
+# quantized at load with 4 bits in groups of 64; TensorFold #1851, "Exactness",
+# Precision: the drafter's 4-bit copies, with bf16 activations and fp32 sums)
+
+QUANT_GROUP = 64
+QUANT_BITS = 4
+
+
+def quantized_names(cfg):
+    """The weights a 4-bit drafter reads quantized: every GEMM weight (fc, the LM head,
+    each layer's q/k/v/o and MLP projections); the embedding (a row gather) and the
+    norm gains stay as they are."""
+    names = ["fc", "lm_head"]
+    for l in range(cfg.n_layers):
+        names += [f"layers.{l}.{t}" for t in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")]
+    return names
+
+
+def quantize_affine(w, group=QUANT_GROUP, bits=QUANT_BITS):
+    """Affine group quantization of a weight matrix [N, K] along K.
+
+    For each run of `group` consecutive weights of a row: bias = the smallest weight,
+    scale = (largest - smallest) / (2^bits - 1) rounded once to bf16, and each code =
+    (w - bias) / scale rounded to the nearest integer (ties to even) and clamped to
+    [0, 2^bits - 1], all in float64. A group whose weights are all equal (or whose
+    scale rounds to zero) gets scale 0 and codes 0. Returns codes uint8 [N, K] and
+    scale, bias float64 [N, K / group] (bf16 values).
+    """
+    w = as_f64(w)
+    N, K = w.shape
+    assert K % group == 0, (K, group)
+    g = w.reshape(N, K // group, group)
+    lo, hi = g.min(axis=-1), g.max(axis=-1)
+    levels = (1 << bits) - 1
+    scale = round_bf16((hi - lo) / levels)
+    safe = np.where(scale > 0, scale, 1.0)[..., None]
+    q = np.where(scale[..., None] > 0, np.rint((g - lo[..., None]) / safe), 0.0)
+    q = np.clip(q, 0, levels).astype(np.uint8)
+    return q.reshape(N, K), scale, lo
+
+
+def dequantize_affine(q, scale, bias, group=QUANT_GROUP):
+    """The weight each code stands for, bias + scale * code, in float64 (exact)."""
+    N, K = q.shape
+    g = q.reshape(N, K // group, group).astype(np.float64)
+    return (bias[..., None] + scale[..., None] * g).reshape(N, K)
+
+
+def quantized_weights(cfg, W):
+    """W with every quantized weight replaced by its dequantized float64 values."""
+    out = dict(W)
+    for name in quantized_names(cfg):
+        out[name] = dequantize_affine(*quantize_affine(W[name]))
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -12,6 +12,7 @@ import types
 import pytest
 
 import test_oracle_pins as P
+import test_oracle_quant as PQ
 import test_oracle_sampling as PS
 import test_oracle_wiring as PW
 
@@ -97,6 +98,15 @@ MUTATIONS = [
     ("no residual", "nxt = sample_index(r if r.sum() > 0 else q, u_sample[s])", "nxt = sample_index(q, u_sample[s])"),
     ("bonus from the target's first row", "nxt = sample_index(tempered_probs(target_logits[s, Bm1], T), u_sample[s])",
      "nxt = sample_index(tempered_probs(target_logits[s, 0], T), u_sample[s])"),
+    # 4-bit weights (explainer section 8)
+    ("4-bit scale over 16 levels", "scale = round_bf16((hi - lo) / levels)", "scale = round_bf16((hi - lo) / (levels + 1))"),
+    ("4-bit bias is the group maximum", "return q.reshape(N, K), scale, lo", "return q.reshape(N, K), scale, hi"),
+    ("4-bit codes truncated", "q = np.where(scale[..., None] > 0, np.rint((g - lo[..., None]) / safe), 0.0)",
+     "q = np.where(scale[..., None] > 0, np.floor((g - lo[..., None]) / safe), 0.0)"),
+    ("4-bit scale kept in float64", "scale = round_bf16((hi - lo) / levels)", "scale = (hi - lo) / levels"),
+    ("4-bit dequantization drops the bias", "return (bias[..., None] + scale[..., None] * g).reshape(N, K)",
+     "return (scale[..., None] * g).reshape(N, K)"),
+    ("4-bit groups of 32", "QUANT_GROUP = 64", "QUANT_GROUP = 32"),
     ("storage sizes: planner counts one copy", "return (2 * n_taps + 2) * hidden * elem_bytes",
      "return (n_taps + 2) * hidden * elem_bytes"),
 ]
@@ -117,7 +127,7 @@ def load_mutant(old, new):
 def pin_calls():
     """Every CPU pin of the oracle, with its parameters."""
     calls = []
-    for mod in (P, PW, PS):
+    for mod in (P, PW, PS, PQ):
         for name in sorted(dir(mod)):
             fn = getattr(mod, name)
             if not name.startswith("test_") or not callable(fn):
