@@ -31,7 +31,13 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16
 FP32_TFLOPS = 157.3
 
 
-def kernel_costs(p, ctx, rows, sampling=False):
+def q4_bytes(N, K):
+    """Bytes of one weight matrix in the 4-bit packing: per 64 weights of a row, 32 bytes
+    of codes and a bf16 scale and bias (rows padded to tiles of 32)."""
+    return (N + 31) // 32 * 32 * (K // 64) * 36
+
+
+def kernel_costs(p, ctx, rows, sampling=False, q4=False):
     """Algorithmic bytes and FLOPs per launch of each kernel of one round.
 
     Bytes are what the method itself must move: each weight once per call that reads
@@ -79,6 +85,12 @@ def kernel_costs(p, ctx, rows, sampling=False):
         k["verify_sampling"] = dict(bytes=(Mm + M) * V * 4 + (2 * Mm + 3 * S + S * B) * 4, flops=0)
     else:
         k["verify"] = dict(bytes=(S * (B - 1) + S * B) * 4 + (3 * S + S * B) * 4, flops=0)
+    if q4:
+        # the GEMMs read the 4-bit weights instead of the bf16 ones
+        wb = {"fuse_fc_gemm": (h, n * h), "inject_kv_gemm": (L * 2 * nkv, h), "qkv_gemm": (nq + 2 * nkv, h),
+              "o_proj_gemm": (h, nq), "gate_up_gemm": (2 * I, h), "down_gemm": (h, I), "lm_head_gemm": (V, h)}
+        for name, (N_, K_) in wb.items():
+            k[name]["bytes"] += q4_bytes(N_, K_) - N_ * K_ * es
     for name in ("qkv_gemm", "qkv_finish", "o_proj_gemm", "gate_up_gemm", "down_gemm"):
         k[name]["launches"] = L
     for name, v in k.items():
@@ -202,6 +214,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay pass")
     ap.add_argument("--defer", action="store_true",
                     help="with --prefill: inject each prompt row only into the layers that will read it")
+    ap.add_argument("--q4", action="store_true",
+                    help="the drafter's 4-bit weights (groups of 64) instead of bf16 (a separate workload)")
     ap.add_argument("--prefill", type=int, default=0,
                     help="instead of the round: fuse + inject this many prompt rows of one stream")
     ap.add_argument("--sampling", type=float, default=0.0,
@@ -222,8 +236,8 @@ def main():
     if args.prefill > 0:
         prefill_main(args, p)
         return
-    print(f"[bench] workload {p.name}: setting up", file=sys.stderr, flush=True)
-    case = RoundCase(p)
+    print(f"[bench] workload {p.name}{' (4-bit weights)' if args.q4 else ''}: setting up", file=sys.stderr, flush=True)
+    case = RoundCase(p, q4=args.q4)
     S, B = p.n_streams, p.block_size
 
     # target row from an untimed round of the same inputs
@@ -300,7 +314,7 @@ def main():
     # eager figure, which stays the headline)
     graph = None if args.no_graph else graph_replay(torch, step, st, args.steps)
 
-    costs = kernel_costs(p, case.ctx, case.rows, sampling=args.sampling > 0)
+    costs = kernel_costs(p, case.ctx, case.rows, sampling=args.sampling > 0, q4=args.q4)
     tot_bytes, tot_flops = round_totals(costs)
     drafted = S * (B - 1)
     value = drafted / (ms * 1e-3)
@@ -329,7 +343,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "drafted tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": (p.note or p.name) + (f", sampled at T={args.sampling}" if args.sampling > 0 else ""),
+        "config": {"workload": (p.note or p.name) + (f", sampled at T={args.sampling}" if args.sampling > 0 else "")
+                   + (", 4-bit drafter weights (groups of 64)" if args.q4 else ""),
                    "preset": p.name, "streams": S, "block": B,
                    "context": case.ctx if S > 1 else case.ctx[0], "rows_fused": case.R,
                    "hidden": p.hidden, "layers": p.n_layers, "vocab": p.vocab},

@@ -74,6 +74,8 @@ def library():
         "dflash_bind_weights": (i32, [_VP, ctypes.POINTER(Weights), ctypes.POINTER(i64)]),
         "dflash_packed_weight_bytes": (sz, [_VP]),
         "dflash_pack_weights": (i32, [_VP, _VP, sz, _VP]),
+        "dflash_q4_weight_bytes": (sz, [_VP]),
+        "dflash_pack_weights_q4": (i32, [_VP, _VP, sz, _VP]),
         "dflash_fused_row_bytes": (i64, [ctypes.POINTER(Config)]),
         "dflash_tap_row_bytes": (i64, [ctypes.POINTER(Config), i32]),
         "dflash_workspace_bytes": (sz, [_VP, i32, i32, i32]),
@@ -106,7 +108,7 @@ def library():
 
 
 EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflash_bind_weights",
-            "dflash_packed_weight_bytes", "dflash_pack_weights",
+            "dflash_packed_weight_bytes", "dflash_pack_weights", "dflash_q4_weight_bytes", "dflash_pack_weights_q4",
             "dflash_fused_row_bytes", "dflash_tap_row_bytes", "dflash_workspace_bytes", "dflash_workspace_init",
             "dflash_fuse_taps", "dflash_inject_kv", "dflash_inject_kv_layers", "dflash_layers_reading",
             "dflash_draft_block", "dflash_draft_block_noalloc", "dflash_verify_greedy",
@@ -244,6 +246,20 @@ class Drafter:
         """Allocate the packed-weight buffer and pack the bound weights into it."""
         buf = torch.empty(self.packed_weight_bytes(), dtype=torch.uint8, device=device)
         self.dflash_pack_weights(buf)
+        return buf
+
+    def q4_weight_bytes(self):
+        return int(self.lib.dflash_q4_weight_bytes(self.h))
+
+    def dflash_pack_weights_q4(self, buf, stream=None):
+        self._check(self.lib.dflash_pack_weights_q4(self.h, _ptr(buf), buf.numel() * buf.element_size(),
+                                                    _stream(stream)))
+        self._packed = buf
+
+    def new_q4_weights(self, device="cuda"):
+        """Allocate the 4-bit weight buffer and quantize the bound weights into it."""
+        buf = torch.empty(self.q4_weight_bytes(), dtype=torch.uint8, device=device)
+        self.dflash_pack_weights_q4(buf)
         return buf
 
     # -- workspace

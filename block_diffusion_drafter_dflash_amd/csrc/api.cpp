@@ -49,6 +49,7 @@ struct dflash {
   size_t trace_cap = 0;
   // the skinny GEMMs' weights in their packed layout (dflash_pack_weights)
   bool packed = false;
+  bool q4 = false;              // the packing is the 4-bit one (dflash_pack_weights_q4)
   struct {
     const void *fc, *lm;
     const void *qkv[DFLASH_MAX_LAYERS], *o[DFLASH_MAX_LAYERS], *gu[DFLASH_MAX_LAYERS], *down[DFLASH_MAX_LAYERS];
@@ -310,21 +311,26 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 struct PackLayout {
   size_t fc, lm, qkv[DFLASH_MAX_LAYERS], o[DFLASH_MAX_LAYERS], gu[DFLASH_MAX_LAYERS], down[DFLASH_MAX_LAYERS], end;
 };
-PackLayout layout_pack(const dflash& h) {
+PackLayout layout_pack(const dflash& h, bool q4) {
   const auto& c = h.cfg;
   const int es = h.esize(), H = c.hidden;
+  auto bytes = [&](int N, int K) { return q4 ? packed_q4_bytes(N, K) : packed_bytes(N, K, es); };
   PackLayout L;
   Region r;
-  L.fc = r.take(packed_bytes(H, c.n_taps * H, es));
-  L.lm = r.take(packed_bytes(c.vocab, H, es));
+  L.fc = r.take(bytes(H, c.n_taps * H));
+  L.lm = r.take(bytes(c.vocab, H));
   for (int l = 0; l < c.n_layers; ++l) {
-    L.qkv[l] = r.take(packed_bytes(h.nq() + 2 * h.nkv(), H, es));
-    L.o[l] = r.take(packed_bytes(H, h.nq(), es));
-    L.gu[l] = r.take(packed_bytes(2 * c.intermediate, H, es));
-    L.down[l] = r.take(packed_bytes(H, c.intermediate, es));
+    L.qkv[l] = r.take(bytes(h.nq() + 2 * h.nkv(), H));
+    L.o[l] = r.take(bytes(H, h.nq()));
+    L.gu[l] = r.take(bytes(2 * c.intermediate, H));
+    L.down[l] = r.take(bytes(H, c.intermediate));
   }
   L.end = r.off;
   return L;
+}
+// Bytes of one packed tile (32 output columns over all of K).
+size_t packed_tile_bytes(const dflash& h, int K) {
+  return h.q4 ? (size_t)(K / kQ4Group) * kQ4Chunk : (size_t)kPackTileRows * K * h.esize();
 }
 
 }  // namespace
@@ -487,16 +493,22 @@ int dflash_bind_weights(dflash* h, const dflash_weights* w, const int64_t* shape
   h->w = *w;
   h->bound = true;
   h->packed = false;
+  h->q4 = false;
   return DFLASH_OK;
 }
 
-size_t dflash_packed_weight_bytes(const dflash* h) { return h ? layout_pack(*h).end : 0; }
+size_t dflash_packed_weight_bytes(const dflash* h) { return h ? layout_pack(*h, false).end : 0; }
 
-int dflash_pack_weights(dflash* h, void* buf, size_t bytes, void* stream) {
+size_t dflash_q4_weight_bytes(const dflash* h) {
+  return h && h->cfg.dtype == DFLASH_BF16 ? layout_pack(*h, true).end : 0;
+}
+
+static int pack_impl(dflash* h, void* buf, size_t bytes, void* stream, bool q4) {
   if (!h) return DFLASH_ERR_ARG;
   if (!h->bound) return fail(h, DFLASH_ERR_STATE, "weights are not bound");
+  if (q4 && h->cfg.dtype != DFLASH_BF16) return fail(h, DFLASH_ERR_CONFIG, "4-bit weights are quantized from bf16 weights");
   if (!buf || ((uintptr_t)buf & 255)) return fail(h, DFLASH_ERR_ARG, "packed weight buffer is NULL or not 256-byte aligned");
-  const PackLayout L = layout_pack(*h);
+  const PackLayout L = layout_pack(*h, q4);
   if (bytes < L.end) return fail(h, DFLASH_ERR_CAPACITY, "packed weights need %zu bytes, the buffer holds %zu", L.end, bytes);
   const auto& c = h->cfg;
   const int es = h->esize(), H = c.hidden;
@@ -516,6 +528,7 @@ int dflash_pack_weights(dflash* h, void* buf, size_t bytes, void* stream) {
     j.w1 = w1;
     j.w2 = w2;
     j.dst = B + off;
+    j.q4 = q4 ? 1 : 0;
     return launch_pack(j, st);
   };
   hipError_t e = job(PACK_PLAIN, H, c.n_taps * H, h->w.fc, nullptr, nullptr, L.fc);
@@ -535,9 +548,14 @@ int dflash_pack_weights(dflash* h, void* buf, size_t bytes, void* stream) {
     h->pk.gu[l] = B + L.gu[l];
     h->pk.down[l] = B + L.down[l];
   }
+  h->q4 = q4;
   h->packed = true;
   return DFLASH_OK;
 }
+
+int dflash_pack_weights(dflash* h, void* buf, size_t bytes, void* stream) { return pack_impl(h, buf, bytes, stream, false); }
+
+int dflash_pack_weights_q4(dflash* h, void* buf, size_t bytes, void* stream) { return pack_impl(h, buf, bytes, stream, true); }
 
 size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_streams, int32_t max_ctx) {
   if (!h || max_rows < 0 || n_streams < 1 || n_streams > h->cfg.max_streams || max_ctx < 0) return 0;
@@ -647,7 +665,7 @@ static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmPara
     b.w0 = static_cast<const char*>(p.w0) + (size_t)g.tail_from * p.K * esz;
     b.w1 = static_cast<const char*>(p.w1) + (size_t)g.tail_from * p.K * esz;
     // packed tiles hold 16 gate and 16 up rows each: skip the tiled kernel's rows
-    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / 16) * kPackTileRows * p.K * esz;
+    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / 16) * kPackTileRows * p.K * esz;   // bf16 packing
     b.m_out = static_cast<char*>(p.m_out) + (size_t)g.tail_from * esz;
     const int mt = 4;
     b.mgroups = (p.M + 16 * mt - 1) / (16 * mt);
@@ -678,6 +696,8 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
   int rc = check_ws(h, ws, ws_bytes, layout_fuse(*h, pass).end);
   if (rc) return rc;
   if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
+  if (h->q4 && gemm_is_tiled(pass))
+    return fail(h, DFLASH_ERR_UNIMPLEMENTED, "4-bit weights run on calls of at most %d rows", kTallMinRows - 1);
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   const size_t es = h->esize();
@@ -691,6 +711,7 @@ int dflash_fuse_taps(dflash* h, const void* const* tap_planes, int64_t plane_row
     p.tap_stride = plane_row_stride;
     p.w0 = h->w.fc;
     p.wp = h->pk.fc;
+    p.q4 = h->q4 ? 1 : 0;
     p.y_out = reinterpret_cast<double*>(W + L.y);
     hipError_t e;
     {
@@ -750,6 +771,8 @@ static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32
   rc = check_ws(h, ws, ws_bytes, layout_inject(*h, pass).end);
   if (rc) return rc;
   if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
+  if (h->q4 && gemm_is_tiled(pass))
+    return fail(h, DFLASH_ERR_UNIMPLEMENTED, "4-bit weights run on calls of at most %d rows", kTallMinRows - 1);
   char* W = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
   for (int r0 = 0; r0 < n_rows; r0 += pass) {
@@ -766,11 +789,13 @@ static int inject_impl(dflash* h, const void* fused, int32_t n_rows, const int32
     p.nkv = h->nkv();
     p.seg_layers = n_sel;
     p.wp_seg_tiles = 2 * h->nkv() / kPackTileRows;
+    p.q4 = h->q4 ? 1 : 0;
     for (int i = 0; i < n_sel; ++i) {
       p.wk_l[i] = h->w.wk[sel[i]];
       p.wv_l[i] = h->w.wv[sel[i]];
       // a layer's [wk | wv] tiles follow its wq tiles in the packed [wq | wk | wv]
-      p.wp_l[i] = static_cast<const char*>(h->pk.qkv[sel[i]]) + (size_t)h->nq() * c.hidden * h->esize();
+      p.wp_l[i] = static_cast<const char*>(h->pk.qkv[sel[i]]) +
+                  (size_t)(h->nq() / kPackTileRows) * packed_tile_bytes(*h, c.hidden);
     }
     p.y_out = reinterpret_cast<double*>(W + L.raw);
     hipError_t e;
@@ -867,6 +892,8 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
   }
   if ((int64_t)n_streams * c.n_kv_heads > kCounterInts) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
   if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
+  if (h->q4 && gemm_is_tiled(n_streams * c.block_size))
+    return fail(h, DFLASH_ERR_UNIMPLEMENTED, "4-bit weights run on drafts of at most %d block rows", kTallMinRows - 1);
 
   const int B = c.block_size, M = n_streams * B, Mm = n_streams * (B - 1);
   char* W = static_cast<char*>(ws);
@@ -944,6 +971,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.w1 = h->w.wk[l];
     p.w2 = h->w.wv[l];
     p.wp = h->pk.qkv[l];
+    p.q4 = h->q4 ? 1 : 0;
     p.nq = h->nq();
     p.nkv = h->nkv();
     p.y_out = qkv_raw;
@@ -1021,6 +1049,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.lda = h->nq();
     p.w0 = h->w.wo[l];
     p.wp = h->pk.o[l];
+    p.q4 = h->q4 ? 1 : 0;
     p.y_out = o_parts;
     {
       ProfScope ps(h, "o_proj_gemm", st);
@@ -1040,6 +1069,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.w0 = h->w.w_gate[l];
     p.w1 = h->w.w_up[l];
     p.wp = h->pk.gu[l];
+    p.q4 = h->q4 ? 1 : 0;
     p.m_out = W + L.m;
     p.ld_out = c.intermediate;
     {
@@ -1056,6 +1086,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.lda = c.intermediate;
     p.w0 = h->w.w_down[l];
     p.wp = h->pk.down[l];
+    p.q4 = h->q4 ? 1 : 0;
     p.y_out = d_parts;
     {
       ProfScope ps(h, "down_gemm", st);
@@ -1075,6 +1106,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
   p.lda = c.hidden;
   p.w0 = h->w.lm_head;
   p.wp = h->pk.lm;
+  p.q4 = h->q4 ? 1 : 0;
   p.logits_out = static_cast<float*>(logits_out);
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
   {

@@ -65,7 +65,28 @@ __device__ __forceinline__ const T* packed_tile(const GemmParams& p, int tile) {
   return static_cast<const T*>(p.wp) + (int64_t)tile * tile_elems;
 }
 
-template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
+// First byte of 4-bit packed tile `tile` (K / 64 chunks of kQ4Chunk bytes).
+__device__ __forceinline__ const unsigned char* packed_tile_q4(const GemmParams& p, int tile) {
+  const int64_t tile_bytes = (int64_t)(p.K / kQ4Group) * kQ4Chunk;
+  if (p.wp_seg_tiles > 0)
+    return static_cast<const unsigned char*>(p.wp_l[tile / p.wp_seg_tiles]) + (int64_t)(tile % p.wp_seg_tiles) * tile_bytes;
+  return static_cast<const unsigned char*>(p.wp) + (int64_t)tile * tile_bytes;
+}
+
+// Eight 4-bit codes (nibble e = code e) -> eight bf16 values, exactly (0..15).
+__device__ __forceinline__ uint4 codes_to_bf16(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  return make_uint4(f32x2_to_bf16x2((float)(lo & 0xffu), (float)(hi & 0xffu)),
+                    f32x2_to_bf16x2((float)((lo >> 8) & 0xffu), (float)((hi >> 8) & 0xffu)),
+                    f32x2_to_bf16x2((float)((lo >> 16) & 0xffu), (float)((hi >> 16) & 0xffu)),
+                    f32x2_to_bf16x2((float)(lo >> 24), (float)(hi >> 24)));
+}
+
+// WQ = 1: B is the 4-bit packing (bf16 only). The MFMAs then run on the codes
+// themselves (exact in bf16) and on all-ones, giving per 64-weight group g the sums
+// P = sum_k x_k q_k and X = sum_k x_k; the group adds scale_g P + bias_g X, which is
+// sum_k x_k (bias_g + scale_g q_k), the product with the dequantized weights.
+template <typename T, int MT, int NT, int EPI, int AM, int WQ, typename Tune>
 __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   using C = GemmCfg<T, Tune>;
   constexpr int E = C::E, U = C::U, KI = C::KI, KW = C::KW, THREADS = C::THREADS;
@@ -91,6 +112,8 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   // turn (wave w: kb + w, kb + w + KW, ...), so at any time the workgroup streams KW
   // consecutive 4 KB chunks of one contiguous region.
   const T* tw = packed_tile<T>(p, tile);
+  const unsigned char* tq = WQ ? packed_tile_q4(p, tile) : nullptr;
+  static_assert(!WQ || (sizeof(T) == 2 && KI == kQ4Group && U == 2 && NT == 2), "4-bit groups are one bf16 chunk");
   int boff[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) boff[nt] = (16 * nt + lr) * KI + lane_k;
@@ -104,10 +127,18 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   const T* abase = static_cast<const T*>(p.a);
   auto load = [&](int it, uint4 (&a)[MT][U], uint4 (&bb)[NT][U]) {
     const int k = it * KI + lane_k;
+    if constexpr (WQ) {
+      // the lane's 16 bytes of codes, then rows lr and 16 + lr's (scale, bias)
+      const unsigned char* ch = tq + (int64_t)it * kQ4Chunk;
+      bb[0][0] = ldg16(ch + 16 * lane);
+      const uint2 sb = *reinterpret_cast<const uint2*>(ch + 1024 + 8 * lr);
+      bb[0][1] = make_uint4(sb.x, sb.y, 0u, 0u);
+    } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int u = 0; u < U; ++u) bb[nt][u] = ldg16(tw + (int64_t)it * (kPackTileRows * KI) + boff[nt] + u * E);
+        for (int u = 0; u < U; ++u) bb[nt][u] = ldg16(tw + (int64_t)it * (kPackTileRows * KI) + boff[nt] + u * E);
+    }
     if constexpr (AM == A_TAPS) {
       // An iteration's KI columns never straddle two planes (hidden % KI == 0).
       const int plane = (it * KI) / p.tap_h;
@@ -139,18 +170,44 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
       uint4 a_n[MT][U], b_n[NT][U];
       const bool more = it + KW < ke;
       if (more) load(it + KW, a_n, b_n);
+      if constexpr (WQ) {
+        // codes of rows lr (dwords x, y) and 16 + lr (z, w), k = 16 lg + 8 u ..
+        uint4 bq[NT][U];
+        bq[0][0] = codes_to_bf16(b_c[0][0].x);
+        bq[0][1] = codes_to_bf16(b_c[0][0].y);
+        bq[1][0] = codes_to_bf16(b_c[0][0].z);
+        bq[1][1] = codes_to_bf16(b_c[0][0].w);
+        const uint32_t sbw[NT] = {b_c[0][1].x, b_c[0][1].y};
+        const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          floatx4 xs = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          // an iteration's U MFMAs (U * KF products) are summed in fp32, then added
-          // into the float64 accumulator
-          floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int u = 0; u < U; ++u) mma_frag(xs, a_c[mt][u], ones, T());
 #pragma unroll
-          for (int u = 0; u < U; ++u) mma_frag(part, a_c[mt][u], b_c[nt][u], T());
+          for (int nt = 0; nt < NT; ++nt) {
+            floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nt][i] += (double)part[i];
+            for (int u = 0; u < U; ++u) mma_frag(part, a_c[mt][u], bq[nt][u], T());
+            const float scale = bf16_to_f32(sbw[nt] & 0xffffu), bias = bf16_to_f32(sbw[nt] >> 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][nt][i] += (double)fmaf(scale, part[i], bias * xs[i]);
+          }
         }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            // an iteration's U MFMAs (U * KF products) are summed in fp32, then added
+            // into the float64 accumulator
+            floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < U; ++u) mma_frag(part, a_c[mt][u], b_c[nt][u], T());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][nt][i] += (double)part[i];
+          }
+      }
       if (more) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -255,7 +312,13 @@ template <typename T, int MT, int NT, int EPI, int AM, typename Tune>
 static hipError_t launch_tuned(const GemmParams& p, hipStream_t st) {
   // columns padded to a multiple of 8 so that every column's row groups share an XCD
   const int grid = (p.n_tiles * p.ksplit + 7) / 8 * 8 * p.mgroups;
-  (void)launch_k(k_gemm<T, MT, NT, EPI, AM, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
+  if constexpr (sizeof(T) == 2) {
+    if (p.q4) {
+      (void)launch_k(k_gemm<T, MT, NT, EPI, AM, 1, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
+      return hipGetLastError();
+    }
+  }
+  (void)launch_k(k_gemm<T, MT, NT, EPI, AM, 0, Tune>, dim3(grid), dim3(GemmCfg<T, Tune>::THREADS), st, p);
   return hipGetLastError();
 }
 

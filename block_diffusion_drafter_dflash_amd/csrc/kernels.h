@@ -42,6 +42,7 @@ struct GemmParams {
   const void* wp;
   int wp_seg_tiles;
   const void* wp_l[kMaxLayers];
+  int q4;               // 1: wp holds 4-bit codes with per-group scale and bias (kQ4Chunk bytes a chunk)
   // B operand of the tiled kernel: one matrix, or segments picked by column
   const void* w0;       // single matrix; or wq / w_gate
   const void* w1;       // wk / w_up
@@ -152,6 +153,7 @@ struct RowNormParams {
 enum PackKind { PACK_PLAIN = 0, PACK_QKV = 1, PACK_SWIGLU = 2 };
 struct PackJob {
   int kind, N, K, esize;
+  int q4;               // 1: quantize to the 4-bit packing (bf16 weights only)
   int nq, nkv;          // PACK_QKV: columns [0, nq) from w0, [nq, nq + nkv) from w1, the rest w2
   const void* w0;       // PACK_PLAIN: the matrix; PACK_SWIGLU: gate rows (tile t: 16 t ..)
   const void* w1;       //   and up rows (the tile's columns 16..31)
@@ -161,6 +163,18 @@ struct PackJob {
 constexpr int kPackTileRows = 32;
 inline size_t packed_bytes(int N, int K, int esize) {
   return (size_t)((N + kPackTileRows - 1) / kPackTileRows) * kPackTileRows * (size_t)K * esize;
+}
+// 4-bit packing (PackJob::q4): every 64-weight group of a row (one chunk of K) as
+// codes (w - bias) / scale, 4 bits each, with the group's bf16 scale and bias (bias the
+// group minimum, scale (max - min) / 15 rounded to bf16, codes rounded to nearest even,
+// all in float64). A chunk of a tile is 1024 bytes of codes, placed so that lane
+// (lr, lg) of the GEMM's wave reads its 16 bytes at 16 (16 lg + lr): rows lr and
+// 16 + lr (8 bytes each), k = 16 lg .. 16 lg + 15, two codes a byte (low nibble
+// first); then 128 bytes of (scale, bias) pairs, rows lr and 16 + lr at 8 lr.
+constexpr int kQ4Group = 64;
+constexpr int kQ4Chunk = 1024 + 128;
+inline size_t packed_q4_bytes(int N, int K) {
+  return (size_t)((N + kPackTileRows - 1) / kPackTileRows) * (size_t)(K / kQ4Group) * kQ4Chunk;
 }
 hipError_t launch_pack(const PackJob& j, hipStream_t st);
 

@@ -435,8 +435,70 @@ __global__ __launch_bounds__(256) void k_pack(const PackJob j) {
   }
 }
 
+// Source row of output column n of a pack job (nullptr past N).
+__device__ __forceinline__ const char* pack_src_row(const PackJob& j, int64_t tile, int row) {
+  const int64_t n = tile * kPackTileRows + row;
+  if (n >= j.N) return nullptr;
+  const int64_t row_bytes = (int64_t)j.K * j.esize;
+  if (j.kind == PACK_SWIGLU)
+    return static_cast<const char*>(row < 16 ? j.w0 : j.w1) + (tile * 16 + (row & 15)) * row_bytes;
+  if (j.kind == PACK_QKV)
+    return n < j.nq ? static_cast<const char*>(j.w0) + n * row_bytes
+                    : (n < j.nq + j.nkv ? static_cast<const char*>(j.w1) + (n - j.nq) * row_bytes
+                                        : static_cast<const char*>(j.w2) + (n - j.nq - j.nkv) * row_bytes);
+  return static_cast<const char*>(j.w0) + n * row_bytes;
+}
+
+// 4-bit packing: one thread a (tile, chunk, row) group of 64 bf16 weights. The group's
+// bias is its minimum, its scale (max - min) / 15 rounded once to bf16 and each code
+// rint((w - bias) / scale) clamped to [0, 15], all in float64 (a zero scale gives
+// codes 0); the codes and the (scale, bias) pair go to the places kQ4Chunk describes.
+__global__ __launch_bounds__(256) void k_pack_q4(const PackJob j) {
+  const int64_t chunks = j.K / kQ4Group;
+  const int64_t tiles = (j.N + kPackTileRows - 1) / kPackTileRows;
+  const int64_t total = tiles * chunks * kPackTileRows;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(i % kPackTileRows);
+    const int64_t chunk = (i / kPackTileRows) % chunks, tile = i / (kPackTileRows * chunks);
+    const char* src = pack_src_row(j, tile, row);
+    float w[kQ4Group];
+#pragma unroll
+    for (int q = 0; q < kQ4Group / 8; ++q) {
+      const uint4 v = src ? ldg16(src + chunk * kQ4Group * 2 + q * 16) : make_uint4(0, 0, 0, 0);
+      unpack(v, w + 8 * q, bf16_t());
+    }
+    float lo = w[0], hi = w[0];
+#pragma unroll
+    for (int k = 1; k < kQ4Group; ++k) {
+      lo = fminf(lo, w[k]);
+      hi = fmaxf(hi, w[k]);
+    }
+    const uint32_t sbits = bf16_from_double(((double)hi - (double)lo) / 15.0);
+    const double scale = (double)bf16_to_f32(sbits);
+    uint32_t codes[8];   // dword 2 lg + d: codes k = 16 lg + 8 d .. + 7, nibble e = code 16 lg + 8 d + e
+#pragma unroll
+    for (int dw = 0; dw < 8; ++dw) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double q = scale > 0.0 ? rint(((double)w[8 * dw + e] - (double)lo) / scale) : 0.0;
+        q = q < 0.0 ? 0.0 : (q > 15.0 ? 15.0 : q);
+        c |= (uint32_t)q << (4 * e);
+      }
+      codes[dw] = c;
+    }
+    char* dst = static_cast<char*>(j.dst) + (tile * chunks + chunk) * kQ4Chunk;
+    const int lr = row & 15, nt = row >> 4;
+#pragma unroll
+    for (int lg = 0; lg < 4; ++lg)
+      *reinterpret_cast<uint2*>(dst + (16 * lg + lr) * 16 + 8 * nt) = make_uint2(codes[2 * lg], codes[2 * lg + 1]);
+    *reinterpret_cast<uint32_t*>(dst + 1024 + 8 * lr + 4 * nt) = sbits | (f32_to_bf16(lo) << 16);
+  }
+}
+
 hipError_t launch_pack(const PackJob& j, hipStream_t st) {
-  (void)launch_k(k_pack, dim3(4096), dim3(256), st, j);
+  if (j.q4) (void)launch_k(k_pack_q4, dim3(4096), dim3(256), st, j);
+  else (void)launch_k(k_pack, dim3(4096), dim3(256), st, j);
   return hipGetLastError();
 }
 

@@ -164,6 +164,24 @@ size_t dflash_packed_weight_bytes(const dflash *h);
 int dflash_pack_weights(dflash *h, void *buf, size_t bytes, void *stream);
 
 /*
+ * 4-bit drafter weights (DFlash explainer, section 8: the drafter quantized at load with
+ * 4 bits in groups of 64; TensorFold #1851, "Exactness", Precision: the drafter's 4-bit
+ * copies beside bf16 activations and fp32 sums). dflash_pack_weights_q4 quantizes the
+ * same GEMM weights as dflash_pack_weights into `buf` (dflash_q4_weight_bytes bytes,
+ * 0 for an fp32 config): each run of 64 weights along a row becomes 64 4-bit codes
+ * and a bf16 (scale, bias), bias = the run's minimum, scale = (max - min) / 15 rounded
+ * once to bf16, code = (w - bias) / scale rounded to nearest even and clamped to
+ * [0, 15], all decided in float64. The GEMMs then compute with bias + scale * code
+ * exactly: sum_k x_k (bias + scale q_k) = scale * sum x q + bias * sum x per group.
+ * The embedding and the norm gains stay bf16. The 4-bit path runs the skinny GEMMs only:
+ * fuse and inject calls of more than 32 rows and drafts of more than 32 block rows are
+ * refused (DFLASH_ERR_UNIMPLEMENTED). Packing again (either kind) replaces it; binding
+ * again drops it. Errors otherwise as dflash_pack_weights.
+ */
+size_t dflash_q4_weight_bytes(const dflash *h);
+int dflash_pack_weights_q4(dflash *h, void *buf, size_t bytes, void *stream);
+
+/*
  * Workspace bytes for calls with at most `max_rows` fused/injected rows, `n_streams`
  * streams in a draft, and context length at most `max_ctx`. The workspace holds split-K
  * partials, block activations, attention partials and self-resetting counters.

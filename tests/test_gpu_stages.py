@@ -100,9 +100,9 @@ def compare_step(gpu, orc, what, stats, dtype):
     st[2] += g.size
 
 
-def run_stages(preset, streams=None):
+def run_stages(preset, streams=None, q4=False):
     p = wl.preset(preset)
-    case = RoundCase(p)
+    case = RoundCase(p, q4=q4)
     S, B = p.n_streams, p.block_size
     buf = torch.zeros(case.dr.trace_bytes(S), dtype=torch.uint8, device="cuda")
     case.dr.set_trace(buf)
@@ -113,6 +113,8 @@ def run_stages(preset, streams=None):
     logits_gpu = case.logits.cpu().numpy().astype(np.float64)
     toks_gpu = case.draft.cpu().numpy()
     W = case.weights_np()
+    if q4:       # the oracle's steps on the dequantized 4-bit weights
+        W = O.quantized_weights(p, {k: O.as_f64(v) for k, v in W.items()})
     d, nq, nkv = p.head_dim, p.n_q_heads, p.n_kv_heads
     stats = {}
     worst_logit = 0.0

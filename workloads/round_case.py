@@ -24,7 +24,7 @@ def to_np(t):
 
 
 class RoundCase:
-    def __init__(self, p, ctx=None, rows=None, device="cuda", permute_pages=True, seed=None, weights=None):
+    def __init__(self, p, ctx=None, rows=None, device="cuda", permute_pages=True, seed=None, weights=None, q4=False):
         self.p = p
         self.device = device
         seed = p.seed if seed is None else seed
@@ -62,7 +62,11 @@ class RoundCase:
                     self.kv.write_rows(l, s, 0, k, v)
         self.dr = D.Drafter(self.cfg)
         self.dr.dflash_bind_weights(self.W)
-        self.dr.new_packed_weights(device=device)
+        self.q4 = q4
+        if q4:
+            self.dr.new_q4_weights(device=device)        # the drafter's 4-bit copies
+        else:
+            self.dr.new_packed_weights(device=device)
         self.ws = self.dr.new_workspace(max(R, 1), S, self.max_ctx, device=device)
         self.fused = torch.zeros((max(R, 1), p.hidden), dtype=self.dtype, device=device)
         self.draft = torch.zeros((S, B - 1), dtype=torch.int32, device=device)
