@@ -56,15 +56,6 @@ __device__ __forceinline__ void top_xor_merge(float& v1, int& i1, float& v2, int
   }
 }
 
-// First element of packed tile `tile` (see GemmParams::wp): K elements a row, 32 rows.
-template <typename T>
-__device__ __forceinline__ const T* packed_tile(const GemmParams& p, int tile) {
-  const int64_t tile_elems = (int64_t)kPackTileRows * p.K;
-  if (p.wp_seg_tiles > 0)
-    return static_cast<const T*>(p.wp_l[tile / p.wp_seg_tiles]) + (int64_t)(tile % p.wp_seg_tiles) * tile_elems;
-  return static_cast<const T*>(p.wp) + (int64_t)tile * tile_elems;
-}
-
 // First byte of 4-bit packed tile `tile` (K / 64 chunks of kQ4Chunk bytes).
 __device__ __forceinline__ const unsigned char* packed_tile_q4(const GemmParams& p, int tile) {
   const int64_t tile_bytes = (int64_t)(p.K / kQ4Group) * kQ4Chunk;

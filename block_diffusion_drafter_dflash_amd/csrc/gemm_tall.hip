@@ -6,8 +6,8 @@
 // a batch of up to 256 rows reads every weight tile from HBM exactly once; wave
 // (wm, wn) computes a 64 x 64 piece as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles (the
 // largest piece whose accumulators fit, which keeps LDS reads at 0.5 per MFMA).
-// K goes in chunks of 64: a chunk's A (256 x 64) and W (128 x 64) tiles are copied
-// straight from global memory into LDS (buffer_load ... lds, XOR-swizzled 16-byte
+// K goes in chunks of 64: a chunk's A (256 x 64) and W (128 x 64, four 4 KB chunks of
+// the packed weights) tiles are copied straight from global memory into LDS (buffer_load ... lds, XOR-swizzled 16-byte
 // pieces so that fragment reads are free of bank conflicts) through a ring of three
 // buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
 // object, so the compiler sees that copies into one never alias the fragment reads
@@ -68,28 +68,6 @@ __device__ __forceinline__ void tall_top_merge(float& v1, int& i1, float& v2, fl
     i1 = bi1;
   } else {
     v2 = fmaxf(v2, bv1);
-  }
-}
-
-// Weight row of tile row r (0..127) of column tile t. SwiGLU tile t: the 64 rows of
-// wave column h = r / 64 are gate rows 64 t + 32 h + 0..31, then the matching up rows.
-template <int EPI>
-__device__ __forceinline__ const bf16_t* tall_wrow(const GemmParams& p, int t, int r) {
-  if constexpr (EPI == EPI_SWIGLU) {
-    const int h = r >> 6, q = r & 63;
-    const int gr = 64 * t + 32 * h + (q & 31);
-    return static_cast<const bf16_t*>(q < 32 ? p.w0 : p.w1) + (int64_t)gr * p.K;
-  } else if constexpr (EPI == EPI_RAW) {
-    const int n = t * BN + r;
-    if (p.seg_layers > 0) {
-      const int l = n / (2 * p.nkv), rem = n % (2 * p.nkv);
-      return static_cast<const bf16_t*>(rem < p.nkv ? p.wk_l[l] : p.wv_l[l]) + (int64_t)(rem % p.nkv) * p.K;
-    }
-    if (p.nq == 0 || n < p.nq) return static_cast<const bf16_t*>(p.w0) + (int64_t)n * p.K;
-    if (n < p.nq + p.nkv) return static_cast<const bf16_t*>(p.w1) + (int64_t)(n - p.nq) * p.K;
-    return static_cast<const bf16_t*>(p.w2) + (int64_t)(n - p.nq - p.nkv) * p.K;
-  } else {
-    return static_cast<const bf16_t*>(p.w0) + (int64_t)(t * BN + r) * p.K;
   }
 }
 
@@ -156,20 +134,22 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       a_off[k] = (ar - ar0) * (int)p.lda + piece * 8;
     }
   }
+  // Weights come packed (dflash_pack_weights): tile row r of column tile ct is row r %
+  // 32 of packed tile 4 ct + r / 32, whose chunk ch is 4 KB at ch * 4096 bytes; a load's
+  // RPL rows lie in one packed tile, so each wave-wide copy reads 1 KB contiguous.
+  // Tiles past the matrix's last packed tile repeat it (their results are never
+  // stored; packed rows past N are zero).
+  const int n_ptiles = (p.N + kPackTileRows - 1) / kPackTileRows;
 #pragma unroll
   for (int k = 0; k < QB; ++k) {
     const int q = QB * w + k;
     const int row = RPL * q + lane / NPC;
     const int piece = (lane % NPC) ^ swz(row);
-    if constexpr (EPI == EPI_SWIGLU) {
-      w_rsrc[k] = rsrc_of(tall_wrow<EPI>(p, ct, RPL * q));   // RPL consecutive gate or up rows
-      w_off[k] = (lane / NPC) * p.K + piece * 8;
-    } else {
-      const int n0 = min(ct * BN + RPL * q, p.N - 1), n = min(ct * BN + row, p.N - 1);
-      w_rsrc[k] = rsrc_of(tall_wrow<EPI>(p, ct, n0 - ct * BN));
-      w_off[k] = (n - n0) * p.K + piece * 8;
-    }
+    const int pt = min(4 * ct + (RPL * q) / kPackTileRows, n_ptiles - 1);
+    w_rsrc[k] = rsrc_of(packed_tile<bf16_t>(p, pt) + ((RPL * q) % kPackTileRows) * BK);
+    w_off[k] = (lane / NPC) * ROWB + piece * 16;   // bytes
   }
+  static_assert(BN == 4 * kPackTileRows && BK * 2 == 128, "a tile is four packed tiles; a chunk is one packed chunk");
   // Wave w copies A tile rows [RPL QA w, + RPL QA); when they all lie past the batch it
   // copies only its W share (their LDS rows are read by no live wave), and its ring
   // waits count only those copies.
@@ -192,7 +172,7 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
 #pragma unroll
     for (int k = 0; k < QB; ++k) {
       const int q = QB * w + k;
-      buf_load_lds16(w_rsrc[k], 2u * (uint32_t)w_off[k], 2u * (uint32_t)k0, buf + ATILE + q * 1024);
+      buf_load_lds16(w_rsrc[k], (uint32_t)w_off[k], (uint32_t)ch * (kPackTileRows * ROWB), buf + ATILE + q * 1024);
     }
   };
 
@@ -282,10 +262,11 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
           if (rv && n < p.N) reinterpret_cast<float*>(p.y_out)[((int64_t)ks * p.M + r) * p.N + n] = acc[i][j][e];
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
-        // column 16 j + lr (j = 0, 1) is gate row 64 ct + 32 wn + 16 j + lr; j + 2 its up row
+        // packed tile 4 ct + 2 wn + j (j = 0, 1): MFMA column tile 2 j holds its 16 gate
+        // rows 64 ct + 32 wn + 16 j + lr, column tile 2 j + 1 the matching up rows
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const double g = acc[i][j][e], u = acc[i][j + 2][e];
+          const double g = acc[i][2 * j][e], u = acc[i][2 * j + 1][e];
           if (rv)
             Elem<bf16_t>::store_d(static_cast<bf16_t*>(p.m_out) + (int64_t)r * p.ld_out + 64 * ct + 32 * wn + 16 * j + lr,
                                   g / (1.0 + exp(-g)) * u);

@@ -178,6 +178,15 @@ inline size_t packed_q4_bytes(int N, int K) {
 }
 hipError_t launch_pack(const PackJob& j, hipStream_t st);
 
+// First element of bf16/fp32 packed tile `tile` of a GEMM (32 rows over all of K).
+template <typename T>
+__device__ __forceinline__ const T* packed_tile(const GemmParams& p, int tile) {
+  const int64_t tile_elems = (int64_t)kPackTileRows * p.K;
+  if (p.wp_seg_tiles > 0)
+    return static_cast<const T*>(p.wp_l[tile / p.wp_seg_tiles]) + (int64_t)(tile % p.wp_seg_tiles) * tile_elems;
+  return static_cast<const T*>(p.wp) + (int64_t)tile * tile_elems;
+}
+
 struct VerifyParams {
   int S, B;
   const int* draft;
