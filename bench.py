@@ -150,6 +150,18 @@ def round_totals(costs):
     return b, f
 
 
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, sample_streams, min_seconds=10.0):
     """The oracle, as it stands, on whole rounds of the chosen streams, repeated until
     at least min_seconds of CPU work have been timed."""
@@ -170,6 +182,7 @@ def cpu_baseline(case, sample_streams, min_seconds=10.0):
     dt = total / reps
     drafted = len(sample_streams) * (case.p.block_size - 1)
     return dict(value=round(drafted / dt, 3), unit="drafted tokens/s", cores=int(threads), kind="oracle",
+                cpu_model=host_cpu_model(), host_threads=os.cpu_count(),
                 sample=f"{reps} whole rounds (fuse {sum(case.rows[s] for s in sample_streams)} rows, inject, "
                        f"draft) of stream(s) {sample_streams} of the same workload, float64 numpy; "
                        f"{dt:.2f} s per round", seconds=round(total, 2)), out
@@ -491,6 +504,7 @@ def prefill_main(args, p):
         except Exception:  # pragma: no cover
             threads = os.cpu_count() or 1
         out["cpu_baseline"] = dict(value=round(1.0 / per_row, 2), unit="rows/s", cores=int(threads), kind="oracle",
+                                   cpu_model=host_cpu_model(),
                                    sample=f"{reps} x fuse + inject of {len(idx)} of the {R} rows, float64 numpy",
                                    seconds=round(total, 2))
     else:
