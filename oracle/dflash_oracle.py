@@ -29,6 +29,9 @@ What it computes (sources are the four pages on DFlash):
   * sampling: inverse-CDF draws from tempered softmax rows, and speculative-
             sampling acceptance with the residual max(p_target - p_draft, 0)
             (explainer section 4, "Sampling decoding").
+  * selector: DFlash2's candidate path over the top-k tokens of each drafted
+            position, with rank-r pair scores and a min-p stop (explainer section 5;
+            TensorFold #1851 item 1; Strata #3457, "Problem and result").
   * 4-bit weights: affine quantization in groups of 64 along each weight row,
             and the dequantized weights used exactly (explainer section 8; TensorFold
             #1851, "Exactness", Precision).
@@ -402,6 +405,71 @@ def verify_sampling(draft, draft_logits, target_logits, T, u_accept, u_sample):
         committed[s, :a] = draft[s, :a]
         committed[s, a] = nxt
     return accept, token, committed
+
+
+# --------------------------------------------------------------------------
+# DFlash2 candidate path selector (DFlash explainer, section 5, "Candidate path
+# selector": top-k candidates at each position, a lightweight score of adjacent
+# candidate pairs, one consistent path; the DFlash2 config's selector_top_k 16 and
+# selector_rank 256; TensorFold #1851 item 1: with rank 0 the edge term is zero and
+# the path comes from each position's marginals; Strata #3457, "Problem and result":
+# --spec-min-p stops a draft where the selector's confidence falls below it).
+
+
+def top_k_ordered(logits, k):
+    """The k largest logits of a row, largest first, ties to the lowest index."""
+    order = np.lexsort((np.arange(logits.shape[-1]), -np.asarray(logits, dtype=np.float64)))
+    return order[:k]
+
+
+def log_softmax(logits):
+    x = np.asarray(logits, dtype=np.float64)
+    m = np.max(x)
+    return x - m - np.log(np.sum(np.exp(x - m)))
+
+
+def select_path(logits, code_u, code_w, k, min_p):
+    """One stream's path over its B-1 drafted positions.
+
+    logits [B-1, V]; code_u, code_w [V, r] token codebooks (r may be 0). Position j
+    keeps its top-k tokens c with node score log softmax(logits_j)(c); adjacent
+    candidates (a at j, b at j+1) add the edge score <code_u[a], code_w[b]>. The path
+    maximises the sum of node and edge scores (a tie goes to the earlier candidate,
+    i.e. the larger logit, at the latest position first). The draft stops before the
+    first position whose chosen token's probability is below min_p. Returns the tokens
+    (-1 past the stop) and the draft length.
+    """
+    Bm1 = logits.shape[0]
+    cand = [top_k_ordered(logits[j], k) for j in range(Bm1)]
+    node = [log_softmax(logits[j])[cand[j]] for j in range(Bm1)]
+    U = as_f64(code_u) if code_u is not None else None
+    Wc = as_f64(code_w) if code_w is not None else None
+
+    def edge(j):          # [k, k]: candidates of j against those of j + 1
+        if U is None or U.shape[1] == 0:
+            return np.zeros((k, k))
+        return U[cand[j]] @ Wc[cand[j + 1]].T
+
+    best = node[0].copy()
+    back = []
+    for j in range(1, Bm1):
+        tot = best[:, None] + edge(j - 1)                  # [from, to]
+        arg = np.argmax(tot, axis=0)                       # first maximum: the earlier candidate
+        back.append(arg)
+        best = tot[arg, np.arange(k)] + node[j]
+    path = [int(np.argmax(best))]
+    for arg in reversed(back):
+        path.append(int(arg[path[-1]]))
+    path.reverse()
+    toks = np.array([cand[j][path[j]] for j in range(Bm1)], dtype=np.int64)
+    probs = np.array([np.exp(node[j][path[j]]) for j in range(Bm1)])
+    length = Bm1
+    for j in range(Bm1):
+        if probs[j] < min_p:
+            length = j
+            break
+    toks[length:] = -1
+    return toks, length
 
 
 # --------------------------------------------------------------------------

@@ -13,6 +13,7 @@ import pytest
 
 import test_oracle_pins as P
 import test_oracle_quant as PQ
+import test_oracle_selector as PSel
 import test_oracle_sampling as PS
 import test_oracle_wiring as PW
 
@@ -107,6 +108,13 @@ MUTATIONS = [
     ("4-bit dequantization drops the bias", "return (bias[..., None] + scale[..., None] * g).reshape(N, K)",
      "return (scale[..., None] * g).reshape(N, K)"),
     ("4-bit groups of 32", "QUANT_GROUP = 64", "QUANT_GROUP = 32"),
+    # the DFlash2 candidate path selector (explainer section 5)
+    ("selector pair score transposed", "return U[cand[j]] @ Wc[cand[j + 1]].T", "return Wc[cand[j]] @ U[cand[j + 1]].T"),
+    ("selector candidates tie to the highest id",
+     "order = np.lexsort((np.arange(logits.shape[-1]), -np.asarray(logits, dtype=np.float64)))",
+     "order = np.lexsort((-np.arange(logits.shape[-1]), -np.asarray(logits, dtype=np.float64)))"),
+    ("selector stops at or below min-p", "        if probs[j] < min_p:", "        if probs[j] <= min_p + 0.06:"),
+    ("selector ignores the node scores", "        best = tot[arg, np.arange(k)] + node[j]", "        best = tot[arg, np.arange(k)]"),
     ("storage sizes: planner counts one copy", "return (2 * n_taps + 2) * hidden * elem_bytes",
      "return (n_taps + 2) * hidden * elem_bytes"),
 ]
@@ -127,7 +135,7 @@ def load_mutant(old, new):
 def pin_calls():
     """Every CPU pin of the oracle, with its parameters."""
     calls = []
-    for mod in (P, PW, PS, PQ):
+    for mod in (P, PW, PS, PQ, PSel):
         for name in sorted(dir(mod)):
             fn = getattr(mod, name)
             if not name.startswith("test_") or not callable(fn):
