@@ -91,6 +91,7 @@ def library():
         "dflash_sample_rows": (i32, [_VP, i32, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, sz, _VP]),
         "dflash_verify_sampling": (i32, [_VP, i32, _VP, _VP, _VP, i64, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
                                          _VP, _VP, sz, _VP]),
+        "dflash_select_path": (i32, [_VP, i32, _VP, i64, _VP, _VP, i32, i32, ctypes.c_float, _VP, _VP, _VP, sz, _VP]),
         "dflash_trace_bytes": (sz, [_VP, i32]),
         "dflash_set_trace": (i32, [_VP, _VP, sz]),
         "dflash_set_profiling": (i32, [_VP, i32]),
@@ -112,7 +113,7 @@ EXPORTED = ["dflash_config_init", "dflash_create", "dflash_tensor_count", "dflas
             "dflash_fused_row_bytes", "dflash_tap_row_bytes", "dflash_workspace_bytes", "dflash_workspace_init",
             "dflash_fuse_taps", "dflash_inject_kv", "dflash_inject_kv_layers", "dflash_layers_reading",
             "dflash_draft_block", "dflash_draft_block_noalloc", "dflash_verify_greedy",
-            "dflash_sample_rows", "dflash_verify_sampling",
+            "dflash_sample_rows", "dflash_verify_sampling", "dflash_select_path",
             "dflash_trace_bytes", "dflash_set_trace", "dflash_set_profiling", "dflash_profile_read", "dflash_last_error", "dflash_destroy", "dflash_version"]
 
 
@@ -187,6 +188,15 @@ class Drafter:
 
     def last_error(self):
         return self.lib.dflash_last_error(self.h).decode()
+
+    def dflash_select_path(self, logits, code_u, code_w, top_k, min_p, draft_out, draft_len, ws, n_streams=None,
+                           stream=None):
+        """DFlash2 path selector over logits [S, B-1, V] (fp32); code_u / code_w bf16 [V, r] or None."""
+        n_streams = logits.shape[0] if n_streams is None else n_streams
+        rank = 0 if code_u is None else int(code_u.shape[1])
+        self._check(self.lib.dflash_select_path(self.h, n_streams, _ptr(logits), logits.stride(1), _ptr(code_u),
+                                                _ptr(code_w), rank, int(top_k), float(min_p), _ptr(draft_out),
+                                                _ptr(draft_len), _ptr(ws), ws.numel(), _stream(stream)))
 
     # -- instrumentation
     def trace_bytes(self, n_streams):

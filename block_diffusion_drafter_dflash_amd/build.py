@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libdflash.so")
-SOURCES = ["gemm.hip", "gemm_tall.hip", "attention.hip", "small.hip", "sampling.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "gemm_tall.hip", "attention.hip", "small.hip", "sampling.hip", "selector.hip", "api.cpp"]
 
 
 def hipcc():

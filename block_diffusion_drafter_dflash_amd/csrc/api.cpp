@@ -571,6 +571,8 @@ size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_strea
   b = std::max(b, layout_draft(*h, n_streams, max_ctx).end);
   b = std::max(b, layout_verify(*h, n_streams).end);
   b = std::max(b, layout_sample(std::max(max_rows, n_streams * h->cfg.block_size)).end);
+  const size_t sel_rows = (size_t)n_streams * (h->cfg.block_size - 1);
+  b = std::max(b, align_up(kCounterInts * 4) + align_up(sel_rows * kSelectMaxK * 4) + sel_rows * kSelectMaxK * 8);
   return b;
 }
 
@@ -1264,6 +1266,49 @@ int dflash_set_trace(dflash* h, void* buf, size_t bytes) {
   if (buf && !aligned16(buf)) return fail(h, DFLASH_ERR_ARG, "trace buffer misaligned");
   h->trace = bytes ? buf : nullptr;
   h->trace_cap = buf ? bytes : 0;
+  return DFLASH_OK;
+}
+
+int dflash_select_path(dflash* h, int32_t n_streams, const float* logits, int64_t row_stride, const void* code_u,
+                       const void* code_w, int32_t rank, int32_t top_k, float min_p, int32_t* draft_out,
+                       int32_t* draft_len, void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_ARG;
+  const auto& c = h->cfg;
+  if (n_streams < 1 || n_streams > c.max_streams)
+    return fail(h, DFLASH_ERR_ARG, "n_streams %d outside [1, %d]", n_streams, c.max_streams);
+  if (!logits || !draft_out || !draft_len) return fail(h, DFLASH_ERR_ARG, "logits, draft_out or draft_len is NULL");
+  if (top_k < 1 || top_k > kSelectMaxK || top_k > c.vocab)
+    return fail(h, DFLASH_ERR_ARG, "top_k %d outside [1, min(%d, vocab)]", top_k, kSelectMaxK);
+  if (rank < 0) return fail(h, DFLASH_ERR_ARG, "rank %d < 0", rank);
+  if (rank > 0 && (!code_u || !code_w)) return fail(h, DFLASH_ERR_ARG, "rank %d needs both codebooks", rank);
+  if (row_stride < c.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
+  if (!(min_p >= 0.f) || !std::isfinite(min_p)) return fail(h, DFLASH_ERR_ARG, "min_p must be finite and >= 0");
+  const size_t rows = (size_t)n_streams * (c.block_size - 1);
+  const size_t need = align_up(kCounterInts * 4) + align_up(rows * kSelectMaxK * 4) + rows * kSelectMaxK * 8;
+  int rc = check_ws(h, ws, ws_bytes, need);
+  if (rc != DFLASH_OK) return rc;
+  char* W = static_cast<char*>(ws);
+  SelectParams sp;
+  sp.S = n_streams;
+  sp.B = c.block_size;
+  sp.V = c.vocab;
+  sp.k = top_k;
+  sp.rank = rank;
+  sp.ld = row_stride;
+  sp.logits = logits;
+  sp.code_u = code_u;
+  sp.code_w = code_w;
+  sp.min_p = min_p;
+  sp.cand_idx = reinterpret_cast<int*>(W + align_up(kCounterInts * 4));
+  sp.cand_node = reinterpret_cast<double*>(W + align_up(kCounterInts * 4) + align_up(rows * kSelectMaxK * 4));
+  sp.draft_out = draft_out;
+  sp.draft_len = draft_len;
+  hipError_t e;
+  {
+    ProfScope ps(h, "select_path", (hipStream_t)stream);
+    e = launch_select(sp, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "select path: %s", hipGetErrorString(e));
   return DFLASH_OK;
 }
 

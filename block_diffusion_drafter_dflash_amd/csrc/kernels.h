@@ -187,6 +187,23 @@ __device__ __forceinline__ const T* packed_tile(const GemmParams& p, int tile) {
   return static_cast<const T*>(p.wp) + (int64_t)tile * tile_elems;
 }
 
+// DFlash2 candidate path selector over [S, B-1] rows of drafted fp32 logits.
+constexpr int kSelectMaxK = 16;
+constexpr int kSelectMaxB = 32;
+struct SelectParams {
+  int S, B, V, k, rank;
+  int64_t ld;             // row stride of logits, in floats
+  const float* logits;
+  const void* code_u;     // bf16 [V, rank] (rank 0: unused)
+  const void* code_w;
+  float min_p;
+  int* cand_idx;          // workspace [S * (B-1)][kSelectMaxK]
+  double* cand_node;      // workspace [S * (B-1)][kSelectMaxK]: log softmax of each candidate
+  int* draft_out;         // [S, B-1], -1 past the stop
+  int* draft_len;         // [S]
+};
+hipError_t launch_select(const SelectParams& p, hipStream_t st);
+
 struct VerifyParams {
   int S, B;
   const int* draft;

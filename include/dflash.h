@@ -364,6 +364,36 @@ int dflash_verify_sampling(dflash *h, int32_t n_streams, const int32_t *draft,
                            void *stream);
 
 /*
+ * DFlash2 candidate path selector (DFlash explainer, section 5: keep the top-k
+ * candidates of every drafted position, score adjacent candidate pairs with a light
+ * selector, pick one consistent path; DFlash2's config: top-k 16, rank 256; TensorFold
+ * #1851 item 1: with no codebooks, rank 0, the pair term is zero and the path comes from
+ * each position's marginals; Strata #3457, "Problem and result": a draft stops where
+ * the selector's confidence falls below min-p).
+ *   logits:   device fp32 [n_streams, B-1] rows of `row_stride` floats (>= vocab), e.g.
+ *             dflash_draft_block's logits_out.
+ *   code_u, code_w: device bf16 [vocab, rank] token codebooks; the pair score of token a
+ *             at position j and token b at j+1 is <code_u[a], code_w[b]>, summed in
+ *             float64. rank 0: no pair term (both may be NULL).
+ *   top_k:    1..16 candidates a position: the largest logits, ties to the lowest id;
+ *             node score log softmax(logits_j)(token), the partition sum in float64.
+ *   The path maximises the sum of node and pair scores over the candidates (a tie goes
+ *   to the earlier candidate, choosing the last position first and walking back).
+ *   min_p:    the draft stops before the first position whose chosen token's
+ *             probability is below min_p (0 keeps every position).
+ *   draft_out: device int32 [n_streams, B-1]: the path's tokens, -1 past the stop (so
+ *             dflash_verify_greedy accepts at most the draft length).
+ *   draft_len: device int32 [n_streams].
+ * ws as for a draft of n_streams streams (dflash_workspace_bytes). Errors: bad counts
+ * or pointers -> DFLASH_ERR_ARG; workspace -> DFLASH_ERR_STATE / DFLASH_ERR_CAPACITY.
+ * Works without bound weights.
+ */
+int dflash_select_path(dflash *h, int32_t n_streams, const float *logits, int64_t row_stride,
+                       const void *code_u, const void *code_w, int32_t rank, int32_t top_k,
+                       float min_p, int32_t *draft_out, int32_t *draft_len, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/*
  * Instrumentation (not part of the round). With profiling enabled, every kernel the
  * handle launches is bracketed by two hipEvents on its stream; dflash_profile_read
  * waits for the recorded events and writes one line per kernel name,
