@@ -4,11 +4,13 @@
 // from HBM exactly once. A workgroup owns one work item: a tile of 32 output columns
 // for 16*MT rows over one of the GEMM's ksplit ranges of K. W comes in the packed
 // layout (dflash_pack_weights): the tile's rows as consecutive 4 KB chunks of 32 rows
-// x 128 bytes, so a K range of a tile is one contiguous region. The KW waves take the
-// range's chunks in turn, so the workgroup streams KW consecutive chunks at a time (a
-// pattern that reads HBM at 6.0 TB/s where 32 rows read side by side, 2 K bytes
-// apart, reach 5.1); each lane reads U*16 bytes of each of its rows per chunk, with
-// the wave's next chunk in flight. Every MFMA's partial (32 products per element for
+// x 128 bytes, so a K range of a tile is one contiguous region, and inside a chunk the
+// bytes stand in MFMA fragment order, so that each of a wave's four loads of a chunk
+// is 1 KB contiguous. The KW waves take the range's chunks in turn, so the workgroup
+// streams KW consecutive chunks at a time, with the wave's next chunk in flight; the
+// loads are nontemporal (the weights are read once). Measured on the 9B shapes, this
+// reads HBM at 5.7-6.7 TB/s where row-major chunks (each load 16 rows x 64 bytes of a
+// 2 KB span) reach 5.0-6.0 and 32 rows read side by side 3.0-5.6. Every MFMA's partial (32 products per element for
 // bf16) is added into a float64 accumulator and the KW wave partials are summed in
 // wave order. With ksplit > 1 each range writes its own float64 partial and the
 // consuming kernel adds the ranges in order (see kernels.h), so no workgroup ever
@@ -56,6 +58,13 @@ __device__ __forceinline__ void top_xor_merge(float& v1, int& i1, float& v2, int
   }
 }
 
+// 16-byte load that bypasses the caches' retention (each weight is read once).
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // First byte of 4-bit packed tile `tile` (K / 64 chunks of kQ4Chunk bytes).
 __device__ __forceinline__ const unsigned char* packed_tile_q4(const GemmParams& p, int tile) {
   const int64_t tile_bytes = (int64_t)(p.K / kQ4Group) * kQ4Chunk;
@@ -98,16 +107,18 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
   const int lane_k = lg * (U * E);
   static_assert(16 * NT == kPackTileRows && KI * (int)sizeof(T) == 128, "a packed chunk is 32 rows of 128 bytes");
 
-  // Packed weights: iteration `it` of this tile is the chunk at tw + it * 32 * KI, rows
-  // 16 nt + lr of it at KI elements apart. The KW waves take the range's chunks in
-  // turn (wave w: kb + w, kb + w + KW, ...), so at any time the workgroup streams KW
-  // consecutive 4 KB chunks of one contiguous region.
+  // Packed weights: iteration `it` of this tile is the chunk at tw + it * 32 * KI, whose
+  // fragment (nt, u) (1 KB at (2 nt + u) * 1 KB) holds at lane l's 16 bytes the piece
+  // this lane multiplies: row 16 nt + lr, elements lane_k + u E .. of the chunk's KI.
+  // The KW waves take the range's chunks in turn (wave w: kb + w, kb + w + KW, ...), so
+  // at any time the workgroup streams KW consecutive 4 KB chunks of one region.
   const T* tw = packed_tile<T>(p, tile);
   const unsigned char* tq = WQ ? packed_tile_q4(p, tile) : nullptr;
   static_assert(!WQ || (sizeof(T) == 2 && KI == kQ4Group && U == 2 && NT == 2), "4-bit groups are one bf16 chunk");
+  static_assert(U == 2 && NT == 2, "a chunk is four 1 KB fragments (nt, u)");
   int boff[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) boff[nt] = (16 * nt + lr) * KI + lane_k;
+  for (int nt = 0; nt < NT; ++nt) boff[nt] = (2 * nt * kWave + lane) * E;
   int64_t aoff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(Tune::KW * kWave) void k_gemm(const GemmParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int u = 0; u < U; ++u) bb[nt][u] = ldg16(tw + (int64_t)it * (kPackTileRows * KI) + boff[nt] + u * E);
+        for (int u = 0; u < U; ++u) bb[nt][u] = ldg16_nt(tw + (int64_t)it * (kPackTileRows * KI) + boff[nt] + u * kWave * E);
     }
     if constexpr (AM == A_TAPS) {
       // An iteration's KI columns never straddle two planes (hidden % KI == 0).

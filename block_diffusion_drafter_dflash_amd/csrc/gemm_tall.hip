@@ -7,9 +7,13 @@
 // (wm, wn) computes a 64 x 64 piece as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles (the
 // largest piece whose accumulators fit, which keeps LDS reads at 0.5 per MFMA).
 // K goes in chunks of 64: a chunk's A (256 x 64) and W (128 x 64, four 4 KB chunks of
-// the packed weights) tiles are copied straight from global memory into LDS (buffer_load ... lds, XOR-swizzled 16-byte
-// pieces so that fragment reads are free of bank conflicts) through a ring of three
-// buffers, two chunks in flight while one is multiplied. Each buffer is its own LDS
+// the packed weights) tiles are copied straight from global memory into LDS
+// (buffer_load ... lds) through a ring of three buffers, two chunks in flight while
+// one is multiplied. A's rows land XOR-swizzled by 16-byte pieces so that fragment
+// reads are free of bank conflicts; W's chunks are copied as they are, since their
+// bytes already stand in fragment order (each fragment read is 1 KB contiguous). A
+// k-step of 32 takes pieces 2 lg + s of the 64 (lane group lg, step s), the order of
+// the packed weights; A's fragments follow it. Each buffer is its own LDS
 // object, so the compiler sees that copies into one never alias the fragment reads
 // of another. The MFMAs accumulate in fp32 over the whole K range, and a K range's
 // result is stored as a float32 partial (the consumers add the ranges in float64). Waves whose 64 rows lie past
@@ -134,22 +138,22 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
       a_off[k] = (ar - ar0) * (int)p.lda + piece * 8;
     }
   }
-  // Weights come packed (dflash_pack_weights): tile row r of column tile ct is row r %
-  // 32 of packed tile 4 ct + r / 32, whose chunk ch is 4 KB at ch * 4096 bytes; a load's
-  // RPL rows lie in one packed tile, so each wave-wide copy reads 1 KB contiguous.
-  // Tiles past the matrix's last packed tile repeat it (their results are never
-  // stored; packed rows past N are zero).
+  // Weights come packed (dflash_pack_weights): column tile ct is packed tiles 4 ct ..
+  // 4 ct + 3, whose chunk ch is 4 KB at ch * 4096 bytes, in fragment order: 1 KB
+  // fragment f = 2 nt + u holds, at lane l's 16 bytes, piece 2 (l / 16) + u of row
+  // 16 nt + l % 16. Copy q brings fragment q % 4 of packed tile 4 ct + q / 4 to LDS
+  // offset q KB of the W tile, unchanged. Tiles past the matrix's last packed tile
+  // repeat it (their results are never stored; packed rows past N are zero).
   const int n_ptiles = (p.N + kPackTileRows - 1) / kPackTileRows;
 #pragma unroll
   for (int k = 0; k < QB; ++k) {
     const int q = QB * w + k;
-    const int row = RPL * q + lane / NPC;
-    const int piece = (lane % NPC) ^ swz(row);
-    const int pt = min(4 * ct + (RPL * q) / kPackTileRows, n_ptiles - 1);
-    w_rsrc[k] = rsrc_of(packed_tile<bf16_t>(p, pt) + ((RPL * q) % kPackTileRows) * BK);
-    w_off[k] = (lane / NPC) * ROWB + piece * 16;   // bytes
+    const int pt = min(4 * ct + q / 4, n_ptiles - 1);
+    w_rsrc[k] = rsrc_of(packed_tile<bf16_t>(p, pt));
+    w_off[k] = (q % 4) * 1024 + lane * 16;   // bytes
   }
-  static_assert(BN == 4 * kPackTileRows && BK * 2 == 128, "a tile is four packed tiles; a chunk is one packed chunk");
+  static_assert(BN == 4 * kPackTileRows && BK * 2 == 128 && WTILE == 16 * 1024,
+                "a tile is four packed tiles; a chunk is one packed chunk of four 1 KB fragments");
   // Wave w copies A tile rows [RPL QA w, + RPL QA); when they all lie past the batch it
   // copies only its W share (their LDS rows are read by no live wave), and its ring
   // waits count only those copies.
@@ -177,17 +181,19 @@ __global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams 
   };
 
   // ---- fragments: A rows 64 wm + 16 i + lr, W rows 64 wn + 16 j + lr; for k-step s
-  // of the chunk, lane group lg reads k = 32 s + 8 lg .. + 7 (piece 4 s + lg). One
-  // buffer plus one offset, so that every read stays attributed to its buffer.
+  // of the chunk, lane group lg reads piece 2 lg + s (k = 16 lg + 8 s .. + 7): from A's
+  // swizzled rows, and from W's fragment (nt, u) = (j % 2, s) of packed tile 2 wn +
+  // j / 2, lane l at 16 l. One buffer plus one offset, so that every read stays
+  // attributed to its buffer.
   constexpr int KS = BK / 32;
   int aoff[KS][4], boff[KS][4];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ra = 64 * wm + 16 * i + lr, rb = 64 * wn + 16 * i + lr;
-      aoff[s][i] = ra * ROWB + (((4 * s + lg) ^ swz(ra)) * 16);
-      boff[s][i] = ATILE + rb * ROWB + (((4 * s + lg) ^ swz(rb)) * 16);
+      const int ra = 64 * wm + 16 * i + lr;
+      aoff[s][i] = ra * ROWB + (((2 * lg + s) ^ swz(ra)) * 16);
+      boff[s][i] = ATILE + (2 * wn + i / 2) * 4096 + (2 * (i % 2) + s) * 1024 + lane * 16;
     }
 
   floatx4 acc[4][4];

@@ -36,9 +36,11 @@ struct GemmParams {
   int tap_h;
   int64_t tap_stride;
   // B operand of the skinny kernel: the packed weights. Tile t (32 output columns) is
-  // K / KI consecutive chunks of [32 rows][KI] elements (KI = 128 bytes of a row), so
-  // a tile over a K range is one contiguous region; wp_seg_tiles > 0 splits the tiles
-  // into per-layer segments with their own bases (inject).
+  // K / KI consecutive 4 KB chunks of 32 rows x KI elements (KI = 128 bytes of a row),
+  // so a tile over a K range is one contiguous region; a chunk's 16-byte pieces are in
+  // fragment order (1 KB fragment 2 nt + u: at 16 l, piece 2 (l / 16) + u of row
+  // 16 nt + l % 16). wp_seg_tiles > 0 splits the tiles into per-layer segments with
+  // their own bases (inject).
   const void* wp;
   int wp_seg_tiles;
   const void* wp_l[kMaxLayers];
@@ -148,8 +150,9 @@ struct RowNormParams {
 };
 
 // One weight matrix copied into the skinny kernel's packed layout (see GemmParams::wp):
-// tile t holds output columns 32 t .. 32 t + 31 (zero rows past N), each as K / KI
-// chunks of 128 bytes a row. Kinds pick the source row of output column n.
+// tile t holds output columns 32 t .. 32 t + 31 (zero rows past N) as K / KI chunks
+// of 128 bytes a row, each chunk in fragment order. Kinds pick the source row of
+// output column n.
 enum PackKind { PACK_PLAIN = 0, PACK_QKV = 1, PACK_SWIGLU = 2 };
 struct PackJob {
   int kind, N, K, esize;

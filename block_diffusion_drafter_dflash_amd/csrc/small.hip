@@ -414,7 +414,10 @@ __global__ __launch_bounds__(256) void k_pack(const PackJob j) {
   const int64_t total = tiles * chunks * (kPackTileRows * 8);
   const int64_t row_bytes = (int64_t)j.K * j.esize;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int piece = (int)(i % 8), row = (int)((i / 8) % kPackTileRows);
+    // 16-byte unit d of a chunk: fragment f = d / 64 (= 2 nt + u), lane l = d % 64
+    // (= 16 lg + lr), holding piece 2 lg + u of tile row 16 nt + lr
+    const int d = (int)(i % (8 * kPackTileRows)), f = d >> 6, l = d & 63;
+    const int row = 16 * (f >> 1) + (l & 15), piece = 2 * (l >> 4) + (f & 1);
     const int64_t chunk = (i / (8 * kPackTileRows)) % chunks, tile = i / (8 * kPackTileRows * chunks);
     const int64_t n = tile * kPackTileRows + row;
     const char* src = nullptr;

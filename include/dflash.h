@@ -154,7 +154,10 @@ int64_t dflash_tap_row_bytes(const dflash_config *cfg, int32_t fusing);
  * 256-byte aligned; else DFLASH_ERR_ARG / DFLASH_ERR_CAPACITY), on `stream`. In the
  * packed layout the 32 output columns a workgroup computes are K / KI consecutive
  * chunks of 32 rows x 128 bytes, so each workgroup streams one contiguous region of
- * HBM instead of 32 rows 2 K bytes apart; the values are the bound weights' own. Every
+ * HBM instead of 32 rows 2 K bytes apart; inside a chunk the 16-byte pieces stand in
+ * the order the MFMAs take them (four 1 KB fragments; fragment 2 nt + u holds, at
+ * 16 l, piece 2 (l / 16) + u of row 16 nt + l % 16), so each wave load is 1 KB
+ * contiguous. The values are the bound weights' own. Every
  * GEMM then reads the packed copy; the bound embedding and norm gains stay in use (and
  * the bound pointers stay the source of any later packing). Required once after
  * dflash_bind_weights, before the first fuse,
