@@ -99,11 +99,15 @@ def kernel_costs(p, ctx, rows, sampling=False, q4=False):
 
 
 # Source files whose kernels a committed traffic measurement covers, per kernel name.
+_GEMM_SOURCES = ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"]
 KERNEL_SOURCES = {
-    "gate_up_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
-    "lm_head_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
-    "down_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
-    "fuse_fc_gemm": ["gemm.hip", "gemm_tall.hip", "common.hpp", "kernels.h"],
+    "gate_up_gemm": _GEMM_SOURCES,
+    "lm_head_gemm": _GEMM_SOURCES,
+    "down_gemm": _GEMM_SOURCES,
+    "qkv_gemm": _GEMM_SOURCES,
+    "o_proj_gemm": _GEMM_SOURCES,
+    "fuse_fc_gemm": _GEMM_SOURCES,
+    "inject_kv_gemm": _GEMM_SOURCES,
     "attention_full": ["attention.hip", "common.hpp", "kernels.h"],
 }
 COPY_CALIBRATION_BYTES = 256 << 20
