@@ -82,6 +82,63 @@ __device__ __forceinline__ uint32_t bit_range16(int a, int e) {
   return e > a ? ((0xffffu >> (16 - (e - a))) << a) : 0u;
 }
 
+// The work item of this block: (chunk c, kv head h, stream s). Narrow batches, and
+// wide ones of more than 64 streams, take the grid's own order. Wide batches of up to
+// 64 streams run their items longest first: a stream's chunks are cpp pages each but
+// the last, which is shorter, and the streams' reaches differ, so in grid order the
+// last workgroups to start can be whole chunks that finish long after the rest. The
+// (stream, chunk) items are ranked by pages (descending), then stream, then chunk,
+// with the kv heads innermost; block i takes item i (each lane of a wave holds one
+// stream's two groups of equal-size chunks and finds their first ranks), and the
+// blocks past the items return at once. An item's arithmetic does not depend on
+// which block runs it.
+__device__ __forceinline__ bool attn_item(const AttnParams& p, int& c, int& h, int& s) {
+  if (!p.wide || p.S > kWave) {
+    c = blockIdx.x;
+    h = blockIdx.y;
+    s = blockIdx.z;
+    return true;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  // this lane's stream: groups (z1 pages x n1 chunks from chunk 0) and (z2 pages, the last)
+  int z1 = -1, n1 = 0, z2 = -1, n_own = 0;
+  if (lane < p.S) {
+    int Cs = p.ctx_len[lane];
+    Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
+    const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
+    const int pages = span_pages(lo, Cs);
+    n_own = attention_chunks(pages, 1);
+    const int cpp = pages > 0 ? attention_chunk_pages(pages, 1) : 0;
+    z1 = cpp;
+    n1 = n_own - 1;
+    z2 = pages - (n_own - 1) * cpp;
+  }
+  // first rank of each group: the items of the groups ordered before it
+  int r1 = 0, r2 = 0;
+  for (int t = 0; t < p.S; ++t) {
+    const int tz1 = __shfl(z1, t, kWave), tn1 = __shfl(n1, t, kWave), tz2 = __shfl(z2, t, kWave);
+    // group (tz1, t, chunk 0) and group (tz2, t, chunk n_own(t) - 1)
+    if (tn1 > 0) {
+      if (tz1 > z1 || (tz1 == z1 && t < lane)) r1 += tn1;
+      if (tz1 > z2 || (tz1 == z2 && t <= lane)) r2 += tn1;   // t == lane: chunks 0.. precede the last
+    }
+    if (tz2 > z1 || (tz2 == z1 && t < lane)) r1 += 1;
+    if (tz2 > z2 || (tz2 == z2 && t < lane)) r2 += 1;
+  }
+  const int q = i / p.n_kv_heads;
+  const bool in1 = lane < p.S && n1 > 0 && q >= r1 && q < r1 + n1;
+  const bool in2 = lane < p.S && q == r2;
+  const uint64_t m1 = __ballot(in1), m2 = __ballot(in2);
+  if (m1 == 0 && m2 == 0) return false;
+  const int src = m1 ? __builtin_ctzll(m1) : __builtin_ctzll(m2);
+  const int cc = in1 ? q - r1 : n_own - 1;
+  s = src;
+  c = __shfl(cc, src, kWave);
+  h = i % p.n_kv_heads;
+  return true;
+}
+
 template <typename T, int D, int QT, int KG>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using C = AttnCfg<T, D>;
@@ -102,7 +159,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int kg = wv / QT, w = wv % QT;   // key group, query wave
-  const int c = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  int c, h, s;
+  if (!attn_item(p, c, h, s)) return;   // a block past the real work items: the whole workgroup leaves
   const int g = p.group, B = p.B;
   const int nq_local = g * B;
 
