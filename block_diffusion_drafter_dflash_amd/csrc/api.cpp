@@ -210,7 +210,7 @@ InjectLayout layout_inject(const dflash& h, int R) {
 struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
-  size_t x, a, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
+  size_t x, a, rope, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
@@ -233,6 +233,7 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   r.take(kCounterInts * 4);
   L.x = r.take((size_t)M * c.hidden * es);
   L.a = r.take((size_t)M * c.hidden * es);
+  L.rope = r.take((size_t)M * (c.head_dim / 2) * 16);
   L.qkv_raw = r.take(L.qkv.part_bytes(M, h.nq() + 2 * h.nkv()));
   L.o_parts = r.take(L.o.part_bytes(M, c.hidden));
   L.d_parts = r.take(L.down.part_bytes(M, c.hidden));
@@ -929,6 +930,11 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
   ep.eps = c.rms_eps;
   ep.x = X;
   ep.a = A;
+  ep.rope = reinterpret_cast<double2*>(W + L.rope);
+  ep.head_dim = c.head_dim;
+  ep.max_ctx = max_ctx_len;
+  ep.theta = c.rope_theta;
+  ep.ctx_len = ctx_len;
   {
     ProfScope ps(h, "embed", st);
     e = launch_embed(c.dtype, ep, st);
@@ -993,11 +999,9 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     qf.raw = qkv_raw;
     qf.ksplit = L.qkv.ksplit;
     qf.raw_f32 = L.qkv.tall ? 1 : 0;
-    qf.ctx_len = ctx_len;
-    qf.max_ctx = max_ctx_len;
+    qf.rope = reinterpret_cast<const double2*>(W + L.rope);
     qf.q_norm = h->w.q_norm[l];
     qf.k_norm = h->w.k_norm[l];
-    qf.theta = c.rope_theta;
     qf.eps = c.rms_eps;
     qf.q = W + L.q;
     qf.kblk = W + L.kblk;

@@ -89,11 +89,10 @@ struct QkvFinishParams {
   const void* raw;      // partials [ksplit, S*B, nq + 2 nkv]
   int ksplit;
   int raw_f32;          // 1: the partials are float32 (tiled GEMM), 0: float64
-  const int* ctx_len;
-  int max_ctx;
+  const double2* rope;  // the round's rotary table (EmbedParams::rope)
   const void* q_norm;
   const void* k_norm;
-  float theta, eps;
+  float eps;
   void* q;              // [S*B, nq]
   void* kblk;           // [S, n_kv, 32, d]
   void* vblk;           // [S, n_kv, d, 32]
@@ -122,6 +121,13 @@ struct EmbedParams {
   float eps;
   void* x;              // [S*B, hidden] residual stream
   void* a;              // [S*B, hidden] round(RMSNorm(x) * gain)
+  // the round's rotary table, shared by every layer: rope[r * head_dim / 2 + i] =
+  // (cos, sin) of pos(r) * theta^(-2 i / head_dim) in float64, pos(r) = clamp(ctx_len[s],
+  // 0, max_ctx) + j for block row r = s * B + j
+  double2* rope;
+  int head_dim, max_ctx;
+  float theta;
+  const int* ctx_len;
 };
 
 // Residual add and RMSNorm of one row: with partials,

@@ -80,6 +80,16 @@ __global__ __launch_bounds__(kNormThreads) void k_embed(const EmbedParams p) {
   T* dst = static_cast<T*>(p.x) + (int64_t)r * p.hidden;
   T* a = static_cast<T*>(p.a) + (int64_t)r * p.hidden;
   const T* gn = static_cast<const T*>(p.gain);
+  if (threadIdx.x < p.head_dim / 2) {
+    // this row's rotary table, for every layer of the round
+    int Cs = p.ctx_len[s];
+    Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
+    const int i = threadIdx.x;
+    const double inv_freq = pow((double)p.theta, -2.0 * (double)i / (double)p.head_dim);
+    double sn, cs;
+    sincos((double)(Cs + j) * inv_freq, &sn, &cs);
+    p.rope[(int64_t)r * (p.head_dim / 2) + i] = make_double2(cs, sn);
+  }
   uint4 v[CH], g[CH];
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
@@ -180,11 +190,11 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(const NormParams p) {
 
 // Block rows' heads: q = RoPE(q_norm(raw q)), k = RoPE(k_norm(raw k)), v = raw v,
 // each rounded once. One wave per (row, head); lane l holds the rotary pair
-// (l, l + D/2). k goes to the stream's block key page [32][D], v to its transposed
-// value page [D][32]; the row-0 wave of a head also clears slots B..31 of both.
+// (l, l + D/2), rotated by the round's table (written by k_embed). k goes to the
+// stream's block key page [32][D], v to its transposed value page [D][32]; the row-0
+// wave of a head also clears slots B..31 of both.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
-  __shared__ double2 tab[D / 2];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int s = r / p.B, j = r % p.B;
   const int n_heads = p.n_q_heads + 2 * p.n_kv_heads;
@@ -192,8 +202,6 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   const bool head_ok = hi < n_heads;
   const int nq = p.n_q_heads * D, ld = nq + 2 * p.n_kv_heads * D;
   const bool on = head_ok && lane < D / 2;
-  // The first eight partials' loads go out before the rotary table is computed, so
-  // their latency overlaps the table's float64 sincos.
   const int64_t src_off = (int64_t)r * ld + (int64_t)(head_ok ? hi : 0) * D;
   const double* src = static_cast<const double*>(p.raw) + src_off;
   const float* srcf = static_cast<const float*>(p.raw) + src_off;
@@ -208,16 +216,6 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
         v1[k] = p.raw_f32 ? (double)srcf[o + D / 2] : src[o + D / 2];
       }
   }
-  int Cs = p.ctx_len[s];
-  Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
-  const int pos = Cs + j;
-  for (int i = tid; i < D / 2; i += 256) {
-    const double inv_freq = pow((double)p.theta, -2.0 * (double)i / (double)D);
-    double sn, cs;
-    sincos((double)pos * inv_freq, &sn, &cs);
-    tab[i] = make_double2(cs, sn);
-  }
-  __syncthreads();
   if (!head_ok) return;
   double x0 = 0.0, x1 = 0.0;
   if (on) {
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const QkvFinishParams p) {
   const T* gn = static_cast<const T*>(is_q ? p.q_norm : p.k_norm);
   const double y0 = x0 * inv * (double)Elem<T>::load1(gn + lane);
   const double y1 = x1 * inv * (double)Elem<T>::load1(gn + lane + D / 2);
-  const double2 cs = tab[lane];
+  const double2 cs = p.rope[(int64_t)r * (D / 2) + lane];
   const double o0 = y0 * cs.x - y1 * cs.y, o1 = y1 * cs.x + y0 * cs.y;
   if (is_q) {
     T* q = static_cast<T*>(p.q) + (int64_t)r * nq + (int64_t)hi * D;
