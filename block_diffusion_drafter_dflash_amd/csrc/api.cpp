@@ -130,7 +130,7 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
 }
 
 struct AttnPlan {
-  int n_chunks, qt, wide;
+  int n_chunks, qt, cls;
   size_t part_o_bytes, part_ml_bytes;
 };
 
@@ -143,8 +143,8 @@ int max_reach_pages(int max_ctx, int window) {
 
 AttnPlan plan_attn(const dflash_config& c, int S, int max_ctx, int window) {
   AttnPlan a;
-  a.wide = attn_is_wide(S * c.block_size) ? 1 : 0;
-  a.n_chunks = attention_chunks(max_reach_pages(max_ctx, window), a.wide);
+  a.cls = attn_class(S * c.block_size);
+  a.n_chunks = attention_chunks(max_reach_pages(max_ctx, window), a.cls);
   a.qt = attention_query_tiles(c.n_q_heads / c.n_kv_heads, c.block_size);
   const size_t sh = (size_t)S * c.n_kv_heads * a.n_chunks;
   a.part_o_bytes = a.n_chunks > 1 ? sh * a.qt * 64 * (c.head_dim / 16) * 4 * 4 : 0;
@@ -1025,7 +1025,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     ap.group = c.n_q_heads / c.n_kv_heads;
     ap.window = c.layer_window[l];
     ap.n_chunks = L.attn[l].n_chunks;
-    ap.wide = L.attn[l].wide;
+    ap.cls = L.attn[l].cls;
     ap.max_ctx = max_ctx_len;
     ap.ctx_len = ctx_len;
     ap.q = W + L.q;

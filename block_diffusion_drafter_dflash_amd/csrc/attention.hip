@@ -82,8 +82,8 @@ __device__ __forceinline__ uint32_t bit_range16(int a, int e) {
   return e > a ? ((0xffffu >> (16 - (e - a))) << a) : 0u;
 }
 
-// The work item of this block: (chunk c, kv head h, stream s). Narrow batches, and
-// wide ones of more than 64 streams, take the grid's own order. Wide batches of up to
+// The work item of this block: (chunk c, kv head h, stream s). Narrow and mid
+// batches, and wide ones of more than 64 streams, take the grid's own order. Wide batches of up to
 // 64 streams run their items longest first: a stream's chunks are cpp pages each but
 // the last, which is shorter, and the streams' reaches differ, so in grid order the
 // last workgroups to start can be whole chunks that finish long after the rest. The
@@ -93,7 +93,7 @@ __device__ __forceinline__ uint32_t bit_range16(int a, int e) {
 // blocks past the items return at once. An item's arithmetic does not depend on
 // which block runs it.
 __device__ __forceinline__ bool attn_item(const AttnParams& p, int& c, int& h, int& s) {
-  if (!p.wide || p.S > kWave) {
+  if (p.cls != 2 || p.S > kWave) {
     c = blockIdx.x;
     h = blockIdx.y;
     s = blockIdx.z;
@@ -108,8 +108,8 @@ __device__ __forceinline__ bool attn_item(const AttnParams& p, int& c, int& h, i
     Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
     const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
     const int pages = span_pages(lo, Cs);
-    n_own = attention_chunks(pages, 1);
-    const int cpp = pages > 0 ? attention_chunk_pages(pages, 1) : 0;
+    n_own = attention_chunks(pages, 2);
+    const int cpp = pages > 0 ? attention_chunk_pages(pages, 2) : 0;
     z1 = cpp;
     n1 = n_own - 1;
     z2 = pages - (n_own - 1) * cpp;
@@ -170,8 +170,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int pg_lo = lo / 16;
   const int n_pages = span_pages(lo, Cs);
   // This stream's own chunking; the grid's chunks past it are empty.
-  const int n_own = attention_chunks(n_pages, p.wide);
-  const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages, p.wide) : 0;
+  const int n_own = attention_chunks(n_pages, p.cls);
+  const int cpp = n_pages > 0 ? attention_chunk_pages(n_pages, p.cls) : 0;
   const int cp0 = c * cpp;
   int n_cp = c < n_own ? ((c + 1) * cpp < n_pages ? (c + 1) * cpp : n_pages) - cp0 : 0;
   n_cp = n_cp > 0 ? n_cp : 0;   // the last chunks of a rounded-up split can be empty
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_attn_combine(const AttnP
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
-  const int n_own = attention_chunks(span_pages(lo, Cs), p.wide);   // >= 1
+  const int n_own = attention_chunks(span_pages(lo, Cs), p.cls);   // >= 1
   // (max, sum) of query qi, chunk c: mq[c]
   const float2* mq = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + (qi < nq_local ? qi : 0)) * p.n_chunks;
   const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_attn_combine_short(const Attn
   int Cs = p.ctx_len[s];
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
-  const int n_own = attention_chunks(span_pages(lo, Cs), p.wide);   // 1 <= n_own <= RC
+  const int n_own = attention_chunks(span_pages(lo, Cs), p.cls);   // 1 <= n_own <= RC
   const float2* mq = reinterpret_cast<const float2*>(p.part_ml) + ((int64_t)sh * (QT * 16) + qi) * p.n_chunks;
   const float* po = p.part_o + (((int64_t)sh * p.n_chunks * QT + qt) * NDT + dt) * (kWave * 4) + lane * 4;
   const int64_t cstride = (int64_t)QT * NDT * (kWave * 4);

@@ -65,8 +65,8 @@ struct GemmParams {
 struct AttnParams {
   int S, B, n_q_heads, n_kv_heads, head_dim, group;
   int window;           // 0 = full
-  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages, wide)
-  int wide;             // 1: the batch is wide (attn_is_wide), chunks of up to 64 pages
+  int n_chunks;         // grid chunks per (stream, kv head): attention_chunks(max pages, cls)
+  int cls;              // the batch's attention class (attn_class): 0 narrow, 1 mid, 2 wide
   int max_ctx;
   const int* ctx_len;
   const void* q;        // [S*B, n_q*d] rotated, normalised queries
@@ -263,24 +263,28 @@ struct SpecVerifyParams {
 };
 
 // Context chunking, in pages of 16 keys, of one stream's reach: a function of that
-// reach and of the batch's class (see attn_is_wide), so a stream's result does not
-// depend on the other streams of a batch of its class. Narrow batches: up to 256
-// pages (4096 keys) a chunk holds kChunkPagesShort pages; up to 2048 pages the chunk
-// count stays at 256 / kChunkPagesShort; beyond, chunks hold at most 64 pages. Wide
-// batches (many streams fill the GPU by themselves): chunks of up to 64 pages, which
-// keeps the per-chunk partials few. No chunk ever exceeds 64 pages (the attention
-// kernel keeps a chunk's page ids one per lane), and the count never decreases as
-// the reach grows, so a grid sized for the longest reach covers every stream.
-constexpr int kChunkPagesShort = 8;
+// reach and of the batch's class (attn_class), so a stream's result does not depend
+// on the other streams of a batch of its class. Narrow and mid batches: chunks of
+// `sp` pages (8 narrow, 16 mid: a mid batch's streams already give the grid more work
+// items), at most kChunksShort of them up to kChunksShort * 64 pages; beyond, chunks
+// of at most 64 pages. Wide batches (many streams fill the GPU by themselves): chunks
+// of up to 64 pages, which keeps the per-chunk partials few. No chunk ever exceeds 64
+// pages (the attention kernel keeps a chunk's page ids one per lane), and the count
+// never decreases as the reach grows, so a grid sized for the longest reach covers
+// every stream.
+constexpr int kChunkPagesNarrow = 8;
+constexpr int kChunkPagesMid = 16;
 constexpr int kChunkPagesMax = 64;
-__host__ __device__ inline int attention_chunks(int pages, int wide) {
-  if (wide) return pages <= kChunkPagesMax ? 1 : (pages + kChunkPagesMax - 1) / kChunkPagesMax;
-  if (pages <= 256) return pages <= kChunkPagesShort ? 1 : (pages + kChunkPagesShort - 1) / kChunkPagesShort;
-  if (pages <= 256 / kChunkPagesShort * kChunkPagesMax) return 256 / kChunkPagesShort;
-  return (pages + kChunkPagesMax - 1) / kChunkPagesMax;
+constexpr int kChunksShort = 32;
+__host__ __device__ inline int attention_chunks(int pages, int cls) {
+  if (cls == 2 || pages > kChunksShort * kChunkPagesMax)
+    return pages <= kChunkPagesMax ? 1 : (pages + kChunkPagesMax - 1) / kChunkPagesMax;
+  const int sp = cls == 1 ? kChunkPagesMid : kChunkPagesNarrow;
+  const int n = (pages + sp - 1) / sp;
+  return n < 1 ? 1 : (n > kChunksShort ? kChunksShort : n);
 }
-__host__ __device__ inline int attention_chunk_pages(int pages, int wide) {
-  const int n = attention_chunks(pages, wide);
+__host__ __device__ inline int attention_chunk_pages(int pages, int cls) {
+  const int n = attention_chunks(pages, cls);
   return (pages + n - 1) / n;
 }
 // Pages touched by the key range [lo, hi) (page-aligned span).
@@ -316,12 +320,14 @@ int gemm_ksplit(int epi, int n_tiles, int iters, int K);
 //    item's A rows for every 32-column tile, so its L2 traffic grows with the row
 //    groups; the tiled kernel copies each weight tile once for up to 256 rows and
 //    skips the MFMAs of 64-row groups past the batch.
-//  - From kAttnWideMinRows rows on, attention takes the 64-page chunking (enough
-//    streams fill the GPU by themselves); fewer rows keep the finer narrow chunking.
+//  - Attention chunking (attention_chunks): up to 32 rows the narrow class, from
+//    kTallMinRows rows the mid class (coarser short chunks), from kAttnWideMinRows
+//    rows the wide class (64-page chunks: enough streams fill the GPU by themselves).
+//    The mid class starts where the tiled GEMMs do, so it adds no class boundary.
 constexpr int kTallMinRows = 33;
 constexpr int kAttnWideMinRows = 65;
 inline bool gemm_is_tiled(int rows) { return rows >= kTallMinRows; }
-inline bool attn_is_wide(int rows) { return rows >= kAttnWideMinRows; }
+inline int attn_class(int rows) { return rows >= kAttnWideMinRows ? 2 : (rows >= kTallMinRows ? 1 : 0); }
 int gemm_tall_ksplit(int epi, int N, int K);
 int gemm_tall_column_tiles(int epi, int N);
 constexpr int kTallRoundTiles = 256;   // column tiles of one round: one per CU

@@ -509,8 +509,9 @@ WIDE = small_variant(MID, name="wide_bf16", n_streams=6, ctx_spec=[300, 77, 1030
 
 @pytest.mark.parametrize("preset", [MID, WIDE], ids=["64_rows", "96_rows"])
 def test_tiled_batch_classes_are_invariant_to_stream_order_bitwise(preset):
-    # 4 streams x block 16 = 64 rows (tiled GEMMs with one live row group, narrow
-    # attention chunks) and 6 x 16 = 96 rows (tiled GEMMs, 64-page attention chunks).
+    # 4 streams x block 16 = 64 rows (tiled GEMMs with one live row group, the mid
+    # class's 16-page attention chunks) and 6 x 16 = 96 rows (tiled GEMMs, 64-page
+    # attention chunks).
     # A stream's result is bitwise the same in any batch of its class; here the same
     # streams drafted in reverse order.
     case = RoundCase(preset)
