@@ -109,6 +109,7 @@ KERNEL_SOURCES = {
     "fuse_fc_gemm": _GEMM_SOURCES,
     "inject_kv_gemm": _GEMM_SOURCES,
     "attention_full": ["attention.hip", "common.hpp", "kernels.h"],
+    "attention_sliding": ["attention.hip", "common.hpp", "kernels.h"],
 }
 COPY_CALIBRATION_BYTES = 256 << 20
 
