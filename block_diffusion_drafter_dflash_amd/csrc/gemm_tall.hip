@@ -3,9 +3,10 @@
 // Y[M, N] = A[M, K] . W[N, K]^T with the same epilogues and outputs as the skinny
 // kernel (float64 K-range partials, SwiGLU, LM-head logits and per-32-column top-2).
 // A workgroup of 8 waves owns a 256-row x 128-column output tile over one K range, so
-// a batch of up to 256 rows reads every weight tile from HBM exactly once; wave
-// (wm, wn) computes a 64 x 64 piece as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles (the
-// largest piece whose accumulators fit, which keeps LDS reads at 0.5 per MFMA).
+// a batch of up to 256 rows reads every weight tile from HBM exactly once (the LM head
+// of up to 64 rows: a 64 x 128 tile, two waves); wave (wm, wn) computes a 64 x 64 piece
+// as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles (the largest piece whose accumulators fit,
+// which keeps LDS reads at 0.5 per MFMA).
 // K goes in chunks of 64: a chunk's A (256 x 64) and W (128 x 64, four 4 KB chunks of
 // the packed weights) tiles are copied straight from global memory into LDS
 // (buffer_load ... lds) through a ring of three buffers, two chunks in flight while
@@ -32,19 +33,32 @@ namespace dfl {
 
 namespace {
 
-constexpr int kWaves = 8, kTallThreads = 64 * kWaves;
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int WM = 4, WN = 2;                // waves along M and N: 64 x 64 each
+constexpr int BN = 128, BK = 64;
+constexpr int WN = 2;                        // waves along N: 64 columns each
 constexpr int kRing = 3;                     // chunk buffers
 constexpr int ROWB = BK * 2;                 // bytes of one tile row in LDS (bf16)
-constexpr int ATILE = BM * ROWB, WTILE = BN * ROWB;
+constexpr int WTILE = BN * ROWB;
 constexpr int NPC = ROWB / 16;               // 16-byte pieces per tile row
 constexpr int RPL = 1024 / ROWB;             // tile rows per wave-wide load
-constexpr int QA = ATILE / 1024 / kWaves;    // A loads per wave per chunk
-constexpr int QB = WTILE / 1024 / kWaves;    // W loads per wave per chunk
-constexpr int LPW = QA + QB;                 // loads per wave per chunk
-static_assert(WM * WN == kWaves && WM * 64 == BM && WN * 64 == BN, "waves tile the output");
-static_assert(ATILE % (1024 * kWaves) == 0 && WTILE % (1024 * kWaves) == 0, "tiles split evenly over the waves");
+
+// Row tile of WM 64-row groups (WM x WN waves, each a 64 x 64 piece). The LM head of
+// a batch of up to 64 rows takes WM = 1: a 64 x 128 tile, two waves and 72 KB of
+// LDS, so two workgroups share a CU and keep twice the copies in flight of one
+// 256-row workgroup whose other six waves would idle. An output element's arithmetic
+// (its MFMAs over the K range, in order) does not depend on the tile, so both shapes
+// give the same bits.
+template <int WM_>
+struct Tall {
+  static constexpr int WM = WM_;
+  static constexpr int kWaves = WM * WN, THREADS = 64 * kWaves;
+  static constexpr int BM = 64 * WM;
+  static constexpr int ATILE = BM * ROWB;
+  static constexpr int QA = ATILE / 1024 / kWaves;   // A loads per wave per chunk
+  static constexpr int QB = WTILE / 1024 / kWaves;   // W loads per wave per chunk
+  static constexpr int LPW = QA + QB;                // loads per wave per chunk
+  static_assert(WN * 64 == BN, "waves tile the output");
+  static_assert(ATILE % (1024 * kWaves) == 0 && WTILE % (1024 * kWaves) == 0, "tiles split evenly over the waves");
+};
 // 16-byte piece p of tile row r sits at piece p ^ swz(r): the 16 rows one fragment
 // read touches (128 bytes apart) land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & (NPC - 1); }
@@ -91,8 +105,10 @@ __device__ __forceinline__ void ring_barrier() {
 
 }  // namespace
 
-template <int EPI, int AM>
-__global__ __launch_bounds__(kTallThreads, 1) void k_gemm_tall(const GemmParams p) {
+template <int EPI, int AM, int WM_>
+__global__ __launch_bounds__(Tall<WM_>::THREADS, 1) void k_gemm_tall(const GemmParams p) {
+  using S = Tall<WM_>;
+  constexpr int BM = S::BM, ATILE = S::ATILE, QA = S::QA, QB = S::QB, LPW = S::LPW;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[ATILE + WTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[ATILE + WTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char buf2[ATILE + WTILE];
@@ -330,18 +346,29 @@ int gemm_tall_ksplit(int epi, int N, int K) {
   return best;
 }
 
-hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st) {
-  const int n_ct = gemm_tall_column_tiles(epi, p.N), n_rt = (p.M + BM - 1) / BM;
+template <int WM>
+static hipError_t launch_tall_shape(int epi, int am, const GemmParams& p, hipStream_t st) {
+  using S = Tall<WM>;
+  const int n_ct = gemm_tall_column_tiles(epi, p.N), n_rt = (p.M + S::BM - 1) / S::BM;
   const int grid = (n_ct * p.ksplit + 7) / 8 * 8 * n_rt;
   if (epi == EPI_RAW && am == A_TAPS)
-    (void)launch_k(k_gemm_tall<EPI_RAW, A_TAPS>, dim3(grid), dim3(kTallThreads), st, p);
+    (void)launch_k(k_gemm_tall<EPI_RAW, A_TAPS, WM>, dim3(grid), dim3(S::THREADS), st, p);
   else if (epi == EPI_RAW)
-    (void)launch_k(k_gemm_tall<EPI_RAW, A_PLAIN>, dim3(grid), dim3(kTallThreads), st, p);
+    (void)launch_k(k_gemm_tall<EPI_RAW, A_PLAIN, WM>, dim3(grid), dim3(S::THREADS), st, p);
   else if (epi == EPI_SWIGLU)
-    (void)launch_k(k_gemm_tall<EPI_SWIGLU, A_PLAIN>, dim3(grid), dim3(kTallThreads), st, p);
+    (void)launch_k(k_gemm_tall<EPI_SWIGLU, A_PLAIN, WM>, dim3(grid), dim3(S::THREADS), st, p);
   else
-    (void)launch_k(k_gemm_tall<EPI_LMHEAD, A_PLAIN>, dim3(grid), dim3(kTallThreads), st, p);
+    (void)launch_k(k_gemm_tall<EPI_LMHEAD, A_PLAIN, WM>, dim3(grid), dim3(S::THREADS), st, p);
   return hipGetLastError();
+}
+
+// The 64-row tile for the LM head of batches of up to 64 rows: its ~1200 column tiles
+// fill the GPU several times over, and two workgroups a CU stream it faster (4-stream
+// long-context round: 318 -> 299 us). The projections have fewer column tiles than
+// CUs; there the eight-wave workgroup, whose idle waves still issue copies, is faster.
+hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st) {
+  if (p.M <= 64 && epi == EPI_LMHEAD) return launch_tall_shape<1>(epi, am, p, st);
+  return launch_tall_shape<4>(epi, am, p, st);
 }
 
 }  // namespace dfl
