@@ -16,7 +16,7 @@ Bars (the oracle keeps float64; the GPU sums in fp32):
     movement at RATE) and mean |d| <= FACTOR x its mean movement, with RATE = 1e-4 and
     FACTOR = 2 pinned on the CPU by tests/test_oracle_conditioning.py. Every step of
     those rounds is held to 1 ulp on identical inputs by tests/test_gpu_stages.py.
-    Each comparison also logs the benchmark spec's own figures: the max-abs against 2e-2
+    Each comparison also logs the plain bar's own figures: the max-abs against 2e-2
     and the drafted tokens that differ where the oracle's top-2 gap exceeds 2e-2;
   * drafted tokens: equal to the oracle's wherever the oracle's top-2 gap exceeds
     the logit tolerance, elsewhere the GPU token's oracle logit lies within the
@@ -125,7 +125,7 @@ def compare_round(case, streams, orc, tol=None, mean_tol=None):
         srt = np.sort(o["logits"], axis=-1)
         sure = (srt[:, -1] - srt[:, -2]) > 2e-2
         ns_off = int(np.sum(toks[s][sure] != O.argmax_lowest(o["logits"])[sure]))
-        log(f"[northstar] {p.name} stream {s}: logits max-abs {d:.4g} vs 2e-2 ({'met' if d <= 2e-2 else 'not met'}); "
+        log(f"[bar-2e-2] {p.name} stream {s}: logits max-abs {d:.4g} vs 2e-2 ({'met' if d <= 2e-2 else 'not met'}); "
             f"tokens differing where the gap > 2e-2: {ns_off} of {int(sure.sum())}")
         t1, t2 = O.top2(o["logits"])
         dt = float(max(np.max(np.abs(top2[s, :, 0] - t1)), np.max(np.abs(top2[s, :, 1] - t2))))

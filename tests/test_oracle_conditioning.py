@@ -1,6 +1,6 @@
 """Pins of the whole-round logit bar used for the 9B- and DFlash2-shaped workloads.
 
-The benchmark spec holds logits to 2e-2 of the float64 oracle. For the wide random-init
+The parity bar holds logits to 2e-2 of the float64 oracle. For the wide random-init
 models that bar lies below the float64 model's own sensitivity to bf16 rounding, so the
 GPU tests of whole rounds at those shapes use
     tol = max(2e-2, FACTOR x the oracle's own max logit movement when a fraction RATE
