@@ -536,6 +536,38 @@ def test_tiled_batch_classes_are_invariant_to_stream_order_bitwise(preset):
         assert torch.equal(dr[i], bdraft[s])
 
 
+# 70 streams of block 4 (280 rows, the wide class): more streams than the attention's
+# longest-first item order ranks (64), so the grid's own order runs; contexts from 0
+# to 1190 keys give every stream one to three 64-page chunks or none.
+MANY = small_variant(MID, name="many70_bf16", n_streams=70, block_size=4,
+                     ctx_spec=[0 if s % 23 == 3 else (s * 389 + 11) % 1193 for s in range(70)], seed=2011)
+
+
+def test_wide_batch_past_64_streams_parity_and_stream_order_bitwise():
+    case = RoundCase(MANY)
+    ctx = case.ctx
+    pick = sorted({0, 69, int(np.argmin(ctx)), int(np.argmax(ctx)), 3, 26, 35, 50})
+    run_case(case, pick)
+    batched, bdraft = case.logits.clone(), case.draft.clone()
+    S = MANY.n_streams
+    perm = list(reversed(range(S)))
+    kv = SimpleNamespace(struct=D.KV())
+    for l in range(MANY.n_layers):
+        kv.struct.k_pool[l] = case.kv.k[l].data_ptr()
+        kv.struct.v_pool[l] = case.kv.v[l].data_ptr()
+    pt = case.kv.page_table[perm].contiguous()
+    kv.struct.page_table = pt.data_ptr()
+    kv.struct.pages_per_stream = case.kv.pages_per_stream
+    out = torch.zeros_like(case.logits)
+    dr = torch.zeros_like(case.draft)
+    case.dr.dflash_draft_block(case.anchor[perm].contiguous(), case.ctx_len[perm].contiguous(), case.max_ctx, kv, dr,
+                               case.ws, logits_out=out)
+    torch.cuda.synchronize()
+    for i, st in enumerate(perm):
+        assert torch.equal(out[i].view(torch.int32), batched[st].view(torch.int32)), f"stream {st}"
+        assert torch.equal(dr[i], bdraft[st])
+
+
 def test_graph_replay_of_a_round_matches_eager_bitwise():
     # One round (fuse, inject, draft, verify) captured as a HIP graph: every replay,
     # with eager rounds and synchronisations between them, writes the eager round's bits.
