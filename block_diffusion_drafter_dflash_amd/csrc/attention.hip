@@ -161,10 +161,16 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int kg = wv / QT, w = wv % QT;   // key group, query wave
   int c, h, s;
   if (!attn_item(p, c, h, s)) return;   // a block past the real work items: the whole workgroup leaves
+  // The item and the stream's context length are the same in every lane; held as
+  // scalars, the masks and branches that derive from them stay scalar too (no
+  // exec-mask branches, and no copies of the running output between their paths).
+  c = __builtin_amdgcn_readfirstlane(c);
+  h = __builtin_amdgcn_readfirstlane(h);
+  s = __builtin_amdgcn_readfirstlane(s);
   const int g = p.group, B = p.B;
   const int nq_local = g * B;
 
-  int Cs = p.ctx_len[s];
+  int Cs = __builtin_amdgcn_readfirstlane(p.ctx_len[s]);
   Cs = Cs < 0 ? 0 : (Cs > p.max_ctx ? p.max_ctx : Cs);
   const int lo = p.window > 0 ? (Cs - p.window > 0 ? Cs - p.window : 0) : 0;
   const int pg_lo = lo / 16;
