@@ -21,7 +21,6 @@ namespace {
 
 thread_local std::string g_create_error = "";
 
-constexpr int64_t kCounterInts = 1 << 16;     // attention chunk counters (self-resetting)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -185,7 +184,6 @@ FuseLayout layout_fuse(const dflash& h, int R) {
   const auto& c = h.cfg;
   L.g = plan_gemm(c.dtype, EPI_RAW, A_TAPS, R, c.hidden, c.n_taps * c.hidden, c.hidden, gemm_is_tiled(R));
   Region r;
-  r.take(kCounterInts * 4);
   L.y = r.take(L.g.part_bytes(R, c.hidden));
   L.end = r.off;
   return L;
@@ -201,7 +199,6 @@ InjectLayout layout_inject(const dflash& h, int R) {
   const int N = c.n_layers * 2 * h.nkv();
   L.g = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, R, N, c.hidden, 0, gemm_is_tiled(R));
   Region r;
-  r.take(kCounterInts * 4);
   L.raw = r.take(L.g.part_bytes(R, N));
   L.end = r.off;
   return L;
@@ -230,7 +227,6 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
     pml = std::max(pml, L.attn.back().part_ml_bytes);
   }
   Region r;
-  r.take(kCounterInts * 4);
   L.x = r.take((size_t)M * c.hidden * es);
   L.a = r.take((size_t)M * c.hidden * es);
   L.rope = r.take((size_t)M * (c.head_dim / 2) * 16);
@@ -257,7 +253,6 @@ struct SampleLayout {
 SampleLayout layout_sample(int rows) {
   SampleLayout L;
   Region r;
-  r.take(kCounterInts * 4);
   L.stats = r.take((size_t)rows * kSlices * 16);
   L.end = r.off;
   return L;
@@ -269,7 +264,6 @@ VerifyLayout layout_verify(const dflash& h, int S) {
   VerifyLayout L;
   const int B = h.cfg.block_size;
   Region r;
-  r.take(kCounterInts * 4);
   L.draft_stats = r.take((size_t)S * (B - 1) * kSlices * 16);
   L.target_stats = r.take((size_t)S * B * kSlices * 16);
   L.row_info = r.take((size_t)S * 4 * 8);
@@ -560,7 +554,7 @@ int dflash_pack_weights_q4(dflash* h, void* buf, size_t bytes, void* stream) { r
 
 size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_streams, int32_t max_ctx) {
   if (!h || max_rows < 0 || n_streams < 1 || n_streams > h->cfg.max_streams || max_ctx < 0) return 0;
-  size_t b = align_up(kCounterInts * 4);
+  size_t b = 0;
   if (max_rows > 0) {
     // a call of up to max_rows rows runs passes of at most min(max_rows, kRowPass)
     // rows, on the skinny kernel (float64 partials) up to 32 rows, tiled from 33
@@ -573,17 +567,15 @@ size_t dflash_workspace_bytes(const dflash* h, int32_t max_rows, int32_t n_strea
   b = std::max(b, layout_verify(*h, n_streams).end);
   b = std::max(b, layout_sample(std::max(max_rows, n_streams * h->cfg.block_size)).end);
   const size_t sel_rows = (size_t)n_streams * (h->cfg.block_size - 1);
-  b = std::max(b, align_up(kCounterInts * 4) + align_up(sel_rows * kSelectMaxK * 4) + sel_rows * kSelectMaxK * 8);
+  b = std::max(b, align_up(sel_rows * kSelectMaxK * 4) + sel_rows * kSelectMaxK * 8);
   return b;
 }
 
 int dflash_workspace_init(dflash* h, void* ws, size_t ws_bytes, void* stream) {
   if (!h) return DFLASH_ERR_ARG;
+  (void)stream;   // nothing is enqueued: no part of a workspace must start at zero
   if (!ws || !aligned16(ws)) return fail(h, DFLASH_ERR_ARG, "workspace is NULL or misaligned");
-  if (ws_bytes < (size_t)kCounterInts * 4)
-    return fail(h, DFLASH_ERR_CAPACITY, "workspace of %zu bytes is smaller than its counter block", ws_bytes);
-  hipError_t e = launch_fill_zero(static_cast<int*>(ws), kCounterInts, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(h, DFLASH_ERR_DEVICE, "workspace init: %s", hipGetErrorString(e));
+  if (ws_bytes == 0) return fail(h, DFLASH_ERR_CAPACITY, "workspace of 0 bytes");
   for (auto& r : h->ws_ready)
     if (r.first == ws) {
       r.second = ws_bytes;
@@ -893,7 +885,6 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     rc = check_ws(h, ws, ws_bytes, L.end);
     if (rc) return rc;
   }
-  if ((int64_t)n_streams * c.n_kv_heads > kCounterInts) return fail(h, DFLASH_ERR_CAPACITY, "too many streams");
   if (!h->packed) return fail(h, DFLASH_ERR_STATE, "weights are not packed (dflash_pack_weights)");
   if (h->q4 && gemm_is_tiled(n_streams * c.block_size))
     return fail(h, DFLASH_ERR_UNIMPLEMENTED, "4-bit weights run on drafts of at most %d block rows", kTallMinRows - 1);
@@ -1288,7 +1279,7 @@ int dflash_select_path(dflash* h, int32_t n_streams, const float* logits, int64_
   if (row_stride < c.vocab) return fail(h, DFLASH_ERR_ARG, "row_stride %lld < vocab", (long long)row_stride);
   if (!(min_p >= 0.f) || !std::isfinite(min_p)) return fail(h, DFLASH_ERR_ARG, "min_p must be finite and >= 0");
   const size_t rows = (size_t)n_streams * (c.block_size - 1);
-  const size_t need = align_up(kCounterInts * 4) + align_up(rows * kSelectMaxK * 4) + rows * kSelectMaxK * 8;
+  const size_t need = align_up(rows * kSelectMaxK * 4) + rows * kSelectMaxK * 8;
   int rc = check_ws(h, ws, ws_bytes, need);
   if (rc != DFLASH_OK) return rc;
   char* W = static_cast<char*>(ws);
@@ -1303,8 +1294,8 @@ int dflash_select_path(dflash* h, int32_t n_streams, const float* logits, int64_
   sp.code_u = code_u;
   sp.code_w = code_w;
   sp.min_p = min_p;
-  sp.cand_idx = reinterpret_cast<int*>(W + align_up(kCounterInts * 4));
-  sp.cand_node = reinterpret_cast<double*>(W + align_up(kCounterInts * 4) + align_up(rows * kSelectMaxK * 4));
+  sp.cand_idx = reinterpret_cast<int*>(W);
+  sp.cand_node = reinterpret_cast<double*>(W + align_up(rows * kSelectMaxK * 4));
   sp.draft_out = draft_out;
   sp.draft_len = draft_len;
   hipError_t e;

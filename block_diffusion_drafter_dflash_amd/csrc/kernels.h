@@ -344,7 +344,6 @@ hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st);
 hipError_t launch_norm(int dtype, const NormParams& p, hipStream_t st);
 hipError_t launch_qkv_finish(int dtype, const QkvFinishParams& p, hipStream_t st);
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
-hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st);
 hipError_t launch_slice_stats(const float* logits, int rows, int V, int64_t ld, float scale, double* stats,
                               hipStream_t st);
 hipError_t launch_sample_rows(const SampleParams& p, hipStream_t st);

@@ -503,11 +503,6 @@ hipError_t launch_pack(const PackJob& j, hipStream_t st) {
   return hipGetLastError();
 }
 
-__global__ void k_fill_zero(int* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
 // Groups of E elements a thread needs for `hidden`: 1, 2 or 4 (hidden <= 4 * 512 * E).
 static int row_groups(int dtype, int hidden) {
   const int per = kNormThreads * (dtype == 0 ? Elem<float>::E : Elem<bf16_t>::E);
@@ -583,13 +578,6 @@ hipError_t launch_rownorm(int dtype, const RowNormParams& p, hipStream_t st) {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st) {
   (void)launch_k(k_verify, dim3(p.S), dim3(64), st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(int* p, int64_t n, hipStream_t st) {
-  int blocks = (int)((n + 255) / 256);
-  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-  (void)launch_k(k_fill_zero, dim3(blocks), dim3(256), st, p, n);
   return hipGetLastError();
 }
 

@@ -188,15 +188,17 @@ int dflash_pack_weights_q4(dflash *h, void *buf, size_t bytes, void *stream);
 /*
  * Workspace bytes for calls with at most `max_rows` fused/injected rows, `n_streams`
  * streams in a draft, and context length at most `max_ctx`. The workspace holds split-K
- * partials, block activations, attention partials and self-resetting counters.
+ * partials, block activations and attention partials, each written before it is read
+ * within a call, so no part of it must start at zero.
  * Returns 0 if the arguments are out of range.
  */
 size_t dflash_workspace_bytes(const dflash *h, int32_t max_rows, int32_t n_streams, int32_t max_ctx);
 
-/* Clear a workspace's counters (one small kernel on `stream`). Required once for every
- * workspace buffer before its first use; afterwards the library keeps it consistent.
- * Calls given a workspace that was not initialised on this handle are refused
- * (DFLASH_ERR_STATE). */
+/* Register a workspace buffer (`ws_bytes` > 0, 16-byte aligned) with the handle;
+ * nothing is enqueued on `stream`. Required once for every workspace buffer before its
+ * first use on a handle, and again if it grows: calls given a workspace that was not
+ * registered, or more bytes than were, are refused (DFLASH_ERR_STATE), which catches a
+ * buffer passed in by mistake. */
 int dflash_workspace_init(dflash *h, void *ws, size_t ws_bytes, void *stream);
 
 /*
