@@ -97,10 +97,13 @@ struct GemmPlan {
   int am, mt, mgroups, n_tiles, iters, ksplit, n_work;
   bool tall;   // many rows: the tiled kernel
   // Tiled SWIGLU whose last round of column tiles would be mostly idle: the tiled
-  // kernel takes gate/up rows [0, tail_from), the skinny kernel the rest (0: no split).
-  int tail_from;
+  // kernel takes gate/up rows [0, tail_from) whole, and the rest (the tail, tail_rows
+  // gate and as many up rows) in tail_ks K ranges that fill one more round, whose
+  // float32 partials k_swiglu_tail adds (0: no split).
+  int tail_from, tail_rows, tail_ks;
   // K-range partials: float64 from the skinny kernel, float32 from the tiled one
   size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * (tall ? 4 : 8); }
+  size_t tail_part_bytes(int M) const { return (size_t)tail_ks * M * 2 * tail_rows * 4; }
 };
 
 // Rows are processed in groups of 16 * mt (mt = 1, 2 or 4), or by the tiled kernel
@@ -118,12 +121,17 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
   g.tall = dtype == DFLASH_BF16 && tiled;
   g.ksplit = g.tall ? gemm_tall_ksplit(epi, N, K) : gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
-  g.tail_from = 0;
+  g.tail_from = g.tail_rows = g.tail_ks = 0;
   if (g.tall && epi == EPI_SWIGLU) {
     // One 128-column tile (64 gate + 64 up rows) per CU and round: a remainder of at
-    // most a quarter round goes to the skinny kernel, which spreads it over all CUs.
+    // most a quarter round is split along K into as many ranges as fill one round
+    // (each range at least four 64-wide chunks). A function of the weight's shape only.
     const int tiles = gemm_tall_column_tiles(epi, N), rem = tiles % kTallRoundTiles;
-    if (tiles > kTallRoundTiles && rem > 0 && rem <= kTallRoundTiles / 4) g.tail_from = (tiles - rem) * 64;
+    if (tiles > kTallRoundTiles && rem > 0 && rem <= kTallRoundTiles / 4) {
+      g.tail_from = (tiles - rem) * 64;
+      g.tail_rows = N / 2 - g.tail_from;
+      g.tail_ks = std::max(1, std::min(kTallRoundTiles / rem, K / 64 / 4));
+    }
   }
   return g;
 }
@@ -207,7 +215,7 @@ InjectLayout layout_inject(const dflash& h, int R) {
 struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
-  size_t x, a, rope, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, part_o, part_ml, tile_res, end;
+  size_t x, a, rope, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, gu_tail, part_o, part_ml, tile_res, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
@@ -238,6 +246,7 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   L.vblk = r.take((size_t)S * c.n_kv_heads * kBlockSlots * c.head_dim * es);
   L.o_buf = r.take((size_t)M * h.nq() * es);
   L.m = r.take((size_t)M * c.intermediate * es);
+  L.gu_tail = r.take(L.gu.tail_part_bytes(M));
   L.part_o = r.take(po);
   L.part_ml = r.take(pml);
   L.tile_res = r.take((size_t)Mm * L.lm.n_tiles * 16);
@@ -647,28 +656,21 @@ static_assert(sizeof(GemmParams) <= 4000, "kernel argument block too large");
 
 static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmParams& p, hipStream_t st) {
   if (g.tall && g.tail_from > 0) {
-    // SWIGLU split by gate/up rows: [0, tail_from) tiled, the rest skinny (16 gate +
-    // 16 up rows a tile, every row group; the whole K in each workgroup).
-    const int half = p.N / 2, tail = half - g.tail_from;
+    // SWIGLU split by gate/up rows: [0, tail_from) tiled whole; the tail's packed tiles
+    // (16 gate + 16 up rows each) as a tiled GEMM in tail_ks K ranges into the float32
+    // partials at p.y_out, which k_swiglu_tail adds into m[:, tail_from:].
     GemmParams a = p;
     a.N = 2 * g.tail_from;
     hipError_t e = launch_gemm_tall(epi, g.am, a, st);
     if (e != hipSuccess) return e;
     GemmParams b = p;
-    const size_t esz = dtype == DFLASH_F32 ? 4 : 2;
-    b.N = 2 * tail;
-    b.w0 = static_cast<const char*>(p.w0) + (size_t)g.tail_from * p.K * esz;
-    b.w1 = static_cast<const char*>(p.w1) + (size_t)g.tail_from * p.K * esz;
-    // packed tiles hold 16 gate and 16 up rows each: skip the tiled kernel's rows
-    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / 16) * kPackTileRows * p.K * esz;   // bf16 packing
-    b.m_out = static_cast<char*>(p.m_out) + (size_t)g.tail_from * esz;
-    const int mt = 4;
-    b.mgroups = (p.M + 16 * mt - 1) / (16 * mt);
-    b.n_tiles = (b.N + gemm_tile_cols(epi) - 1) / gemm_tile_cols(epi);
-    b.iters = p.K / gemm_k_per_iter(dtype, epi, g.am, p.K, 0);
-    b.ksplit = 1;
-    b.n_work = b.n_tiles * b.mgroups;
-    return launch_gemm(dtype, epi, g.am, b, mt, st);
+    b.N = 2 * g.tail_rows;
+    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / 16) * kPackTileRows * p.K * 2;   // bf16 packing
+    b.ksplit = g.tail_ks;
+    e = launch_gemm_tall(EPI_RAW, g.am, b, st);
+    if (e != hipSuccess) return e;
+    return launch_swiglu_tail(reinterpret_cast<const float*>(p.y_out), g.tail_ks, p.M, g.tail_rows, p.ld_out,
+                              static_cast<char*>(p.m_out) + (size_t)g.tail_from * 2, st);   // bf16 m
   }
   if (g.tall) return launch_gemm_tall(epi, g.am, p, st);
   return launch_gemm(dtype, epi, g.am, p, g.mt, st);
@@ -1069,6 +1071,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
     p.q4 = h->q4 ? 1 : 0;
     p.m_out = W + L.m;
     p.ld_out = c.intermediate;
+    p.y_out = reinterpret_cast<double*>(W + L.gu_tail);   // the tail's K-range partials (if any)
     {
       ProfScope ps(h, "gate_up_gemm", st);
       e = run_gemm(c.dtype, L.gu, EPI_SWIGLU, p, st);

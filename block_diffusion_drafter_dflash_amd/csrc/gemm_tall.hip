@@ -321,6 +321,34 @@ __global__ __launch_bounds__(Tall<WM_>::THREADS, 1) void k_gemm_tall(const GemmP
     }
 }
 
+// The SwiGLU product of the gate/up rows past a split (the tail): their ks K-range
+// partials ([ks][M][2 tail] float32, in the packed column order of the tail's weights:
+// packed tile j holds gate rows 16 j .. 16 j + 15, then the matching up rows) are added
+// in range order in float64, as every consumer of K-range partials adds them, and
+// silu(g) u is rounded once, as in the tiled kernel's own epilogue. Thread i of row r
+// makes m[r][i].
+__global__ __launch_bounds__(256) void k_swiglu_tail(const float* part, int ks, int M, int tail, int64_t ld_out,
+                                                     bf16_t* m_out) {
+  const int r = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= tail) return;
+  const int64_t N = 2 * (int64_t)tail;
+  const int cg = (i / 16) * 32 + i % 16, cu = cg + 16;
+  double g = 0.0, u = 0.0;
+  for (int k = 0; k < ks; ++k) {
+    const float* pr = part + ((int64_t)k * M + r) * N;
+    g += (double)pr[cg];
+    u += (double)pr[cu];
+  }
+  Elem<bf16_t>::store_d(m_out + (int64_t)r * ld_out + i, g / (1.0 + exp(-g)) * u);
+}
+
+hipError_t launch_swiglu_tail(const float* part, int ks, int M, int tail_rows, int64_t ld_out, void* m_out,
+                              hipStream_t st) {
+  (void)launch_k(k_swiglu_tail, dim3((tail_rows + 255) / 256, M), dim3(256), st, part, ks, M, tail_rows, ld_out,
+                 static_cast<bf16_t*>(m_out));
+  return hipGetLastError();
+}
+
 int gemm_tall_column_tiles(int epi, int N) { return epi == EPI_SWIGLU ? N / BN : (N + BN - 1) / BN; }
 
 // K ranges of the tiled GEMM, a function of the weight's shape only (so that a row's

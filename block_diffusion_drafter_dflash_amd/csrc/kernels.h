@@ -332,6 +332,8 @@ int gemm_tall_ksplit(int epi, int N, int K);
 int gemm_tall_column_tiles(int epi, int N);
 constexpr int kTallRoundTiles = 256;   // column tiles of one round: one per CU
 hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st);
+hipError_t launch_swiglu_tail(const float* part, int ks, int M, int tail_rows, int64_t ld_out, void* m_out,
+                              hipStream_t st);   // m_out: bf16, the tail's first column
 int gemm_tile_cols(int epi);
 hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,
