@@ -419,8 +419,40 @@ WIDE_TAIL = small_variant(MID, name="wide_tail_bf16", n_layers=2, layer_window=[
 
 def test_round_parity_wide_swiglu_tail():
     # 96 rows (a wide batch) and 2 * 17408 gate/up rows: 272 tiled column tiles, of
-    # which the last 16 (a sixteenth of a round) are computed by the skinny kernel.
+    # which the last 16 (a sixteenth of a round) go through the tiled kernel in 16 K
+    # ranges whose float32 partials a finish kernel adds before the SiLU product.
     run_case(RoundCase(WIDE_TAIL), list(range(WIDE_TAIL.n_streams)))
+
+
+def redraft_in_order(case, perm):
+    """Draft the case's streams again in the order perm (same cache, same workspace);
+    returns (logits, drafts), row i holding stream perm[i]."""
+    kv = SimpleNamespace(struct=D.KV())
+    for l in range(case.p.n_layers):
+        kv.struct.k_pool[l] = case.kv.k[l].data_ptr()
+        kv.struct.v_pool[l] = case.kv.v[l].data_ptr()
+    pt = case.kv.page_table[perm].contiguous()
+    kv.struct.page_table = pt.data_ptr()
+    kv.struct.pages_per_stream = case.kv.pages_per_stream
+    out = torch.zeros_like(case.logits)
+    dr = torch.zeros_like(case.draft)
+    case.dr.dflash_draft_block(case.anchor[perm].contiguous(), case.ctx_len[perm].contiguous(), case.max_ctx, kv, dr,
+                               case.ws, logits_out=out)
+    torch.cuda.synchronize()
+    return out, dr
+
+
+def test_swiglu_tail_is_stream_order_invariant_bitwise():
+    # The K-split gate/up tail (and its finish kernel) keeps a row's arithmetic
+    # independent of the other rows: the same streams in reversed order get the same bits.
+    case = RoundCase(WIDE_TAIL)
+    case.run_gpu()
+    batched, bdraft = case.logits.clone(), case.draft.clone()
+    perm = list(reversed(range(WIDE_TAIL.n_streams)))
+    out, dr = redraft_in_order(case, perm)
+    for i, st in enumerate(perm):
+        assert torch.equal(out[i].view(torch.int32), batched[st].view(torch.int32)), f"stream {st}"
+        assert torch.equal(dr[i], bdraft[st])
 
 
 def test_round_parity_9b_ctx4k():
@@ -549,20 +581,8 @@ def test_wide_batch_past_64_streams_parity_and_stream_order_bitwise():
     pick = sorted({0, 69, int(np.argmin(ctx)), int(np.argmax(ctx)), 3, 26, 35, 50})
     run_case(case, pick)
     batched, bdraft = case.logits.clone(), case.draft.clone()
-    S = MANY.n_streams
-    perm = list(reversed(range(S)))
-    kv = SimpleNamespace(struct=D.KV())
-    for l in range(MANY.n_layers):
-        kv.struct.k_pool[l] = case.kv.k[l].data_ptr()
-        kv.struct.v_pool[l] = case.kv.v[l].data_ptr()
-    pt = case.kv.page_table[perm].contiguous()
-    kv.struct.page_table = pt.data_ptr()
-    kv.struct.pages_per_stream = case.kv.pages_per_stream
-    out = torch.zeros_like(case.logits)
-    dr = torch.zeros_like(case.draft)
-    case.dr.dflash_draft_block(case.anchor[perm].contiguous(), case.ctx_len[perm].contiguous(), case.max_ctx, kv, dr,
-                               case.ws, logits_out=out)
-    torch.cuda.synchronize()
+    perm = list(reversed(range(MANY.n_streams)))
+    out, dr = redraft_in_order(case, perm)
     for i, st in enumerate(perm):
         assert torch.equal(out[i].view(torch.int32), batched[st].view(torch.int32)), f"stream {st}"
         assert torch.equal(dr[i], bdraft[st])
