@@ -182,6 +182,25 @@ def test_round_calls_refuse_on_the_host_before_any_enqueue():
     assert lib.dflash_verify_greedy(dr.h, 0, fake, fake, fake, fake, fake, None, None) == -1
 
 
+def test_workspace_registration_enqueues_nothing_and_bounds_later_calls():
+    # dflash_workspace_init only records the buffer (no kernel: it works without a GPU);
+    # a call given more bytes than were registered is refused before any launch, and
+    # registering the buffer again with more bytes is accepted.
+    p = wl.preset("tiny_f32")
+    dr = D.Drafter(cfg_of("tiny_f32"))
+    dr.dflash_bind_weights(fake_tensors(p))
+    lib = D.library()
+    fake = ctypes.c_void_p(1 << 24)
+    assert lib.dflash_workspace_init(dr.h, fake, 1 << 20, None) == 0
+    planes = (ctypes.c_void_p * 3)(1 << 24, 1 << 25, 1 << 26)
+    rc = lib.dflash_fuse_taps(dr.h, planes, 256, 4, fake, fake, 1 << 21, None)
+    assert rc == -5 and "initialised" in dr.last_error()
+    assert lib.dflash_workspace_init(dr.h, fake, 1 << 21, None) == 0
+    assert lib.dflash_workspace_init(dr.h, fake, 0, None) == -4
+    assert lib.dflash_workspace_init(dr.h, None, 1 << 20, None) == -1
+    assert lib.dflash_workspace_init(dr.h, ctypes.c_void_p((1 << 24) + 8), 1 << 20, None) == -1
+
+
 def test_workspace_sizes_grow_with_the_request():
     dr = D.Drafter(cfg_of("9b_long_x4"))
     a = dr.workspace_bytes(16, 1, 4096)
