@@ -74,8 +74,15 @@ __device__ __forceinline__ const unsigned char* packed_tile_q4(const GemmParams&
 }
 
 // Eight 4-bit codes (nibble e = code e) -> eight bf16 values, exactly (0..15).
+// The two masks leave each code in a byte of its own, so that every code is one
+// byte-to-float conversion (v_cvt_f32_ubyte0..3 read any byte directly). The empty
+// asm statements (no instruction) keep lo and hi opaque: otherwise the compiler
+// folds each (lo >> 8k) & 0xff back into a bit-field extract from c, one more
+// instruction a code.
 __device__ __forceinline__ uint4 codes_to_bf16(uint32_t c) {
-  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  asm("" : "+v"(lo));
+  asm("" : "+v"(hi));
   return make_uint4(f32x2_to_bf16x2((float)(lo & 0xffu), (float)(hi & 0xffu)),
                     f32x2_to_bf16x2((float)((lo >> 8) & 0xffu), (float)((hi >> 8) & 0xffu)),
                     f32x2_to_bf16x2((float)((lo >> 16) & 0xffu), (float)((hi >> 16) & 0xffu)),
