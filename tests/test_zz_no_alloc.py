@@ -70,6 +70,22 @@ def test_noalloc_draft_matches_the_workspace_draft_twice_then_smaller():
     both_ways(case, [1], 77)                          # 16 rows, a shorter context
 
 
+def test_noalloc_draft_with_a_k_split_gate_up_tail():
+    # 2 * 17408 gate/up rows: the tiled kernel's last 16 column tiles go through K ranges
+    # whose partials also live in the device array (96 block rows, then 16).
+    p = small_variant(MID, name="noalloc_tail_bf16", intermediate=17408, n_streams=6,
+                      ctx_spec=[300, 77, 1030, 0, 513, 64], seed=2103)
+    case = RoundCase(p)
+    case.fuse()
+    case.inject()
+    torch.cuda.synchronize()
+    assert case.dr.workspace_bytes(0, 6, case.max_ctx) <= 32 << 20
+    print(f"[noalloc] {p.name}: 6 streams, ctx {case.ctx}", flush=True)
+    both_ways(case, list(range(6)), case.max_ctx)
+    print("[noalloc] second call: 1 stream, ctx 300", flush=True)
+    both_ways(case, [0], 300)
+
+
 def test_noalloc_refuses_a_draft_past_its_array():
     case = RoundCase(small_variant(MID, n_streams=1, ctx_spec=[64]))
     S = 1
