@@ -98,7 +98,7 @@ struct GemmPlan {
   bool tall;   // many rows: the tiled kernel
   // Tiled SWIGLU whose last round of column tiles would be mostly idle: the tiled
   // kernel takes gate/up rows [0, tail_from) whole, and the rest (the tail, tail_rows
-  // gate and as many up rows) in tail_ks K ranges that fill one more round, whose
+  // gate and as many up rows) in tail_ks K ranges (half a round of workgroups), whose
   // float32 partials k_swiglu_tail adds (0: no split).
   int tail_from, tail_rows, tail_ks;
   // K-range partials: float64 from the skinny kernel, float32 from the tiled one
@@ -124,13 +124,14 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
   g.tail_from = g.tail_rows = g.tail_ks = 0;
   if (g.tall && epi == EPI_SWIGLU) {
     // One 128-column tile (64 gate + 64 up rows) per CU and round: a remainder of at
-    // most a quarter round is split along K into as many ranges as fill one round
-    // (each range at least four 64-wide chunks). A function of the weight's shape only.
+    // most a quarter round is split along K into as many ranges as fill half a round
+    // (each range at least four 64-wide chunks; C4: 16 tiles x 8 ranges, against 16 or
+    // 4 ranges: 119.8 against 120.2 and 124.4 us). A function of the weight's shape only.
     const int tiles = gemm_tall_column_tiles(epi, N), rem = tiles % kTallRoundTiles;
     if (tiles > kTallRoundTiles && rem > 0 && rem <= kTallRoundTiles / 4) {
       g.tail_from = (tiles - rem) * 64;
       g.tail_rows = N / 2 - g.tail_from;
-      g.tail_ks = std::max(1, std::min(kTallRoundTiles / rem, K / 64 / 4));
+      g.tail_ks = std::max(1, std::min(kTallRoundTiles / rem / 2, K / 64 / 4));
     }
   }
   return g;

@@ -419,7 +419,7 @@ WIDE_TAIL = small_variant(MID, name="wide_tail_bf16", n_layers=2, layer_window=[
 
 def test_round_parity_wide_swiglu_tail():
     # 96 rows (a wide batch) and 2 * 17408 gate/up rows: 272 tiled column tiles, of
-    # which the last 16 (a sixteenth of a round) go through the tiled kernel in 16 K
+    # which the last 16 (a sixteenth of a round) go through the tiled kernel in 8 K
     # ranges whose float32 partials a finish kernel adds before the SiLU product.
     run_case(RoundCase(WIDE_TAIL), list(range(WIDE_TAIL.n_streams)))
 
