@@ -1,5 +1,5 @@
 // Small kernels of the draft round (gfx950): block input gather, row RMSNorms, the
-// block heads' norm + RoPE, injected K/V placement, greedy verify, workspace clearing.
+// block heads' norm + RoPE, injected K/V placement, greedy verify.
 #include <type_traits>
 
 #include "common.hpp"
