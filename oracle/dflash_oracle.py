@@ -46,7 +46,7 @@ Logits stay float64. This follows the TensorFold page's "Exactness" list
 (bf16 activations with fp32 sums) and the Strata page's "Validation" list
 (a native drafter checked against an f64 host reference).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   taps concatenated in ascending tap-id order; fc then hidden_norm; RMSNorm is
   x / sqrt(mean(x^2) + eps) * g; no biases; the eleven layer tensors are
   in_norm, wq, wk, wv, wo, q_norm, k_norm, post_norm, w_gate, w_up, w_down;
