@@ -559,18 +559,34 @@ def quantized_weights(cfg, W):
 # A whole round for several streams (reference driver for the tests)
 
 
+def context_from_taps(cfg, ctx_taps, W):
+    """A stream's existing context built the way a round builds its new rows (steps 1
+    and 2 above): the tap planes of its n context rows fused, then injected at
+    positions 0..n-1. Returns per-layer lists k_ctx, v_ctx of [n, n_kv, head_dim]."""
+    n = ctx_taps[0].shape[0]
+    if n == 0:
+        e = np.zeros((0, cfg.n_kv_heads, cfg.head_dim))
+        return [e] * cfg.n_layers, [e] * cfg.n_layers
+    kv = inject_kv(cfg, fuse_taps(cfg, ctx_taps, W), np.arange(n), W)
+    return [k for k, _ in kv], [v for _, v in kv]
+
+
 def run_round(cfg, W, streams, target_rows=None):
     """One round over several independent streams.
 
     streams: list of dicts with keys taps (list of [R, h] planes), C (context
-    length the block sees after this round's injection), k_ctx/v_ctx (per
-    layer, rows for positions 0..C-R-1 already in the cache), anchor.
+    length the block sees after this round's injection), anchor, and the rows
+    for positions 0..C-R-1 already in the cache: either k_ctx/v_ctx (per layer)
+    or ctx_taps (their tap planes, built here by context_from_taps).
     The R new rows are fused and injected at positions C-R..C-1.
     Returns per-stream dicts with fused, kv (new rows), logits, tokens, and
     (when target_rows is given) accept, bonus, committed.
     """
     out = []
     for s, st in enumerate(streams):
+        if "k_ctx" not in st:
+            k_ctx, v_ctx = context_from_taps(cfg, st["ctx_taps"], W)
+            st = dict(st, k_ctx=k_ctx, v_ctx=v_ctx)
         fused = fuse_taps(cfg, st["taps"], W)
         R = fused.shape[0]
         C = st["C"]

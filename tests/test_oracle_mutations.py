@@ -115,6 +115,11 @@ MUTATIONS = [
      "order = np.lexsort((-np.arange(logits.shape[-1]), -np.asarray(logits, dtype=np.float64)))"),
     ("selector stops at or below min-p", "        if probs[j] < min_p:", "        if probs[j] <= min_p + 0.06:"),
     ("selector ignores the node scores", "        best = tot[arg, np.arange(k)] + node[j]", "        best = tot[arg, np.arange(k)]"),
+    ("context from taps placed one position later", "fuse_taps(cfg, ctx_taps, W), np.arange(n), W)",
+     "fuse_taps(cfg, ctx_taps, W), np.arange(1, n + 1), W)"),
+    ("context from taps injected without fusing (first plane as the row)",
+     "kv = inject_kv(cfg, fuse_taps(cfg, ctx_taps, W), np.arange(n), W)",
+     "kv = inject_kv(cfg, as_f64(ctx_taps[0]), np.arange(n), W)"),
     ("storage sizes: planner counts one copy", "return (2 * n_taps + 2) * hidden * elem_bytes",
      "return (n_taps + 2) * hidden * elem_bytes"),
 ]

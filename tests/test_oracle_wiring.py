@@ -215,3 +215,48 @@ def test_zero_output_projection_leaves_the_mlp_on_the_layer_input():
         X = X + F.linear(F.silu(F.linear(b, t(W[p + "w_gate"]))) * F.linear(b, t(W[p + "w_up"])), t(W[p + "w_down"]))
     ref = F.linear(rms(X[1:], W["norm"], cfg.rms_eps), t(W["lm_head"])).numpy()
     np.testing.assert_allclose(logits, ref, rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------- context built from taps
+
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+def test_context_from_taps_agrees_with_the_second_implementation(dtype):
+    # The existing context built the way a round builds its rows (fuse, then inject at
+    # positions 0..n-1), against the textbook fuse and K/V of the second implementation.
+    cfg = cfg_small(dtype=dtype)
+    W = rounded_weights(cfg)
+    rng = np.random.default_rng(71)
+    n = 11
+    taps = [O.round_to(rng.normal(0, 1, (n, cfg.hidden)), dtype) for _ in range(cfg.n_taps)]
+    k_ctx, v_ctx = O.context_from_taps(cfg, taps, W)
+    tb = TB.Textbook(cfg, W)
+    f = tb.fuse(taps)
+    for l in range(cfg.n_layers):
+        k, v = tb.context_kv(f, torch.arange(n), l)
+        if dtype == "f64":
+            np.testing.assert_allclose(k_ctx[l], k.numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(v_ctx[l], v.numpy(), rtol=1e-12, atol=1e-12)
+        else:
+            np.testing.assert_array_equal(k_ctx[l], k.numpy())
+            np.testing.assert_array_equal(v_ctx[l], v.numpy())
+    e_k, e_v = O.context_from_taps(cfg, [t[:0] for t in taps], W)
+    assert all(x.shape == (0, cfg.n_kv_heads, cfg.head_dim) for x in e_k + e_v)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_round_over_a_context_from_taps_does_not_depend_on_where_the_round_starts(dtype):
+    # The same n + R tap rows, split as n context rows and R round rows or as n + R - 2
+    # and 2: each row lands at its own position either way, so the round's cache and
+    # its logits are the same bits (a context row placed one position off would move them).
+    cfg = cfg_small(dtype=dtype)
+    W = rounded_weights(cfg)
+    rng = np.random.default_rng(72)
+    n, R = 9, 4
+    taps = [O.round_to(rng.normal(0, 1, (n + R, cfg.hidden)), dtype) for _ in range(cfg.n_taps)]
+    a = O.run_round(cfg, W, [dict(taps=[t[n:] for t in taps], C=n + R, ctx_taps=[t[:n] for t in taps], anchor=5)])
+    b = O.run_round(cfg, W, [dict(taps=[t[n + R - 2:] for t in taps], C=n + R, ctx_taps=[t[:n + R - 2] for t in taps],
+                                  anchor=5)])
+    np.testing.assert_array_equal(a[0]["logits"], b[0]["logits"])
+    np.testing.assert_array_equal(a[0]["tokens"], b[0]["tokens"])
+    for l in range(cfg.n_layers):
+        np.testing.assert_array_equal(a[0]["kv"][l][0][R - 2:], b[0]["kv"][l][0])
