@@ -6,7 +6,7 @@ inputs from it without sharing any computation.
 """
 from .presets import PRESETS, Preset, preset  # noqa: F401
 from .synth import (  # noqa: F401
-    make_weights, make_taps, make_context_kv, make_page_table, make_anchor,
+    make_weights, make_taps, make_context_taps, make_context_kv, make_page_table, make_anchor,
     make_target_rows, draw_accept_lengths, round_rows, tensor_names, ctx_lens,
     tensor_shape, LAYER_TENSORS,
 )

@@ -33,6 +33,10 @@ class Preset:
     page_size: int = 16
     mask_token_id: Optional[int] = None
     note: str = ""
+    # True: the streams' existing context is built as a round builds its new rows,
+    # seeded tap planes fused and injected (each side with its own fuse + inject);
+    # False: seeded N(0, 1) K/V rows written straight into the cache.
+    context_from_taps: bool = False
 
     def __post_init__(self):
         if self.mask_token_id is None:
@@ -53,14 +57,14 @@ PRESETS = {
         n_kv_heads=2, head_dim=64, intermediate=768, vocab=2048, n_taps=3,
         tap_layer_ids=[2, 5, 7], target_n_layers=8, block_size=8,
         layer_window=[32, 0], n_streams=1, ctx_spec=128,
-        accept_spec=("uniform",), seed=1001,
+        accept_spec=("uniform",), seed=1001, context_from_taps=True,
         note="tiny fp32 round: hidden 256, 2 layers (sliding 32, full), block 8, ctx 128, vocab 2048"),
     "9b_ctx4k": Preset(
         name="9b_ctx4k", dtype="bf16", hidden=4096, n_layers=6, n_q_heads=32,
         n_kv_heads=8, head_dim=128, intermediate=12288, vocab=151936, n_taps=8,
         tap_layer_ids=[1, 5, 9, 13, 17, 21, 25, 29], target_n_layers=32,
         block_size=16, layer_window=[0] * 6, n_streams=1, ctx_spec=4096,
-        accept_spec=("full",), seed=1002,
+        accept_spec=("full",), seed=1002, context_from_taps=True,
         note="9B-shaped v1 drafter, 8 taps, block 16, ctx 4096, all layers full"),
     "9b_ctx32k": Preset(
         name="9b_ctx32k", dtype="bf16", hidden=4096, n_layers=6, n_q_heads=32,

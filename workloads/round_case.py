@@ -3,9 +3,11 @@
 parity tests, smoke() and the benchmark; not imported by the oracle, nor by
 workloads/__init__.
 
-The existing context of each stream is written straight into the paged caches as
-seeded N(0, 1) rows (positions 0 .. C-R-1); the round then fuses and injects its own
-R rows at positions C-R .. C-1, drafts at C .. C+B-1, and verifies against a
+The existing context of each stream (positions 0 .. C-R-1) is built, for presets with
+context_from_taps, from seeded tap planes through the library's own fuse + inject
+(the oracle fuses and injects the same planes itself), and otherwise written straight
+into the paged caches as seeded N(0, 1) rows. The round then fuses and injects its
+own R rows at positions C-R .. C-1, drafts at C .. C+B-1, and verifies against a
 synthetic target row.
 """
 import numpy as np
@@ -52,14 +54,19 @@ class RoundCase:
         self.pool_pages = pool
         self.cfg = D.config_from_preset(p, max_streams=S, pool_pages=pool)
         self.kv = D.PagedKV(self.cfg, self.page_table, pool, self.dtype, device=device)
-        # pre-existing context rows
-        for l in range(p.n_layers):
-            for s in range(S):
-                n = self.ctx[s] - self.rows[s]
-                if n > 0:
-                    k = wl.make_context_kv(p, l, s, n, "k", device=device, seed=seed)
-                    v = wl.make_context_kv(p, l, s, n, "v", device=device, seed=seed)
-                    self.kv.write_rows(l, s, 0, k, v)
+        # Pre-existing context rows: built from seeded tap planes through the library's
+        # own fuse + inject (presets with context_from_taps; the 4-bit drafter runs
+        # calls of at most 32 rows, so its cases take the written rows), or seeded
+        # K/V rows written straight into the cache.
+        self.ctx_from_taps = bool(p.context_from_taps) and not q4
+        if not self.ctx_from_taps:
+            for l in range(p.n_layers):
+                for s in range(S):
+                    n = self.ctx[s] - self.rows[s]
+                    if n > 0:
+                        k = wl.make_context_kv(p, l, s, n, "k", device=device, seed=seed)
+                        v = wl.make_context_kv(p, l, s, n, "v", device=device, seed=seed)
+                        self.kv.write_rows(l, s, 0, k, v)
         self.dr = D.Drafter(self.cfg)
         self.dr.dflash_bind_weights(self.W)
         self.q4 = q4
@@ -67,6 +74,8 @@ class RoundCase:
             self.dr.new_q4_weights(device=device)        # the drafter's 4-bit copies
         else:
             self.dr.new_packed_weights(device=device)
+        if self.ctx_from_taps:
+            self._prefill_context()
         self.ws = self.dr.new_workspace(max(R, 1), S, self.max_ctx, device=device)
         self.fused = torch.zeros((max(R, 1), p.hidden), dtype=self.dtype, device=device)
         self.draft = torch.zeros((S, B - 1), dtype=torch.int32, device=device)
@@ -78,6 +87,29 @@ class RoundCase:
         self.target = None
 
     # ---------------------------------------------------------------- GPU path
+    def _prefill_context(self):
+        """Stream s's context rows 0..C_s-R_s-1: its seeded context tap planes fused
+        (dflash_fuse_taps) and injected at those positions (dflash_inject_kv), one call
+        each per stream."""
+        p, dev = self.p, self.device
+        ns = [c - r for c, r in zip(self.ctx, self.rows)]
+        nmax = max(ns + [0])
+        if nmax == 0:
+            return
+        ws = self.dr.new_workspace(nmax, p.n_streams, self.max_ctx, device=dev)
+        fused = torch.empty((nmax, p.hidden), dtype=self.dtype, device=dev)
+        for s, n in enumerate(ns):
+            if n <= 0:
+                continue
+            taps = wl.make_context_taps(p, s, n, device=dev, seed=self.seed)
+            self.dr.dflash_fuse_taps(taps, fused, ws, n_rows=n)
+            rs = torch.full((n,), s, dtype=torch.int32, device=dev)
+            rp = torch.arange(n, dtype=torch.int32, device=dev)
+            self.dr.dflash_inject_kv(fused, rs, rp, self.kv, ws, n_rows=n)
+            del taps
+        torch.cuda.synchronize()
+        del ws, fused
+
     def fuse(self):
         self.dr.dflash_fuse_taps(self.taps, self.fused, self.ws, n_rows=self.R)
 
@@ -112,7 +144,9 @@ class RoundCase:
         return self._wnp
 
     def oracle_streams(self, streams):
-        """Oracle stream dicts (taps, C, k_ctx, v_ctx, anchor) for the chosen streams."""
+        """Oracle stream dicts for the chosen streams: taps, C, anchor, and the existing
+        context as given K/V rows (k_ctx, v_ctx) or, when it was built from taps, as
+        those tap planes (ctx_taps) for the oracle to fuse and inject itself."""
         p = self.p
         out = []
         off = np.cumsum([0] + self.rows)
@@ -120,6 +154,11 @@ class RoundCase:
         anchor = self.anchor.cpu().numpy()
         for s in streams:
             n = self.ctx[s] - self.rows[s]
+            if self.ctx_from_taps:
+                ctx_taps = [to_np(t) for t in wl.make_context_taps(p, s, max(n, 0), device=self.device, seed=self.seed)]
+                out.append(dict(taps=[t[off[s]:off[s + 1]] for t in taps], C=self.ctx[s], ctx_taps=ctx_taps,
+                                anchor=int(anchor[s])))
+                continue
             kc, vc = [], []
             for l in range(p.n_layers):
                 if n > 0:

@@ -3,9 +3,10 @@
 Every tensor is drawn from its own torch.Generator, seeded from the preset's
 seed and the tensor's index, so any tensor can be regenerated on its own.
 Distributions: weight matrices 0.02 * N(0, 1); RMSNorm gains 1 + 0.02 * N(0, 1);
-tap planes and pre-written context K/V N(0, 1); all cast to the preset's dtype
-(bf16 by round-to-nearest-even, or fp32). Nothing here computes any part of
-the round: drafted tokens enter make_target_rows only as given values.
+tap planes (the round's and the context's) and pre-written context K/V N(0, 1);
+all cast to the preset's dtype (bf16 by round-to-nearest-even, or fp32). Nothing
+here computes any part of the round: drafted tokens enter make_target_rows only
+as given values.
 """
 import numpy as np
 import torch
@@ -79,6 +80,14 @@ def make_taps(p, n_rows, device="cpu", seed=None):
     """n_taps tap planes, each [n_rows, hidden], N(0, 1), in ascending tap order."""
     seed = (p.seed if seed is None else seed) * 31 + 5
     return [_randn((n_rows, p.hidden), device, seed * 1009 + t, _torch_dtype(p))
+            for t in range(p.n_taps)]
+
+
+def make_context_taps(p, stream, n_rows, device="cpu", seed=None):
+    """Tap planes of stream `stream`'s existing context rows (positions 0..n_rows-1),
+    n_taps planes [n_rows, hidden], N(0, 1), drawn apart from the round's own taps."""
+    seed = (p.seed if seed is None else seed) * 37 + 11
+    return [_randn((n_rows, p.hidden), device, (seed * 1009 + stream) * 131 + t, _torch_dtype(p))
             for t in range(p.n_taps)]
 
 
