@@ -749,6 +749,29 @@ def test_zero_rows_are_a_no_op():
     assert torch.equal(before, case.fused)
 
 
+def test_out_of_range_ctx_len_and_anchor_are_clamped_as_documented():
+    # The draft's device inputs past their ranges (dflash.h, dflash_draft_block): a
+    # context length above max_ctx_len is taken as max_ctx_len and a negative one as 0;
+    # an anchor id is clamped to [0, vocab). Each draws bitwise what the clamped value does.
+    p = small_variant(MID, name="clamp_bf16", n_streams=3, ctx_spec=[300, 1030, 77], seed=2011)
+    case = RoundCase(p)
+    case.run_gpu()
+    V, top = p.vocab, case.max_ctx
+    log(f"[case] clamp: ctx {case.ctx}, max_ctx_len {top}, vocab {V}")
+
+    def draft(anchor, ctx):
+        out, dr = torch.zeros_like(case.logits), torch.zeros_like(case.draft)
+        case.dr.dflash_draft_block(torch.tensor(anchor, dtype=torch.int32, device="cuda"),
+                                   torch.tensor(ctx, dtype=torch.int32, device="cuda"), top, case.kv, dr, case.ws,
+                                   logits_out=out)
+        torch.cuda.synchronize()
+        return out.view(torch.int32).clone(), dr.clone()
+
+    a_out, c_out = draft([V + 7, -4, 5], [top + 50, -5, 77])
+    a_in, c_in = draft([V - 1, 0, 5], [top, 0, 77])
+    assert torch.equal(a_out, a_in) and torch.equal(c_out, c_in)
+
+
 def test_unpacked_weights_are_refused_and_rebinding_drops_the_packing():
     case = RoundCase(NARROW2)          # 32 block rows: the skinny GEMMs, which read the packing
     case.run_gpu()
