@@ -266,22 +266,27 @@ struct SpecVerifyParams {
 // reach and of the batch's class (attn_class), so a stream's result does not depend
 // on the other streams of a batch of its class. Narrow and mid batches: chunks of
 // `sp` pages (8 narrow, 16 mid: a mid batch's streams already give the grid more work
-// items), at most kChunksShort of them up to kChunksShort * 64 pages; beyond, chunks
-// of at most 64 pages. Wide batches (many streams fill the GPU by themselves): chunks
+// items) while that makes at most kChunksShort of them; a longer reach is cut into
+// chunks of 32 pages, at least kChunksShort and at most 2 * kChunksShort of them
+// (up to 4096 pages: a single long stream still fills the GPU); beyond, chunks of
+// at most 64 pages. Wide batches (many streams fill the GPU by themselves): chunks
 // of up to 64 pages, which keeps the per-chunk partials few. No chunk ever exceeds 64
 // pages (the attention kernel keeps a chunk's page ids one per lane), and the count
 // never decreases as the reach grows, so a grid sized for the longest reach covers
 // every stream.
 constexpr int kChunkPagesNarrow = 8;
 constexpr int kChunkPagesMid = 16;
+constexpr int kChunkPagesLong = 32;
 constexpr int kChunkPagesMax = 64;
 constexpr int kChunksShort = 32;
 __host__ __device__ inline int attention_chunks(int pages, int cls) {
-  if (cls == 2 || pages > kChunksShort * kChunkPagesMax)
+  if (cls == 2 || pages > 2 * kChunksShort * kChunkPagesMax)
     return pages <= kChunkPagesMax ? 1 : (pages + kChunkPagesMax - 1) / kChunkPagesMax;
   const int sp = cls == 1 ? kChunkPagesMid : kChunkPagesNarrow;
   const int n = (pages + sp - 1) / sp;
-  return n < 1 ? 1 : (n > kChunksShort ? kChunksShort : n);
+  if (n <= kChunksShort) return n < 1 ? 1 : n;
+  const int m = (pages + kChunkPagesLong - 1) / kChunkPagesLong;
+  return m < kChunksShort ? kChunksShort : (m > 2 * kChunksShort ? 2 * kChunksShort : m);
 }
 __host__ __device__ inline int attention_chunk_pages(int pages, int cls) {
   const int n = attention_chunks(pages, cls);
