@@ -96,21 +96,23 @@ namespace {
 struct GemmPlan {
   int am, mt, mgroups, n_tiles, iters, ksplit, n_work;
   bool tall;   // many rows: the tiled kernel
-  // Tiled SWIGLU whose last round of column tiles would be mostly idle: the tiled
-  // kernel takes gate/up rows [0, tail_from) whole, and the rest (the tail, tail_rows
-  // gate and as many up rows) in tail_ks K ranges (half a round of workgroups), whose
-  // float32 partials k_swiglu_tail adds (0: no split).
-  int tail_from, tail_rows, tail_ks;
+  // Tiled GEMMs whose last round of column tiles would be mostly idle: the tiled kernel
+  // takes the outputs before the split whole and the rest (the tail) in tail_ks K
+  // ranges, whose float32 partials a finish kernel adds (tail_ks 0: no split).
+  // SWIGLU: gate/up rows [0, tail_from) whole, the tail tail_rows gate and as many up
+  // rows (k_swiglu_tail). LM head: columns [0, tail_from) whole, the tail tail_rows
+  // columns (k_lmhead_tail: logits and each 32-column group's top two).
+  int tail_from, tail_rows, tail_ks, tail_cols;   // tail_cols: columns of the tail's partials
   // K-range partials: float64 from the skinny kernel, float32 from the tiled one
   size_t part_bytes(int M, int N) const { return (size_t)ksplit * M * N * (tall ? 4 : 8); }
-  size_t tail_part_bytes(int M) const { return (size_t)tail_ks * M * 2 * tail_rows * 4; }
+  size_t tail_part_bytes(int M) const { return (size_t)tail_ks * M * tail_cols * 4; }
 };
 
 // Rows are processed in groups of 16 * mt (mt = 1, 2 or 4), or by the tiled kernel
 // when `tiled` (bf16 batches of kTallMinRows rows or more). The tiling of N, the K
 // ranges and the wave split of each range depend only on the weight's shape, so a
 // row's arithmetic depends on M only through the batch's class.
-GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, bool tiled) {
+GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, bool tiled, bool lm_tail = false) {
   GemmPlan g;
   g.am = am;
   g.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -121,7 +123,7 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
   g.tall = dtype == DFLASH_BF16 && tiled;
   g.ksplit = g.tall ? gemm_tall_ksplit(epi, N, K) : gemm_ksplit(epi, g.n_tiles, g.iters, K);
   g.n_work = g.n_tiles * g.mgroups * g.ksplit;
-  g.tail_from = g.tail_rows = g.tail_ks = 0;
+  g.tail_from = g.tail_rows = g.tail_ks = g.tail_cols = 0;
   if (g.tall && epi == EPI_SWIGLU) {
     // One 128-column tile (64 gate + 64 up rows) per CU and round: a remainder of at
     // most a quarter round is split along K into as many ranges as fill half a round
@@ -132,6 +134,20 @@ GemmPlan plan_gemm(int dtype, int epi, int am, int M, int N, int K, int tap_h, b
       g.tail_from = (tiles - rem) * 64;
       g.tail_rows = N / 2 - g.tail_from;
       g.tail_ks = std::max(1, std::min(kTallRoundTiles / rem / 2, K / 64 / 4));
+      g.tail_cols = 2 * g.tail_rows;
+    }
+  }
+  if (g.tall && epi == EPI_LMHEAD && lm_tail) {
+    // The vocabulary's last round of 128-column tiles (at the 9B vocabulary 163 of 1187)
+    // costs close to a full round; in three K ranges its workgroups fill the GPU. Taken
+    // for mid batches (33-64 block rows), whose float32 tail partials are small (C5: LM
+    // head 302 -> 280 us); for wide ones (C4, 240 rows) they cost what the split saves.
+    // A function of the weight's shape and the batch's class only.
+    const int tiles = gemm_tall_column_tiles(epi, N), rem = tiles % kTallRoundTiles;
+    if (tiles > kTallRoundTiles && rem > 0) {
+      g.tail_from = (tiles - rem) * 128;
+      g.tail_rows = g.tail_cols = N - g.tail_from;
+      g.tail_ks = std::max(1, std::min(3, K / 64 / 4));
     }
   }
   return g;
@@ -216,7 +232,7 @@ InjectLayout layout_inject(const dflash& h, int R) {
 struct DraftLayout {
   GemmPlan qkv, o, gu, down, lm;
   std::vector<AttnPlan> attn;
-  size_t x, a, rope, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, gu_tail, part_o, part_ml, tile_res, end;
+  size_t x, a, rope, qkv_raw, o_parts, d_parts, q, kblk, vblk, o_buf, m, gu_tail, part_o, part_ml, tile_res, lm_tail, end;
 };
 DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   DraftLayout L;
@@ -228,7 +244,7 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   L.o = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, h.nq(), 0, tiled);
   L.gu = plan_gemm(c.dtype, EPI_SWIGLU, A_PLAIN, M, 2 * c.intermediate, c.hidden, 0, tiled);
   L.down = plan_gemm(c.dtype, EPI_RAW, A_PLAIN, M, c.hidden, c.intermediate, 0, tiled);
-  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, Mm, c.vocab, c.hidden, 0, tiled);
+  L.lm = plan_gemm(c.dtype, EPI_LMHEAD, A_PLAIN, Mm, c.vocab, c.hidden, 0, tiled, attn_class(M) == 1);
   size_t po = 0, pml = 0;
   for (int l = 0; l < c.n_layers; ++l) {
     L.attn.push_back(plan_attn(c, S, max_ctx, c.layer_window[l]));
@@ -251,6 +267,7 @@ DraftLayout layout_draft(const dflash& h, int S, int max_ctx) {
   L.part_o = r.take(po);
   L.part_ml = r.take(pml);
   L.tile_res = r.take((size_t)Mm * L.lm.n_tiles * 16);
+  L.lm_tail = r.take(L.lm.tail_part_bytes(Mm));
   L.end = r.off;
   return L;
 }
@@ -656,7 +673,25 @@ static GemmParams gemm_base(const GemmPlan& g, int M, int N, int K) {
 static_assert(sizeof(GemmParams) <= 4000, "kernel argument block too large");
 
 static hipError_t run_gemm(int dtype, const GemmPlan& g, int epi, const GemmParams& p, hipStream_t st) {
-  if (g.tall && g.tail_from > 0) {
+  if (g.tall && g.tail_ks > 0 && epi == EPI_LMHEAD) {
+    // LM head split by columns: [0, tail_from) tiled whole (logits at row stride N);
+    // the tail's packed tiles (32 columns each) as a tiled GEMM in tail_ks K ranges into
+    // the float32 partials at p.y_out, which k_lmhead_tail finishes.
+    GemmParams a = p;
+    a.N = g.tail_from;
+    a.ld_out = p.N;
+    hipError_t e = launch_gemm_tall(EPI_LMHEAD, g.am, a, st);
+    if (e != hipSuccess) return e;
+    GemmParams b = p;
+    b.N = g.tail_rows;
+    b.wp = static_cast<const char*>(p.wp) + (size_t)(g.tail_from / kPackTileRows) * kPackTileRows * p.K * 2;   // bf16 packing
+    b.ksplit = g.tail_ks;
+    e = launch_gemm_tall(EPI_RAW, g.am, b, st);
+    if (e != hipSuccess) return e;
+    return launch_lmhead_tail(reinterpret_cast<const float*>(p.y_out), g.tail_ks, p.M, g.tail_rows, p.N, g.tail_from,
+                              p.n_tiles, p.logits_out, p.tile_res, st);
+  }
+  if (g.tall && g.tail_ks > 0) {
     // SWIGLU split by gate/up rows: [0, tail_from) tiled whole; the tail's packed tiles
     // (16 gate + 16 up rows each) as a tiled GEMM in tail_ks K ranges into the float32
     // partials at p.y_out, which k_swiglu_tail adds into m[:, tail_from:].
@@ -1110,6 +1145,7 @@ static int draft_impl(dflash* h, int32_t n_streams, const int32_t* anchor, const
   p.q4 = h->q4 ? 1 : 0;
   p.logits_out = static_cast<float*>(logits_out);
   p.tile_res = reinterpret_cast<float*>(W + L.tile_res);
+  p.y_out = reinterpret_cast<double*>(W + L.lm_tail);   // the tail's K-range partials (if any)
   {
     ProfScope ps(h, "lm_head_gemm", st);
     e = run_gemm(c.dtype, L.lm, EPI_LMHEAD, p, st);

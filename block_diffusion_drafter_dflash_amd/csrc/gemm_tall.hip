@@ -303,7 +303,7 @@ __global__ __launch_bounds__(Tall<WM_>::THREADS, 1) void k_gemm_tall(const GemmP
             const int n = ct * BN + 64 * wn + 32 * jg + 16 * jj + lr;
             const float v = acc[i][2 * jg + jj][e];
             if (n < p.N) {
-              if (rv && p.logits_out) p.logits_out[(int64_t)r * p.N + n] = v;
+              if (rv && p.logits_out) p.logits_out[(int64_t)r * (p.ld_out > 0 ? p.ld_out : p.N) + n] = v;
               tall_top_merge(v1, i1, v2, v, n, -INFINITY);
             }
           }
@@ -340,6 +340,44 @@ __global__ __launch_bounds__(256) void k_swiglu_tail(const float* part, int ks, 
     u += (double)pr[cu];
   }
   Elem<bf16_t>::store_d(m_out + (int64_t)r * ld_out + i, g / (1.0 + exp(-g)) * u);
+}
+
+// The LM head's columns past a split (the tail): their ks K-range partials ([ks][M][tail]
+// float32, in vocabulary order) are added in range order in float64 and rounded once
+// to the fp32 logit; each 32-column group's largest and second largest logit and the
+// largest one's id (lowest on a tie) go to the tile results, as the tiled kernel's own
+// epilogue writes them. Block (x, r) takes row r's groups 8 x .. 8 x + 7, a half wave
+// (32 lanes) each: lane i of group g, column col0 + 32 g + i.
+__global__ __launch_bounds__(256) void k_lmhead_tail(const float* part, int ks, int M, int tail, int64_t N, int col0,
+                                                     int n_tiles, float* logits, float4* tile_res) {
+  const int r = blockIdx.y, g = blockIdx.x * 8 + (threadIdx.x >> 5), i = threadIdx.x & 31;
+  const int c = 32 * g + i;
+  float v1 = -INFINITY, v2 = -INFINITY;
+  int i1 = 0x7fffffff;
+  if (c < tail) {
+    double s = 0.0;
+    for (int k = 0; k < ks; ++k) s += (double)part[((int64_t)k * M + r) * tail + c];
+    v1 = (float)s;
+    i1 = col0 + c;
+    if (logits) logits[(int64_t)r * N + i1] = v1;
+  }
+  for (int m = 1; m < 32; m <<= 1) {   // within the half wave
+    const float o1 = __shfl_xor(v1, m, kWave);
+    const int oi = __shfl_xor(i1, m, kWave);
+    const float o2 = __shfl_xor(v2, m, kWave);
+    tall_top_merge(v1, i1, v2, o1, oi, o2);
+  }
+  const int grp = col0 / 32 + g;
+  if (i == 0 && 32 * g < tail && grp < n_tiles)
+    tile_res[(int64_t)r * n_tiles + grp] = make_float4(v1, __int_as_float(i1), v2, 0.f);
+}
+
+hipError_t launch_lmhead_tail(const float* part, int ks, int M, int tail, int64_t N, int col0, int n_tiles,
+                              float* logits, float* tile_res, hipStream_t st) {
+  const int groups = (tail + 31) / 32;
+  (void)launch_k(k_lmhead_tail, dim3((groups + 7) / 8, M), dim3(256), st, part, ks, M, tail, N, col0, n_tiles, logits,
+                 reinterpret_cast<float4*>(tile_res));
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_tail(const float* part, int ks, int M, int tail_rows, int64_t ld_out, void* m_out,

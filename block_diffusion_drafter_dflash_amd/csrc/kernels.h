@@ -57,7 +57,7 @@ struct GemmParams {
   double* y_out;        // EPI_RAW: partials [ksplit, M, N], float64 (skinny kernel) or
                         // float32 (tiled kernel, whose sums are fp32) in the same buffer
   void* m_out;          // EPI_SWIGLU: [M, ld_out]
-  int ld_out;
+  int ld_out;           // also the tiled LM head's logits row stride when > 0 (else N)
   float* logits_out;    // EPI_LMHEAD (nullable), fp32
   float* tile_res;      // EPI_LMHEAD: [M, n_tiles] x (max, argmax bits, second max, -)
 };
@@ -339,6 +339,8 @@ constexpr int kTallRoundTiles = 256;   // column tiles of one round: one per CU
 hipError_t launch_gemm_tall(int epi, int am, const GemmParams& p, hipStream_t st);
 hipError_t launch_swiglu_tail(const float* part, int ks, int M, int tail_rows, int64_t ld_out, void* m_out,
                               hipStream_t st);   // m_out: bf16, the tail's first column
+hipError_t launch_lmhead_tail(const float* part, int ks, int M, int tail, int64_t N, int col0, int n_tiles,
+                              float* logits, float* tile_res, hipStream_t st);   // logits: nullable, row stride N
 int gemm_tile_cols(int epi);
 hipError_t launch_gemm(int dtype, int epi, int am, const GemmParams& p, int mt, hipStream_t st);
 hipError_t launch_argmax_final(const float* tile_res, int n_tiles, int rows, int* draft_out, float* top2_out,

@@ -537,9 +537,16 @@ def test_batched_equals_solo_bitwise():
 
 
 WIDE = small_variant(MID, name="wide_bf16", n_streams=6, ctx_spec=[300, 77, 1030, 0, 513, 4100], seed=2003)
+# a mid batch (64 rows) whose LM head has more than one round of 128-column tiles (313:
+# the last 57, the last one part empty, in three K ranges finished by k_lmhead_tail)
+MID_VOCAB = small_variant(MID, name="mid_vocab_bf16", vocab=40000, seed=2012)
 
 
-@pytest.mark.parametrize("preset", [MID, WIDE], ids=["64_rows", "96_rows"])
+def test_round_parity_mid_batch_lm_head_tail():
+    run_case(RoundCase(MID_VOCAB), list(range(MID_VOCAB.n_streams)))
+
+
+@pytest.mark.parametrize("preset", [MID, WIDE, MID_VOCAB], ids=["64_rows", "96_rows", "64_rows_lm_head_tail"])
 def test_tiled_batch_classes_are_invariant_to_stream_order_bitwise(preset):
     # 4 streams x block 16 = 64 rows (tiled GEMMs with one live row group, the mid
     # class's 16-page attention chunks) and 6 x 16 = 96 rows (tiled GEMMs, 64-page
